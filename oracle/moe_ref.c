@@ -1,0 +1,320 @@
+/*
+ * CPU oracle of the int4 routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  The product
+ * (the HIP library and its Python binding) never links, loads or calls it, and
+ * it shares no code, header or table with the product.
+ *
+ * It is deliberately plain: each step is its definition written out, in fp64,
+ * with sequential sums (OpenMP only splits independent output rows across
+ * threads; each row is still summed in order).
+ *
+ * What it computes (the pages describe the path of each token through a MoE
+ * layer as route -> union -> place -> overlap -> learn; colibri 技术解读
+ * (linlog.top), "引擎结构：一个 C 文件，五步 token 路径"; colibrì README
+ * (简体中文), 工作原理 › 每个 token 的处理路径).  Place, overlap and learn only
+ * decide where bytes come from and how fast, never the result, so the layer's
+ * value is:
+ *
+ *   z[t,e] = sum_i x[t,i] * Wr[e,i] + b[e]                        (router)
+ *   S_t    = the k experts of largest z[t,.], ties to the lower id (top-k)
+ *   w[t,j] = softmax(z[t,.])[S_tj] / sum_j' softmax(z[t,.])[S_tj'] (renormalised)
+ *   U      = distinct experts of all S_t, each read once           (batch union)
+ *   y_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x))                        (SwiGLU FFN)
+ *   out[t] = sum_j w[t,j] * y_{S_tj}(x[t])                         (recombine)
+ *
+ * The pages name top-8-of-256 routing and the batch union (colibri 技术解读,
+ * "MoE 的稀疏性" and the five-step path; README 工作原理 › 绝不为同一次磁盘读取
+ * 等待两遍) but not the gate function, the FFN form or the weight layout; the
+ * readings taken here (softmax over all experts, top-k on the logits,
+ * renormalisation, SwiGLU, signed two's-complement int4 with one fp16 scale per
+ * 64 consecutive input weights, element 2i in the low nibble) are listed with
+ * their reasons in the design notes.
+ *
+ * Expert blob (the three matrices stored next to each other so one read fetches
+ * an expert: README 工作原理 › 绝不为同一次磁盘读取等待两遍):
+ *   gate codes [f][d/2] | up codes [f][d/2] | down codes [d][f/2]
+ *   | gate scales [f][d/64] | up scales [f][d/64] | down scales [d][f/64]
+ * codes are bytes holding two 4-bit weights, scales are IEEE binary16.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define REF_GROUP 64
+#define REF_PRENORM 1u
+#define REF_RESIDUAL 2u
+
+/* ---- encodings ------------------------------------------------------------ */
+
+/* Weight number c of a row of 4-bit codes: byte c/2, low nibble when c is
+ * even, high nibble when odd; the nibble is a two's-complement int4. */
+int ref_nibble(const uint8_t* row_codes, int64_t c) {
+  int b = row_codes[c / 2];
+  int n = (c % 2 == 0) ? (b & 0xF) : (b >> 4);
+  return n >= 8 ? n - 16 : n;
+}
+
+/* IEEE 754 binary16 -> double, from the format's definition. */
+double ref_f16(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int ex = (h >> 10) & 0x1F;
+  int man = h & 0x3FF;
+  double v;
+  if (ex == 0)
+    v = ldexp((double)man, -24); /* subnormal: m/1024 * 2^-14 */
+  else if (ex == 31)
+    v = man ? NAN : INFINITY;
+  else
+    v = ldexp(1.0 + man / 1024.0, ex - 15);
+  return sign ? -v : v;
+}
+
+/* bfloat16 -> double: the upper half of an IEEE binary32. */
+double ref_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* ---- expert blob ----------------------------------------------------------- */
+
+int64_t ref_blob_bytes(int d, int f) { return 3LL * f * d / 2 + 2LL * (3LL * f * d / REF_GROUP); }
+
+/* which: 0 gate [f x d], 1 up [f x d], 2 down [d x f]. */
+static void mat_view(const uint8_t* blob, int d, int f, int which, const uint8_t** codes,
+                     const uint16_t** scales, int* rows, int* cols) {
+  int64_t fd = (int64_t)f * d;
+  *codes = blob + which * (fd / 2);
+  *scales = (const uint16_t*)(blob + 3 * (fd / 2)) + which * (fd / REF_GROUP);
+  *rows = which == 2 ? d : f;
+  *cols = which == 2 ? f : d;
+}
+
+/* Row r of a matrix, dequantised: w[c] = q[r,c] * s[r, c/64] (exact in fp64). */
+static void dequant_row(const uint8_t* codes, const uint16_t* scales, int cols, int r, double* w) {
+  const uint8_t* rc = codes + (int64_t)r * (cols / 2);
+  const uint16_t* rs = scales + (int64_t)r * (cols / REF_GROUP);
+  for (int c = 0; c < cols; ++c) w[c] = (double)ref_nibble(rc, c) * ref_f16(rs[c / REF_GROUP]);
+}
+
+/* Dense dequantised matrix (rows x cols doubles), for tests on small shapes. */
+void ref_dequant(const uint8_t* blob, int d, int f, int which, double* W) {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  int rows, cols;
+  mat_view(blob, d, f, which, &codes, &scales, &rows, &cols);
+  for (int r = 0; r < rows; ++r) dequant_row(codes, scales, cols, r, W + (int64_t)r * cols);
+}
+
+double ref_silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* SwiGLU expert FFN on n input rows x[n][d] -> y[n][d], reading the blob once:
+ *   g = Wg x, u = Wu x, a = silu(g) * u, y = Wd a.
+ * The pages only say the chosen experts run their feed-forward computation
+ * (colibri 技术解读, "集群模式与开放问题清单"); SwiGLU is the reading taken. */
+void ref_expert_ffn(int d, int f, const uint8_t* blob, const double* x, int n, double* y) {
+  const uint8_t *gc, *uc, *dc;
+  const uint16_t *gs, *us, *ds;
+  int rows, cols;
+  mat_view(blob, d, f, 0, &gc, &gs, &rows, &cols);
+  mat_view(blob, d, f, 1, &uc, &us, &rows, &cols);
+  mat_view(blob, d, f, 2, &dc, &ds, &rows, &cols);
+  double* a = (double*)malloc(sizeof(double) * (size_t)n * f);
+#pragma omp parallel
+  {
+    double* wg = (double*)malloc(sizeof(double) * d);
+    double* wu = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+    for (int r = 0; r < f; ++r) {
+      dequant_row(gc, gs, d, r, wg);
+      dequant_row(uc, us, d, r, wu);
+      for (int t = 0; t < n; ++t) {
+        const double* xt = x + (int64_t)t * d;
+        double g = 0.0, u = 0.0;
+        for (int c = 0; c < d; ++c) {
+          g += wg[c] * xt[c];
+          u += wu[c] * xt[c];
+        }
+        a[(int64_t)t * f + r] = ref_silu(g) * u;
+      }
+    }
+    free(wg);
+    free(wu);
+    double* wd = (double*)malloc(sizeof(double) * f);
+#pragma omp for schedule(static)
+    for (int c = 0; c < d; ++c) {
+      dequant_row(dc, ds, f, c, wd);
+      for (int t = 0; t < n; ++t) {
+        const double* at = a + (int64_t)t * f;
+        double acc = 0.0;
+        for (int r = 0; r < f; ++r) acc += wd[r] * at[r];
+        y[(int64_t)t * d + c] = acc;
+      }
+    }
+    free(wd);
+  }
+  free(a);
+}
+
+/* ---- router ---------------------------------------------------------------- */
+
+typedef struct {
+  double z;
+  int e;
+} zpair;
+
+/* Order: larger logit first; equal logits -> lower expert id first. */
+static int zpair_cmp(const void* pa, const void* pb) {
+  const zpair* a = (const zpair*)pa;
+  const zpair* b = (const zpair*)pb;
+  if (a->z > b->z) return -1;
+  if (a->z < b->z) return 1;
+  return (a->e > b->e) - (a->e < b->e);
+}
+
+static double x_at(const void* x, int x_is_bf16, int64_t i) {
+  return x_is_bf16 ? ref_bf16(((const uint16_t*)x)[i]) : (double)((const float*)x)[i];
+}
+
+/* Router logits, top-k and renormalised weights for T tokens.
+ * z[t][e] (optional output) is the fp64 logit; idx[t][j] the j-th largest
+ * (slot order); w[t][j] the renormalised softmax weight.  The router picking
+ * 8 of 256 experts per token and layer is on the pages (colibri 技术解读,
+ * "MoE 的稀疏性"); the softmax/top-k/renormalise gate is the reading taken. */
+void ref_route(int d, int E, int k, const void* x, int x_is_bf16, int T, const float* Wr,
+               const float* bias, int32_t* idx, double* w, double* z_out) {
+  double* z = (double*)malloc(sizeof(double) * (size_t)T * E);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i)
+        acc += x_at(x, x_is_bf16, (int64_t)t * d + i) * (double)Wr[(int64_t)e * d + i];
+      z[(int64_t)t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+  zpair* pr = (zpair*)malloc(sizeof(zpair) * E);
+  double* p = (double*)malloc(sizeof(double) * E);
+  for (int t = 0; t < T; ++t) {
+    const double* zt = z + (int64_t)t * E;
+    for (int e = 0; e < E; ++e) {
+      pr[e].z = zt[e];
+      pr[e].e = e;
+    }
+    qsort(pr, E, sizeof(zpair), zpair_cmp);
+    /* softmax over all E experts */
+    double m = pr[0].z, den = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp(zt[e] - m);
+      den += p[e];
+    }
+    for (int e = 0; e < E; ++e) p[e] /= den;
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j) sel += p[pr[j].e];
+    for (int j = 0; j < k; ++j) {
+      idx[(int64_t)t * k + j] = pr[j].e;
+      w[(int64_t)t * k + j] = p[pr[j].e] / sel;
+    }
+  }
+  if (z_out) memcpy(z_out, z, sizeof(double) * (size_t)T * E);
+  free(p);
+  free(pr);
+  free(z);
+}
+
+/* ---- batch union ----------------------------------------------------------- */
+
+/* Distinct experts of a batch, each listed once, ascending id; for each, the
+ * slots (t*k + j) that chose it, ascending t.  Returns U.  (Repeated picks of
+ * one expert in a batch become a single read: README 工作原理 › 绝不为同一次
+ * 磁盘读取等待两遍.)  uniq and offsets need min(E, T*k) and that + 1 entries. */
+int ref_union(int E, int k, int T, const int32_t* idx, int32_t* uniq, int32_t* offsets,
+              int32_t* rows) {
+  char* seen = (char*)calloc(E, 1);
+  for (int64_t i = 0; i < (int64_t)T * k; ++i) seen[idx[i]] = 1;
+  int U = 0, pos = 0;
+  for (int e = 0; e < E; ++e) {
+    if (!seen[e]) continue;
+    uniq[U] = e;
+    offsets[U] = pos;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (idx[(int64_t)t * k + j] == e) rows[pos++] = t * k + j;
+    ++U;
+  }
+  offsets[U] = pos;
+  free(seen);
+  return U;
+}
+
+/* ---- RMSNorm (unit gain) --------------------------------------------------- */
+
+/* xn = h / sqrt(mean(h^2) + eps), mean and root in fp64, rounded to fp32. */
+void ref_rmsnorm(int d, const float* h, double eps, float* xn) {
+  double ss = 0.0;
+  for (int i = 0; i < d; ++i) ss += (double)h[i] * (double)h[i];
+  double r = 1.0 / sqrt(ss / d + eps);
+  for (int i = 0; i < d; ++i) xn[i] = (float)((double)h[i] * r);
+}
+
+/* ---- whole layer ----------------------------------------------------------- */
+
+/* One MoE layer over T tokens.  table[e] points at expert e's blob (any
+ * memory; entries of experts no token selects may be NULL).  flags:
+ *   REF_PRENORM  route and run experts on RMSNorm(x) (x fp32)
+ *   REF_RESIDUAL out = x + MoE(...) (x fp32)
+ * Outputs: out[T][d] (fp64), idx/w [T][k], uniq/offsets/rows as ref_union,
+ * reads[E] += 1 for every time an expert's blob is read.  Returns U, or -1 if
+ * a selected expert has no blob. */
+int ref_layer_forward(int d, int f, int E, int k, const void* x, int x_is_bf16, int T,
+                      const float* Wr, const float* bias, const uint8_t* const* table,
+                      uint32_t flags, double eps, double* out, int32_t* idx, double* w,
+                      int32_t* uniq, int32_t* offsets, int32_t* rows, int32_t* reads) {
+  const void* xin = x;
+  int xin_bf16 = x_is_bf16;
+  float* xn = NULL;
+  if (flags & REF_PRENORM) {
+    xn = (float*)malloc(sizeof(float) * (size_t)T * d);
+    for (int t = 0; t < T; ++t) ref_rmsnorm(d, (const float*)x + (int64_t)t * d, eps, xn + (int64_t)t * d);
+    xin = xn;
+    xin_bf16 = 0;
+  }
+  ref_route(d, E, k, xin, xin_bf16, T, Wr, bias, idx, w, NULL);
+  int U = ref_union(E, k, T, idx, uniq, offsets, rows);
+  for (int u = 0; u < U; ++u)
+    if (!table[uniq[u]]) {
+      free(xn);
+      return -1;
+    }
+
+  double* yslot = (double*)malloc(sizeof(double) * (size_t)T * k * d);
+  for (int u = 0; u < U; ++u) {
+    int e = uniq[u];
+    int n = offsets[u + 1] - offsets[u];
+    double* xs = (double*)malloc(sizeof(double) * (size_t)n * d);
+    double* ys = (double*)malloc(sizeof(double) * (size_t)n * d);
+    for (int i = 0; i < n; ++i) {
+      int t = rows[offsets[u] + i] / k;
+      for (int c = 0; c < d; ++c) xs[(int64_t)i * d + c] = x_at(xin, xin_bf16, (int64_t)t * d + c);
+    }
+    ref_expert_ffn(d, f, table[e], xs, n, ys); /* the one read of expert e */
+    reads[e] += 1;
+    for (int i = 0; i < n; ++i)
+      memcpy(yslot + (int64_t)rows[offsets[u] + i] * d, ys + (int64_t)i * d, sizeof(double) * d);
+    free(xs);
+    free(ys);
+  }
+  for (int t = 0; t < T; ++t)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w[(int64_t)t * k + j] * yslot[((int64_t)t * k + j) * d + c];
+      if (flags & REF_RESIDUAL) acc += (double)((const float*)x)[(int64_t)t * d + c];
+      out[(int64_t)t * d + c] = acc;
+    }
+  free(yslot);
+  free(xn);
+  return U;
+}

@@ -1,0 +1,415 @@
+"""Pins of the CPU oracle against things other than itself: exhaustive
+encodings, closed forms, special cases that reduce to textbook routines, brute
+force on tiny inputs and the invariants the pages state.
+
+Every oracle function is covered by at least one pin that a plausible slip
+(dropped term, wrong sign, swapped index, transposed operand, gate/up swap,
+wrong nibble order, wrong scale group) would fail.
+"""
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import oracle
+import synth
+from synth import configs
+
+# ---------------------------------------------------------------- encodings
+
+
+def test_nibble_decode_exhaustive():
+    # closed form of a two's-complement nibble: ((n ^ 8) - 8)
+    for b in range(256):
+        row = np.array([b], dtype=np.uint8)
+        assert oracle.nibble(row, 0) == ((b & 15) ^ 8) - 8
+        assert oracle.nibble(row, 1) == ((b >> 4) ^ 8) - 8
+
+
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    ours = np.array([oracle.f16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_bf16_decode():
+    for b in [0x0000, 0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0xC2F7]:
+        ref = np.array([b << 16], dtype=np.uint32).view(np.float32)[0]
+        assert oracle.bf16(b) == float(ref)
+
+
+# ------------------------------------------------------------- blob helpers
+
+
+def np_dequant(blob, d, f, which):
+    """Independent dense dequantisation with numpy vector ops."""
+    fd = f * d
+    rows, cols = (d, f) if which == 2 else (f, d)
+    codes = blob[which * fd // 2:(which + 1) * fd // 2].reshape(rows, cols // 2)
+    q = np.empty((rows, cols), dtype=np.int64)
+    q[:, 0::2] = ((codes & 15).astype(np.int64) ^ 8) - 8
+    q[:, 1::2] = ((codes >> 4).astype(np.int64) ^ 8) - 8
+    sb = 3 * fd // 2
+    n = fd // 64
+    s = blob[sb + 2 * which * n: sb + 2 * (which + 1) * n].view(np.float16).astype(np.float64)
+    s = np.repeat(s.reshape(rows, cols // 64), 64, axis=1)
+    return q * s
+
+
+def make_blob(d, f, codes=None, scales=None):
+    """Blob from explicit int4 matrices (gate [f][d], up [f][d], down [d][f])
+    and fp16 scale matrices, packed element 2i -> low nibble."""
+    def pack(q):
+        n = (np.asarray(q, dtype=np.int64) & 15).astype(np.uint8)
+        return (n[:, 0::2] | (n[:, 1::2] << 4)).reshape(-1)
+
+    nib = np.concatenate([pack(c) for c in codes])
+    sc = np.concatenate([np.asarray(s, dtype=np.float16).reshape(-1) for s in scales])
+    return np.concatenate([nib, sc.view(np.uint8)])
+
+
+def np_silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+# -------------------------------------------------------------- dequant/FFN
+
+
+@pytest.mark.parametrize("d,f", [(256, 128), (128, 192), (64, 64)])
+def test_dequant_brute_force(d, f):
+    blob = synth.expert_blob(3, 0, 1, d, f)
+    for which in range(3):
+        assert np.array_equal(oracle.dequant(blob, d, f, which), np_dequant(blob, d, f, which))
+
+
+def test_one_hot_weight_gives_scale_times_input():
+    d, f = 128, 64
+    rng = np.random.default_rng(1)
+    x = rng.normal(size=d)
+    for r, c, q, s in [(0, 0, 1, 0.5), (5, 77, -8, 0.0078125), (63, 127, 7, 0.01953125)]:
+        gate = np.zeros((f, d), int)
+        gate[r, c] = q
+        blob = make_blob(d, f, [gate, np.zeros((f, d)), np.zeros((d, f))],
+                         [np.full((f, d // 64), s), np.ones((f, d // 64)), np.ones((d, f // 64))])
+        W = oracle.dequant(blob, d, f, 0)
+        assert W[r, c] == q * np.float16(s) and np.count_nonzero(W) == 1
+        assert (W @ x)[r] == q * float(np.float16(s)) * x[c]
+
+
+def test_swiglu_closed_form_with_permutations():
+    """gate row r picks x[pg[r]], up row r picks x[pu[r]], down row c picks
+    a[pd[c]]; then y[c] = sd*silu(sg*x[pg[pd[c]]]) * su*x[pu[pd[c]]].  d != f and
+    distinct permutations catch transposed operands, swapped gate/up and
+    wrong indices."""
+    d, f = 128, 64
+    rng = np.random.default_rng(2)
+    pg = rng.permutation(d)[:f]
+    pu = rng.permutation(d)[:f]
+    pd = rng.integers(0, f, size=d)
+    gate = np.zeros((f, d), int)
+    up = np.zeros((f, d), int)
+    down = np.zeros((d, f), int)
+    gate[np.arange(f), pg] = 1
+    up[np.arange(f), pu] = 1
+    down[np.arange(d), pd] = 1
+    sg, su, sd = 0.75, 0.375, 1.5
+    blob = make_blob(d, f, [gate, up, down], [np.full((f, d // 64), sg), np.full((f, d // 64), su),
+                                              np.full((d, f // 64), sd)])
+    x = rng.normal(size=(3, d)) * 2
+    y = oracle.expert_ffn(blob, x, d, f)
+    for t in range(3):
+        g = sg * x[t, pg[pd]]
+        u = su * x[t, pu[pd]]
+        ref = sd * (g / (1 + np.exp(-g))) * u
+        np.testing.assert_allclose(y[t], ref, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("d,f,n", [(256, 128, 3), (128, 64, 1), (192, 128, 2)])
+def test_ffn_brute_force(d, f, n):
+    blob = synth.expert_blob(4, 1, 2, d, f)
+    x = np.random.default_rng(3).normal(size=(n, d))
+    Wg, Wu, Wd = (np_dequant(blob, d, f, i) for i in range(3))
+    ref = (np_silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    y = oracle.expert_ffn(blob, x, d, f)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def _set_scales(blob, d, f, which, value, group=None, row=None):
+    b = blob.copy()
+    fd = f * d
+    sb = 3 * fd // 2
+    n = fd // 64
+    s = b[sb + 2 * which * n: sb + 2 * (which + 1) * n].view(np.float16)
+    cols = f if which == 2 else d
+    s2 = s.reshape(-1, cols // 64)
+    if group is None:
+        s2[...] = value if not callable(value) else value(s2)
+    else:
+        s2[:, group] = value
+    return b
+
+
+def test_zero_scale_group_removes_exactly_its_inputs():
+    d, f = 256, 128
+    blob = synth.expert_blob(5, 0, 0, d, f)
+    x = np.random.default_rng(4).normal(size=(2, d))
+    for g in range(d // 64):
+        b0 = _set_scales(_set_scales(blob, d, f, 0, 0.0, group=g), d, f, 1, 0.0, group=g)
+        x0 = x.copy()
+        x0[:, 64 * g:64 * (g + 1)] = 0.0
+        assert np.array_equal(oracle.expert_ffn(b0, x, d, f), oracle.expert_ffn(blob, x0, d, f))
+
+
+def test_down_scale_doubling_doubles_output_exactly():
+    d, f = 256, 128
+    blob = synth.expert_blob(6, 0, 0, d, f)
+    x = np.random.default_rng(5).normal(size=(2, d))
+    b2 = _set_scales(blob, d, f, 2, lambda s: s * np.float16(2))
+    assert np.array_equal(oracle.expert_ffn(b2, x, d, f), 2 * oracle.expert_ffn(blob, x, d, f))
+
+
+def test_zero_gate_gives_zero_output():
+    d, f = 256, 128
+    b = _set_scales(synth.expert_blob(7, 0, 0, d, f), d, f, 0, 0.0)
+    y = oracle.expert_ffn(b, np.random.default_rng(6).normal(size=(2, d)), d, f)
+    assert np.all(y == 0.0)
+
+
+def test_silu_limits_and_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1e3) == 1e3
+    assert oracle.silu(-1e3) == 0.0 and np.signbit(oracle.silu(-1e3))
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+
+
+# ------------------------------------------------------------------- router
+
+
+def _np_topk(z, k):
+    out = []
+    for row in z:
+        order = np.lexsort((np.arange(row.size), -row))  # -z ascending, then id
+        out.append(order[:k])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(4, 256, 16, 2), (7, 128, 64, 8), (3, 64, 256, 8)])
+def test_route_brute_force(T, d, E, k):
+    rng = np.random.default_rng(T * E)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    Wr = (0.02 * rng.normal(size=(E, d))).astype(np.float32)
+    b = synth.zipf_bias(E)
+    idx, w, z = oracle.route(x, Wr, b, k)
+    zr = x.astype(np.float64) @ Wr.astype(np.float64).T + b.astype(np.float64)
+    np.testing.assert_allclose(z, zr, rtol=0, atol=1e-13)
+    assert np.array_equal(idx, _np_topk(z, k))
+    p = softmax(zr, axis=1)
+    ps = np.take_along_axis(p, idx, 1)
+    np.testing.assert_allclose(w, ps / ps.sum(1, keepdims=True), rtol=1e-13)
+
+
+def test_route_all_ties_go_to_lowest_ids():
+    E, d, k = 16, 64, 4
+    x = np.random.default_rng(0).normal(size=(3, d)).astype(np.float32)
+    idx, w, _ = oracle.route(x, np.zeros((E, d), np.float32), None, k)
+    assert np.array_equal(idx, np.tile(np.arange(k), (3, 1)))
+    assert np.all(w == 1.0 / k)
+
+
+def test_route_partial_tie_breaks_to_lower_id():
+    E, d, k = 8, 64, 3
+    b = np.array([5, 1, 0, 3, 0, 3, 0, 0], np.float32)  # 3 and 5 tie for 2nd
+    x = np.zeros((1, d), np.float32)
+    idx, _, _ = oracle.route(x, np.zeros((E, d), np.float32), b, k)
+    assert list(idx[0]) == [0, 3, 5]
+    b[3] = 0.0  # now 5 is alone in 2nd place and 1 in 3rd
+    idx, _, _ = oracle.route(x, np.zeros((E, d), np.float32), b, k)
+    assert list(idx[0]) == [0, 5, 1]
+
+
+def test_route_k_equals_E_is_plain_softmax():
+    E, d = 32, 128
+    rng = np.random.default_rng(8)
+    x = rng.normal(size=(2, d)).astype(np.float32)
+    Wr = rng.normal(size=(E, d)).astype(np.float32) * np.float32(0.02)
+    idx, w, z = oracle.route(x, Wr, None, E)
+    for t in range(2):
+        np.testing.assert_allclose(w[t], softmax(z[t])[idx[t]], rtol=1e-14)
+        assert np.all(np.diff(z[t, idx[t]]) <= 0)
+        assert sorted(idx[t]) == list(range(E))
+
+
+def test_route_k1_weight_is_one():
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(5, 64)).astype(np.float32)
+    Wr = rng.normal(size=(16, 64)).astype(np.float32)
+    idx, w, z = oracle.route(x, Wr, None, 1)
+    assert np.all(w == 1.0)
+    assert np.array_equal(idx[:, 0], np.argmax(z, 1))
+
+
+def test_renormalised_softmax_equals_softmax_of_selected_logits():
+    rng = np.random.default_rng(10)
+    x = rng.normal(size=(6, 256)).astype(np.float32)
+    Wr = (0.05 * rng.normal(size=(64, 256))).astype(np.float32)
+    idx, w, z = oracle.route(x, Wr, synth.zipf_bias(64), 8)
+    for t in range(6):
+        np.testing.assert_allclose(w[t], softmax(z[t, idx[t]]), rtol=1e-13)
+
+
+def test_route_bf16_input_is_widened_exactly():
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(3, 128)).astype(np.float32)
+    xb = synth.to_bf16_bits(x)
+    xw = configs.bf16_bits_to_f32(xb)
+    Wr = rng.normal(size=(16, 128)).astype(np.float32)
+    i1, w1, z1 = oracle.route(xb, Wr, None, 2, x_bf16=True)
+    i2, w2, z2 = oracle.route(xw, Wr, None, 2)
+    assert np.array_equal(z1, z2) and np.array_equal(i1, i2) and np.array_equal(w1, w2)
+
+
+# -------------------------------------------------------------------- union
+
+
+def _naive_union(idx, k):
+    s = sorted(set(idx.reshape(-1).tolist()))
+    rows = []
+    offs = [0]
+    for e in s:
+        rows += [t * k + j for t in range(idx.shape[0]) for j in range(k) if idx[t, j] == e]
+        offs.append(len(rows))
+    return np.array(s), np.array(offs), np.array(rows)
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(1, 256, 8, 0), (8, 256, 8, 1), (64, 16, 2, 2),
+                                        (512, 256, 8, 3), (5, 8, 8, 4)])
+def test_union_brute_force_and_invariants(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    idx = np.array([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)],
+                   dtype=np.int32)
+    uniq, offs, rows = oracle.union(idx, E)
+    nu, no, nr = _naive_union(idx, k)
+    assert np.array_equal(uniq, nu) and np.array_equal(offs, no) and np.array_equal(rows, nr)
+    assert offs[-1] == T * k and np.all(np.diff(offs) > 0)
+    assert len(uniq) <= min(E, T * k)
+    assert sorted(rows.tolist()) == list(range(T * k))
+    for u in range(len(uniq)):
+        r = rows[offs[u]:offs[u + 1]]
+        assert np.all(idx.reshape(-1)[r] == uniq[u]) and np.all(np.diff(r // k) > 0)
+    if T == 1:
+        assert len(uniq) == k
+
+
+# -------------------------------------------------------------- RMSNorm
+
+
+def test_rmsnorm_closed_forms():
+    h = np.full(64, 3.0, np.float32)
+    assert np.all(oracle.rmsnorm(h, eps=0.0) == 1.0)
+    h = np.array([3.0, -4.0] * 32, np.float32)
+    xn = oracle.rmsnorm(h, eps=0.0)  # rms = 5/sqrt(2)
+    np.testing.assert_allclose(xn, h / (5 / np.sqrt(2)), rtol=1e-7)
+    h = np.random.default_rng(0).normal(size=6144).astype(np.float32) * 7
+    ref = (h.astype(np.float64) / np.sqrt(np.mean(h.astype(np.float64) ** 2) + 1e-6)).astype(np.float32)
+    assert np.array_equal(oracle.rmsnorm(h), ref)
+
+
+# -------------------------------------------------------------- whole layer
+
+
+def _tiny_layer(seed=0, E=16, d=256, f=128):
+    rng = np.random.default_rng(seed)
+    Wr = (0.02 * rng.normal(size=(E, d))).astype(np.float32)
+    blobs = [synth.expert_blob(seed + 100, 0, e, d, f) for e in range(E)]
+    return Wr, blobs
+
+
+def test_layer_single_expert_equals_expert_ffn_exactly():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer()
+    x = np.random.default_rng(1).normal(size=(1, d)).astype(np.float32)
+    r = oracle.layer_forward(x, Wr, None, blobs, d, f, k=1)
+    e = r["idx"][0, 0]
+    assert np.array_equal(r["out"], oracle.expert_ffn(blobs[e], x, d, f))
+
+
+def test_layer_k_equals_E_is_full_softmax_mixture():
+    d, f, E = 128, 64, 8
+    Wr, blobs = _tiny_layer(3, E, d, f)
+    x = np.random.default_rng(2).normal(size=(2, d)).astype(np.float32)
+    r = oracle.layer_forward(x, Wr, None, blobs, d, f, k=E)
+    z = x.astype(np.float64) @ Wr.astype(np.float64).T
+    ys = np.stack([oracle.expert_ffn(blobs[e], x, d, f) for e in range(E)], 1)  # [T][E][d]
+    ref = (softmax(z, axis=1)[:, :, None] * ys).sum(1)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_layer_reads_each_distinct_expert_once():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer(4)
+    x = np.random.default_rng(3).normal(size=(12, d)).astype(np.float32)
+    r = oracle.layer_forward(x, Wr, synth.zipf_bias(16), blobs, d, f, k=2)
+    reads = r["reads"]
+    assert np.all(reads[r["uniq"]] == 1) and reads.sum() == r["U"]
+
+
+def test_layer_output_independent_of_placement():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer(5)
+    x = np.random.default_rng(4).normal(size=(4, d)).astype(np.float32)
+    r1 = oracle.layer_forward(x, Wr, None, blobs, d, f, k=2)
+    moved = [np.concatenate([np.zeros(37, np.uint8), b])[37:] for b in blobs]  # other addresses
+    r2 = oracle.layer_forward(x, Wr, None, moved, d, f, k=2)
+    assert np.array_equal(r1["out"], r2["out"])
+
+
+def test_layer_unselected_experts_may_be_absent():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer(6)
+    x = np.random.default_rng(5).normal(size=(2, d)).astype(np.float32)
+    r1 = oracle.layer_forward(x, Wr, None, blobs, d, f, k=2)
+    sparse = [b if e in set(r1["uniq"].tolist()) else None for e, b in enumerate(blobs)]
+    r2 = oracle.layer_forward(x, Wr, None, sparse, d, f, k=2)
+    assert np.array_equal(r1["out"], r2["out"])
+    with pytest.raises(ValueError):
+        oracle.layer_forward(x, Wr, None, [None] * 16, d, f, k=2)
+
+
+def test_layer_residual_with_zero_down_leaves_h_unchanged():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer(7)
+    blobs = [_set_scales(b, d, f, 2, 0.0) for b in blobs]
+    h = np.random.default_rng(6).normal(size=(1, d)).astype(np.float32) * 3
+    r = oracle.layer_forward(h, Wr, None, blobs, d, f, k=2,
+                             flags=oracle.PRENORM | oracle.RESIDUAL)
+    assert np.array_equal(r["out"].astype(np.float32), h)
+
+
+def test_layer_prenorm_routes_on_normalised_input():
+    d, f = 256, 128
+    Wr, blobs = _tiny_layer(8)
+    h = np.random.default_rng(7).normal(size=(3, d)).astype(np.float32) * 5
+    r = oracle.layer_forward(h, Wr, None, blobs, d, f, k=2, flags=oracle.PRENORM)
+    xn = np.stack([oracle.rmsnorm(row) for row in h])
+    r2 = oracle.layer_forward(xn, Wr, None, blobs, d, f, k=2)
+    assert np.array_equal(r["out"], r2["out"]) and np.array_equal(r["idx"], r2["idx"])
+
+
+def test_tiny_workload_golden():
+    """The tiny workload's outputs against the committed fixture written by
+    tests/golden/make_golden.py (which calls only the oracle): guards the oracle
+    against silent drift once its pins pass."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_layer.json")
+    g = json.load(open(path))
+    w = configs.WORKLOADS["tiny"]
+    Wr, bias = configs.router(w)
+    x, _ = configs.tokens(w)
+    r = oracle.layer_forward(x, Wr, bias, list(configs.experts(w)), w.d, w.f, w.top_k)
+    assert r["idx"].tolist() == g["idx"]
+    assert r["uniq"].tolist() == g["uniq"] and r["rows"].tolist() == g["rows"]
+    np.testing.assert_allclose(r["out"], np.array(g["out"]), rtol=1e-12, atol=1e-12)
