@@ -1,0 +1,186 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) int4 routed-expert MoE layer library.
+ *
+ * One sparse MoE layer forward pass over group-scaled int4 routed experts:
+ * each token's router picks k of E experts; the picks of a batch are merged
+ * into a union of distinct experts so each expert's bytes are read once; each
+ * chosen expert runs a SwiGLU FFN on its int4 weights; the outputs are summed
+ * with the router weights.
+ *
+ * Sources for the method (pages on the colibrì engine):
+ *  - the per-token path through a MoE layer is route -> union -> place ->
+ *    overlap -> learn, with repeated picks of one expert in a batch merged into
+ *    a single read: colibri 技术解读 (linlog.top), "引擎结构：一个 C 文件，五步
+ *    token 路径"; colibrì README (简体中文), 工作原理 › 绝不为同一次磁盘读取等待两遍;
+ *  - 8 of 256 routed experts per token and layer, about 19 MB each at int4:
+ *    colibri 技术解读, "MoE 的稀疏性"; README 核心概念;
+ *  - the three matrices of an expert stored next to each other and fetched in
+ *    one read: README 工作原理 › 绝不为同一次磁盘读取等待两遍;
+ *  - group-scaled int4 ("gs64") as the weight container: README 开始使用 › 获取模型;
+ *  - where an expert's bytes live decides only speed, never the result:
+ *    README 工作原理 › 每个 token 的处理路径.
+ * The pages do not fix the gate function, the FFN form or the bit layout.  The
+ * readings this library implements (and its CPU oracle checks) are:
+ *  - gate: softmax over all E logits, the k largest logits chosen (ties to the
+ *    lower expert id), their softmax weights renormalised to sum to 1; logits
+ *    are accumulated in fp64 so the choice does not depend on summation order;
+ *  - expert: y = Wd (silu(Wg x) * (Wu x)), silu(v) = v / (1 + exp(-v));
+ *  - weights: signed two's-complement int4, element 2i of a row in the low
+ *    nibble of byte i, one IEEE binary16 scale per 64 consecutive weights along
+ *    the input (contiguous) dimension, w = q * s.
+ *
+ * Expert blob (canonical layout, 64-byte aligned sections for d, f % 64 == 0):
+ *   gate codes [f][d/2] | up codes [f][d/2] | down codes [d][f/2]
+ *   | gate scales [f][d/64] | up scales [f][d/64] | down scales [d][f/64]
+ * Size: moe_expert_blob_bytes(); 20,054,016 bytes at d = 6144, f = 2048.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers (or host memory mapped into the device
+ *    address space, e.g. from hipHostMalloc) unless said otherwise.  `dims`
+ *    points at host memory.  The caller owns every buffer; the library
+ *    allocates and frees nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it; nothing is synchronised, nothing is copied to the host.
+ *    Calls enqueue only kernels (no memset/memcpy), so they may be captured in
+ *    a HIP graph.
+ *  - `ws` is a caller-provided device workspace of at least
+ *    moe_workspace_bytes(dims, T) bytes.  It must be zero-filled before its
+ *    first use; every call leaves its internal counters at zero again.  Calls
+ *    that share a workspace must not overlap in time.
+ *  - All arguments are validated before anything is enqueued; on error the
+ *    call returns a negative code and enqueues nothing.  Device-side faults
+ *    surface at the caller's next synchronisation.  There is no CPU fallback.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_dims {
+  int32_t d;          /* hidden size; multiple of 64, 64..65536 */
+  int32_t f;          /* expert FFN width; multiple of 64, 64..65536 */
+  int32_t n_experts;  /* E; 1..1024 */
+  int32_t top_k;      /* k; 1..min(E, 32) */
+  int32_t group_size; /* weights per fp16 scale; must be 64 */
+} moe_dims;
+
+/* Activation dtypes (x_dtype). */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* moe_layer_forward flags. */
+enum {
+  MOE_PRENORM_RMS = 1u, /* route and run experts on RMSNorm(x), unit gain (x must be f32) */
+  MOE_RESIDUAL = 2u     /* out = x + MoE(...) (x must be f32) */
+};
+
+/* Return codes. */
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* null or inconsistent argument, T < 1 */
+  MOE_EUNSUPPORTED = -2, /* group_size != 64, d/f not multiples of 64, k > 32, E > 1024, bad dtype/flags */
+  MOE_ENOSPC = -3,       /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_EHIP = -4          /* a kernel launch failed; moe_strerror() names the HIP error */
+};
+
+/* Bytes of one expert blob (canonical layout above); 0 for invalid dims. */
+size_t moe_expert_blob_bytes(const moe_dims* dims);
+
+/* Workspace bytes any entry point needs for up to T_max tokens (or rows);
+ * 0 for invalid dims or T_max < 1. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t T_max);
+
+/* Static text for a return code (MOE_EHIP: includes the last HIP error seen
+ * by this thread). */
+const char* moe_strerror(int code);
+
+/*
+ * moe_route — router logits, top-k and renormalised weights.
+ *   x          [T][d] activations, f32 or bf16 (x_dtype), row-major
+ *   w_router   [E][d] f32 router matrix, row-major
+ *   bias       [E] f32 added to the logits before selection and softmax, or NULL
+ *   topk_idx   [T][k] int32 out: chosen expert ids, slot j in descending logit
+ *              order, equal logits ordered by ascending id
+ *   topk_w     [T][k] f32 out: softmax(z)[id] / sum over the token's k ids
+ * Logits z[t][e] = sum_i x[t][i] * w_router[e][i] + bias[e] are accumulated
+ * in fp64 (each fp32 product is exact in fp64).
+ * Source: the router picks 8 of 256 routed experts per token and layer —
+ * colibri 技术解读, "MoE 的稀疏性" and "引擎结构：一个 C 文件，五步 token 路径".
+ */
+int moe_route(const moe_dims* dims, const void* x, int x_dtype, int32_t T, const float* w_router,
+              const float* bias, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream);
+
+/*
+ * moe_union — batch union of the routed experts.
+ *   topk_idx   [T][k] int32 expert ids, each in [0, E), distinct within a token
+ *   uniq       [min(E, T*k)] int32 out: the U distinct ids ascending, then -1
+ *   n_uniq     [1] int32 out: U (stays on the device)
+ *   offsets    [min(E, T*k) + 1] int32 out: expert uniq[u] owns
+ *              rows[offsets[u] .. offsets[u+1]); entries after U equal
+ *              offsets[U] (= T*k when every id is valid)
+ *   rows       [T*k] int32 out: slot ids t*k + j grouped by expert in uniq
+ *              order, ascending t within an expert
+ * Each distinct expert appears once, so a consumer that walks uniq reads each
+ * expert's bytes once per batch.
+ * Source: repeated picks of one expert across the positions of a batch are
+ * merged into one read ("batch union") — colibrì README (简体中文), 工作原理 ›
+ * 绝不为同一次磁盘读取等待两遍; colibri 技术解读, "引擎结构：一个 C 文件，五步 token 路径".
+ * Ids outside [0, E) are skipped: they are listed under no expert, offsets
+ * after U then equal the number of valid ids, and the tail of rows beyond
+ * offsets[U] is left unwritten.
+ */
+int moe_union(const moe_dims* dims, const int32_t* topk_idx, int32_t T, int32_t* uniq,
+              int32_t* n_uniq, int32_t* offsets, int32_t* rows, void* stream);
+
+/*
+ * moe_expert_ffn — one expert's SwiGLU FFN on n activation rows.
+ *   expert_blob  the expert's canonical blob (device or host-mapped memory)
+ *   x            [*][d] activations (f32 or bf16)
+ *   rows         [n] int32 indices into x (each a valid row of x), or NULL
+ *                for rows 0..n-1
+ *   y            [n][d] f32 out: y[i] = Wd (silu(Wg x[rows[i]]) * (Wu x[rows[i]]))
+ * The result does not depend on where the blob's bytes live.
+ * Source: the chosen experts run their feed-forward computation — colibri
+ * 技术解读, "集群模式与开放问题清单"; blob of three adjacent matrices — README
+ * 工作原理 › 绝不为同一次磁盘读取等待两遍.
+ */
+int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x, int x_dtype,
+                   const int32_t* rows, int32_t n, float* y, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * moe_layer_forward — the whole layer for T tokens.
+ *   x             [T][d] f32 or bf16 layer input
+ *   w_router      [E][d] f32; bias [E] f32 or NULL
+ *   expert_table  device array of E pointers to expert blobs (each device or
+ *                 host-mapped memory); entries of experts no token picks are
+ *                 never dereferenced
+ *   out           [T][d] f32 out: out[t] = sum_j w[t][j] * y_{idx[t][j]}(x'[t])
+ *                 (+ x[t] with MOE_RESIDUAL), summed in ascending slot j, where
+ *                 x' = RMSNorm(x) with MOE_PRENORM_RMS, else x.  out may alias x.
+ *   flags         MOE_PRENORM_RMS | MOE_RESIDUAL (both need x_dtype MOE_F32)
+ *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
+ *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]
+ *                 = number of tokens that picked expert e
+ * Routing is as moe_route, the union as moe_union; each distinct expert's
+ * bytes are streamed once for the whole batch.  Results are bit-reproducible
+ * run to run (no floating-point atomics).
+ * Source: route -> union -> place -> overlap -> learn per token and layer —
+ * colibri 技术解读, "引擎结构：一个 C 文件，五步 token 路径"; the residual stream kept
+ * on the device across layers — README 工作原理 › 绝不为同一次磁盘读取等待两遍.
+ */
+int moe_layer_forward(const moe_dims* dims, const void* x, int x_dtype, int32_t T,
+                      const float* w_router, const float* bias, const void* const* expert_table,
+                      float* out, uint32_t flags, float rms_eps, int32_t* stats, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,168 @@
+"""Python binding of libmoe.so, the gfx950 int4 routed-expert MoE layer.
+
+Thin ctypes marshalling over the C ABI in include/moe.h: the functions below
+carry the same names as the C entry points, take torch tensors (device memory
+owned by the caller) and pass their pointers, sizes and the current HIP
+stream.  Every step of the layer runs in the library's HIP kernels; there is no
+Python or CPU fallback, and importing this package fails if the library has not
+been built (``python -m int4_routed_expert_softmax_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_PRENORM_RMS, MOE_RESIDUAL = 1, 2
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
+
+# Every function include/moe.h declares.
+EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_route",
+           "moe_union", "moe_expert_ffn", "moe_layer_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("f", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    d: int
+    f: int
+    n_experts: int
+    top_k: int
+    group_size: int = 64
+
+    def c(self) -> moe_dims:
+        return moe_dims(self.d, self.f, self.n_experts, self.top_k, self.group_size)
+
+
+def _hip_runtimes():
+    """Paths of every HIP runtime mapped into this process."""
+    try:
+        with open("/proc/self/maps") as fh:
+            return sorted({l.split()[-1] for l in fh if "libamdhip64" in l})
+    except OSError:
+        return []
+
+
+def _load():
+    # torch ships its own HIP runtime (soname libamdhip64.so.7).  Loading torch
+    # first makes libmoe.so bind to that same runtime, so the library and torch
+    # share one set of streams and allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m int4_routed_expert_softmax_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_uint32
+    dp = ctypes.POINTER(moe_dims)
+    L.moe_expert_blob_bytes.restype = sz
+    L.moe_expert_blob_bytes.argtypes = [dp]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_workspace_bytes.argtypes = [dp, i32]
+    L.moe_strerror.restype = ctypes.c_char_p
+    L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_union.restype = ctypes.c_int
+    L.moe_union.argtypes = [dp, vp, i32, vp, vp, vp, vp, vp]
+    L.moe_expert_ffn.restype = ctypes.c_int
+    L.moe_expert_ffn.argtypes = [dp, vp, vp, ctypes.c_int, vp, i32, vp, vp, sz, vp]
+    L.moe_layer_forward.restype = ctypes.c_int
+    L.moe_layer_forward.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, u32,
+                                    ctypes.c_float, vp, vp, sz, vp]
+    rt = _hip_runtimes()
+    if len(rt) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {rt}")
+    return L
+
+
+lib = _load()
+
+
+def strerror(code: int) -> str:
+    return lib.moe_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != MOE_OK:
+        raise MoeError(code, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _xdtype(x) -> int:
+    import torch
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+
+
+def expert_blob_bytes(dims: Dims) -> int:
+    return lib.moe_expert_blob_bytes(ctypes.byref(dims.c()))
+
+
+def workspace_bytes(dims: Dims, T_max: int) -> int:
+    return lib.moe_workspace_bytes(ctypes.byref(dims.c()), T_max)
+
+
+def make_workspace(dims: Dims, T_max: int, device="cuda"):
+    """A zero-filled workspace (the library keeps its counters at zero)."""
+    import torch
+    return torch.zeros(workspace_bytes(dims, T_max), dtype=torch.uint8, device=device)
+
+
+def moe_route(dims: Dims, x, w_router, bias, topk_idx, topk_w, ws, stream=None):
+    T = x.shape[0]
+    _check(lib.moe_route(ctypes.byref(dims.c()), _ptr(x), _xdtype(x), T, _ptr(w_router),
+                         _ptr(bias), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
+                         _stream(stream)), "moe_route")
+
+
+def moe_union(dims: Dims, topk_idx, uniq, n_uniq, offsets, rows, stream=None):
+    T = topk_idx.shape[0]
+    _check(lib.moe_union(ctypes.byref(dims.c()), _ptr(topk_idx), T, _ptr(uniq), _ptr(n_uniq),
+                         _ptr(offsets), _ptr(rows), _stream(stream)), "moe_union")
+
+
+def moe_expert_ffn(dims: Dims, expert_blob, x, rows, n, y, ws, stream=None):
+    """expert_blob: a uint8 tensor, or an int device/host-mapped address."""
+    blob = expert_blob if isinstance(expert_blob, int) else _ptr(expert_blob)
+    _check(lib.moe_expert_ffn(ctypes.byref(dims.c()), blob, _ptr(x), _xdtype(x), _ptr(rows), n,
+                              _ptr(y), _ptr(ws), ws.numel(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_layer_forward(dims: Dims, x, w_router, bias, expert_table, out, flags=0, rms_eps=1e-6,
+                      stats=None, ws=None, stream=None):
+    """expert_table: int64 device tensor of E blob addresses."""
+    T = x.shape[0]
+    _check(lib.moe_layer_forward(ctypes.byref(dims.c()), _ptr(x), _xdtype(x), T, _ptr(w_router),
+                                 _ptr(bias), _ptr(expert_table), _ptr(out), flags, rms_eps,
+                                 _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_layer_forward")

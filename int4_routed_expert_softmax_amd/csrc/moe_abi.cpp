@@ -1,0 +1,222 @@
+// extern "C" entry points of libmoe.so (declared in include/moe.h): argument
+// validation, workspace carving and the launch sequence of each call.
+// Validation never calls into HIP, so an invalid call touches no device.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout(int d, int f, int E, int k, int T) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t Tk = (size_t)T * k;
+  const size_t cap = (size_t)(E < (long)Tk ? E : Tk);
+  L.tickets = take(256);
+  L.z = take((size_t)T * E * sizeof(double));
+  L.xn = take((size_t)T * d * sizeof(float));
+  L.xq = take((size_t)T * (d / kChunk) * kChunkDigitBytes);
+  L.xsx = take((size_t)T * (d / kChunk) * sizeof(int32_t));
+  L.xsc = take((size_t)T * (d / kGroup) * sizeof(float));
+  L.idx = take(Tk * sizeof(int32_t));
+  L.w = take(Tk * sizeof(float));
+  L.uniq = take(cap * sizeof(int32_t));
+  L.offs = take((cap + 1) * sizeof(int32_t));
+  L.nuniq = take(sizeof(int32_t));
+  L.rows = take(Tk * sizeof(int32_t));
+  L.aq = take(Tk * (f / kChunk) * kChunkDigitBytes);
+  L.asx = take(Tk * (f / kChunk) * sizeof(int32_t));
+  L.asc = take(Tk * (f / kGroup) * sizeof(float));
+  L.y = take(Tk * d * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_hip_msg[192];
+
+int dims_status(const moe_dims* dm) {
+  if (!dm) return MOE_EINVAL;
+  if (dm->d <= 0 || dm->f <= 0 || dm->n_experts <= 0 || dm->top_k <= 0) return MOE_EINVAL;
+  if (dm->top_k > dm->n_experts) return MOE_EINVAL;
+  if (dm->group_size != kGroup) return MOE_EUNSUPPORTED;
+  if (dm->d % kGroup || dm->f % kGroup || dm->d > 65536 || dm->f > 65536) return MOE_EUNSUPPORTED;
+  if (dm->n_experts > 1024 || dm->top_k > 32) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error: %s", hipGetErrorString(e));
+  return MOE_EHIP;
+}
+
+#define MOE_TRY(call)                       \
+  do {                                      \
+    const int _st = hip_status(call);       \
+    if (_st != MOE_OK) return _st;          \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+Digits x_digits(void* ws, const Layout& L) {
+  return Digits{at<int8_t>(ws, L.xq), at<int32_t>(ws, L.xsx), at<float>(ws, L.xsc)};
+}
+
+Digits a_digits(void* ws, const Layout& L) {
+  return Digits{at<int8_t>(ws, L.aq), at<int32_t>(ws, L.asx), at<float>(ws, L.asc)};
+}
+
+}  // namespace
+
+MOE_API size_t moe_expert_blob_bytes(const moe_dims* dm) {
+  if (dims_status(dm) != MOE_OK) return 0;
+  const size_t fd = (size_t)dm->f * dm->d;
+  return 3 * fd / 2 + 2 * (3 * fd / kGroup);
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_dims* dm, int32_t T_max) {
+  if (dims_status(dm) != MOE_OK || T_max < 1) return 0;
+  return layout(dm->d, dm->f, dm->n_experts, dm->top_k, T_max).total;
+}
+
+MOE_API const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null/misaligned pointer, inconsistent dims, T < 1)";
+    case MOE_EUNSUPPORTED:
+      return "unsupported (group_size != 64, d or f not a multiple of 64, k > 32, E > 1024, "
+             "bad dtype or flags)";
+    case MOE_ENOSPC: return "workspace too small (see moe_workspace_bytes)";
+    case MOE_EHIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_route(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
+                      const float* w_router, const float* bias, int32_t* topk_idx, float* topk_w,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (T < 1 || !x || !w_router || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_EINVAL;
+  const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, T);
+  if (ws_bytes < L.total) return MOE_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* z = at<double>(ws, L.z);
+  MOE_TRY(launch_logits(x, x_dtype == MOE_BF16, T, dm->d, dm->n_experts, w_router, bias, z, s));
+  MOE_TRY(launch_topk(z, T, dm->n_experts, dm->top_k, topk_idx, topk_w, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_union(const moe_dims* dm, const int32_t* topk_idx, int32_t T, int32_t* uniq,
+                      int32_t* n_uniq, int32_t* offsets, int32_t* rows, void* stream) {
+  int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (T < 1 || !topk_idx || !uniq || !n_uniq || !offsets || !rows) return MOE_EINVAL;
+  MOE_TRY(launch_union(topk_idx, T, dm->n_experts, dm->top_k, uniq, n_uniq, offsets, rows, nullptr,
+                       static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const void* x, int x_dtype,
+                           const int32_t* rows, int32_t n, float* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (n < 1 || !expert_blob || !x || !y || !ws) return MOE_EINVAL;
+  if (!aligned(expert_blob, 16) || !aligned(x, 4) || !aligned(y, 4)) return MOE_EINVAL;
+  const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, n);
+  if (ws_bytes < L.total) return MOE_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
+  MOE_TRY(launch_digitize(x, x_dtype == MOE_BF16, rows, n, dm->d, xd, s));
+  ExpertList EL{};
+  EL.single = static_cast<const uint8_t*>(expert_blob);
+  EL.single_n = n;
+  EL.kdiv = 1;
+  MOE_TRY(launch_gateup(EL, 1, dm->d, dm->f, xd, ad, s));
+  MOE_TRY(launch_down(EL, 1, dm->d, dm->f, ad, y, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
+                              const float* w_router, const float* bias,
+                              const void* const* expert_table, float* out, uint32_t flags,
+                              float rms_eps, int32_t* stats, void* ws, size_t ws_bytes,
+                              void* stream) {
+  int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL)) return MOE_EUNSUPPORTED;
+  if (flags && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
+  if (T < 1 || !x || !w_router || !expert_table || !out || !ws) return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4)) return MOE_EINVAL;
+  if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
+  const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
+  const Layout L = layout(d, f, E, k, T);
+  if (ws_bytes < L.total) return MOE_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const void* xr = x;  // what the router and the experts see
+  int xr_bf16 = x_dtype == MOE_BF16;
+  if (flags & MOE_PRENORM_RMS) {
+    float* xn = at<float>(ws, L.xn);
+    MOE_TRY(launch_rmsnorm(static_cast<const float*>(x), xn, T, d, rms_eps, s));
+    xr = xn;
+    xr_bf16 = 0;
+  }
+  double* z = at<double>(ws, L.z);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* w = at<float>(ws, L.w);
+  int32_t* uniq = at<int32_t>(ws, L.uniq);
+  int32_t* offs = at<int32_t>(ws, L.offs);
+  int32_t* nuniq = at<int32_t>(ws, L.nuniq);
+  int32_t* rows = at<int32_t>(ws, L.rows);
+  float* y = at<float>(ws, L.y);
+  const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
+
+  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
+  MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
+  MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
+  MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
+  ExpertList EL{};
+  EL.table = reinterpret_cast<const uint8_t* const*>(expert_table);
+  EL.uniq = uniq;
+  EL.n_uniq = nuniq;
+  EL.offsets = offs;
+  EL.list = rows;
+  EL.kdiv = k;
+  const int maxU = E < T * k ? E : T * k;
+  MOE_TRY(launch_gateup(EL, maxU, d, f, xd, ad, s));
+  MOE_TRY(launch_down(EL, maxU, d, f, ad, y, s));
+  MOE_TRY(launch_combine(y, w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out,
+                         T, d, k, s));
+  return MOE_OK;
+}

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, sizes blobs and workspaces, and rejects invalid arguments
+before touching any device (the validation paths make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_routed_expert_softmax_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+GLM = moe.Dims(6144, 2048, 256, 8)
+TINY = moe.Dims(256, 128, 16, 2)
+FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = declared()
+    assert set(names) == set(moe.EXPORTS)
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    ours = {l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("moe_")}
+    assert ours == set(moe.EXPORTS)
+
+
+def test_blob_and_workspace_sizes():
+    assert moe.expert_blob_bytes(GLM) == 20054016
+    assert moe.expert_blob_bytes(TINY) == 52224
+    assert moe.expert_blob_bytes(moe.Dims(6144, 2048, 256, 8, group_size=32)) == 0
+    w1 = moe.workspace_bytes(GLM, 1)
+    w512 = moe.workspace_bytes(GLM, 512)
+    assert 0 < w1 < 4 << 20 and w512 > w1
+    assert moe.workspace_bytes(GLM, 0) == 0
+
+
+def call_route(dims, x=FAKE, dtype=moe.MOE_F32, T=1, wr=FAKE, idx=FAKE, w=FAKE, ws=FAKE,
+               ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(1, moe.workspace_bytes(dims, max(T, 1)))
+    return moe.lib.moe_route(ctypes.byref(dims.c()), x, dtype, T, wr, None, idx, w, ws, ws_bytes,
+                             None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    (moe.Dims(6144, 2048, 256, 8, 32), moe.MOE_EUNSUPPORTED),
+    (moe.Dims(6100, 2048, 256, 8), moe.MOE_EUNSUPPORTED),
+    (moe.Dims(6144, 2000, 256, 8), moe.MOE_EUNSUPPORTED),
+    (moe.Dims(6144, 2048, 2048, 8), moe.MOE_EUNSUPPORTED),
+    (moe.Dims(6144, 2048, 256, 33), moe.MOE_EUNSUPPORTED),
+    (moe.Dims(6144, 2048, 4, 8), moe.MOE_EINVAL),
+    (moe.Dims(0, 2048, 256, 8), moe.MOE_EINVAL),
+])
+def test_route_rejects_bad_dims(dims, code):
+    assert call_route(dims, ws_bytes=1 << 30) == code
+
+
+def test_route_rejects_bad_arguments():
+    assert call_route(GLM, T=0) == moe.MOE_EINVAL
+    assert call_route(GLM, x=None) == moe.MOE_EINVAL
+    assert call_route(GLM, x=FAKE + 4) == moe.MOE_EINVAL  # misaligned
+    assert call_route(GLM, dtype=7) == moe.MOE_EUNSUPPORTED
+    assert call_route(GLM, ws=None) == moe.MOE_EINVAL
+    assert call_route(GLM, ws_bytes=16) == moe.MOE_ENOSPC
+    assert moe.lib.moe_route(None, FAKE, 0, 1, FAKE, None, FAKE, FAKE, FAKE, 1 << 30,
+                             None) == moe.MOE_EINVAL
+
+
+def test_union_rejects_bad_arguments():
+    d = GLM.c()
+    assert moe.lib.moe_union(ctypes.byref(d), None, 1, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert moe.lib.moe_union(ctypes.byref(d), FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EINVAL
+
+
+def test_expert_ffn_rejects_bad_arguments():
+    d = GLM.c()
+    ws = moe.workspace_bytes(GLM, 4)
+    f = moe.lib.moe_expert_ffn
+    assert f(ctypes.byref(d), None, FAKE, 0, None, 4, FAKE, FAKE, ws, None) == moe.MOE_EINVAL
+    assert f(ctypes.byref(d), FAKE + 8, FAKE, 0, None, 4, FAKE, FAKE, ws, None) == moe.MOE_EINVAL
+    assert f(ctypes.byref(d), FAKE, FAKE, 0, None, 0, FAKE, FAKE, ws, None) == moe.MOE_EINVAL
+    assert f(ctypes.byref(d), FAKE, FAKE, 0, None, 4, FAKE, FAKE, ws - 1, None) == moe.MOE_ENOSPC
+    assert f(ctypes.byref(d), FAKE, FAKE, 3, None, 4, FAKE, FAKE, ws, None) == moe.MOE_EUNSUPPORTED
+
+
+def test_layer_forward_rejects_bad_arguments():
+    d = GLM.c()
+    ws = moe.workspace_bytes(GLM, 2)
+    f = moe.lib.moe_layer_forward
+
+    def call(**kw):
+        a = dict(x=FAKE, dt=moe.MOE_F32, T=2, wr=FAKE, table=FAKE, out=FAKE, flags=0, eps=1e-6,
+                 ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(ctypes.byref(d), a["x"], a["dt"], a["T"], a["wr"], None, a["table"], a["out"],
+                 a["flags"], a["eps"], None, a["ws"], a["wsb"], None)
+
+    assert call(table=None) == moe.MOE_EINVAL
+    assert call(out=None) == moe.MOE_EINVAL
+    assert call(T=-1) == moe.MOE_EINVAL
+    assert call(flags=4) == moe.MOE_EUNSUPPORTED
+    assert call(flags=moe.MOE_RESIDUAL, dt=moe.MOE_BF16) == moe.MOE_EUNSUPPORTED
+    assert call(flags=moe.MOE_PRENORM_RMS, eps=-1.0) == moe.MOE_EINVAL
+    assert call(wsb=ws - 256) == moe.MOE_ENOSPC
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, 99):
+        assert isinstance(moe.strerror(c), str) and moe.strerror(c)
+
+
+def test_one_hip_runtime_in_process():
+    assert len(moe._hip_runtimes()) == 1

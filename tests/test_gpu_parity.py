@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: routing indices, union lists and per-expert slot lists (ties to the
+lower expert id).  Floating point: layer and expert outputs within
+max-abs-error <= 2e-3 * max|ref| (the oracle is fp64); router weights within
+1e-6 relative.  Full-size GLM-5.2-shaped layers (d=6144, f=2048, 256 experts,
+top-8) run at batch 1, 8 and 512; the 512-token prefill chunk is compared in
+full for routing and union and on sampled tokens for outputs.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import int4_routed_expert_softmax_amd as moe
+import oracle
+import synth
+from synth import configs
+
+from moe_harness import DEV, DeviceLayer, assert_close, check_union, say
+
+pytestmark = pytest.mark.gpu
+
+W = configs.WORKLOADS
+
+
+def small(name, d, f, E, k, T, zipf=True, seed=7, x_kind="normal"):
+    return configs.Workload(name, d=d, f=f, n_experts=E, top_k=k, T=T, seed=seed, zipf=zipf,
+                            x_kind=x_kind)
+
+
+def full_parity(w: configs.Workload, flags=0, layer=None):
+    say(f"parity: {w.name} d={w.d} f={w.f} E={w.n_experts} k={w.top_k} T={w.T} flags={flags}")
+    L = layer or DeviceLayer(w)
+    x, bf = configs.tokens(w)
+    xd = L.x_device(x, bf)
+    ref = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=bf,
+                               flags=flags)
+    if not flags:
+        idx, wts = L.route(xd)
+        assert np.array_equal(idx, ref["idx"]), "routing indices differ"
+        np.testing.assert_allclose(wts, ref["w"], rtol=1e-6, atol=1e-7)
+        check_union(L, idx)
+    out, stats = L.forward(xd, flags=flags)
+    st = stats.cpu().numpy()
+    assert st[0] == ref["U"]
+    cnt = np.zeros(w.n_experts, np.int64)
+    np.add.at(cnt, ref["idx"].reshape(-1), 1)
+    assert np.array_equal(st[1:], cnt)
+    rel = assert_close(out.cpu().numpy(), ref["out"])
+    say(f"parity: {w.name} U={ref['U']} rel err {rel:.2e}")
+    return L, ref, out
+
+
+def test_tiny_layer():
+    full_parity(W["tiny"])
+
+
+@pytest.mark.parametrize("w", [
+    small("t1", 256, 128, 16, 2, 1),
+    small("ragged", 320, 192, 100, 5, 130),
+    small("k1", 256, 128, 16, 1, 9),
+    small("kE", 128, 64, 16, 16, 3, zipf=False),
+    small("wide", 2112, 704, 64, 8, 70),
+    small("bf16", 256, 128, 32, 4, 33, x_kind="bf16"),
+], ids=lambda w: w.name)
+def test_edge_shapes(w):
+    full_parity(w)
+
+
+def test_prenorm_residual_tiny():
+    w = small("chainlike", 256, 128, 16, 2, 5)
+    full_parity(w, flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL)
+    full_parity(w, flags=moe.MOE_PRENORM_RMS)
+    full_parity(w, flags=moe.MOE_RESIDUAL)
+
+
+def test_all_ties_choose_lowest_ids():
+    w = small("ties", 256, 128, 16, 4, 6, zipf=False)
+    L = DeviceLayer(w, Wr=np.zeros((16, 256), np.float32), bias=None)
+    x, _ = configs.tokens(w)
+    idx, wts = L.route(L.x_device(x, False))
+    assert np.array_equal(idx, np.tile(np.arange(4), (6, 1)))
+    assert np.all(wts == np.float32(0.25))
+
+
+def test_zero_down_with_residual_leaves_h_unchanged():
+    w = small("zerodown", 256, 128, 16, 2, 3)
+    blobs = configs.experts(w).copy()
+    nib, nsc = synth.blob_sizes(w.d, w.f)
+    per = nsc // 3
+    blobs[:, nib + 4 * per: nib + 6 * per] = 0  # down scales = +0.0
+    L = DeviceLayer(w, blobs=blobs)
+    h = configs.tokens(w)[0] * 3
+    hd = L.x_device(h, False)
+    out, _ = L.forward(hd, flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL)
+    assert torch.equal(out.cpu(), torch.from_numpy(h))
+
+
+def test_in_place_residual():
+    w = small("inplace", 256, 128, 16, 2, 4)
+    L = DeviceLayer(w)
+    h = configs.tokens(w)[0]
+    hd = L.x_device(h, False)
+    ref, _ = L.forward(hd.clone(), flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL)
+    L.forward(hd, flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL, out=hd)
+    assert torch.equal(hd, ref)
+
+
+# ---------------------------------------------------------------- GLM-shaped
+
+
+@pytest.fixture(scope="module")
+def decode_layer():
+    return DeviceLayer(W["decode1"])
+
+
+def test_glm_decode_batch1(decode_layer):
+    full_parity(W["decode1"], layer=decode_layer)
+
+
+def test_glm_decode_deterministic_and_placement_invariant(decode_layer):
+    L = decode_layer
+    x, _ = configs.tokens(W["decode1"])
+    xd = L.x_device(x, False)
+    a, _ = L.forward(xd)
+    b, _ = L.forward(xd)
+    assert torch.equal(a, b), "two runs differ"
+    # the same bytes at other device addresses: a reversed copy of the expert array
+    moved = torch.flip(L.blobs_d, dims=[0]).contiguous()
+    E = W["decode1"].n_experts
+    L2 = DeviceLayer.__new__(DeviceLayer)
+    L2.__dict__.update(L.__dict__)
+    L2.table = torch.tensor([moved[E - 1 - e].data_ptr() for e in range(E)], dtype=torch.int64,
+                            device=DEV)
+    c, _ = L2.forward(xd)
+    assert torch.equal(a, c), "output depends on where the expert bytes live"
+
+
+def test_glm_expert_ffn_device_and_host_mapped(decode_layer):
+    w = W["decode1"]
+    L = decode_layer
+    e = 3
+    blob = L.blobs[e]
+    x = configs.tokens(W["verify8"])[0][:5]
+    xd = torch.from_numpy(x).to(DEV)
+    rows = torch.tensor([4, 0, 2], dtype=torch.int32, device=DEV)
+    y = torch.empty(3, w.d, dtype=torch.float32, device=DEV)
+    ws = moe.make_workspace(L.dims, 3, DEV)
+    moe.moe_expert_ffn(L.dims, L.blobs_d[e], xd, rows, 3, y, ws)
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(blob, x[[4, 0, 2]].astype(np.float64), w.d, w.f)
+    rel = assert_close(y.cpu().numpy(), ref, "expert_ffn")
+    say(f"expert_ffn GLM n=3 rel err {rel:.2e}")
+
+    # the same blob in pinned host memory mapped into the device address space
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hptr = ctypes.c_void_p()
+    assert hip.hipHostMalloc(ctypes.byref(hptr), ctypes.c_size_t(blob.size), ctypes.c_uint(2)) == 0
+    try:
+        ctypes.memmove(hptr, blob.ctypes.data, blob.size)
+        dptr = ctypes.c_void_p()
+        assert hip.hipHostGetDevicePointer(ctypes.byref(dptr), hptr, ctypes.c_uint(0)) == 0
+        y2 = torch.empty_like(y)
+        moe.moe_expert_ffn(L.dims, dptr.value, xd, rows, 3, y2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), "host-mapped blob gives a different result"
+    finally:
+        torch.cuda.synchronize()
+        hip.hipHostFree(hptr)
+
+    # bf16 input
+    xb = synth.to_bf16_bits(x)
+    xbd = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    y3 = torch.empty(5, w.d, dtype=torch.float32, device=DEV)
+    moe.moe_expert_ffn(L.dims, L.blobs_d[e], xbd, None, 5, y3, moe.make_workspace(L.dims, 5, DEV))
+    torch.cuda.synchronize()
+    ref3 = oracle.expert_ffn(blob, configs.bf16_bits_to_f32(xb).astype(np.float64), w.d, w.f)
+    assert_close(y3.cpu().numpy(), ref3, "expert_ffn bf16")
+
+
+def test_glm_verify_batch8():
+    L, ref, _ = full_parity(W["verify8"])
+    say(f"verify8: union of {ref['U']} distinct experts for 64 picks")
+
+
+def test_glm_prefill512_routing_union_and_sampled_outputs():
+    w = W["prefill512"]
+    L = DeviceLayer(w)
+    x, bf = configs.tokens(w)
+    xd = L.x_device(x, bf)
+    say("prefill512: routing 512 tokens")
+    idx, wts = L.route(xd)
+    ridx, rw, _ = oracle.route(x, L.Wr, L.bias, w.top_k, x_bf16=True)
+    assert np.array_equal(idx, ridx)
+    np.testing.assert_allclose(wts, rw, rtol=1e-6, atol=1e-7)
+    U = check_union(L, idx)
+    say(f"prefill512: U = {U}")
+    out, stats = L.forward(xd)
+    assert stats[0].item() == U
+    out = out.cpu().numpy()
+    for t in [0, 1, 137, 255, 400, 511]:
+        r = oracle.layer_forward(x[t:t + 1], L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k,
+                                 x_bf16=True)
+        rel = assert_close(out[t:t + 1], r["out"], f"prefill token {t}")
+        say(f"prefill512: token {t} rel err {rel:.2e}")
