@@ -1,0 +1,181 @@
+"""Benchmark of the gfx950 int4 routed-expert MoE layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1]
+                    [--layers R] [--cpu-seconds S | --no-cpu]
+
+A step is one full layer forward (router, top-k, union, expert FFNs, combine)
+over one batch of seeded synthetic tokens.  The default workload is a
+GLM-5.2-shaped MoE layer at decode batch 1 (d=6144, f=2048, 256 experts,
+top-8, gs64 int4, about 20 MB per expert).  Steps rotate over R independently
+seeded layers, all resident in HBM, so that the 160 MB one decode step reads
+are not served from the 256 MB Infinity Cache of the previous step.
+
+Prints one JSON line: whole-layer tokens/s (value), expert-weight GB/s, the
+dominant kernel's roofline (its algorithmic bytes per launch over its average
+duration, measured with HIP events recorded around every launch of the timed
+region) and the CPU oracle's throughput on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "MoE-layer tokens/s + int4 expert-weight HBM GB/s (% peak), d=6144 top-8/256"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode1",
+                   choices=["decode1", "verify8", "prefill512"])
+    p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": f"--gpus {a.gpus}: this benchmark runs on one GPU only; the "
+                          "layer is measured at one GPU's share"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import int4_routed_expert_softmax_amd as moe
+    from synth import configs
+
+    w = configs.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    blob = w.blob_bytes
+    nib_gu = 2 * (w.f * w.d // 2 + 2 * (w.f * w.d // 64))   # gate + up codes and scales
+    nib_dn = w.f * w.d // 2 + 2 * (w.f * w.d // 64)
+
+    print(f"bench: {w.name} T={w.T} layers={a.layers} generating + uploading "
+          f"{a.layers * w.n_experts * blob / 1e9:.1f} GB", file=sys.stderr, flush=True)
+    layers = []
+    for l in range(a.layers):
+        Wr, bias = configs.router(w, l)
+        blobs = torch.from_numpy(configs.experts(w, l)).to(dev)
+        table = torch.tensor([blobs[e].data_ptr() for e in range(w.n_experts)], dtype=torch.int64,
+                             device=dev)
+        x, bf = configs.tokens(w, l)
+        xd = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if bf
+              else torch.from_numpy(x).to(dev))
+        layers.append(dict(Wr=torch.from_numpy(Wr).to(dev),
+                           bias=None if bias is None else torch.from_numpy(bias).to(dev),
+                           blobs=blobs, table=table, x=xd))
+        print(f"bench: layer {l} resident", file=sys.stderr, flush=True)
+    out = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+    stats = torch.zeros(a.layers, 1 + w.n_experts, dtype=torch.int32, device=dev)
+    ws = moe.make_workspace(dims, w.T, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L = layers[i % a.layers]
+        moe.moe_layer_forward(dims, L["x"], L["Wr"], L["bias"], L["table"], out,
+                              stats=stats[i % a.layers], ws=ws, stream=stream.cuda_stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    U = stats[:, 0].cpu().numpy().astype(np.float64)  # distinct experts per layer
+
+    # timed region: every launch of the two FFN kernels records HIP events
+    K = a.steps
+    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(K)]) for k in ("gateup", "down")}
+    arms = {k: moe.moe_timing_arm(k, *ev[k]) for k in ev}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    counts = {k: moe.moe_timing_disarm(arms[k]) for k in arms}
+    assert all(c == K for c in counts.values()), counts
+    dur = {k: np.array([s.elapsed_time(e) for s, e in zip(*ev[k])]) * 1e-3 for k in ev}  # seconds
+
+    sec = (t1 - t0) / K
+    u_steps = np.array([U[i % a.layers] for i in range(K)])
+    tok_s = w.T / sec
+    weight_bytes_step = u_steps.mean() * blob
+    gu_bytes = u_steps * nib_gu
+    dn_bytes = u_steps * nib_dn
+    gu_gbps = float(np.mean(gu_bytes / dur["gateup"]) / 1e9)
+    dn_gbps = float(np.mean(dn_bytes / dur["down"]) / 1e9)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
+        "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
+                               f"top-{w.top_k}, T={w.T} tokens, gs64 int4 experts "
+                               f"({blob} B each), {a.layers} rotating HBM-resident layers",
+                   "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
+                   "layers_rotated": a.layers, "distinct_experts_per_step": float(u_steps.mean())},
+        "expert_weight_GBps": round(weight_bytes_step / sec / 1e9, 1),
+        "expert_weight_frac_hbm_peak": round(weight_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "gateup (gate+up projections, SwiGLU)",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": float(gu_bytes.mean()),
+                     "avg_launch_us": round(float(dur["gateup"].mean() * 1e6), 3)},
+        "roofline_down": {"bound": "hbm", "achieved": round(dn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_launch": float(dn_bytes.mean()),
+                          "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle, as it is, on single-token layer forwards of layer 0 of
+    the same workload, repeated until `seconds` have passed."""
+    import oracle
+    from synth import configs
+
+    Wr, bias = configs.router(w, 0)
+    table = list(configs.experts(w, 0))
+    x, bf = configs.tokens(w, 0)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        t = n % x.shape[0]
+        oracle.layer_forward(x[t:t + 1], Wr, bias, table, w.d, w.f, w.top_k, x_bf16=bf)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} single-token forwards of {w.name} layer 0 (fp64 C oracle, OpenMP over "
+                      f"output rows), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -38,7 +38,8 @@
  *  - Pointers are device pointers (or host memory mapped into the device
  *    address space, e.g. from hipHostMalloc) unless said otherwise.  `dims`
  *    points at host memory.  The caller owns every buffer; the library
- *    allocates and frees nothing and keeps no state between calls.
+ *    allocates and frees nothing and keeps no state between calls (apart
+ *    from the opt-in kernel timing below).
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *    enqueued on it; nothing is synchronised, nothing is copied to the host.
  *    Calls enqueue only kernels (no memset/memcpy), so they may be captured in
@@ -178,6 +179,32 @@ int moe_layer_forward(const moe_dims* dims, const void* x, int x_dtype, int32_t 
                       const float* w_router, const float* bias, const void* const* expert_table,
                       float* out, uint32_t flags, float rms_eps, int32_t* stats, void* ws,
                       size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing — instrumentation, not part of the layer's computation.
+ * Kernels of the library, by name:                                          */
+enum {
+  MOE_KERNEL_RMSNORM = 0,
+  MOE_KERNEL_LOGITS = 1,
+  MOE_KERNEL_TOPK = 2,
+  MOE_KERNEL_UNION = 3,
+  MOE_KERNEL_DIGITIZE = 4,
+  MOE_KERNEL_GATEUP = 5, /* gate/up projections + SwiGLU (the largest byte stream) */
+  MOE_KERNEL_DOWN = 6,   /* down projection */
+  MOE_KERNEL_COMBINE = 7,
+  MOE_KERNEL_COUNT = 8
+};
+/*
+ * moe_timing_arm — the next n launches of `kernel` record start_events[i]
+ * when launch i starts executing and stop_events[i] when it ends (hipEvent_t
+ * handles created by the caller, recorded on the launch's stream through
+ * hipExtLaunchKernelGGL).  The handle arrays are host memory that must stay
+ * valid until the n launches have been enqueued or the kernel is re-armed;
+ * n = 0 disarms.  Returns how many launches the previous arming recorded, or
+ * MOE_EINVAL for a bad kernel id, negative n, or n > 0 with NULL arrays.
+ * Process-wide state: not for concurrent use from several threads.
+ */
+int moe_timing_arm(int kernel, void* const* start_events, void* const* stop_events, int n);
 
 #ifdef __cplusplus
 }

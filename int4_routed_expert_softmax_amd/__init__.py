@@ -22,7 +22,11 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 
 # Every function include/moe.h declares.
 EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_route",
-           "moe_union", "moe_expert_ffn", "moe_layer_forward")
+           "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_timing_arm")
+
+# Kernel ids for moe_timing_arm.
+KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
+           "down": 6, "combine": 7}
 
 
 class MoeError(RuntimeError):
@@ -86,6 +90,8 @@ def _load():
     L.moe_layer_forward.restype = ctypes.c_int
     L.moe_layer_forward.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, u32,
                                     ctypes.c_float, vp, vp, sz, vp]
+    L.moe_timing_arm.restype = ctypes.c_int
+    L.moe_timing_arm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int]
     rt = _hip_runtimes()
     if len(rt) > 1:
         raise ImportError(f"more than one HIP runtime is loaded: {rt}")
@@ -166,3 +172,28 @@ def moe_layer_forward(dims: Dims, x, w_router, bias, expert_table, out, flags=0,
                                  _ptr(bias), _ptr(expert_table), _ptr(out), flags, rms_eps,
                                  _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_timing_arm(kernel: str, start_events, stop_events):
+    """Arm kernel timing: launch i of `kernel` records start_events[i] and
+    stop_events[i] (torch.cuda.Event objects with timing enabled; they are
+    recorded once here so that their HIP handles exist).  Returns a handle
+    that keeps the handle arrays alive; pass it to moe_timing_disarm."""
+    import torch
+    n = len(start_events)
+    assert len(stop_events) == n
+    for ev in (*start_events, *stop_events):
+        if ev.cuda_event == 0:
+            ev.record()
+    torch.cuda.synchronize()
+    arr_t = ctypes.c_void_p * n
+    starts = arr_t(*[ev.cuda_event for ev in start_events])
+    stops = arr_t(*[ev.cuda_event for ev in stop_events])
+    kid = KERNELS[kernel]
+    lib.moe_timing_arm(kid, ctypes.cast(starts, ctypes.c_void_p), ctypes.cast(stops, ctypes.c_void_p), n)
+    return (kid, starts, stops)
+
+
+def moe_timing_disarm(handle) -> int:
+    """Disarm; returns how many launches were recorded."""
+    return lib.moe_timing_arm(handle[0], None, None, 0)

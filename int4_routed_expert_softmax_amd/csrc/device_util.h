@@ -12,23 +12,60 @@ namespace moe {
 
 // DPP lane exchange within rows of 16 lanes.
 template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
 }
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp_i<kCtrl>(__float_as_int(v)));
+}
+
+// DPP controls that, applied in this order, form a butterfly over a row of 16
+// lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+// After the first two every quad is uniform, so the mirrors pair whole quads
+// and then whole half-rows.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 // Sum over the 64 lanes, the same value in every lane, in a fixed order:
 // butterflies inside each row of 16 lanes (DPP quad permutes and mirrors),
 // then the four row sums read out in row order.
 __device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp<0x141>(v);  // row_half_mirror
-  v += dpp<0x140>(v);  // row_mirror
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (a + b) + (c + d);
+}
+
+// Transposed reduction of 8 per-lane values over the wave: on return, lanes
+// 8i .. 8i+7 hold the sum over all 64 lanes of v[i].  Each exchange step halves
+// the values a lane carries (a lane keeps the half selected by one lane-index
+// bit and receives its partner's copy of that half), then the last three
+// steps are DPP butterflies inside groups of 8 lanes.  Fixed order, so
+// bit-reproducible.  All 64 lanes must be active.
+__device__ __forceinline__ float reduce8(const float (&v)[8], int lane) {
+  const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+  float a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = h5 ? v[i + 4] : v[i], send = h5 ? v[i] : v[i + 4];
+    a[i] = keep + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = h4 ? a[i + 2] : a[i], send = h4 ? a[i] : a[i + 2];
+    b[i] = keep + __shfl_xor(send, 16, 64);
+  }
+  float c = (h3 ? b[1] : b[0]) + __shfl_xor(h3 ? b[0] : b[1], 8, 64);
+  c += dpp<kDppXor1>(c);
+  c += dpp<kDppXor2>(c);
+  c += dpp<kDppHalfMirror>(c);
+  return c;
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
@@ -60,14 +97,40 @@ __device__ __forceinline__ int digit_pos(int cc) {
   return (2 * blk + odd) * 4 + byte;
 }
 
-// One wave turns the 64 values of group g of a row (lane l holds column
-// 64g + l) into digit form.  With m the group's largest magnitude and E the
-// exponent with m < 2^E <= 2m, X = rint(v * 2^(20-E)) so |X| <= 2^20 and the
-// absolute error is at most 2^(E-21) <= m * 2^-20; X = D2*2^14 + D1*2^7 + D0
-// with D0, D1 in [-64, 63] and D2 in [-64, 64].
-__device__ __forceinline__ void digitize_group(float v, int lane, int g, int8_t* q_row,
-                                               int32_t* sx_row, float* sc_row) {
-  const float m = wave_max(fabsf(v));
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<kCtrl>(__float_as_int(v)));
+}
+
+// Max and integer sum over each row of 16 lanes (every lane of the row gets
+// the result).  All 64 lanes must be active.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ int row16_sum(int v) {
+  v += dpp_i<kDppXor1>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
+  return v;
+}
+
+// Digit split of one 16-wide group per row of 16 lanes: lane l holds column
+// `col` of a row of activations, and the 16 lanes of its DPP row hold the 16
+// columns of one group (col & ~15 the same for all of them).  With m the
+// group's largest magnitude and E the exponent with m < 2^E <= 2m,
+// X = rint(v * 2^(20-E)), so |X| <= 2^20 and the absolute error is at most
+// 2^(E-21) <= m * 2^-20; X = D2*2^14 + D1*2^7 + D0 with D0, D1 in [-64, 63]
+// and D2 in [-64, 64].  `valid` = false rows still take part in the DPP
+// exchange but store nothing.
+__device__ __forceinline__ void digitize16(float v, int col, bool valid, int8_t* q_row,
+                                           int32_t* sx_row, float* sc_row) {
+  const float m = row16_max(fabsf(v));
   int E = 0;
   if (m > 0.0f) (void)frexpf(m, &E);
   const int X = m > 0.0f ? (int)rintf(ldexpf(v, kFixBits - E)) : 0;
@@ -75,18 +138,20 @@ __device__ __forceinline__ void digitize_group(float v, int lane, int g, int8_t*
   const int X1 = (X - D0) / 128;
   const int D1 = ((X1 + 64) & 127) - 64;
   const int D2 = (X1 - D1) / 128;
-  const int c = 2 * g + (lane >> 5);
-  int8_t* plane = q_row + (size_t)c * kChunkDigitBytes;
-  const int pos = digit_pos(lane & 31);
+  const int sx = row16_sum(X);
+  if (!valid) return;
+  int8_t* plane = q_row + (size_t)(col >> 5) * kChunkDigitBytes;
+  const int pos = digit_pos(col & 31);
   plane[pos] = (int8_t)D0;
   plane[kChunk + pos] = (int8_t)D1;
   plane[2 * kChunk + pos] = (int8_t)D2;
-  const int sx = half_sum(X);
-  if ((lane & 31) == 0) sx_row[c] = sx;
-  if (lane == 0) sc_row[g] = ldexpf(1.0f, E - kFixBits);
+  if ((col & 15) == 0) {
+    sx_row[col >> 4] = sx;
+    sc_row[col >> 4] = ldexpf(1.0f, E - kFixBits);
+  }
 }
 
-// Digits of one chunk held in registers: planes[p][w] is word w of plane p.
+// Digits of one chunk held in registers: w[p][i] is word i of plane p.
 struct ChunkDigits {
   int w[kPlanes][8];
 };
@@ -103,11 +168,13 @@ __device__ __forceinline__ ChunkDigits load_chunk_digits(const int8_t* plane_bas
   return cd;
 }
 
-// Exact sum over a chunk of n'_c * X_c, where n'_c = q_c + 8 is the offset
-// binary form of the int4 weight (flip bit 3 of every nibble) and X_c the
-// activation's fixed-point value; products and sums are exact in int32
-// (|result| < 2^30).  The caller subtracts 8 * sum(X) to get sum q_c X_c.
-__device__ __forceinline__ int chunk_dot(const uint4 codes, const ChunkDigits& cd) {
+// Exact sums over the two 16-column halves of a chunk of n'_c * X_c, where
+// n'_c = q_c + 8 is the offset-binary form of the int4 weight (bit 3 of every
+// nibble flipped) and X_c the activation's fixed-point value.  Products and
+// sums are exact in int32 (|result| < 2^30).  The caller subtracts 8 * sum(X)
+// per half to get sum q_c X_c.  Code words 0-1 hold columns 0-15, words 2-3
+// columns 16-31; digit words 0-3 and 4-7 of each plane match them.
+__device__ __forceinline__ int2 chunk_dot2(const uint4 codes, const ChunkDigits& cd) {
   const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
   int lo[4], hi[4];
 #pragma unroll
@@ -116,25 +183,20 @@ __device__ __forceinline__ int chunk_dot(const uint4 codes, const ChunkDigits& c
     lo[i] = (int)(v & 0x0F0F0F0Fu);
     hi[i] = (int)((v >> 4) & 0x0F0F0F0Fu);
   }
-  int acc = 0;
+  int acc[2] = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = __builtin_amdgcn_sdot4(lo[i], cd.w[2][2 * i], acc, false);
-    acc = __builtin_amdgcn_sdot4(hi[i], cd.w[2][2 * i + 1], acc, false);
-  }
-  acc *= 128;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = __builtin_amdgcn_sdot4(lo[i], cd.w[1][2 * i], acc, false);
-    acc = __builtin_amdgcn_sdot4(hi[i], cd.w[1][2 * i + 1], acc, false);
-  }
-  acc *= 128;
+    for (int p = kPlanes - 1; p >= 0; --p) {
+      if (p != kPlanes - 1) acc[h] *= 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = __builtin_amdgcn_sdot4(lo[i], cd.w[0][2 * i], acc, false);
-    acc = __builtin_amdgcn_sdot4(hi[i], cd.w[0][2 * i + 1], acc, false);
+      for (int i = 2 * h; i < 2 * h + 2; ++i) {
+        acc[h] = __builtin_amdgcn_sdot4(lo[i], cd.w[p][2 * i], acc[h], false);
+        acc[h] = __builtin_amdgcn_sdot4(hi[i], cd.w[p][2 * i + 1], acc[h], false);
+      }
+    }
   }
-  return acc;
+  return make_int2(acc[0], acc[1]);
 }
 
 __device__ __forceinline__ float f16_to_f32(const _Float16* p) { return (float)*p; }

@@ -6,25 +6,33 @@
 // The expert is y = Wd (silu(Wg x) * (Wu x)) on signed int4 weights with one
 // fp16 scale per 64 inputs.
 //
-// HBM-bound design: every lane streams its rows' 4-bit codes with coalesced
-// 16-byte loads (64 lanes cover 1 KB of a row per instruction), applies the
-// fp16 group scale in registers and the wave reduces each row across lanes.
-// The int4 x activation products are exact integer dot products
-// (v_dot4_i32_i8 on the activation's three int8 digit planes), so one weight
-// costs about 1.3 VALU operations — well inside the ~2.6 per weight that the
-// chip's vector rate allows at full HBM bandwidth.
+// HBM-bound design.  The lanes of a wave read 64 consecutive 16-byte chunks of
+// a weight row (1 KB, one coalesced instruction), so a lane only needs the
+// activation digits of its one 32-column chunk in registers and a wave keeps
+// many rows' loads in flight.  The fp16 group scale is applied in registers,
+// each row is reduced across the wave with DPP and across column slices
+// through LDS in a fixed order.  The int4 x activation products are exact
+// integer dot products (v_dot4_i32_i8 on the activation's three int8 digit
+// planes), about 1.7 VALU operations per weight including the reductions,
+// inside the ~2.6 per weight the chip's vector rate allows at full HBM
+// bandwidth.
+//
+// No kernel waits on another workgroup of the same launch: on this chip a
+// device-scope release/acquire writes back and invalidates the L2 of the
+// XCD, which costs far more than a kernel boundary.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "select.h"
 
 namespace moe {
 
-constexpr int kRowsPerWave = 16;
-constexpr int kWaves = 4;
-constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // = kGroup: one group of a per block
+constexpr int kStreams = 4;                          // row streams per block
+constexpr int kRowsPerStream = 16;
+constexpr int kRowsPerBlock = kStreams * kRowsPerStream;  // 64 rows of one expert per block
 
 struct ExpertRef {
   const uint8_t* blob;
@@ -45,192 +53,294 @@ __device__ __forceinline__ ExpertRef expert_ref(const ExpertList& L, int u) {
   return r;
 }
 
-__device__ __forceinline__ int slot_of(const ExpertList& L, const ExpertRef& x, int i) {
-  return L.single ? i : L.list[x.beg + i];
+// Digit form of chunk c of activation row `row` (zeros when inactive).
+struct ChunkAct {
+  ChunkDigits dig;
+  int2 sx8;  // 8 * (sum of X) per half chunk
+  float2 sc;
+};
+
+__device__ __forceinline__ ChunkAct load_act(const Digits& D, int row, int nch, int c, bool act) {
+  ChunkAct a;
+  if (act) {
+    a.dig = load_chunk_digits(D.q + ((size_t)row * nch + c) * kChunkDigitBytes);
+    const int2 sx = *reinterpret_cast<const int2*>(D.sx + (size_t)row * 2 * nch + 2 * c);
+    a.sx8 = make_int2(8 * sx.x, 8 * sx.y);
+    a.sc = *reinterpret_cast<const float2*>(D.sc + (size_t)row * 2 * nch + 2 * c);
+  } else {
+    a.dig = ChunkDigits{};
+    a.sx8 = make_int2(0, 0);
+    a.sc = make_float2(0.0f, 0.0f);
+  }
+  return a;
+}
+
+// sum over a chunk of q * x: exact integer half-chunk sums, each scaled by its
+// activation group's unit, times the weight row's group scale s.
+__device__ __forceinline__ float chunk_term(uint4 codes, float s, const ChunkAct& a) {
+  const int2 p = chunk_dot2(codes, a.dig);
+  return s * ((float)(p.x - a.sx8.x) * a.sc.x + (float)(p.y - a.sx8.y) * a.sc.y);
+}
+
+// Weight bytes are read once per batch and never again soon: non-temporal
+// loads keep them from displacing the activations and small tables in cache.
+// The pointers are cast to the global address space so the loads are
+// global_load (not flat_load).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4u* gv4u_ptr;
+typedef __attribute__((address_space(1))) const unsigned short* gu16_ptr;
+__device__ __forceinline__ uint4 stream_load16(const uint8_t* p) {
+  const v4u v = __builtin_nontemporal_load((gv4u_ptr)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float stream_scale(const _Float16* p) {
+  const unsigned short b = __builtin_nontemporal_load((gu16_ptr)(p));
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Rows are processed in batches whose loads are all issued before any is
+// used, so each lane keeps 2 * kBatch (gate/up) or kBatch (down) 16-byte
+// loads in flight.  Lanes whose chunk lies past the end of the row read chunk
+// 0 of the row instead (always in bounds) and add zero (their activation
+// digits and units are zero).
+constexpr int kGUBatch = 4;
+constexpr int kDnBatch = 4;
+
+// Routing of a small batch, recomputed by every gate/up block.
+struct SmallRoute {
+  int32_t idx[kSmallPicks];
+  float w[kSmallPicks];
+  int32_t uniq[kSmallPicks];
+  int32_t offsets[kSmallPicks + 1];
+  int32_t rows[kSmallPicks];
+  int32_t sorted[kSmallPicks];
+  int32_t n;
+};
+
+// Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
+// of g and u, reduced over the wave, is left in s_g / s_u[j][row][slice].
+template <int C, int NT>
+__device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t* ucode,
+                                            const _Float16* gsc, const _Float16* usc, int d,
+                                            int r0, int rl0, int slice, int lane,
+                                            const Digits& xd, const int (&xrow)[NT], int nt,
+                                            float (*s_g)[kRowsPerBlock][C],
+                                            float (*s_u)[kRowsPerBlock][C]) {
+  const int nch = d / kChunk, ngx = d / kGroup;
+  constexpr int kB = kGUBatch, kNB = kRowsPerStream / kGUBatch;
+  for (int p = 0; p * 64 * C < nch; ++p) {
+    const int c = (p * C + slice) * 64 + lane;
+    const bool act = c < nch;
+    const int cl = act ? c : 0;
+    // software pipeline: the loads of batch i+1 are in flight while batch i
+    // is computed
+    uint4 wg[2][kB], wu[2][kB];
+    float sg[2][kB], su[2][kB];
+    auto issue = [&](int buf, int rb0) {
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const size_t r = (size_t)r0 + rb0 + b;
+        wg[buf][b] = stream_load16(gcode + r * (d / 2) + (unsigned)cl * 16u);
+        wu[buf][b] = stream_load16(ucode + r * (d / 2) + (unsigned)cl * 16u);
+        sg[buf][b] = stream_scale(gsc + r * ngx + (unsigned)cl / 2u);
+        su[buf][b] = stream_scale(usc + r * ngx + (unsigned)cl / 2u);
+      }
+    };
+    issue(0, 0);
+    ChunkAct xa[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) xa[j] = load_act(xd, xrow[j], nch, c, act && j < nt);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < kNB) issue(cur ^ 1, (i + 1) * kB);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float v[8];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          v[b] = chunk_term(wg[cur][b], sg[cur][b], xa[j]);
+          v[kB + b] = chunk_term(wu[cur][b], su[cur][b], xa[j]);
+        }
+        const float tot = reduce8(v, lane);  // lanes 8m..8m+7: value m
+        if ((lane & 7) == 0) {
+          const int m = lane >> 3;
+          const int row = rl0 + i * kB + (m & (kB - 1));
+          float* dst = m < kB ? &s_g[j][row][slice] : &s_u[j][row][slice];
+          *dst = p == 0 ? tot : *dst + tot;
+        }
+      }
+    }
+  }
 }
 
 // Gate/up: block (rb, u) computes rows [64 rb, 64 rb + 64) of gate and up of
-// union expert u for all its tokens, forms a = silu(g) * u and stores that
-// 64-wide group of a in digit form, ready for the down projection.
-// CPL = 16-byte code chunks per lane per pass (d = 6144 -> 192 chunks -> 3,
-// one pass); NT = tokens whose digits a lane holds in registers at a time.
-template <int CPL, int NT>
-__global__ __launch_bounds__(256) void k_gateup(ExpertList L, int d, int f, Digits xd, Digits ad) {
-  const int u = blockIdx.y;
-  if (!L.single && u >= *L.n_uniq) return;
-  const ExpertRef ex = expert_ref(L, u);
-  const int rb = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = d / kChunk, ngx = d / kGroup;
+// union expert u for all its tokens, forms a = silu(g) * u and stores those
+// four 16-wide groups of a in digit form for the down projection.  The block
+// has 4 row streams x C column slices of 64 chunks (d = 6144: 192 chunks,
+// C = 3, 12 waves).  SMALL: the block first recomputes top-k and the union
+// from the logits in ro.z; block (0, 0) publishes them.
+template <int C, bool SMALL, int NT>
+__global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, int d, int f,
+                                                    Digits xd, Digits ad) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay scalar
+  const int stream = wave / C, slice = wave % C;
+  const int u = blockIdx.y, rb = blockIdx.x;
+  __shared__ float s_g[NT][kRowsPerBlock][C], s_u[NT][kRowsPerBlock][C];
+  ExpertRef ex;
+  const int32_t* list;
+  int kdiv;
+  if constexpr (SMALL) {
+    __shared__ SmallRoute sr;
+    const int T = ro.T, E = ro.E, k = ro.k;
+    const int n = T * k;
+    for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
+    __syncthreads();
+    if (wave == 0) wave_union_small(sr.idx, n, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
+    __syncthreads();
+    if (rb == 0 && u == 0) {
+      const int cap = min(E, n);
+      for (int i = threadIdx.x; i < n; i += 256 * C) {
+        ro.idx[i] = sr.idx[i];
+        ro.w[i] = sr.w[i];
+        ro.rows[i] = sr.rows[i];
+      }
+      for (int i = threadIdx.x; i <= cap; i += 256 * C) {
+        ro.offsets[i] = sr.offsets[i];
+        if (i < cap) ro.uniq[i] = sr.uniq[i];
+      }
+      if (threadIdx.x == 0) *ro.n_uniq = sr.n;
+      if (ro.stats) {
+        if (threadIdx.x == 0) ro.stats[0] = sr.n;
+        for (int e = threadIdx.x; e < E; e += 256 * C) ro.stats[1 + e] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < sr.n; i += 256 * C)
+          ro.stats[1 + sr.uniq[i]] = sr.offsets[i + 1] - sr.offsets[i];
+      }
+    }
+    if (u >= sr.n) return;
+    ex.blob = L.table[sr.uniq[u]];
+    ex.beg = sr.offsets[u];
+    ex.n = sr.offsets[u + 1] - ex.beg;
+    list = sr.rows;
+    kdiv = k;
+  } else {
+    if (!L.single && u >= *L.n_uniq) return;
+    ex = expert_ref(L, u);
+    list = L.single ? nullptr : L.list;
+    kdiv = L.kdiv;
+  }
   const size_t fd = (size_t)f * d;
   const uint8_t* gcode = ex.blob;
   const uint8_t* ucode = ex.blob + fd / 2;
   const _Float16* gsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2);
   const _Float16* usc = gsc + fd / kGroup;
-  const int r0 = rb * kRowsPerBlock + wave * kRowsPerWave;
-  __shared__ float s_g[NT][kRowsPerBlock], s_u[NT][kRowsPerBlock];
+  const int rl0 = stream * kRowsPerStream;
+  const int r0 = rb * kRowsPerBlock + rl0;
+  auto slot_at = [&](int i) { return list ? list[ex.beg + i] : i; };
 
   for (int t0 = 0; t0 < ex.n; t0 += NT) {
     const int nt = min(NT, ex.n - t0);
     int xrow[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) xrow[j] = j < nt ? slot_of(L, ex, t0 + j) / L.kdiv : 0;
-    for (int c0 = 0; c0 < nch; c0 += 64 * CPL) {
-      ChunkDigits xdig[CPL][NT];
-      int xs[CPL][NT];
-      float xc[CPL][NT];
-      bool act[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = c0 + lane + 64 * i;
-        act[i] = c < nch;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          if (act[i] && j < nt) {
-            xdig[i][j] = load_chunk_digits(xd.q + ((size_t)xrow[j] * nch + c) * kChunkDigitBytes);
-            xs[i][j] = xd.sx[(size_t)xrow[j] * nch + c];
-            xc[i][j] = xd.sc[(size_t)xrow[j] * ngx + c / 2];
-          } else {
-            xdig[i][j] = ChunkDigits{};
-            xs[i][j] = 0;
-            xc[i][j] = 0.0f;
-          }
-        }
-      }
-#pragma unroll 2
-      for (int rr = 0; rr < kRowsPerWave; ++rr) {
-        const size_t r = (size_t)(r0 + rr);
-        uint4 wg[CPL], wu[CPL];
-        float sg[CPL], su[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          const int c = c0 + lane + 64 * i;
-          if (act[i]) {
-            wg[i] = *reinterpret_cast<const uint4*>(gcode + r * (d / 2) + (size_t)c * 16);
-            wu[i] = *reinterpret_cast<const uint4*>(ucode + r * (d / 2) + (size_t)c * 16);
-            sg[i] = f16_to_f32(gsc + r * ngx + c / 2);
-            su[i] = f16_to_f32(usc + r * ngx + c / 2);
-          }
-        }
-        float ag[NT], au[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) ag[j] = au[j] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          if (!act[i]) continue;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const int pg = chunk_dot(wg[i], xdig[i][j]) - 8 * xs[i][j];
-            const int pu = chunk_dot(wu[i], xdig[i][j]) - 8 * xs[i][j];
-            ag[j] += (float)pg * (sg[i] * xc[i][j]);
-            au[j] += (float)pu * (su[i] * xc[i][j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const float g = wave_sum(ag[j]);
-          const float uu = wave_sum(au[j]);
-          if (lane == 0) {
-            const int row = wave * kRowsPerWave + rr;
-            s_g[j][row] = c0 == 0 ? g : s_g[j][row] + g;
-            s_u[j][row] = c0 == 0 ? uu : s_u[j][row] + uu;
-          }
-        }
-      }
-    }
+    for (int j = 0; j < NT; ++j) xrow[j] = j < nt ? slot_at(t0 + j) / kdiv : 0;
+    gateup_rows<C, NT>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u);
     __syncthreads();
-    for (int j = wave; j < nt; j += kWaves) {
-      const int slot = slot_of(L, ex, t0 + j);
-      const int nca = f / kChunk, nga = f / kGroup;
-      const float a = silu(s_g[j][lane]) * s_u[j][lane];
-      digitize_group(a, lane, rb, ad.q + (size_t)slot * nca * kChunkDigitBytes,
-                     ad.sx + (size_t)slot * nca, ad.sc + (size_t)slot * nga);
+    if (wave < nt) {
+      // wave j: token j, the block's 64 rows (four 16-wide groups of a)
+      const int j = wave;
+      float g = 0.0f, uu = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < C; ++sl) {
+        g += s_g[j][lane][sl];
+        uu += s_u[j][lane][sl];
+      }
+      const int slot = slot_at(t0 + j);
+      const int nca = f / kChunk, nga = f / kXGroup;
+      digitize16(silu(g) * uu, rb * kRowsPerBlock + lane, true,
+                 ad.q + (size_t)slot * nca * kChunkDigitBytes, ad.sx + (size_t)slot * nga,
+                 ad.sc + (size_t)slot * nga);
     }
     __syncthreads();
   }
 }
 
+// Rows [r0, r0 + 16) of the down projection for NT tokens into s_y[j][row].
+template <int NT>
+__device__ __forceinline__ void down_rows(const uint8_t* dcode, const _Float16* dsc, int f, int r0,
+                                          int rl0, int lane, const Digits& ad,
+                                          const int (&slot)[NT], int nt,
+                                          float (*s_y)[kRowsPerBlock]) {
+  const int nch = f / kChunk, nga = f / kGroup;
+  constexpr int kB = kDnBatch, kNB = kRowsPerStream / kDnBatch;
+  for (int p = 0; p * 64 < nch; ++p) {
+    const int c = p * 64 + lane;
+    const bool act = c < nch;
+    const int cl = act ? c : 0;
+    uint4 wd[2][kB];
+    float sd[2][kB];
+    auto issue = [&](int buf, int rb0) {
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const size_t r = (size_t)r0 + rb0 + b;
+        wd[buf][b] = stream_load16(dcode + r * (f / 2) + (unsigned)cl * 16u);
+        sd[buf][b] = stream_scale(dsc + r * nga + (unsigned)cl / 2u);
+      }
+    };
+    issue(0, 0);
+    ChunkAct aa[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < kNB) issue(cur ^ 1, (i + 1) * kB);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        float v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) v[b] = b < kB ? chunk_term(wd[cur][b], sd[cur][b], aa[j]) : 0.0f;
+        const float tot = reduce8(v, lane);
+        if ((lane & 7) == 0 && (lane >> 3) < kB) {
+          const int row = rl0 + i * kB + (lane >> 3);
+          s_y[j][row] = p == 0 ? tot : s_y[j][row] + tot;
+        }
+      }
+    }
+  }
+}
+
 // Down: block (rb, u) computes rows [64 rb, 64 rb + 64) of y = Wd a for every
-// token of union expert u; y is indexed by slot.
-template <int CPL, int NT>
+// token of union expert u (4 waves x 16 rows); y is indexed by slot.
+template <int NT>
 __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits ad,
                                               float* __restrict__ y) {
   const int u = blockIdx.y;
   if (!L.single && u >= *L.n_uniq) return;
   const ExpertRef ex = expert_ref(L, u);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay scalar
   const int rb = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = f / kChunk, nga = f / kGroup;
   const size_t fd = (size_t)f * d;
   const uint8_t* dcode = ex.blob + fd;
   const _Float16* dsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup);
-  const int r0 = rb * kRowsPerBlock + wave * kRowsPerWave;
+  const int rl0 = wave * kRowsPerStream;
+  const int r0 = rb * kRowsPerBlock + rl0;
   __shared__ float s_y[NT][kRowsPerBlock];
+  auto slot_at = [&](int i) { return L.single ? i : L.list[ex.beg + i]; };
 
   for (int t0 = 0; t0 < ex.n; t0 += NT) {
     const int nt = min(NT, ex.n - t0);
     int slot[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) slot[j] = j < nt ? slot_of(L, ex, t0 + j) : 0;
-    for (int c0 = 0; c0 < nch; c0 += 64 * CPL) {
-      ChunkDigits adig[CPL][NT];
-      int as[CPL][NT];
-      float ac[CPL][NT];
-      bool act[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = c0 + lane + 64 * i;
-        act[i] = c < nch;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          if (act[i] && j < nt) {
-            adig[i][j] = load_chunk_digits(ad.q + ((size_t)slot[j] * nch + c) * kChunkDigitBytes);
-            as[i][j] = ad.sx[(size_t)slot[j] * nch + c];
-            ac[i][j] = ad.sc[(size_t)slot[j] * nga + c / 2];
-          } else {
-            adig[i][j] = ChunkDigits{};
-            as[i][j] = 0;
-            ac[i][j] = 0.0f;
-          }
-        }
-      }
-#pragma unroll 8
-      for (int rr = 0; rr < kRowsPerWave; ++rr) {
-        const size_t r = (size_t)(r0 + rr);
-        uint4 wd[CPL];
-        float sd[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          const int c = c0 + lane + 64 * i;
-          if (act[i]) {
-            wd[i] = *reinterpret_cast<const uint4*>(dcode + r * (f / 2) + (size_t)c * 16);
-            sd[i] = f16_to_f32(dsc + r * nga + c / 2);
-          }
-        }
-        float acc[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          if (!act[i]) continue;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const int p = chunk_dot(wd[i], adig[i][j]) - 8 * as[i][j];
-            acc[j] += (float)p * (sd[i] * ac[i][j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const float sum = wave_sum(acc[j]);
-          if (lane == 0) {
-            const int row = wave * kRowsPerWave + rr;
-            s_y[j][row] = c0 == 0 ? sum : s_y[j][row] + sum;
-          }
-        }
-      }
-    }
+    for (int j = 0; j < NT; ++j) slot[j] = j < nt ? slot_at(t0 + j) : 0;
+    down_rows<NT>(dcode, dsc, f, r0, rl0, lane, ad, slot, nt, s_y);
     __syncthreads();
-    for (int j = wave; j < nt; j += kWaves) y[(size_t)slot[j] * d + rb * kRowsPerBlock + lane] = s_y[j][lane];
+    for (int i = threadIdx.x; i < nt * kRowsPerBlock; i += 256) {
+      const int j = i / kRowsPerBlock, row = i % kRowsPerBlock;
+      y[(size_t)slot_at(t0 + j) * d + (size_t)rb * kRowsPerBlock + row] = s_y[j][row];
+    }
     __syncthreads();
   }
 }
@@ -248,24 +358,46 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   out[(size_t)t * d + c] = acc;
 }
 
-hipError_t launch_gateup(const ExpertList& L, int max_experts, int d, int f, Digits xd, Digits ad,
-                         hipStream_t s) {
-  const dim3 grid(f / kRowsPerBlock, max_experts);
-  hipLaunchKernelGGL((k_gateup<3, 1>), grid, dim3(256), 0, s, L, d, f, xd, ad);
-  return hipGetLastError();
+// Column slices: ceil(chunks per row / 64), at most 4 (wider rows take passes).
+static int slices(int K) {
+  const int c = (K / kChunk + 63) / 64;
+  return c < 1 ? 1 : (c > 4 ? 4 : c);
+}
+
+template <bool SMALL, int NT>
+static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, int d, int f,
+                           Digits xd, Digits ad, hipStream_t s) {
+  const dim3 grid(f / kRowsPerBlock, maxU);
+  switch (slices(d)) {
+    case 1: return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
+    case 2: return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
+    case 3: return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
+    default: return launch(5, k_gateup<4, SMALL, NT>, grid, dim3(1024), s, L, ro, d, f, xd, ad);
+  }
+}
+
+// tokens_per_expert_max: an upper bound on any expert's token count (1 selects
+// the single-token kernels).
+hipError_t launch_gateup(const ExpertList& L, const RouteOut* ro, int max_experts, int d, int f,
+                         Digits xd, Digits ad, int tokens_per_expert_max, hipStream_t s) {
+  if (tokens_per_expert_max <= 1) {
+    if (ro) return gateup_c<true, 1>(L, *ro, max_experts, d, f, xd, ad, s);
+    return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, s);
+  }
+  if (ro) return gateup_c<true, 2>(L, *ro, max_experts, d, f, xd, ad, s);
+  return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, s);
 }
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
-                       hipStream_t s) {
+                       int tokens_per_expert_max, hipStream_t s) {
   const dim3 grid(d / kRowsPerBlock, max_experts);
-  hipLaunchKernelGGL((k_down<1, 1>), grid, dim3(256), 0, s, L, d, f, ad, y);
-  return hipGetLastError();
+  if (tokens_per_expert_max <= 1) return launch(6, k_down<1>, grid, dim3(256), s, L, d, f, ad, y);
+  return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((d + 255) / 256, T), dim3(256), 0, s, y, w, resid, out, d, k);
-  return hipGetLastError();
+  return launch(7, k_combine, dim3((d + 255) / 256, T), dim3(256), s, y, w, resid, out, d, k);
 }
 
 }  // namespace moe

@@ -1,7 +1,7 @@
 // extern "C" entry points of libmoe.so (declared in include/moe.h): argument
 // validation, workspace carving and the launch sequence of each call.
 // Validation never calls into HIP, so an invalid call touches no device.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -16,6 +16,9 @@ namespace moe {
 
 static size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Reserved counters at the start of the workspace (unused: kept zero).
+constexpr int kTicketWords = 64;
+
 Layout layout(int d, int f, int E, int k, int T) {
   Layout L{};
   size_t o = 0;
@@ -26,12 +29,12 @@ Layout layout(int d, int f, int E, int k, int T) {
   };
   const size_t Tk = (size_t)T * k;
   const size_t cap = (size_t)(E < (long)Tk ? E : Tk);
-  L.tickets = take(256);
+  L.tickets = take(kTicketWords * sizeof(uint32_t));
   L.z = take((size_t)T * E * sizeof(double));
   L.xn = take((size_t)T * d * sizeof(float));
   L.xq = take((size_t)T * (d / kChunk) * kChunkDigitBytes);
-  L.xsx = take((size_t)T * (d / kChunk) * sizeof(int32_t));
-  L.xsc = take((size_t)T * (d / kGroup) * sizeof(float));
+  L.xsx = take((size_t)T * (d / kXGroup) * sizeof(int32_t));
+  L.xsc = take((size_t)T * (d / kXGroup) * sizeof(float));
   L.idx = take(Tk * sizeof(int32_t));
   L.w = take(Tk * sizeof(float));
   L.uniq = take(cap * sizeof(int32_t));
@@ -39,12 +42,14 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.nuniq = take(sizeof(int32_t));
   L.rows = take(Tk * sizeof(int32_t));
   L.aq = take(Tk * (f / kChunk) * kChunkDigitBytes);
-  L.asx = take(Tk * (f / kChunk) * sizeof(int32_t));
-  L.asc = take(Tk * (f / kGroup) * sizeof(float));
+  L.asx = take(Tk * (f / kXGroup) * sizeof(int32_t));
+  L.asc = take(Tk * (f / kXGroup) * sizeof(float));
   L.y = take(Tk * d * sizeof(float));
   L.total = o;
   return L;
 }
+
+TimingSlot g_timing[8];
 
 }  // namespace moe
 
@@ -129,7 +134,21 @@ MOE_API int moe_route(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
   if (ws_bytes < L.total) return MOE_ENOSPC;
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* z = at<double>(ws, L.z);
-  MOE_TRY(launch_logits(x, x_dtype == MOE_BF16, T, dm->d, dm->n_experts, w_router, bias, z, s));
+  if (T <= kSmallBatch) {
+    RouterArgs ra{};
+    ra.x = x;
+    ra.x_bf16 = x_dtype == MOE_BF16;
+    ra.T = T;
+    ra.d = dm->d;
+    ra.E = dm->n_experts;
+    ra.k = dm->top_k;
+    ra.Wr = w_router;
+    ra.bias = bias;
+    ra.z = z;
+    MOE_TRY(launch_router_front(ra, s));
+  } else {
+    MOE_TRY(launch_logits(x, x_dtype == MOE_BF16, T, dm->d, dm->n_experts, w_router, bias, z, s));
+  }
   MOE_TRY(launch_topk(z, T, dm->n_experts, dm->top_k, topk_idx, topk_w, s));
   return MOE_OK;
 }
@@ -161,8 +180,8 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   EL.single = static_cast<const uint8_t*>(expert_blob);
   EL.single_n = n;
   EL.kdiv = 1;
-  MOE_TRY(launch_gateup(EL, 1, dm->d, dm->f, xd, ad, s));
-  MOE_TRY(launch_down(EL, 1, dm->d, dm->f, ad, y, s));
+  MOE_TRY(launch_gateup(EL, nullptr, 1, dm->d, dm->f, xd, ad, n, s));
+  MOE_TRY(launch_down(EL, 1, dm->d, dm->f, ad, y, n, s));
   return MOE_OK;
 }
 
@@ -184,14 +203,6 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   if (ws_bytes < L.total) return MOE_ENOSPC;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const void* xr = x;  // what the router and the experts see
-  int xr_bf16 = x_dtype == MOE_BF16;
-  if (flags & MOE_PRENORM_RMS) {
-    float* xn = at<float>(ws, L.xn);
-    MOE_TRY(launch_rmsnorm(static_cast<const float*>(x), xn, T, d, rms_eps, s));
-    xr = xn;
-    xr_bf16 = 0;
-  }
   double* z = at<double>(ws, L.z);
   int32_t* idx = at<int32_t>(ws, L.idx);
   float* w = at<float>(ws, L.w);
@@ -201,11 +212,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   int32_t* rows = at<int32_t>(ws, L.rows);
   float* y = at<float>(ws, L.y);
   const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
-
-  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
-  MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
-  MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
-  MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
+  const float* resid = (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr;
   ExpertList EL{};
   EL.table = reinterpret_cast<const uint8_t* const*>(expert_table);
   EL.uniq = uniq;
@@ -214,9 +221,57 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.list = rows;
   EL.kdiv = k;
   const int maxU = E < T * k ? E : T * k;
-  MOE_TRY(launch_gateup(EL, maxU, d, f, xd, ad, s));
-  MOE_TRY(launch_down(EL, maxU, d, f, ad, y, s));
-  MOE_TRY(launch_combine(y, w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out,
-                         T, d, k, s));
+
+  if (T <= kSmallBatch && T * k <= kSmallPicks) {
+    // 1: [RMSNorm], logits, digit split; 2: top-k + union (recomputed per
+    // block) and gate/up; 3: down; 4: combine
+    RouterArgs ra{};
+    ra.x = x;
+    ra.x_bf16 = x_dtype == MOE_BF16;
+    ra.T = T;
+    ra.d = d;
+    ra.E = E;
+    ra.k = k;
+    ra.prenorm = (flags & MOE_PRENORM_RMS) != 0;
+    ra.eps = rms_eps;
+    ra.Wr = w_router;
+    ra.bias = bias;
+    ra.z = z;
+    ra.xd = xd;
+    MOE_TRY(launch_router_front(ra, s));
+    RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats};
+    MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, T, s));
+    MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
+    MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
+    return MOE_OK;
+  }
+
+  const void* xr = x;  // what the router and the experts see
+  int xr_bf16 = x_dtype == MOE_BF16;
+  if (flags & MOE_PRENORM_RMS) {
+    float* xn = at<float>(ws, L.xn);
+    MOE_TRY(launch_rmsnorm(static_cast<const float*>(x), xn, T, d, rms_eps, s));
+    xr = xn;
+    xr_bf16 = 0;
+  }
+  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
+  MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
+  MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
+  MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
+  MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, s));
+  MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
+  MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
   return MOE_OK;
+}
+
+MOE_API int moe_timing_arm(int kernel, void* const* start_events, void* const* stop_events, int n) {
+  if (kernel < 0 || kernel >= MOE_KERNEL_COUNT || n < 0) return MOE_EINVAL;
+  if (n > 0 && (!start_events || !stop_events)) return MOE_EINVAL;
+  TimingSlot& t = g_timing[kernel];
+  const int recorded = t.next;
+  t.start = reinterpret_cast<hipEvent_t const*>(start_events);
+  t.stop = reinterpret_cast<hipEvent_t const*>(stop_events);
+  t.n = n;
+  t.next = 0;
+  return recorded;
 }

@@ -2,6 +2,7 @@
 // argument blocks and launchers.  Not part of the public ABI (include/moe.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -13,11 +14,13 @@ namespace moe {
 constexpr int kGroup = 64;
 // Columns covered by one 16-byte load of 4-bit codes.
 constexpr int kChunk = 32;
-// Activations enter the int4 dot products as 21-bit fixed point per 64-wide
+// Activations enter the int4 dot products as 21-bit fixed point per 16-wide
 // group, split into three signed int8 digit planes of base 2^7.  A 32-column
-// chunk therefore carries 3 x 32 digit bytes.
+// chunk (one 16-byte load of codes) therefore carries 3 x 32 digit bytes and
+// two groups.
 constexpr int kPlanes = 3;
 constexpr int kChunkDigitBytes = kPlanes * kChunk;
+constexpr int kXGroup = 16;
 // Exponent offset of the fixed point: a group whose largest magnitude is below
 // 2^E is stored as X = rint(v * 2^(kFixBits - E)), |X| <= 2^kFixBits.
 constexpr int kFixBits = 20;
@@ -27,8 +30,8 @@ constexpr int kFixBits = 20;
 //      bytes of each plane in code order (per 8 columns: the 4 even columns,
 //      then the 4 odd columns), matching how a 32-bit word of nibbles splits
 //      into its low and high nibbles
-//   sx [rows][K/32] int32: sum of X over the chunk
-//   sc [rows][K/64] f32:   value of one unit of X in the group, 2^(E - 20)
+//   sx [rows][K/16] int32: sum of X over the group
+//   sc [rows][K/16] f32:   value of one unit of X in the group, 2^(E - 20)
 struct Digits {
   int8_t* q;
   int32_t* sx;
@@ -55,6 +58,55 @@ struct ExpertList {
   int kdiv;
 };
 
+// Opt-in kernel timing (moe_timing_arm): launches of an armed kernel record
+// caller-provided start/stop events around their execution.
+struct TimingSlot {
+  hipEvent_t const* start = nullptr;
+  hipEvent_t const* stop = nullptr;
+  int n = 0, next = 0;
+};
+extern TimingSlot g_timing[8];
+
+template <typename K, typename... Args>
+hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  TimingSlot& t = g_timing[kernel_id];
+  if (t.next < t.n) {
+    const int i = t.next++;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start[i], t.stop[i], 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+  return hipGetLastError();
+}
+
+// Arguments of the small-batch router front end (optional RMSNorm, logits and
+// digit split in one launch; xd.q == nullptr skips the digit split).
+struct RouterArgs {
+  const void* x;
+  int x_bf16, T, d, E, k, prenorm;
+  float eps;
+  const float* Wr;
+  const float* bias;
+  double* z;
+  Digits xd;
+};
+constexpr int kSmallBatch = 8;
+// The small-batch path recomputes routing inside the gate/up kernel with one
+// wave for the union, so it needs T * k <= 64 picks.
+constexpr int kSmallPicks = 64;
+
+// Routing results of a small batch: the gate/up kernel recomputes top-k and
+// the union from the logits at the start of every block (cheaper than a
+// separate launch) and block (0, 0) publishes them here.
+struct RouteOut {
+  const double* z;
+  int T, E, k;
+  int32_t* idx;
+  float* w;
+  int32_t *uniq, *n_uniq, *offsets, *rows, *stats;
+};
+
+hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
 hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const float* Wr,
                          const float* bias, double* z, hipStream_t s);
@@ -64,10 +116,11 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
                         int32_t* offsets, int32_t* rows, int32_t* stats, hipStream_t s);
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
                            Digits out, hipStream_t s);
-hipError_t launch_gateup(const ExpertList& L, int max_experts, int d, int f, Digits xd, Digits ad,
-                         hipStream_t s);
+hipError_t launch_gateup(const ExpertList& L, const RouteOut* small_route, int max_experts, int d,
+                         int f, Digits xd, Digits ad, int tokens_per_expert_max, hipStream_t s);
+
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
-                       hipStream_t s);
+                       int tokens_per_expert_max, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 

@@ -1,0 +1,299 @@
+// Device code shared by the routing kernels and the gate/up kernel (which
+// recomputes top-k and the union for small batches): wave-level top-k with
+// renormalised softmax weights, and the batch union of a block.
+//
+// The router picks 8 of 256 routed experts per token and layer, and the picks
+// of a batch are merged so each distinct expert is read once (colibri 技术解读
+// (linlog.top), "MoE 的稀疏性" and "引擎结构：一个 C 文件，五步 token 路径";
+// colibrì README (简体中文), 工作原理 › 绝不为同一次磁盘读取等待两遍).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cstdint>
+
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- top-k
+// Selection order: larger logit first, equal logits -> lower expert id.
+// e == INT_MAX marks "no candidate", ranked after everything.
+__device__ __forceinline__ bool ranks_before(double bz, int be, double az, int ae) {
+  if (be == INT_MAX) return false;
+  if (ae == INT_MAX) return true;
+  return bz > az || (bz == az && be < ae);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void argmax_step(double& z, int& e) {
+  const long long b = __double_as_longlong(z);
+  const int hi = dpp_i<kCtrl>((int)(b >> 32));
+  const int lo = dpp_i<kCtrl>((int)b);
+  const int oe = dpp_i<kCtrl>(e);
+  const double oz = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+  if (ranks_before(oz, oe, z, e)) {
+    z = oz;
+    e = oe;
+  }
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Wave-wide best (z, e) under ranks_before, the same in every lane: a DPP
+// butterfly inside each row of 16 lanes, then the four row winners in order.
+__device__ __forceinline__ void wave_argmax(double& z, int& e) {
+  argmax_step<kDppXor1>(z, e);
+  argmax_step<kDppXor2>(z, e);
+  argmax_step<kDppHalfMirror>(z, e);
+  argmax_step<kDppMirror>(z, e);
+  double bz = readlane_f64(z, 0);
+  int be = __builtin_amdgcn_readlane(e, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const double cz = readlane_f64(z, 16 * r);
+    const int ce = __builtin_amdgcn_readlane(e, 16 * r);
+    if (ranks_before(cz, ce, bz, be)) {
+      bz = cz;
+      be = ce;
+    }
+  }
+  z = bz;
+  e = be;
+}
+
+constexpr int kMaxPerLane = 16;  // E <= 1024
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 1024;
+
+// One wave picks the top k of the E logits zt[] of one token (slot order =
+// selection order) and their renormalised softmax weights: softmax over all E
+// restricted to the chosen ids and renormalised equals
+// exp(z_j - z_0) / sum_j' exp(z_j' - z_0) over the chosen logits, z_0 the
+// largest (fp64).  Lane l holds the logits of experts l, l+64, ... (MPER of
+// them, E <= 64 * MPER); each of the k rounds takes every lane's best
+// remaining logit and a DPP arg-max across the wave.  Every lane must be
+// active.
+template <int MPER>
+__device__ __forceinline__ void wave_topk_n(const double* zt, int E, int k, int32_t* idx_out,
+                                            float* w_out) {
+  const int lane = threadIdx.x & 63;
+  double v[MPER];
+#pragma unroll
+  for (int m = 0; m < MPER; ++m) {
+    const int e = lane + 64 * m;
+    v[m] = e < E ? zt[e] : 0.0;
+  }
+  uint32_t taken = 0;
+  double my_z = 0.0;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    double bz = 0.0;
+    int be = INT_MAX;
+#pragma unroll
+    for (int m = 0; m < MPER; ++m) {
+      const int e = lane + 64 * m;
+      if (e < E && !((taken >> m) & 1u) && (be == INT_MAX || v[m] > bz)) {
+        bz = v[m];
+        be = e;
+      }
+    }
+    wave_argmax(bz, be);
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) {
+      my_z = bz;
+      my_e = be;
+    }
+  }
+  const double z0 = readlane_f64(my_z, 0);
+  const double p = lane < k ? exp(my_z - z0) : 0.0;
+  const double den = wave_sum(p);
+  if (lane < k) {
+    idx_out[lane] = my_e;
+    w_out[lane] = (float)(p / den);
+  }
+}
+
+__device__ __forceinline__ void wave_topk(const double* zt, int E, int k, int32_t* idx_out,
+                                          float* w_out) {
+  if (E <= 64) wave_topk_n<1>(zt, E, k, idx_out, w_out);
+  else if (E <= 128) wave_topk_n<2>(zt, E, k, idx_out, w_out);
+  else if (E <= 256) wave_topk_n<4>(zt, E, k, idx_out, w_out);
+  else if (E <= 512) wave_topk_n<8>(zt, E, k, idx_out, w_out);
+  else wave_topk_n<16>(zt, E, k, idx_out, w_out);
+}
+
+// Batch union of n <= 64 picks by one wave.  Lane l holds pick l (slot l,
+// expert idx[l]); its key id * 64 + l orders picks by expert, then slot
+// (= token order).  A pick's rank among all keys is its position in rows; the
+// first pick of each expert opens a union entry.  uniq/offsets as
+// union_body; cnt_out[u] = picks of uniq[u].  s_sorted: n ints of scratch LDS.
+__device__ __forceinline__ void wave_union_small(const int32_t* idx, int n, int E, int32_t* uniq,
+                                                 int32_t* n_uniq, int32_t* offsets, int32_t* rows,
+                                                 int32_t* s_sorted) {
+  const int lane = threadIdx.x & 63;
+  const bool valid = lane < n;
+  const int id = valid ? idx[lane] : 0;
+  const int key = valid ? id * 64 + lane : INT_MAX;
+  int rank = 0;
+  for (int s = 0; s < 64; ++s) rank += __builtin_amdgcn_readlane(key, s) < key;
+  if (valid) {
+    rows[rank] = lane;
+    s_sorted[rank] = id;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // lane r now looks at sorted position r
+  const int sid = valid ? s_sorted[lane] : 0;
+  const int prev = (valid && lane > 0) ? s_sorted[lane - 1] : -1;
+  const bool first = valid && sid != prev;
+  const uint64_t fm = __ballot(first);
+  const int U = __popcll(fm);
+  if (first) {
+    const int u = __popcll(fm & ((1ull << lane) - 1ull));
+    uniq[u] = sid;
+    offsets[u] = lane;
+  }
+  const int cap = min(E, n);
+  if (lane >= U && lane <= cap) {
+    offsets[lane] = n;
+    if (lane < cap) uniq[lane] = -1;
+  }
+  if (lane == 0) *n_uniq = U;
+}
+
+// ---------------------------------------------------------------- union
+// cnt[e] by LDS histogram, offsets by an exclusive scan, uniq by a scan over
+// the non-empty flags.  Slots are placed in ascending token order without
+// relying on the order of atomics: tokens are taken 64 at a time, each expert
+// gets a 64-bit mask of the tokens of the block that picked it, and a slot's
+// rank inside the block is the popcount of the mask bits below its token.
+struct UnionLds {
+  int cnt[kMaxE], off[kMaxE], cur[kMaxE];
+  uint32_t mlo[kMaxE], mhi[kMaxE];
+  int wave_a[16], wave_b[16];
+};
+
+// Exclusive block scan of two ints at once over NTH threads.
+template <int NTH>
+__device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb,
+                                            UnionLds& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int na = __shfl_up(ia, o, 64), nb = __shfl_up(ib, o, 64);
+    if (lane >= o) {
+      ia += na;
+      ib += nb;
+    }
+  }
+  if (lane == 63) {
+    sm.wave_a[wave] = ia;
+    sm.wave_b[wave] = ib;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < NTH / 64; ++i) {
+    const int wa = sm.wave_a[i], wb = sm.wave_b[i];
+    if (i < wave) {
+      ba += wa;
+      bb += wb;
+    }
+    sa += wa;
+    sb += wb;
+  }
+  __syncthreads();
+  ea = ba + ia - a;
+  eb = bb + ib - b;
+  ta = sa;
+  tb = sb;
+}
+
+template <int NTH>
+__device__ void union_body(const int32_t* idx, int T, int E, int k, int32_t* uniq,
+                           int32_t* n_uniq, int32_t* offsets, int32_t* rows, int32_t* stats,
+                           UnionLds& sm) {
+  const int tid = threadIdx.x;
+  const int n = T * k;
+  const int cap = min(E, n);
+  for (int e = tid; e < kMaxE; e += NTH) {
+    sm.cnt[e] = 0;
+    sm.cur[e] = 0;
+    sm.mlo[e] = 0;
+    sm.mhi[e] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NTH) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&sm.cnt[e], 1);  // ids outside [0, E) are ignored
+  }
+  __syncthreads();
+  // each thread owns a contiguous run of experts
+  const int ept = (E + NTH - 1) / NTH;
+  const int e0 = min(E, tid * ept), e1 = min(E, e0 + ept);
+  int csum = 0, nz = 0;
+  for (int e = e0; e < e1; ++e) {
+    csum += sm.cnt[e];
+    nz += sm.cnt[e] > 0;
+  }
+  int off, pos, tot_slots, U;
+  block_scan2<NTH>(csum, nz, off, pos, tot_slots, U, sm);
+  for (int e = e0; e < e1; ++e) {
+    const int c = sm.cnt[e];
+    sm.off[e] = off;
+    if (c > 0) {
+      uniq[pos] = e;
+      offsets[pos] = off;
+      ++pos;
+    }
+    if (stats) stats[1 + e] = c;
+    off += c;
+  }
+  for (int u = U + tid; u <= cap; u += NTH) {
+    offsets[u] = tot_slots;
+    if (u < cap) uniq[u] = -1;
+  }
+  if (tid == 0) {
+    *n_uniq = U;
+    if (stats) stats[0] = U;
+  }
+  __syncthreads();
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int ne = min(64, T - t0) * k;
+    for (int i = tid; i < ne; i += NTH) {
+      const int e = idx[t0 * k + i];
+      const int tl = i / k;
+      if ((unsigned)e < (unsigned)E) atomicOr(tl < 32 ? &sm.mlo[e] : &sm.mhi[e], 1u << (tl & 31));
+    }
+    __syncthreads();
+    for (int i = tid; i < ne; i += NTH) {
+      const int e = idx[t0 * k + i];
+      if ((unsigned)e >= (unsigned)E) continue;
+      const int tl = i / k;
+      const uint32_t lo = sm.mlo[e], hi = sm.mhi[e];
+      const int r = tl < 32 ? __popc(lo & ((1u << tl) - 1u))
+                            : __popc(lo) + __popc(hi & ((1u << (tl - 32)) - 1u));
+      rows[sm.off[e] + sm.cur[e] + r] = t0 * k + i;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += NTH) {
+      sm.cur[e] += __popc(sm.mlo[e]) + __popc(sm.mhi[e]);
+      sm.mlo[e] = 0;
+      sm.mhi[e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace moe
