@@ -80,12 +80,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Sum within each 32-lane half of the wave.
-__device__ __forceinline__ int half_sum(int v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // Byte position of column cc (0..31) of a chunk inside one 32-byte digit
 // plane: a 32-bit word of codes holds columns 8b..8b+7 as nibbles; masking it
@@ -120,17 +114,27 @@ __device__ __forceinline__ int row16_sum(int v) {
   return v;
 }
 
-// Digit split of one 16-wide group per row of 16 lanes: lane l holds column
-// `col` of a row of activations, and the 16 lanes of its DPP row hold the 16
-// columns of one group (col & ~15 the same for all of them).  With m the
-// group's largest magnitude and E the exponent with m < 2^E <= 2m,
+// Max and integer sum over each half (32 lanes) of the wave.
+__device__ __forceinline__ float half_max(float v) {
+  return fmaxf(row16_max(v), __shfl_xor(row16_max(v), 16, 64));
+}
+
+__device__ __forceinline__ int half_sum(int v) {
+  const int r = row16_sum(v);
+  return r + __shfl_xor(r, 16, 64);
+}
+
+// Digit split of one 32-wide group per half wave: lane l holds column `col`
+// of a row of activations, and the 32 lanes of its half hold the 32 columns
+// of one group (col & ~31 the same for all of them).  With m the group's
+// largest magnitude and E the exponent with m < 2^E <= 2m,
 // X = rint(v * 2^(20-E)), so |X| <= 2^20 and the absolute error is at most
 // 2^(E-21) <= m * 2^-20; X = D2*2^14 + D1*2^7 + D0 with D0, D1 in [-64, 63]
-// and D2 in [-64, 64].  `valid` = false rows still take part in the DPP
-// exchange but store nothing.
-__device__ __forceinline__ void digitize16(float v, int col, bool valid, int8_t* q_row,
+// and D2 in [-64, 64].  `valid` = false halves still take part in the lane
+// exchanges but store nothing.  All 64 lanes must be active.
+__device__ __forceinline__ void digitize32(float v, int col, bool valid, int8_t* q_row,
                                            int32_t* sx_row, float* sc_row) {
-  const float m = row16_max(fabsf(v));
+  const float m = half_max(fabsf(v));
   int E = 0;
   if (m > 0.0f) (void)frexpf(m, &E);
   const int X = m > 0.0f ? (int)rintf(ldexpf(v, kFixBits - E)) : 0;
@@ -138,16 +142,16 @@ __device__ __forceinline__ void digitize16(float v, int col, bool valid, int8_t*
   const int X1 = (X - D0) / 128;
   const int D1 = ((X1 + 64) & 127) - 64;
   const int D2 = (X1 - D1) / 128;
-  const int sx = row16_sum(X);
+  const int sx = half_sum(X);
   if (!valid) return;
   int8_t* plane = q_row + (size_t)(col >> 5) * kChunkDigitBytes;
   const int pos = digit_pos(col & 31);
   plane[pos] = (int8_t)D0;
   plane[kChunk + pos] = (int8_t)D1;
   plane[2 * kChunk + pos] = (int8_t)D2;
-  if ((col & 15) == 0) {
-    sx_row[col >> 4] = sx;
-    sc_row[col >> 4] = ldexpf(1.0f, E - kFixBits);
+  if ((col & 31) == 0) {
+    sx_row[col >> 5] = sx;
+    sc_row[col >> 5] = ldexpf(1.0f, E - kFixBits);
   }
 }
 
@@ -168,13 +172,13 @@ __device__ __forceinline__ ChunkDigits load_chunk_digits(const int8_t* plane_bas
   return cd;
 }
 
-// Exact sums over the two 16-column halves of a chunk of n'_c * X_c, where
-// n'_c = q_c + 8 is the offset-binary form of the int4 weight (bit 3 of every
-// nibble flipped) and X_c the activation's fixed-point value.  Products and
-// sums are exact in int32 (|result| < 2^30).  The caller subtracts 8 * sum(X)
-// per half to get sum q_c X_c.  Code words 0-1 hold columns 0-15, words 2-3
-// columns 16-31; digit words 0-3 and 4-7 of each plane match them.
-__device__ __forceinline__ int2 chunk_dot2(const uint4 codes, const ChunkDigits& cd) {
+// Exact sum over a chunk of n'_c * X_c, where n'_c = q_c + 8 is the
+// offset-binary form of the int4 weight (bit 3 of every nibble flipped) and
+// X_c the activation's fixed-point value: digit plane by digit plane, most
+// significant first, each partial sum scaled by 2^7 before the next.  Products
+// and sums are exact in int32 (|result| < 2^30).  The caller subtracts
+// 8 * sum(X) to get sum q_c X_c.
+__device__ __forceinline__ int chunk_dot(const uint4 codes, const ChunkDigits& cd) {
   const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
   int lo[4], hi[4];
 #pragma unroll
@@ -183,20 +187,17 @@ __device__ __forceinline__ int2 chunk_dot2(const uint4 codes, const ChunkDigits&
     lo[i] = (int)(v & 0x0F0F0F0Fu);
     hi[i] = (int)((v >> 4) & 0x0F0F0F0Fu);
   }
-  int acc[2] = {0, 0};
+  int acc = 0;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int p = kPlanes - 1; p >= 0; --p) {
+    if (p != kPlanes - 1) acc *= 128;
 #pragma unroll
-    for (int p = kPlanes - 1; p >= 0; --p) {
-      if (p != kPlanes - 1) acc[h] *= 128;
-#pragma unroll
-      for (int i = 2 * h; i < 2 * h + 2; ++i) {
-        acc[h] = __builtin_amdgcn_sdot4(lo[i], cd.w[p][2 * i], acc[h], false);
-        acc[h] = __builtin_amdgcn_sdot4(hi[i], cd.w[p][2 * i + 1], acc[h], false);
-      }
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_amdgcn_sdot4(lo[i], cd.w[p][2 * i], acc, false);
+      acc = __builtin_amdgcn_sdot4(hi[i], cd.w[p][2 * i + 1], acc, false);
     }
   }
-  return make_int2(acc[0], acc[1]);
+  return acc;
 }
 
 __device__ __forceinline__ float f16_to_f32(const _Float16* p) { return (float)*p; }

@@ -56,30 +56,28 @@ __device__ __forceinline__ ExpertRef expert_ref(const ExpertList& L, int u) {
 // Digit form of chunk c of activation row `row` (zeros when inactive).
 struct ChunkAct {
   ChunkDigits dig;
-  int2 sx8;  // 8 * (sum of X) per half chunk
-  float2 sc;
+  int sx8;   // 8 * (sum of X) over the chunk
+  float sc;  // value of one unit of X
 };
 
 __device__ __forceinline__ ChunkAct load_act(const Digits& D, int row, int nch, int c, bool act) {
   ChunkAct a;
   if (act) {
     a.dig = load_chunk_digits(D.q + ((size_t)row * nch + c) * kChunkDigitBytes);
-    const int2 sx = *reinterpret_cast<const int2*>(D.sx + (size_t)row * 2 * nch + 2 * c);
-    a.sx8 = make_int2(8 * sx.x, 8 * sx.y);
-    a.sc = *reinterpret_cast<const float2*>(D.sc + (size_t)row * 2 * nch + 2 * c);
+    a.sx8 = 8 * D.sx[(size_t)row * nch + c];
+    a.sc = D.sc[(size_t)row * nch + c];
   } else {
     a.dig = ChunkDigits{};
-    a.sx8 = make_int2(0, 0);
-    a.sc = make_float2(0.0f, 0.0f);
+    a.sx8 = 0;
+    a.sc = 0.0f;
   }
   return a;
 }
 
-// sum over a chunk of q * x: exact integer half-chunk sums, each scaled by its
-// activation group's unit, times the weight row's group scale s.
+// sum over a chunk of q * x: the exact integer sum, times the activation
+// group's unit and the weight row's group scale s.
 __device__ __forceinline__ float chunk_term(uint4 codes, float s, const ChunkAct& a) {
-  const int2 p = chunk_dot2(codes, a.dig);
-  return s * ((float)(p.x - a.sx8.x) * a.sc.x + (float)(p.y - a.sx8.y) * a.sc.y);
+  return (float)(chunk_dot(codes, a.dig) - a.sx8) * (s * a.sc);
 }
 
 // Weight bytes are read once per batch and never again soon: non-temporal
@@ -258,7 +256,7 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
       }
       const int slot = slot_at(t0 + j);
       const int nca = f / kChunk, nga = f / kXGroup;
-      digitize16(silu(g) * uu, rb * kRowsPerBlock + lane, true,
+      digitize32(silu(g) * uu, rb * kRowsPerBlock + lane, true,
                  ad.q + (size_t)slot * nca * kChunkDigitBytes, ad.sx + (size_t)slot * nga,
                  ad.sc + (size_t)slot * nga);
     }
@@ -345,6 +343,75 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
   }
 }
 
+// Down projection and combine for small batches.  Block rb owns output rows
+// [8 rb, 8 rb + 8) for every union expert (wave w takes experts w, w + 4,
+// ...), so each expert's down matrix is still read exactly once, and the
+// block forms out[t][rows] = (x[t][rows]) + sum_j w[t][j] y[t*k+j][rows] in
+// ascending j from its own results: no other block is involved.
+constexpr int kDcRows = 8;
+constexpr int kDcWaves = 4;
+
+template <int NT>
+__global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(ExpertList L, int d, int f,
+                                                                 Digits ad, CombineArgs cb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = blockIdx.x * kDcRows;
+  const int U = *L.n_uniq;
+  const int nch = f / kChunk, nga = f / kGroup;
+  const size_t fd = (size_t)f * d;
+  __shared__ float s_y[kSmallPicks][kDcRows];
+
+  for (int u = wave; u < U; u += kDcWaves) {
+    const ExpertRef ex = expert_ref(L, u);
+    const uint8_t* dcode = ex.blob + fd + (size_t)r0 * (f / 2);
+    const _Float16* dsc =
+        reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+    for (int p = 0; p * 64 < nch; ++p) {
+      const int c = p * 64 + lane;
+      const bool act = c < nch;
+      const unsigned cl = act ? (unsigned)c : 0u;
+      uint4 wd[kDcRows];
+      float sd[kDcRows];
+#pragma unroll
+      for (int b = 0; b < kDcRows; ++b) {
+        wd[b] = stream_load16(dcode + (size_t)b * (f / 2) + cl * 16u);
+        sd[b] = stream_scale(dsc + (size_t)b * nga + cl / 2u);
+      }
+      for (int t0 = 0; t0 < ex.n; t0 += NT) {
+        const int nt = min(NT, ex.n - t0);
+        int slot[NT];
+        ChunkAct aa[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          slot[j] = j < nt ? L.list[ex.beg + t0 + j] : 0;
+          aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          float v[8];
+#pragma unroll
+          for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
+          const float tot = reduce8(v, lane);
+          if ((lane & 7) == 0 && j < nt) {
+            float* dst = &s_y[slot[j]][lane >> 3];
+            *dst = p == 0 ? tot : *dst + tot;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cb.T * kDcRows; i += 64 * kDcWaves) {
+    const int t = i / kDcRows, b = i % kDcRows;
+    float acc = 0.0f;
+    for (int j = 0; j < cb.k; ++j) acc += cb.w[t * cb.k + j] * s_y[t * cb.k + j][b];
+    const size_t o = (size_t)t * d + r0 + b;
+    if (cb.resid) acc = cb.resid[o] + acc;
+    cb.out[o] = acc;
+  }
+}
+
 // out[t][c] = (x[t][c] if resid) + sum_j w[t][j] * y[t*k + j][c], ascending j.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w, const float* resid,
@@ -393,6 +460,14 @@ hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digit
   const dim3 grid(d / kRowsPerBlock, max_experts);
   if (tokens_per_expert_max <= 1) return launch(6, k_down<1>, grid, dim3(256), s, L, d, f, ad, y);
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
+}
+
+hipError_t launch_down_combine(const ExpertList& L, int d, int f, Digits ad,
+                               const CombineArgs& cb, int tokens_per_expert_max, hipStream_t s) {
+  const dim3 grid(d / kDcRows);
+  if (tokens_per_expert_max <= 1)
+    return launch(6, k_down_combine<1>, grid, dim3(64 * kDcWaves), s, L, d, f, ad, cb);
+  return launch(6, k_down_combine<2>, grid, dim3(64 * kDcWaves), s, L, d, f, ad, cb);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,

@@ -224,7 +224,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
 
   if (T <= kSmallBatch && T * k <= kSmallPicks) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (recomputed per
-    // block) and gate/up; 3: down; 4: combine
+    // block) and gate/up; 3: down + combine
     RouterArgs ra{};
     ra.x = x;
     ra.x_bf16 = x_dtype == MOE_BF16;
@@ -241,8 +241,8 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     MOE_TRY(launch_router_front(ra, s));
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats};
     MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, T, s));
-    MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
-    MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
+    CombineArgs cb{w, resid, out, T, k};
+    MOE_TRY(launch_down_combine(EL, d, f, ad, cb, T, s));
     return MOE_OK;
   }
 

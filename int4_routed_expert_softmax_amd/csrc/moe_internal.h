@@ -14,13 +14,13 @@ namespace moe {
 constexpr int kGroup = 64;
 // Columns covered by one 16-byte load of 4-bit codes.
 constexpr int kChunk = 32;
-// Activations enter the int4 dot products as 21-bit fixed point per 16-wide
-// group, split into three signed int8 digit planes of base 2^7.  A 32-column
-// chunk (one 16-byte load of codes) therefore carries 3 x 32 digit bytes and
-// two groups.
+// Activations enter the int4 dot products as 21-bit fixed point per 32-wide
+// group, split into three signed int8 digit planes of base 2^7.  A group is
+// one 32-column chunk (one 16-byte load of codes) and carries 3 x 32 digit
+// bytes.
 constexpr int kPlanes = 3;
 constexpr int kChunkDigitBytes = kPlanes * kChunk;
-constexpr int kXGroup = 16;
+constexpr int kXGroup = 32;
 // Exponent offset of the fixed point: a group whose largest magnitude is below
 // 2^E is stored as X = rint(v * 2^(kFixBits - E)), |X| <= 2^kFixBits.
 constexpr int kFixBits = 20;
@@ -30,8 +30,8 @@ constexpr int kFixBits = 20;
 //      bytes of each plane in code order (per 8 columns: the 4 even columns,
 //      then the 4 odd columns), matching how a 32-bit word of nibbles splits
 //      into its low and high nibbles
-//   sx [rows][K/16] int32: sum of X over the group
-//   sc [rows][K/16] f32:   value of one unit of X in the group, 2^(E - 20)
+//   sx [rows][K/32] int32: sum of X over the group
+//   sc [rows][K/32] f32:   value of one unit of X in the group, 2^(E - 20)
 struct Digits {
   int8_t* q;
   int32_t* sx;
@@ -121,6 +121,16 @@ hipError_t launch_gateup(const ExpertList& L, const RouteOut* small_route, int m
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
                        int tokens_per_expert_max, hipStream_t s);
+
+// Down projection fused with the combine, for small batches (T * k <= 64).
+struct CombineArgs {
+  const float* w;      // [T][k] router weights
+  const float* resid;  // [T][d] or nullptr
+  float* out;          // [T][d]
+  int T, k;
+};
+hipError_t launch_down_combine(const ExpertList& L, int d, int f, Digits ad,
+                               const CombineArgs& cb, int tokens_per_expert_max, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 

@@ -115,11 +115,11 @@ __global__ __launch_bounds__(kUnionThreads) void k_union(const int32_t* __restri
 // ---------------------------------------------------------------- router front end
 // For batches of up to kSmallBatch tokens, one launch computes every logit and
 // the activations' digit form: one workgroup per expert computes that
-// expert's logits for every token (RMSNorm first if asked, recomputed in the
-// same order in every workgroup so all agree bit for bit), and the workgroups
-// share out the digit split.  Top-k and the union run at the start of the
-// next kernel (the gate/up projection), which needs them first; nothing here
-// waits on another workgroup.
+// expert's logits for every token, and extra workgroups after them make the
+// digit split in parallel (RMSNorm first if asked, recomputed in the same
+// order in every workgroup so all agree bit for bit).  Top-k and the union
+// run at the start of the next kernel (the gate/up projection), which needs
+// them first; nothing here waits on another workgroup.
 template <int TB>
 __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
   const int e = blockIdx.x;
@@ -162,6 +162,17 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     return a.prenorm ? (float)((double)v * s_r[t]) : v;
   };
 
+  if (e >= E) {
+    // workgroups past the last expert: the digit split, one wave per 64
+    // columns of a token
+    const int nb = d / 64, nch = d / kChunk, ng = d / kXGroup;
+    for (int it = (e - E) * 4 + wave; it < T * nb; it += (gridDim.x - E) * 4) {
+      const int t = it / nb, col = (it % nb) * 64 + lane;
+      digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
+                 a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
+    }
+    return;
+  }
   const float4* w4 = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d);
   double acc[TB];
 #pragma unroll
@@ -189,16 +200,6 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     const double sj = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
     a.z[(size_t)tid * E + e] = sj + (a.bias ? (double)a.bias[e] : 0.0);
   }
-
-  // this workgroup's share of the digit split: one wave per 64 columns of a token
-  if (a.xd.q) {
-    const int nb = d / 64, nch = d / kChunk, ng = d / kXGroup;
-    for (int it = e * 4 + wave; it < T * nb; it += gridDim.x * 4) {
-      const int t = it / nb, col = (it % nb) * 64 + lane;
-      digitize16(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
-                 a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
-    }
-  }
 }
 
 // ---------------------------------------------------------------- digit split
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(256) void k_digitize(const void* __restrict__ x, in
     const size_t i = (size_t)src * K + col;
     const float v = x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16)
                            : static_cast<const float*>(x)[i];
-    digitize16(v, col, true, out.q + (size_t)r * nch * kChunkDigitBytes, out.sx + (size_t)r * ng,
+    digitize32(v, col, true, out.q + (size_t)r * nch * kChunkDigitBytes, out.sx + (size_t)r * ng,
                out.sc + (size_t)r * ng);
   }
 }
@@ -245,10 +246,12 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 }
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s) {
-  if (a.T <= 1) return launch(1, k_router_front<1>, dim3(a.E), dim3(256), s, a);
-  if (a.T <= 2) return launch(1, k_router_front<2>, dim3(a.E), dim3(256), s, a);
-  if (a.T <= 4) return launch(1, k_router_front<4>, dim3(a.E), dim3(256), s, a);
-  return launch(1, k_router_front<8>, dim3(a.E), dim3(256), s, a);
+  const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + 3) / 4 : 0;
+  const dim3 grid(a.E + dig_blocks);
+  if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(256), s, a);
+  if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(256), s, a);
+  if (a.T <= 4) return launch(1, k_router_front<4>, grid, dim3(256), s, a);
+  return launch(1, k_router_front<8>, grid, dim3(256), s, a);
 }
 
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
