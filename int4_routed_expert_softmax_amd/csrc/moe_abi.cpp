@@ -45,6 +45,12 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.asx = take(Tk * (f / kXGroup) * sizeof(int32_t));
   L.asc = take(Tk * (f / kXGroup) * sizeof(float));
   L.y = take(Tk * d * sizeof(float));
+  L.xh = take((size_t)T * d * sizeof(uint16_t));
+  L.xunit = take((size_t)T * sizeof(float));
+  L.a32 = take(Tk * f * sizeof(float));
+  L.ah = take(Tk * f * sizeof(uint16_t));
+  L.aunit = take(Tk * sizeof(float));
+  L.mbo = take((cap + 1) * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -94,6 +100,25 @@ Digits x_digits(void* ws, const Layout& L) {
 
 Digits a_digits(void* ws, const Layout& L) {
   return Digits{at<int8_t>(ws, L.aq), at<int32_t>(ws, L.asx), at<float>(ws, L.asc)};
+}
+
+MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
+  MfmaArgs m{};
+  m.d = d;
+  m.f = f;
+  m.xh = at<_Float16>(ws, L.xh);
+  m.xunit = at<float>(ws, L.xunit);
+  m.a32 = at<float>(ws, L.a32);
+  m.ah = at<_Float16>(ws, L.ah);
+  m.aunit = at<float>(ws, L.aunit);
+  m.mbo = at<int32_t>(ws, L.mbo);
+  return m;
+}
+
+// Row offsets inside the packed activations are 32-bit element indices.
+bool rows_fit(size_t rows, const moe_dims* dm) {
+  const size_t K = dm->d > dm->f ? dm->d : dm->f;
+  return rows * K < (size_t(1) << 31);
 }
 
 }  // namespace
@@ -173,13 +198,26 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   if (!aligned(expert_blob, 16) || !aligned(x, 4) || !aligned(y, 4)) return MOE_EINVAL;
   const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, n);
   if (ws_bytes < L.total) return MOE_ENOSPC;
+  if (!rows_fit((size_t)n * dm->top_k, dm)) return MOE_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
-  MOE_TRY(launch_digitize(x, x_dtype == MOE_BF16, rows, n, dm->d, xd, s));
   ExpertList EL{};
   EL.single = static_cast<const uint8_t*>(expert_blob);
   EL.single_n = n;
   EL.kdiv = 1;
+  if (n > kSmallBatch) {
+    MfmaArgs m = mfma_args(ws, L, dm->d, dm->f);
+    m.L = EL;
+    m.x = x;
+    m.x_bf16 = x_dtype == MOE_BF16;
+    m.x_rows = n;
+    m.x_gather = rows;
+    m.slots = n;
+    m.y = y;
+    MOE_TRY(launch_ffn_mfma(m, s));
+    return MOE_OK;
+  }
+  const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
+  MOE_TRY(launch_digitize(x, x_dtype == MOE_BF16, rows, n, dm->d, xd, s));
   MOE_TRY(launch_gateup(EL, nullptr, 1, dm->d, dm->f, xd, ad, n, s));
   MOE_TRY(launch_down(EL, 1, dm->d, dm->f, ad, y, n, s));
   return MOE_OK;
@@ -201,6 +239,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
   const Layout L = layout(d, f, E, k, T);
   if (ws_bytes < L.total) return MOE_ENOSPC;
+  if (!rows_fit((size_t)T * k, dm)) return MOE_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   double* z = at<double>(ws, L.z);
@@ -257,9 +296,15 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
   MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
   MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
-  MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
-  MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, s));
-  MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
+  MfmaArgs m = mfma_args(ws, L, d, f);
+  m.L = EL;
+  m.x = xr;
+  m.x_bf16 = xr_bf16;
+  m.x_rows = T;
+  m.slots = T * k;
+  m.mb_bound = maxU + (T * k + mfma_mblock() - 1) / mfma_mblock();
+  m.y = y;
+  MOE_TRY(launch_ffn_mfma(m, s));
   MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
   return MOE_OK;
 }

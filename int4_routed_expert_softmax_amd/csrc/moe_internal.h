@@ -39,7 +39,8 @@ struct Digits {
 };
 
 struct Layout {
-  size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y, total;
+  size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
+  size_t xh, xunit, a32, ah, aunit, mbo, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -133,5 +134,30 @@ hipError_t launch_down_combine(const ExpertList& L, int d, int f, Digits ad,
                                const CombineArgs& cb, int tokens_per_expert_max, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
+
+// Grouped-GEMM expert FFN on the MFMA units (multi-token batches).  x rows are
+// packed to fp16 with a power of two per row (xh, xunit), gate/up writes
+// silu(g) * u per slot (a32), which is packed the same way (ah, aunit), and
+// down writes y per slot.  Slots of the union: list entries; x row = slot /
+// kdiv.  A single expert: slot i = x row i.
+struct MfmaArgs {
+  ExpertList L;
+  int d, f;
+  const void* x;
+  int x_bf16;
+  int x_rows;                // rows to pack (T tokens, or n rows of a single expert)
+  const int32_t* x_gather;   // source row of packed row r (nullptr: r)
+  int slots;                 // rows of a32 / ah / y
+  int mb_bound;              // union: upper bound on the number of M-blocks
+  _Float16* xh;
+  float* xunit;
+  float* a32;
+  _Float16* ah;
+  float* aunit;
+  int32_t* mbo;              // [n_experts + 1]
+  float* y;
+};
+int mfma_mblock();
+hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s);
 
 }  // namespace moe

@@ -180,6 +180,36 @@ def test_glm_expert_ffn_device_and_host_mapped(decode_layer):
     assert_close(y3.cpu().numpy(), ref3, "expert_ffn bf16")
 
 
+def test_glm_expert_ffn_batched_mfma(decode_layer):
+    """Single expert over many rows (the grouped-GEMM path): a gathered fp32
+    batch spanning three M-blocks with a ragged tail, and a bf16 batch."""
+    w = W["decode1"]
+    L = decode_layer
+    xb, _ = configs.tokens(W["prefill512"])          # bf16 bits [512][d]
+    xf = configs.bf16_bits_to_f32(xb)
+    rng = np.random.default_rng(5)
+    for e, n in [(0, 150), (77, 21)]:
+        sel = rng.choice(xf.shape[0], size=n, replace=False).astype(np.int32)
+        xd = torch.from_numpy(np.ascontiguousarray(xf * 1.5)).to(DEV)
+        rows = torch.from_numpy(sel).to(DEV)
+        y = torch.empty(n, w.d, dtype=torch.float32, device=DEV)
+        say(f"expert_ffn batched: expert {e} n={n} fp32 gathered")
+        moe.moe_expert_ffn(L.dims, L.blobs_d[e], xd, rows, n, y, moe.make_workspace(L.dims, n, DEV))
+        torch.cuda.synchronize()
+        ref = oracle.expert_ffn(L.blobs[e], (xf[sel] * 1.5).astype(np.float64), w.d, w.f)
+        rel = assert_close(y.cpu().numpy(), ref, f"expert_ffn batched e={e} n={n}")
+        say(f"expert_ffn batched: expert {e} n={n} rel err {rel:.2e}")
+    n = 40
+    xbd = torch.from_numpy(xb[:n].view(np.int16)).to(DEV).view(torch.bfloat16)
+    y = torch.empty(n, w.d, dtype=torch.float32, device=DEV)
+    say(f"expert_ffn batched: expert 5 n={n} bf16")
+    moe.moe_expert_ffn(L.dims, L.blobs_d[5], xbd, None, n, y, moe.make_workspace(L.dims, n, DEV))
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(L.blobs[5], xf[:n].astype(np.float64), w.d, w.f)
+    rel = assert_close(y.cpu().numpy(), ref, "expert_ffn batched bf16")
+    say(f"expert_ffn batched: bf16 n={n} rel err {rel:.2e}")
+
+
 def test_glm_verify_batch8():
     L, ref, _ = full_parity(W["verify8"])
     say(f"verify8: union of {ref['U']} distinct experts for 64 picks")
