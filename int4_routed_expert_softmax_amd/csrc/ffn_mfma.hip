@@ -5,18 +5,26 @@
 // of its tokens, so its bytes are read once (colibri 技术解读 (linlog.top),
 // "集群模式与开放问题清单"; colibrì README (简体中文), 工作原理 › 绝不为同一次磁盘读取等待两遍).
 //
-// Operands of v_mfma_f32_16x16x32_f16 (fp32 accumulate):
-//  - B (weights): a wave owns 64 weight rows.  Their int4 codes arrive in
-//    512-column stages through wave-private LDS (coalesced 256-byte row
-//    pieces, prefetched one stage ahead into registers) and are dequantised in
-//    registers: a code becomes the fp16 number 1032 + q (one AND/OR per two
-//    codes), 1032 is subtracted exactly, and the product with the group's fp16
-//    scale is rounded once to fp16.
-//  - A (activations): rows in fp16 scaled by a power of two per row (k_pack)
-//    and read straight from L2; the row's power of two multiplies the result.
-// A 32-bit word of 8 codes splits into fp16 pairs (column j, column j + 4),
-// so k_pack stores each block of 8 columns in that order: position p holds
-// column (p >> 1) + 4 (p & 1).
+// Arithmetic:
+//   x = x' * unit[m]      x' in fp16 (k_pack: a power of two per row, |x'| < 2^14)
+//   W[n][k] = fp16(q * s[n][g])    q in [-8, 7] is formed exactly as the fp16
+//                         number 1032 + q (one AND/OR per two codes) minus 1032;
+//                         the product with the group's fp16 scale is rounded
+//                         once (relative error <= 2^-11, exact when q * s fits)
+//   out[m][n] = unit[m] * sum_k x'[m][k] W[n][k]    v_mfma_f32_16x16x32_f16, fp32
+//                         accumulation straight through the MFMA C operand
+// q * s stays a normal fp16 number for 2^-14 <= |s| <= 2^12; smaller scales
+// lose relative precision gradually (fp16 subnormals), larger ones overflow.
+//
+// Work unit: one block (4 waves) = one expert x one M-block of up to 32 of its
+// tokens x 256 weight rows (64 per wave; gate/up: 32 rows of gate and the same
+// 32 rows of up, so SwiGLU is local to the wave).  K is walked in 128-column
+// stages copied global -> LDS without passing through registers, into a ring
+// of 3 stages; the A and B fragments come from LDS.  d and f must be multiples
+// of 512.
+// A 32-bit word of 8 codes splits into fp16 pairs (column j, column j + 4), so
+// k_pack stores each block of 8 columns in that order: position p holds column
+// (p >> 1) + 4 (p & 1).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,14 +40,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4* g_u32x4_ptr;
 
-constexpr int kNt = 4;                               // 16-row N-tiles per wave
-constexpr int kWaveRows = kNt * 16;                  // weight rows per wave
-constexpr int kGWaves = 4;                           // waves per block
-constexpr int kStageCols = 512;                      // columns per LDS stage
-constexpr int kStageBytes = kStageCols / 2;          // code bytes per row per stage
-constexpr int kStagePieces = kWaveRows * kStageBytes / 16 / 64;  // 16-byte loads per lane
-constexpr int kLdsStride = kStageBytes + 8;          // padded LDS row (bytes)
-constexpr int kPackExp = 14;                         // packed |value| < 2^14
+constexpr int kNt = 4;                                  // 16-row N-tiles per wave
+constexpr int kWaveRows = kNt * 16;                     // weight rows per wave
+constexpr int kGWaves = 4;                              // waves per block
+constexpr int kPackExp = 14;                            // packed |x'| < 2^14
+constexpr float kBias = 1032.0f;
 
 __device__ __forceinline__ int slot_of_col(int e) { return 2 * (e & 3) + (e >> 2); }
 
@@ -47,17 +52,16 @@ __device__ __forceinline__ u32x4 nt_load16(const uint8_t* p) {
   return __builtin_nontemporal_load((g_u32x4_ptr)(p));
 }
 
-// 8 codes (a 32-bit word, column j in bits 4j..4j+3) times one fp16 scale ->
-// 8 fp16 weights in slot order (col 0, 4, 1, 5, 2, 6, 3, 7).
+// 8 codes (column j in bits 4j..4j+3) and their group's scale (both halves)
+// -> 8 fp16 weights q * s in slot order (col 0, 4, 1, 5, 2, 6, 3, 7).
 __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s2) {
-  const uint32_t v = w ^ 0x88888888u;  // offset binary: q + 8
-  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 off = {(_Float16)kBias, (_Float16)kBias};
   f16x8 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t h = ((v >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // 1024 + q + 8
-    const f16x2 q = __builtin_bit_cast(f16x2, h) - off;               // exact
-    const f16x2 ws = q * s2;                                          // one rounding
+    const uint32_t h = (((w >> (4 * j)) & 0x000F000Fu) ^ 0x00080008u) | 0x64006400u;
+    const f16x2 q = __builtin_bit_cast(f16x2, h) - off;  // exact
+    const f16x2 ws = q * s2;                             // one rounding
     r[2 * j] = ws[0];
     r[2 * j + 1] = ws[1];
   }
@@ -76,10 +80,10 @@ __device__ __forceinline__ int find_bucket(const int32_t* p, int n, int j) {
 }
 
 // ---------------------------------------------------------------- packing
-// One wave per row: max |v| over the row, then fp16(v * 2^(14 - e)) with
+// One wave per row: max |v| over the row, then x' = fp16(v * 2^(14 - e)) with
 // max|v| < 2^e, columns permuted within blocks of 8; unit[r] = 2^(e - 14).
-// With mbo set, the last block instead writes the union's M-block prefix:
-// mbo[u] = sum over u' < u of ceil(count(u') / mblock), u = 0..U.
+// With mbo set, the last block instead writes the union's M-block prefix: mbo[u] = sum over u' < u of
+// ceil(count(u') / mblock), u = 0..U.
 struct PackArgs {
   const void* src;
   int src_bf16, K, rows;
@@ -89,6 +93,7 @@ struct PackArgs {
   const int32_t* offsets;
   const int32_t* n_uniq;
   int32_t* mbo;
+  int32_t* blk_u;
   int mblock;
 };
 
@@ -133,7 +138,10 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
-      if (u < U) p.mbo[u] = run;
+      if (u < U) {
+        p.mbo[u] = run;
+        for (int j = 0; j < c[i]; ++j) p.blk_u[run + j] = u;
+      }
       run += c[i];
     }
     if (t == 0) p.mbo[U] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
@@ -172,189 +180,222 @@ enum { kGateUp = 0, kDown = 1 };
 
 struct GemmArgs {
   ExpertList L;
-  const int32_t* mbo;  // union M-block prefix (unused for a single expert)
+  const int32_t* mbo;    // union: M-block prefix
+  const int32_t* blk_u;  // union: expert of each M-block
   int d, f;
-  const _Float16* a;   // packed A rows
-  const float* unit;   // their units
-  float* out;          // gate/up: silu(g) * u [slots][f]; down: y [slots][d]
+  const _Float16* a;     // packed A rows [rows][K]
+  const float* unit;     // [rows]
+  float* out;            // gate/up: silu(g) * u [slots][f]; down: y [slots][d]
 };
 
-// One block: 4 independent waves (no block-wide barrier), each owning 64
-// weight rows (gate/up: 32 rows of gate and the same 32 rows of up), times one
-// M-block of up to 16 * MW tokens of one expert.
-template <int MODE, int MW>
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// Global -> LDS copies that bypass registers: lane l's 16 bytes land at
+// lds + 16 l, `lds` being wave-uniform (M0); completion is tracked by vmcnt
+// only.  They are issued as inline assembly so that the compiler, which
+// cannot tell which LDS bytes a copy writes, does not drain every copy in
+// flight before each LDS read; the ring protocol below waits for exactly the
+// stage it reads.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8_t*)p);
+}
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
+}
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt unconstrained)
+#define MOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70)
+
+// LDS: a ring of kRing stages, each covering 128 K-columns (two scale groups),
+//   B  [wave][64 rows][64 B]   codes; row r holds its 16-byte piece p at slot
+//                              p ^ ((r >> 1) & 3)
+//   A  [32 rows][256 B]        packed activations; piece p (8 columns) of row r
+//                              at slot p ^ (r & 7)
+// followed by per-wave scales, two buffers of [64 rows][8 groups] fp16 (8
+// groups = 4 stages), refilled every 4 stages.
+constexpr int kSC = 128;
+constexpr int kRing = 3;
+constexpr int kMBlock = 32;
+constexpr int kBWave = kWaveRows * (kSC / 2);
+constexpr int kStageB = kGWaves * kBWave;
+constexpr int kStage = kStageB + kMBlock * kSC * 2;
+constexpr int kScaleOff = kRing * kStage;
+constexpr int kScaleWave = 2 * kWaveRows * 16;
+constexpr int kLdsBytes = kScaleOff + kGWaves * kScaleWave;
+static_assert(2 * kLdsBytes <= 160 * 1024, "two blocks per CU");
+// copies per wave and stage: 4 (codes) + 2 (activations), plus 1 (scales) in
+// stages 0, 4, 8, ...
+constexpr int kCopies = 6;
+
+// One block: 4 waves, each owning 64 weight rows, times one M-block of up to
+// 32 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
+// every copy of stage st is issued before any of stage st + 1, so "stage st has
+// landed" is "at most the copies of stage st + 1 are in flight".
+template <int MODE>
 __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
-  constexpr int MB = 16 * MW;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wv = blockIdx.x * kGWaves + wave;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kLdsBytes];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int d = g.d, f = g.f;
   const int K = MODE == kGateUp ? d : f;
-  const int nwaves = MODE == kGateUp ? f / 32 : d / kWaveRows;
-  if (wv >= nwaves) return;
+  const int ng = K / 64;
 
+  // ---- the block's expert and tokens
   const ExpertList& L = g.L;
   int off, cnt, tok0;
   const uint8_t* blob;
   if (L.single) {
     off = 0;
     cnt = L.single_n;
-    tok0 = blockIdx.y * MB;
+    tok0 = blockIdx.y * kMBlock;
     if (tok0 >= cnt) return;
     blob = L.single;
   } else {
-    const int U = *L.n_uniq;
     const int j = blockIdx.y;
-    if (j >= g.mbo[U]) return;
-    const int u = find_bucket(g.mbo, U, j);
+    if (j >= g.mbo[*L.n_uniq]) return;
+    const int u = g.blk_u[j];
     off = L.offsets[u];
     cnt = L.offsets[u + 1] - off;
-    tok0 = (j - g.mbo[u]) * MB;
+    tok0 = (j - g.mbo[u]) * kMBlock;
     blob = L.table[L.uniq[u]];
   }
-  const int ntok = min(MB, cnt - tok0);
-  const int nmt = (ntok + 15) >> 4;
-  const int n = lane & 15, kg = lane >> 4;
+  const int nmt = (min(kMBlock, cnt - tok0) + 15) >> 4;
+  // packed row of the block's token i (past the last token: the last one)
+  auto row_of = [&](int i) -> uint32_t {
+    const int ti = min(tok0 + i, cnt - 1);
+    if (L.single) return (uint32_t)ti;
+    const int slot = L.list[off + ti];
+    return (uint32_t)(MODE == kGateUp ? slot / L.kdiv : slot);
+  };
 
-  // A rows of this lane (row n of every M-tile); rows past the expert's last
-  // token repeat its last token and are dropped in the epilogue
-  uint32_t arow[MW];
-#pragma unroll
-  for (int mt = 0; mt < MW; ++mt) {
-    const int i = min(tok0 + 16 * mt + n, cnt - 1);
-    int r = i;
-    if (!L.single) {
-      const int slot = L.list[off + i];
-      r = MODE == kGateUp ? slot / L.kdiv : slot;
-    }
-    arow[mt] = (uint32_t)r * (uint32_t)K;
-  }
-
-  // weight rows: LDS rows 0..31 and 32..63 come from two base pointers
+  // ---- this wave's weight rows (ring rows 0..31 and 32..63); waves past the
+  // last row copy the last wave's rows and compute nothing
+  const int nwaves = MODE == kGateUp ? f / 32 : d / kWaveRows;
+  const int wv = blockIdx.x * kGWaves + wave;
+  const bool active = wv < nwaves;
+  const int wc = min(wv, nwaves - 1);
   const size_t fd = (size_t)f * d;
-  const int ng = K / 64;
   const _Float16* sbase = reinterpret_cast<const _Float16*>(blob + 3 * (fd / 2));
   const uint8_t *c0, *c1;
   const _Float16 *s0, *s1;
   if (MODE == kGateUp) {
-    c0 = blob + (size_t)(32 * wv) * (K / 2);
+    c0 = blob + (size_t)(32 * wc) * (K / 2);
     c1 = c0 + fd / 2;
-    s0 = sbase + (size_t)(32 * wv) * ng;
+    s0 = sbase + (size_t)(32 * wc) * ng;
     s1 = s0 + fd / 64;
   } else {
-    c0 = blob + fd + (size_t)(64 * wv) * (K / 2);
+    c0 = blob + fd + (size_t)(64 * wc) * (K / 2);
     c1 = c0 + (size_t)32 * (K / 2);
-    s0 = sbase + 2 * (fd / 64) + (size_t)(64 * wv) * ng;
+    s0 = sbase + 2 * (fd / 64) + (size_t)(64 * wc) * ng;
     s1 = s0 + (size_t)32 * ng;
   }
+  const int n = lane & 15, kg = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[kGWaves * kWaveRows * kLdsStride];
-  uint8_t* s_b = s_codes + wave * kWaveRows * kLdsStride;
+  // ---- per-lane copy sources
+  // codes, copy i: lane l -> ring row 16 i + l / 4, slot l % 4 (piece slot ^ swizzle)
+  const uint32_t b_piece = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
+  const uint32_t b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + b_piece * 16u;
+  const uint32_t b_half = 16u * (uint32_t)(K / 2);
+  // activations, copy i of wave w: lane l -> row 8 w + 4 i + l / 16, slot l % 16
+  uint32_t a_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * wave + 4 * i + (lane >> 4);
+    a_off[i] = row_of(r) * (uint32_t)K + (uint32_t)((lane & 15) ^ (r & 7)) * 8u;
+  }
+  // scales: lane l -> ring row l, 8 groups
+  const _Float16* s_lane = (lane < 32 ? s0 : s1) + (size_t)(lane & 31) * ng;
+  uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
 
-  // stage prefetch: piece p = lane + 64 i covers LDS row p / 16 (i < 8: base
-  // c0, rows 4 i + lane / 16) and 16 bytes at (p % 16) * 16 of the stage
-  const uint32_t lrow = lane >> 4, lpiece = lane & 15;
-  const uint32_t lane_off = lrow * (uint32_t)(K / 2) + lpiece * 16u;
-  const int nst = (K + kStageCols - 1) / kStageCols;
-  u32x4 pre[kStagePieces];
-  uint4 spre[kNt];  // 8 fp16 scales per tile
-  auto fetch = [&](int st) {
-    const uint32_t so = (uint32_t)st * kStageBytes;
-    const bool full = (st + 1) * kStageCols <= K;
-    const bool piece_ok = full || so + lpiece * 16u < (uint32_t)(K / 2);
+  const int nst = K / kSC;
+  auto issue = [&](int st) {
+    uint8_t* base = s_lds + (st % kRing) * kStage;
+    const uint32_t so = (uint32_t)st * (kSC / 2);
 #pragma unroll
-    for (int i = 0; i < kStagePieces; ++i) {
-      const uint8_t* cb = i < kStagePieces / 2 ? c0 : c1;
-      const uint32_t ro = (uint32_t)(4 * (i % (kStagePieces / 2))) * (uint32_t)(K / 2);
-      pre[i] = piece_ok ? nt_load16(cb + ro + so + lane_off) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // scales of rows 16 nt + n, groups 8 st .. 8 st + 7
+    for (int i = 0; i < 4; ++i)
+      dma16((i < 2 ? c0 : c1) + (i & 1) * b_half + so + b_off, base + wave * kBWave + i * 1024);
 #pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) {
-      const _Float16* sr = (nt < 2 ? s0 : s1) + (size_t)(16 * (nt & 1) + n) * ng;
-      if ((ng & 7) == 0) {
-        spre[nt] = *reinterpret_cast<const uint4*>(sr + 8 * st);
-      } else {
-        uint16_t h[8];
-#pragma unroll
-        for (int gg = 0; gg < 8; ++gg)
-          h[gg] = __builtin_bit_cast(uint16_t, sr[min(8 * st + gg, ng - 1)]);
-        spre[nt] = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16,
-                              h[4] | (uint32_t)h[5] << 16, h[6] | (uint32_t)h[7] << 16);
-      }
-    }
+    for (int i = 0; i < 2; ++i)
+      dma16(g.a + a_off[i] + st * kSC, base + kStageB + (8 * wave + 4 * i) * (kSC * 2));
+    if ((st & 3) == 0)
+      dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
   };
 
-  f32x4 acc[MW][kNt];
+  f32x4 acc[2][kNt];
 #pragma unroll
-  for (int mt = 0; mt < MW; ++mt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto kblock = [&](int st, int kb, const uint4 (&sc)[kNt]) {
-    f16x8 b[kNt];
+  // scale group 2 st + gg of a landed stage.  Lane (n, kg) takes, for MFMA
+  // step j, columns 16 kg + 8 j .. + 8 of the group: dword 2 kg + j of the
+  // row's 32 code bytes and 8-column block 2 kg + j of the activations.
+  auto group = [&](int st, int gg) {
+    const uint8_t* base = s_lds + (st % kRing) * kStage;
+    const int gi = 2 * st + gg;
+    const uint8_t* sc = s_scales + ((gi >> 3) & 1) * (kWaveRows * 16) + (gi & 7) * 2;
+    f16x8 b0[kNt], b1[kNt];
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
-      const uint32_t w =
-          *reinterpret_cast<const uint32_t*>(s_b + (16 * nt + n) * kLdsStride + kb * 16 + 4 * kg);
-      const int gg = kb >> 1;
-      const uint32_t word = (gg >> 1) == 0 ? sc[nt].x : (gg >> 1) == 1 ? sc[nt].y
-                            : (gg >> 1) == 2 ? sc[nt].z : sc[nt].w;
-      const uint32_t h = (gg & 1) ? word >> 16 : word & 0xFFFFu;
-      b[nt] = dequant8(w, __builtin_bit_cast(f16x2, h | h << 16));
+      const int r = 16 * nt + n;
+      const int slot = (2 * gg + (kg >> 1)) ^ ((r >> 1) & 3);
+      const uint2 w = *reinterpret_cast<const uint2*>(base + wave * kBWave + r * (kSC / 2) +
+                                                      slot * 16 + 8 * (kg & 1));
+      const uint32_t h = *reinterpret_cast<const uint16_t*>(sc + r * 16);
+      const f16x2 s2 = __builtin_bit_cast(f16x2, h | (h << 16));
+      b0[nt] = dequant8(w.x, s2);
+      b1[nt] = dequant8(w.y, s2);
     }
-    const uint32_t col = (uint32_t)(st * kStageCols + kb * 32 + 8 * kg);
 #pragma unroll
-    for (int mt = 0; mt < MW; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
       if (mt < nmt) {
-        const f16x8 av = *reinterpret_cast<const f16x8*>(g.a + arow[mt] + col);
+        const uint8_t* ar = base + kStageB + (16 * mt + n) * (kSC * 2);
+        const int p0 = 8 * gg + 2 * kg;
+        const f16x8 a0 = *reinterpret_cast<const f16x8*>(ar + (p0 ^ (n & 7)) * 16);
+        const f16x8 a1 = *reinterpret_cast<const f16x8*>(ar + ((p0 + 1) ^ (n & 7)) * 16);
 #pragma unroll
-        for (int nt = 0; nt < kNt; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[nt], acc[mt][nt], 0, 0, 0);
+        for (int nt = 0; nt < kNt; ++nt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1[nt], acc[mt][nt], 0, 0, 0);
+        }
       }
     }
   };
 
-  fetch(0);
+  issue(0);
+  issue(1);
   for (int st = 0; st < nst; ++st) {
-#pragma unroll
-    for (int i = 0; i < kStagePieces; ++i) {
-      const int p = lane + 64 * i;
-      uint8_t* dst = s_b + (p >> 4) * kLdsStride + (p & 15) * 16;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pre[i].x, pre[i].y);
-      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(pre[i].z, pre[i].w);
-    }
-    uint4 sc[kNt];
-#pragma unroll
-    for (int nt = 0; nt < kNt; ++nt) sc[nt] = spre[nt];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (st + 1 < nst) fetch(st + 1);
-    const int nkb = min(kStageCols, K - st * kStageCols) / 32;
-    if (nkb == kStageCols / 32) {
-#pragma unroll
-      for (int kb = 0; kb < kStageCols / 32; ++kb) kblock(st, kb, sc);
+    if (st + 1 < nst) {
+      if (((st + 1) & 3) == 0) MOE_WAIT_VM_LGKM0(kCopies + 1);
+      else MOE_WAIT_VM_LGKM0(kCopies);
     } else {
-      for (int kb = 0; kb < nkb; ++kb) kblock(st, kb, sc);
+      MOE_WAIT_VM_LGKM0(0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // every wave is past stage st - 1: its ring slot takes stage st + 2
+    if (st + 2 < nst) issue(st + 2);
+    if (active) {
+      group(st, 0);
+      group(st, 1);
+    }
   }
+  if (!active) return;
 
   // epilogue: lane (n, kg) holds, per tile, tokens 4 kg + i of the M-tile for
   // weight row 16 nt + n
 #pragma unroll
-  for (int mt = 0; mt < MW; ++mt) {
+  for (int mt = 0; mt < 2; ++mt) {
     if (mt >= nmt) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = tok0 + 16 * mt + 4 * kg + i;
-      if (t >= cnt) continue;
-      const int slot = L.single ? t : L.list[off + t];
+      const int ti = tok0 + 16 * mt + 4 * kg + i;
+      if (ti >= cnt) continue;
+      const int slot = L.single ? ti : L.list[off + ti];
       if (MODE == kGateUp) {
-        const int xr = L.single ? t : slot / L.kdiv;
+        const int xr = L.single ? ti : slot / L.kdiv;
         const float us = g.unit[xr];
         float* orow = g.out + (size_t)slot * f + 32 * wv;
 #pragma unroll
@@ -374,15 +415,14 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------- launchers
 
-constexpr int kMfmaMW = 4;
-constexpr int kMBlock = 16 * kMfmaMW;
-
 int mfma_mblock() { return kMBlock; }
+
+bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   const ExpertList& L = m.L;
   hipError_t e;
-  // x rows -> fp16 (and the union's M-block prefix)
+  // x rows -> fp16 (and the union's M-block map)
   PackArgs px{};
   px.src = m.x;
   px.src_bf16 = m.x_bf16;
@@ -395,6 +435,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     px.offsets = L.offsets;
     px.n_uniq = L.n_uniq;
     px.mbo = m.mbo;
+    px.blk_u = m.blk_u;
     px.mblock = kMBlock;
   }
   const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
@@ -403,9 +444,9 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
 
   const unsigned mb = L.single ? (unsigned)((L.single_n + kMBlock - 1) / kMBlock)
                                : (unsigned)m.mb_bound;
-  GemmArgs ga{L, m.mbo, m.d, m.f, m.xh, m.xunit, m.a32};
+  GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
   const unsigned wg = (unsigned)((m.f / 32 + kGWaves - 1) / kGWaves);
-  e = launch(5, k_gemm<kGateUp, kMfmaMW>, dim3(wg, mb), dim3(64 * kGWaves), s, ga);
+  e = launch(5, k_gemm<kGateUp>, dim3(wg, mb), dim3(64 * kGWaves), s, ga);
   if (e != hipSuccess) return e;
 
   PackArgs pa{};
@@ -417,9 +458,9 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   e = launch(4, k_pack, dim3((unsigned)((m.slots + 3) / 4)), dim3(256), s, pa);
   if (e != hipSuccess) return e;
 
-  GemmArgs gd{L, m.mbo, m.d, m.f, m.ah, m.aunit, m.y};
+  GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
   const unsigned wd = (unsigned)((m.d / kWaveRows + kGWaves - 1) / kGWaves);
-  return launch(6, k_gemm<kDown, kMfmaMW>, dim3(wd, mb), dim3(64 * kGWaves), s, gd);
+  return launch(6, k_gemm<kDown>, dim3(wd, mb), dim3(64 * kGWaves), s, gd);
 }
 
 }  // namespace moe

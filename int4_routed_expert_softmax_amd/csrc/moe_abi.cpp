@@ -51,6 +51,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.ah = take(Tk * f * sizeof(uint16_t));
   L.aunit = take(Tk * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
+  L.blku = take((cap + Tk / mfma_mblock() + 1) * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -112,6 +113,7 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.ah = at<_Float16>(ws, L.ah);
   m.aunit = at<float>(ws, L.aunit);
   m.mbo = at<int32_t>(ws, L.mbo);
+  m.blk_u = at<int32_t>(ws, L.blku);
   return m;
 }
 
@@ -204,7 +206,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   EL.single = static_cast<const uint8_t*>(expert_blob);
   EL.single_n = n;
   EL.kdiv = 1;
-  if (n > kSmallBatch) {
+  if (n > kSmallBatch && mfma_shape_ok(dm->d, dm->f)) {
     MfmaArgs m = mfma_args(ws, L, dm->d, dm->f);
     m.L = EL;
     m.x = x;
@@ -296,15 +298,21 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
   MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
   MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
-  MfmaArgs m = mfma_args(ws, L, d, f);
-  m.L = EL;
-  m.x = xr;
-  m.x_bf16 = xr_bf16;
-  m.x_rows = T;
-  m.slots = T * k;
-  m.mb_bound = maxU + (T * k + mfma_mblock() - 1) / mfma_mblock();
-  m.y = y;
-  MOE_TRY(launch_ffn_mfma(m, s));
+  if (mfma_shape_ok(d, f)) {
+    MfmaArgs m = mfma_args(ws, L, d, f);
+    m.L = EL;
+    m.x = xr;
+    m.x_bf16 = xr_bf16;
+    m.x_rows = T;
+    m.slots = T * k;
+    m.mb_bound = maxU + (T * k + mfma_mblock() - 1) / mfma_mblock();
+    m.y = y;
+    MOE_TRY(launch_ffn_mfma(m, s));
+  } else {
+    MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
+    MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, s));
+    MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
+  }
   MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
   return MOE_OK;
 }

@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, a32, ah, aunit, mbo, total;
+  size_t xh, xunit, a32, ah, aunit, mbo, blku, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -155,9 +155,12 @@ struct MfmaArgs {
   _Float16* ah;
   float* aunit;
   int32_t* mbo;              // [n_experts + 1]
+  int32_t* blk_u;            // [mb_bound]
   float* y;
 };
 int mfma_mblock();
+// The grouped GEMM needs d and f to be multiples of 512.
+bool mfma_shape_ok(int d, int f);
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s);
 
 }  // namespace moe

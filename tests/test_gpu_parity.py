@@ -64,13 +64,20 @@ def test_tiny_layer():
     small("kE", 128, 64, 16, 16, 3, zipf=False),
     small("wide", 2112, 704, 64, 8, 70),
     small("bf16", 256, 128, 32, 4, 33, x_kind="bf16"),
+    # multi-token batches on the grouped-GEMM path (d, f multiples of 512)
+    small("mfma", 512, 512, 16, 4, 40),
+    small("mfma_ragged", 1024, 512, 64, 8, 75),
+    small("mfma_bf16", 512, 1024, 32, 4, 37, x_kind="bf16"),
+    small("mfma_k1_hot", 512, 512, 8, 1, 70),
 ], ids=lambda w: w.name)
 def test_edge_shapes(w):
     full_parity(w)
 
 
-def test_prenorm_residual_tiny():
-    w = small("chainlike", 256, 128, 16, 2, 5)
+@pytest.mark.parametrize("w", [small("chainlike", 256, 128, 16, 2, 5),
+                               small("chainlike_mfma", 512, 512, 16, 4, 24)],
+                         ids=lambda w: w.name)
+def test_prenorm_residual(w):
     full_parity(w, flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL)
     full_parity(w, flags=moe.MOE_PRENORM_RMS)
     full_parity(w, flags=moe.MOE_RESIDUAL)
@@ -98,8 +105,10 @@ def test_zero_down_with_residual_leaves_h_unchanged():
     assert torch.equal(out.cpu(), torch.from_numpy(h))
 
 
-def test_in_place_residual():
-    w = small("inplace", 256, 128, 16, 2, 4)
+@pytest.mark.parametrize("w", [small("inplace", 256, 128, 16, 2, 4),
+                               small("inplace_mfma", 512, 512, 16, 4, 20)],
+                         ids=lambda w: w.name)
+def test_in_place_residual(w):
     L = DeviceLayer(w)
     h = configs.tokens(w)[0]
     hd = L.x_device(h, False)
