@@ -16,8 +16,8 @@
 // q * s stays a normal fp16 number for 2^-14 <= |s| <= 2^12; smaller scales
 // lose relative precision gradually (fp16 subnormals), larger ones overflow.
 //
-// Work unit: one block (4 waves) = one expert x one M-block of up to 32 of its
-// tokens x 256 weight rows (64 per wave; gate/up: 32 rows of gate and the same
+// Work unit: one block (8 waves) = one expert x one M-block of up to 64 of its
+// tokens x 512 weight rows (64 per wave; gate/up: 32 rows of gate and the same
 // 32 rows of up, so SwiGLU is local to the wave).  K is walked in 128-column
 // stages copied global -> LDS without passing through registers, into a ring
 // of 3 stages; the A and B fragments come from LDS.  d and f must be multiples
@@ -42,7 +42,7 @@ typedef __attribute__((address_space(1))) const u32x4* g_u32x4_ptr;
 
 constexpr int kNt = 4;                                  // 16-row N-tiles per wave
 constexpr int kWaveRows = kNt * 16;                     // weight rows per wave
-constexpr int kGWaves = 4;                              // waves per block
+constexpr int kGWaves = 8;                              // waves per block
 constexpr int kPackExp = 14;                            // packed |x'| < 2^14
 constexpr float kBias = 1032.0f;
 
@@ -209,26 +209,28 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 // LDS: a ring of kRing stages, each covering 128 K-columns (two scale groups),
 //   B  [wave][64 rows][64 B]   codes; row r holds its 16-byte piece p at slot
 //                              p ^ ((r >> 1) & 3)
-//   A  [32 rows][256 B]        packed activations; piece p (8 columns) of row r
+//   A  [64 rows][256 B]        packed activations; piece p (8 columns) of row r
 //                              at slot p ^ (r & 7)
 // followed by per-wave scales, two buffers of [64 rows][8 groups] fp16 (8
 // groups = 4 stages), refilled every 4 stages.
 constexpr int kSC = 128;
 constexpr int kRing = 3;
-constexpr int kMBlock = 32;
+constexpr int kMBlock = 64;
+constexpr int kMT = kMBlock / 16;
 constexpr int kBWave = kWaveRows * (kSC / 2);
 constexpr int kStageB = kGWaves * kBWave;
 constexpr int kStage = kStageB + kMBlock * kSC * 2;
 constexpr int kScaleOff = kRing * kStage;
 constexpr int kScaleWave = 2 * kWaveRows * 16;
 constexpr int kLdsBytes = kScaleOff + kGWaves * kScaleWave;
-static_assert(2 * kLdsBytes <= 160 * 1024, "two blocks per CU");
+static_assert(kLdsBytes <= 160 * 1024, "one block per CU");
 // copies per wave and stage: 4 (codes) + 2 (activations), plus 1 (scales) in
-// stages 0, 4, 8, ...
+// stages 0, 4, 8, ...  Activation rows past the block's tokens copy the last
+// token's row, so every wave issues the same copies.
 constexpr int kCopies = 6;
 
-// One block: 4 waves, each owning 64 weight rows, times one M-block of up to
-// 32 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
+// One block: 8 waves, each owning 64 weight rows, times one M-block of up to
+// 64 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
 template <int MODE>
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
   const uint32_t b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + b_piece * 16u;
   const uint32_t b_half = 16u * (uint32_t)(K / 2);
   // activations, copy i of wave w: lane l -> row 8 w + 4 i + l / 16, slot l % 16
+  // (M-tile w / 2)
   uint32_t a_off[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -322,9 +325,9 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
   };
 
-  f32x4 acc[2][kNt];
+  f32x4 acc[kMT][kNt];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
       b1[nt] = dequant8(w.y, s2);
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
       if (mt < nmt) {
         const uint8_t* ar = base + kStageB + (16 * mt + n) * (kSC * 2);
         const int p0 = 8 * gg + 2 * kg;
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
   // epilogue: lane (n, kg) holds, per tile, tokens 4 kg + i of the M-tile for
   // weight row 16 nt + n
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < kMT; ++mt) {
     if (mt >= nmt) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -30,7 +30,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   const size_t Tk = (size_t)T * k;
   const size_t cap = (size_t)(E < (long)Tk ? E : Tk);
   L.tickets = take(kTicketWords * sizeof(uint32_t));
-  L.z = take((size_t)T * E * sizeof(double));
+  L.z = take((size_t)T * E * (T > kSmallBatch ? kLogSplit : 1) * sizeof(double));
   L.xn = take((size_t)T * d * sizeof(float));
   L.xq = take((size_t)T * (d / kChunk) * kChunkDigitBytes);
   L.xsx = take((size_t)T * (d / kXGroup) * sizeof(int32_t));
@@ -173,10 +173,11 @@ MOE_API int moe_route(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
     ra.bias = bias;
     ra.z = z;
     MOE_TRY(launch_router_front(ra, s));
+    MOE_TRY(launch_topk(z, 1, nullptr, T, dm->n_experts, dm->top_k, topk_idx, topk_w, s));
   } else {
-    MOE_TRY(launch_logits(x, x_dtype == MOE_BF16, T, dm->d, dm->n_experts, w_router, bias, z, s));
+    MOE_TRY(launch_logits(x, x_dtype == MOE_BF16, T, dm->d, dm->n_experts, w_router, z, s));
+    MOE_TRY(launch_topk(z, kLogSplit, bias, T, dm->n_experts, dm->top_k, topk_idx, topk_w, s));
   }
-  MOE_TRY(launch_topk(z, T, dm->n_experts, dm->top_k, topk_idx, topk_w, s));
   return MOE_OK;
 }
 
@@ -295,8 +296,8 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     xr = xn;
     xr_bf16 = 0;
   }
-  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, bias, z, s));
-  MOE_TRY(launch_topk(z, T, E, k, idx, w, s));
+  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, z, s));
+  MOE_TRY(launch_topk(z, kLogSplit, bias, T, E, k, idx, w, s));
   MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
   if (mfma_shape_ok(d, f)) {
     MfmaArgs m = mfma_args(ws, L, d, f);

@@ -109,10 +109,15 @@ struct RouteOut {
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
+// Logits of batches above kSmallBatch tokens: kLogSplit partial sums per
+// logit, zp[s][t][e] (no bias); launch_topk(nsplit = kLogSplit, bias) adds
+// them.  The small-batch front end writes complete logits (nsplit = 1, bias
+// already added).
+constexpr int kLogSplit = 8;
 hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const float* Wr,
-                         const float* bias, double* z, hipStream_t s);
-hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* idx, float* w,
-                       hipStream_t s);
+                         double* zp, hipStream_t s);
+hipError_t launch_topk(const double* z, int nsplit, const float* bias, int T, int E, int k,
+                       int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, int32_t* n_uniq,
                         int32_t* offsets, int32_t* rows, int32_t* stats, hipStream_t s);
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,

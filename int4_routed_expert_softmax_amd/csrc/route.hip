@@ -39,64 +39,96 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h,
 // z[t][e] = sum_i x[t][i] * Wr[e][i] + b[e] in fp64.  A fp32 x fp32 product has
 // at most 48 significant bits, so every product is exact in fp64 and only the
 // (fp64) summation order differs from a sequential sum: ~1e-16 relative, far
-// below the gap between neighbouring logits.  One workgroup per (expert,
-// block of TB tokens); the router row is read once per token block.
-template <int TB>
+// below the gap between neighbouring logits.
+//
+// Batches of more than kSmallBatch tokens: a block = kLogTok tokens x 256
+// experts x one of kLogSplit column ranges, one thread per expert.  Router
+// columns pass through LDS (64 at a time, rows padded against bank
+// conflicts) and each x value is widened to fp64 once per block; thread e
+// writes zp[s][t][e], the partial sum over range s.  k_topk adds the ranges
+// and the bias in a fixed order, so the result does not depend on scheduling.
+constexpr int kLogTok = 16;
+constexpr int kLogCols = 64;
+
 __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int x_bf16, int T,
                                                 int d, int E, const float* __restrict__ Wr,
-                                                const float* __restrict__ bias,
-                                                double* __restrict__ z) {
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * TB;
-  const int nt = min(TB, T - t0);
-  const float4* w4 = reinterpret_cast<const float4*>(Wr + (size_t)e * d);
-  double acc[TB];
+                                                double* __restrict__ zp) {
+  __shared__ float s_w[256][kLogCols + 1];
+  __shared__ __attribute__((aligned(16))) double s_x[kLogCols][kLogTok];
+  const int t = threadIdx.x;
+  const int t0 = blockIdx.x * kLogTok;
+  const int nt = min(kLogTok, T - t0);
+  const int split = blockIdx.y;
+  const int e0 = blockIdx.z * 256;
+  const int e = e0 + t;
+  const int nchunk = d / kLogCols;
+  const int c_begin = split * nchunk / kLogSplit, c_end = (split + 1) * nchunk / kLogSplit;
+  double acc[kLogTok];
 #pragma unroll
-  for (int j = 0; j < TB; ++j) acc[j] = 0.0;
-  const int n4 = d >> 2;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 w = w4[i];
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      if (j < nt) {
-        float4 v;
-        if (x_bf16) {
-          const uint2 b = reinterpret_cast<const uint2*>(
-              static_cast<const uint16_t*>(x) + (size_t)(t0 + j) * d)[i];
-          v.x = __uint_as_float(b.x << 16);
-          v.y = __uint_as_float(b.x & 0xFFFF0000u);
-          v.z = __uint_as_float(b.y << 16);
-          v.w = __uint_as_float(b.y & 0xFFFF0000u);
-        } else {
-          v = reinterpret_cast<const float4*>(static_cast<const float*>(x) + (size_t)(t0 + j) * d)[i];
-        }
-        acc[j] += (double)w.x * (double)v.x;
-        acc[j] += (double)w.y * (double)v.y;
-        acc[j] += (double)w.z * (double)v.z;
-        acc[j] += (double)w.w * (double)v.w;
-      }
+  for (int j = 0; j < kLogTok; ++j) acc[j] = 0.0;
+  for (int c = c_begin; c < c_end; ++c) {
+    const int col0 = c * kLogCols;
+    // 256 rows x 16 float4 of the router, coalesced along each row
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int q = i * 256 + t, row = q >> 4, c4 = q & 15;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e0 + row < E)
+        v = *reinterpret_cast<const float4*>(Wr + (size_t)(e0 + row) * d + col0 + 4 * c4);
+      s_w[row][4 * c4] = v.x;
+      s_w[row][4 * c4 + 1] = v.y;
+      s_w[row][4 * c4 + 2] = v.z;
+      s_w[row][4 * c4 + 3] = v.w;
     }
-  }
-  __shared__ double part[TB][4];
+    // kLogTok tokens x 64 columns of x, widened to fp64, stored [column][token]
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const double s = wave_sum(acc[j]);
-    if ((threadIdx.x & 63) == 0) part[j][threadIdx.x >> 6] = s;
+    for (int i = 0; i < kLogTok * kLogCols / 256; ++i) {
+      const int q = i * 256 + t, tok = q / kLogCols, col = q % kLogCols;
+      double v = 0.0;
+      if (tok < nt) {
+        const size_t at = (size_t)(t0 + tok) * d + col0 + col;
+        v = x_bf16 ? (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[at] << 16)
+                   : (double)static_cast<const float*>(x)[at];
+      }
+      s_x[col][tok] = v;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int col = 0; col < kLogCols; ++col) {
+      const double w = (double)s_w[t][col];
+#pragma unroll
+      for (int j = 0; j < kLogTok; ++j) acc[j] += w * s_x[col][j];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < nt) {
-    const int j = threadIdx.x;
-    const double s = (part[j][0] + part[j][1]) + (part[j][2] + part[j][3]);
-    z[(size_t)(t0 + j) * E + e] = s + (bias ? (double)bias[e] : 0.0);
+  if (e < E) {
+    for (int j = 0; j < nt; ++j) zp[((size_t)split * T + t0 + j) * E + e] = acc[j];
   }
 }
 
-// One wave per token.
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ z, int T, int E, int k,
+// ---------------------------------------------------------------- top-k
+// One wave per token.  With nsplit > 1 the logits are the fixed-order sum of
+// the per-range partials plus the bias, formed in LDS first.
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ z, int nsplit,
+                                              const float* __restrict__ bias, int T, int E, int k,
                                               int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ double s_z[4][kMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  wave_topk(z + (size_t)t * E, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+  const double* zt = z + (size_t)t * E;
+  if (nsplit > 1) {
+    for (int e = lane; e < E; e += 64) {
+      double v = 0.0;
+      for (int s = 0; s < nsplit; ++s) v += z[((size_t)s * T + t) * E + e];
+      s_z[wave][e] = v + (bias ? (double)bias[e] : 0.0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    zt = s_z[wave];
+  }
+  wave_topk(zt, E, k, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------- union
@@ -229,14 +261,14 @@ hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hi
 }
 
 hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const float* Wr,
-                         const float* bias, double* z, hipStream_t s) {
-  if (T <= 1) return launch(1, k_logits<1>, dim3(E, T), dim3(256), s, x, x_bf16, T, d, E, Wr, bias, z);
-  return launch(1, k_logits<8>, dim3(E, (T + 7) / 8), dim3(256), s, x, x_bf16, T, d, E, Wr, bias, z);
+                         double* zp, hipStream_t s) {
+  const dim3 grid((T + kLogTok - 1) / kLogTok, kLogSplit, (E + 255) / 256);
+  return launch(1, k_logits, grid, dim3(256), s, x, x_bf16, T, d, E, Wr, zp);
 }
 
-hipError_t launch_topk(const double* z, int T, int E, int k, int32_t* idx, float* w,
-                       hipStream_t s) {
-  return launch(2, k_topk, dim3((T + 3) / 4), dim3(256), s, z, T, E, k, idx, w);
+hipError_t launch_topk(const double* z, int nsplit, const float* bias, int T, int E, int k,
+                       int32_t* idx, float* w, hipStream_t s) {
+  return launch(2, k_topk, dim3((T + 3) / 4), dim3(256), s, z, nsplit, bias, T, E, k, idx, w);
 }
 
 hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, int32_t* n_uniq,
