@@ -37,10 +37,11 @@ METRIC = "MoE-layer tokens/s + int4 expert-weight HBM GB/s (% peak), d=6144 top-
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 200; chain48: 64)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; chain48: 2)")
     p.add_argument("--workload", default="decode1",
-                   choices=["decode1", "verify8", "prefill512"])
+                   choices=["decode1", "verify8", "prefill512", "chain48"])
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
@@ -101,6 +102,13 @@ def main():
         print(json.dumps({"error": f"--gpus {a.gpus}: this benchmark runs on one GPU only; the "
                           "layer is measured at one GPU's share"}), flush=True)
         sys.exit(2)
+
+    if a.workload == "chain48":
+        a.steps = 64 if a.steps is None else a.steps
+        a.warmup = 2 if a.warmup is None else a.warmup
+        return run_chain(a)
+    a.steps = 200 if a.steps is None else a.steps
+    a.warmup = 10 if a.warmup is None else a.warmup
 
     import torch
 
@@ -210,6 +218,162 @@ def main():
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def run_chain(a):
+    """48 chained decode layers, h <- h + MoE_l(RMSNorm(h)), one token per
+    step, all 48 x 256 experts resident.  Each step starts from a fresh seeded
+    h0; layer 0 reads it and writes h in place for the other 47.  The timed
+    steps are one HIP graph of K x 48 layer calls."""
+    import torch
+
+    import int4_routed_expert_softmax_amd as moe
+    from synth import configs
+
+    w = configs.WORKLOADS["chain48"]
+    dev = torch.device("cuda:0")
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    blob = w.blob_bytes
+    nib_gu = 2 * (w.f * w.d // 2 + 2 * (w.f * w.d // 64))
+    nib_dn = w.f * w.d // 2 + 2 * (w.f * w.d // 64)
+    L = w.layers
+    K, Wm = a.steps, a.warmup
+    eps = 1e-6
+    flags = moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL
+    print(f"bench: chain48 generating + uploading {L * w.n_experts * blob / 1e9:.1f} GB",
+          file=sys.stderr, flush=True)
+    layers = []
+    t_up = time.perf_counter()
+    for l in range(L):
+        Wr, bias = configs.router(w, l)
+        blobs = torch.from_numpy(configs.experts(w, l)).to(dev)
+        table = torch.tensor([blobs[e].data_ptr() for e in range(w.n_experts)], dtype=torch.int64,
+                             device=dev)
+        layers.append((torch.from_numpy(Wr).to(dev), torch.from_numpy(bias).to(dev), blobs, table))
+        print(f"bench: layer {l} resident ({time.perf_counter() - t_up:.0f} s)", file=sys.stderr,
+              flush=True)
+    n_h0 = Wm + K
+    h0 = torch.from_numpy(np.concatenate([configs.tokens(w, s % 64)[0] for s in range(n_h0)])).to(dev)
+    h = torch.empty(n_h0, w.d, dtype=torch.float32, device=dev)
+    stats = torch.zeros(n_h0, L, 1 + w.n_experts, dtype=torch.int32, device=dev)
+    ws = moe.make_workspace(dims, 1, dev)
+
+    def step(s, stream):
+        for l in range(L):
+            Wr, bias, _, table = layers[l]
+            x = h0[s:s + 1] if l == 0 else h[s:s + 1]
+            moe.moe_layer_forward(dims, x, Wr, bias, table, h[s:s + 1], flags=flags, rms_eps=eps,
+                                  stats=stats[s, l], ws=ws, stream=stream)
+
+    cur = torch.cuda.current_stream()
+    for s in range(Wm):
+        step(s, cur.cuda_stream)
+    torch.cuda.synchronize()
+
+    # eager timing of the same K steps (launch-bound reference)
+    t0 = time.perf_counter()
+    for s in range(Wm, Wm + K):
+        step(s, cur.cuda_stream)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / K
+
+    # the timed region: one replay of a graph holding the K steps
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for s in range(Wm, Wm + K):
+            step(s, side.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = (t1 - t0) / K
+    U = stats[Wm:, :, 0].cpu().numpy().astype(np.float64)  # [K][L]
+    weight_bytes_step = U.sum(axis=1).mean() * blob
+
+    # instrumented eager pass: HIP events around every gate/up and down launch
+    n_launch = K * L
+    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(n_launch)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]) for k in ("gateup", "down")}
+    arms = {k: moe.moe_timing_arm(k, *ev[k]) for k in ev}
+    for s in range(Wm, Wm + K):
+        step(s, cur.cuda_stream)
+    torch.cuda.synchronize()
+    counts = {k: moe.moe_timing_disarm(arms[k]) for k in arms}
+    assert all(c == n_launch for c in counts.values()), counts
+    dur = {k: np.array([x.elapsed_time(y) for x, y in zip(*ev[k])]) * 1e-3 for k in ev}
+    u_launch = U.reshape(-1)
+    gu_gbps = float(np.mean(u_launch * nib_gu / dur["gateup"]) / 1e9)
+    dn_gbps = float(np.mean(u_launch * nib_dn / dur["down"]) / 1e9)
+
+    res = {
+        "metric": METRIC,
+        "value": round(1.0 / sec, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "data": "synthetic (seeded; random-init GLM-5.2-shaped experts, 48 fresh layers)",
+        "config": {"workload": f"chain48: {L} chained decode layers h <- h + MoE(RMSNorm(h)), T=1, "
+                               f"d={w.d} f={w.f} E={w.n_experts} top-{w.top_k}, all "
+                               f"{L * w.n_experts} experts resident ({L * w.n_experts * blob / 1e9:.1f} GB), "
+                               f"one HIP graph of {K} steps",
+                   "T": 1, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
+                   "layers": L, "distinct_experts_per_layer": float(U.mean())},
+        "ms_per_step_eager": round(eager * 1e3, 4),
+        "expert_weight_GBps": round(weight_bytes_step / sec / 1e9, 1),
+        "expert_weight_frac_hbm_peak": round(weight_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "gateup (gate+up projections, SwiGLU)",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": committed_traffic("decode1"),
+                     "bytes_per_launch": float(u_launch.mean() * nib_gu),
+                     "avg_launch_us": round(float(dur["gateup"].mean() * 1e6), 3)},
+        "roofline_down": {"bound": "hbm", "achieved": round(dn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
+                          "bytes_per_launch": float(u_launch.mean() * nib_dn),
+                          "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_chain(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_chain(w, seconds):
+    """The CPU oracle on the chain: layer after layer of step 0 (RMSNorm,
+    residual), each layer's experts generated on demand, until `seconds`
+    have passed; tokens/s = layers/s / 48."""
+    import oracle
+    from synth import configs
+
+    h, _ = configs.tokens(w, 0)
+    n = 0
+    t_ffn = 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n < w.layers:
+        Wr, bias = configs.router(w, n)
+        idx, _, _ = oracle.route(oracle.rmsnorm(h, 1e-6), Wr, bias, w.top_k)
+        table = [None] * w.n_experts
+        for e in set(int(e) for e in idx.reshape(-1)):
+            table[e] = configs.one_expert(w, n, e)
+        t1 = time.perf_counter()
+        h = oracle.layer_forward(h, Wr, bias, table, w.d, w.f, w.top_k, flags=3,
+                                 eps=1e-6)["out"].astype(np.float32)
+        t_ffn += time.perf_counter() - t1
+        n += 1
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n / t_ffn / w.layers, 5), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} chained layers of step 0 (fp64 C oracle, OpenMP over output rows; "
+                      f"expert generation excluded), {t_ffn:.1f} s"}
 
 
 def cpu_baseline(w, seconds):
