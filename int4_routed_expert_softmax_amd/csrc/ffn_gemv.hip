@@ -193,6 +193,10 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     __shared__ SmallRoute sr;
     const int T = ro.T, E = ro.E, k = ro.k;
     const int n = T * k;
+    // the expert table travels alongside the routing, so the blob address is
+    // in LDS once the union is known
+    __shared__ const uint8_t* s_tab[kMaxE];
+    for (int e = threadIdx.x; e < E; e += 256 * C) s_tab[e] = L.table[e];
     for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
     __syncthreads();
     if (wave == 0) wave_union_small(sr.idx, n, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
       }
     }
     if (u >= sr.n) return;
-    ex.blob = L.table[sr.uniq[u]];
+    ex.blob = s_tab[sr.uniq[u]];
     ex.beg = sr.offsets[u];
     ex.n = sr.offsets[u + 1] - ex.beg;
     list = sr.rows;
@@ -361,41 +365,97 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(ExpertList L, in
   const int nch = f / kChunk, nga = f / kGroup;
   const size_t fd = (size_t)f * d;
   __shared__ float s_y[kSmallPicks][kDcRows];
+  // union entries and their blob addresses, gathered once per block
+  __shared__ const uint8_t* s_blob[kSmallPicks];
+  for (int i = threadIdx.x; i < U; i += 64 * kDcWaves) s_blob[i] = L.table[L.uniq[i]];
+  __syncthreads();
 
-  for (int u = wave; u < U; u += kDcWaves) {
-    const ExpertRef ex = expert_ref(L, u);
-    const uint8_t* dcode = ex.blob + fd + (size_t)r0 * (f / 2);
-    const _Float16* dsc =
-        reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
-    for (int p = 0; p * 64 < nch; ++p) {
-      const int c = p * 64 + lane;
-      const bool act = c < nch;
-      const unsigned cl = act ? (unsigned)c : 0u;
-      uint4 wd[kDcRows];
-      float sd[kDcRows];
+  if constexpr (NT == 1) {
+    // one token per expert: a wave takes two experts at a time and issues all
+    // of both experts' loads before using any
+    for (int u = wave; u < U; u += 2 * kDcWaves) {
+      const int u2 = u + kDcWaves;
+      const bool two = u2 < U;
+      ExpertRef e0, e1;
+      e0.blob = s_blob[u];
+      e0.beg = L.offsets[u];
+      e1.blob = s_blob[two ? u2 : u];
+      e1.beg = L.offsets[two ? u2 : u];
+      const int slot0 = L.list[e0.beg], slot1 = L.list[e1.beg];
+      const uint8_t* dc0 = e0.blob + fd + (size_t)r0 * (f / 2);
+      const uint8_t* dc1 = e1.blob + fd + (size_t)r0 * (f / 2);
+      const _Float16* ds0 = reinterpret_cast<const _Float16*>(e0.blob + 3 * fd / 2) +
+                            2 * (fd / kGroup) + (size_t)r0 * nga;
+      const _Float16* ds1 = reinterpret_cast<const _Float16*>(e1.blob + 3 * fd / 2) +
+                            2 * (fd / kGroup) + (size_t)r0 * nga;
+      for (int p = 0; p * 64 < nch; ++p) {
+        const int c = p * 64 + lane;
+        const bool act = c < nch;
+        const unsigned cl = act ? (unsigned)c : 0u;
+        uint4 w0[kDcRows], w1[kDcRows];
+        float s0[kDcRows], s1[kDcRows];
 #pragma unroll
-      for (int b = 0; b < kDcRows; ++b) {
-        wd[b] = stream_load16(dcode + (size_t)b * (f / 2) + cl * 16u);
-        sd[b] = stream_scale(dsc + (size_t)b * nga + cl / 2u);
-      }
-      for (int t0 = 0; t0 < ex.n; t0 += NT) {
-        const int nt = min(NT, ex.n - t0);
-        int slot[NT];
-        ChunkAct aa[NT];
+        for (int b = 0; b < kDcRows; ++b) {
+          w0[b] = stream_load16(dc0 + (size_t)b * (f / 2) + cl * 16u);
+          w1[b] = stream_load16(dc1 + (size_t)b * (f / 2) + cl * 16u);
+          s0[b] = stream_scale(ds0 + (size_t)b * nga + cl / 2u);
+          s1[b] = stream_scale(ds1 + (size_t)b * nga + cl / 2u);
+        }
+        const ChunkAct a0 = load_act(ad, slot0, nch, c, act);
+        const ChunkAct a1 = load_act(ad, slot1, nch, c, act && two);
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          slot[j] = j < nt ? L.list[ex.beg + t0 + j] : 0;
-          aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
+        for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(w0[b], s0[b], a0);
+        float tot = reduce8(v, lane);
+        if ((lane & 7) == 0) {
+          float* dst = &s_y[slot0][lane >> 3];
+          *dst = p == 0 ? tot : *dst + tot;
         }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          float v[8];
-#pragma unroll
-          for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
-          const float tot = reduce8(v, lane);
-          if ((lane & 7) == 0 && j < nt) {
-            float* dst = &s_y[slot[j]][lane >> 3];
-            *dst = p == 0 ? tot : *dst + tot;
+        for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(w1[b], s1[b], a1);
+        tot = reduce8(v, lane);
+        if (two && (lane & 7) == 0) {
+          float* dst = &s_y[slot1][lane >> 3];
+          *dst = p == 0 ? tot : *dst + tot;
+        }
+      }
+    }
+  } else {
+    for (int u = wave; u < U; u += kDcWaves) {
+      const ExpertRef ex = expert_ref(L, u);
+      const uint8_t* dcode = ex.blob + fd + (size_t)r0 * (f / 2);
+      const _Float16* dsc =
+          reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+      for (int p = 0; p * 64 < nch; ++p) {
+        const int c = p * 64 + lane;
+        const bool act = c < nch;
+        const unsigned cl = act ? (unsigned)c : 0u;
+        uint4 wd[kDcRows];
+        float sd[kDcRows];
+  #pragma unroll
+        for (int b = 0; b < kDcRows; ++b) {
+          wd[b] = stream_load16(dcode + (size_t)b * (f / 2) + cl * 16u);
+          sd[b] = stream_scale(dsc + (size_t)b * nga + cl / 2u);
+        }
+        for (int t0 = 0; t0 < ex.n; t0 += NT) {
+          const int nt = min(NT, ex.n - t0);
+          int slot[NT];
+          ChunkAct aa[NT];
+  #pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            slot[j] = j < nt ? L.list[ex.beg + t0 + j] : 0;
+            aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
+          }
+  #pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            float v[8];
+  #pragma unroll
+            for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
+            const float tot = reduce8(v, lane);
+            if ((lane & 7) == 0 && j < nt) {
+              float* dst = &s_y[slot[j]][lane >> 3];
+              *dst = p == 0 ? tot : *dst + tot;
+            }
           }
         }
       }
