@@ -63,12 +63,17 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}), flush=True)
 
 
+# Sources the decode gate/up kernel is built from.
+GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "select.h")
+
+
 def kernel_source_hash():
-    """sha256 of the HIP sources: a counter summary is only reused while it matches."""
+    """sha256 of the gate/up kernel's sources: a counter summary is only
+    reused while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_routed_expert_softmax_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GATEUP_SOURCES:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
