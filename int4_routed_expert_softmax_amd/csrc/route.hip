@@ -164,18 +164,54 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     return a.x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.x)[(size_t)t * d + i] << 16)
                     : static_cast<const float*>(a.x)[(size_t)t * d + i];
   };
+  auto xval4 = [&](int t, int i4) -> float4 {
+    if (a.x_bf16) {
+      const uint2 b = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.x) + (size_t)t * d)[i4];
+      return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                         __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+    }
+    return reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * d)[i4];
+  };
+  // Rows of up to 8192 columns stay in registers (8 float4 per thread): the
+  // router row is requested before the RMSNorm reduction so the two overlap,
+  // and a single token's x is read once.
+  constexpr int kReg = 8;
+  const int n4 = d >> 2;
+  const bool in_regs = n4 <= 256 * kReg;
+  float4 wr[kReg], xr[kReg];
+  if (in_regs) {
+#pragma unroll
+    for (int m = 0; m < kReg; ++m) {
+      const int i4 = tid + 256 * m;
+      if (e < E && i4 < n4) wr[m] = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d)[i4];
+      if (TB == 1 && i4 < n4) xr[m] = xval4(0, i4);
+    }
+  }
   if (a.prenorm) {
     // r_t = 1 / sqrt(mean(h_t^2) + eps) in fp64
     double ss[TB];
 #pragma unroll
     for (int j = 0; j < TB; ++j) ss[j] = 0.0;
-    for (int i = tid; i < d; i += 256)
+    if (TB == 1 && in_regs) {
 #pragma unroll
-      for (int j = 0; j < TB; ++j)
-        if (j < T) {
-          const double h = xval(j, i);
-          ss[j] += h * h;
+      for (int m = 0; m < kReg; ++m) {
+        if (tid + 256 * m < n4) {
+          const float4 v = xr[m];
+          ss[0] += (double)v.x * (double)v.x;
+          ss[0] += (double)v.y * (double)v.y;
+          ss[0] += (double)v.z * (double)v.z;
+          ss[0] += (double)v.w * (double)v.w;
         }
+      }
+    } else {
+      for (int i = tid; i < d; i += 256)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+          if (j < T) {
+            const double h = xval(j, i);
+            ss[j] += h * h;
+          }
+    }
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       const double sj = wave_sum(ss[j]);
@@ -189,10 +225,8 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     __syncthreads();
   }
   // the value the router and the experts see: x, or RMSNorm(x) rounded to f32
-  auto xin = [&](int t, size_t i) -> float {
-    const float v = xval(t, i);
-    return a.prenorm ? (float)((double)v * s_r[t]) : v;
-  };
+  auto norm = [&](int t, float v) -> float { return a.prenorm ? (float)((double)v * s_r[t]) : v; };
+  auto xin = [&](int t, size_t i) -> float { return norm(t, xval(t, i)); };
 
   if (e >= E) {
     // workgroups past the last expert: the digit split, one wave per 64
@@ -205,19 +239,39 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     }
     return;
   }
-  const float4* w4 = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d);
   double acc[TB];
 #pragma unroll
   for (int j = 0; j < TB; ++j) acc[j] = 0.0;
-  for (int i = tid; i < d / 4; i += 256) {
-    const float4 w = w4[i];
+  if (in_regs) {
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      if (j < T) {
-        acc[j] += (double)w.x * (double)xin(j, 4 * i);
-        acc[j] += (double)w.y * (double)xin(j, 4 * i + 1);
-        acc[j] += (double)w.z * (double)xin(j, 4 * i + 2);
-        acc[j] += (double)w.w * (double)xin(j, 4 * i + 3);
+    for (int m = 0; m < kReg; ++m) {
+      const int i4 = tid + 256 * m;
+      if (i4 < n4) {
+        const float4 w = wr[m];
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+          if (j < T) {
+            const float4 v = TB == 1 ? xr[m] : xval4(j, i4);
+            acc[j] += (double)w.x * (double)norm(j, v.x);
+            acc[j] += (double)w.y * (double)norm(j, v.y);
+            acc[j] += (double)w.z * (double)norm(j, v.z);
+            acc[j] += (double)w.w * (double)norm(j, v.w);
+          }
+        }
+      }
+    }
+  } else {
+    const float4* w4 = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d);
+    for (int i = tid; i < n4; i += 256) {
+      const float4 w = w4[i];
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        if (j < T) {
+          acc[j] += (double)w.x * (double)xin(j, 4 * i);
+          acc[j] += (double)w.y * (double)xin(j, 4 * i + 1);
+          acc[j] += (double)w.z * (double)xin(j, 4 * i + 2);
+          acc[j] += (double)w.w * (double)xin(j, 4 * i + 3);
+        }
       }
     }
   }
