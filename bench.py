@@ -220,9 +220,61 @@ def main():
                           "bytes_per_launch": float(dn_bytes.mean()),
                           "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
     }
+    if w.T > 8:
+        res["mfma"] = mfma_figures(moe, torch, w, layers[0], dims, gu_bytes, dur, U)
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+
+
+def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
+    """fp16 MFMA throughput of the grouped gate/up GEMM: for the whole layer
+    (useful flops 2 * T*k * d * 2f over its measured launches), and for one
+    expert alone at M = 512 tokens and at the token count of the hottest
+    expert of the batch (moe_expert_ffn, same kernels), each timed with HIP
+    events over 20 launches.  One expert fills 8 x ceil(M/64) blocks of 8
+    waves, one per CU, so its figure is also given per occupied CU."""
+    import oracle
+    from synth import configs
+
+    dev = torch.device("cuda:0")
+    layer_flops = 2.0 * w.T * w.top_k * w.d * 2 * w.f
+    layer_tflops = layer_flops / float(dur["gateup"].mean()) / 1e12
+    x, bf = configs.tokens(w, 0)
+    Wr, bias = configs.router(w, 0)
+    idx, _, _ = oracle.route(x, Wr, bias, w.top_k, x_bf16=bf)
+    cnt = np.bincount(idx.reshape(-1), minlength=w.n_experts)
+    hot_e = int(np.argmax(cnt))
+    xd = L0["x"]
+    out = {"layer_gateup_tflops": round(layer_tflops, 1),
+           "layer_gateup_frac": round(layer_tflops / MFMA_PEAK_TFLOPS, 4),
+           "peak_tflops": MFMA_PEAK_TFLOPS, "dtype": "fp16 x fp16 -> fp32 (v_mfma_f32_16x16x32_f16)"}
+    for label, e, n in (("m512", 0, 512), ("hot", hot_e, int(cnt[hot_e]))):
+        blob = L0["blobs"][e]
+        y = torch.empty(n, w.d, dtype=torch.float32, device=dev)
+        ws = moe.make_workspace(dims, n, dev)
+        for _ in range(3):
+            moe.moe_expert_ffn(dims, blob, xd[:n], None, n, y, ws)
+        reps = 20
+        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(reps)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(reps)])
+        h = moe.moe_timing_arm("gateup", *ev)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            moe.moe_expert_ffn(dims, blob, xd[:n], None, n, y, ws)
+        torch.cuda.synchronize()
+        assert moe.moe_timing_disarm(h) == reps
+        t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
+        flops = 2.0 * n * w.d * 2 * w.f
+        blocks = (w.f // 32 // 8) * ((n + 63) // 64)
+        tf = flops / t / 1e12
+        out[label] = {"expert": e, "M": n, "gateup_us": round(t * 1e6, 2), "tflops": round(tf, 1),
+                      "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "blocks": blocks,
+                      "frac_per_occupied_cu": round(tf / (MFMA_PEAK_TFLOPS * min(blocks, 256) / 256), 4)}
+    return out
 
 
 def run_chain(a):
