@@ -41,68 +41,95 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h,
 // (fp64) summation order differs from a sequential sum: ~1e-16 relative, far
 // below the gap between neighbouring logits.
 //
-// Batches of more than kSmallBatch tokens: a block = kLogTok tokens x 256
-// experts x one of kLogSplit column ranges, one thread per expert.  Router
-// columns pass through LDS (64 at a time, rows padded against bank
-// conflicts) and each x value is widened to fp64 once per block; thread e
-// writes zp[s][t][e], the partial sum over range s.  k_topk adds the ranges
-// and the bias in a fixed order, so the result does not depend on scheduling.
-constexpr int kLogTok = 16;
-constexpr int kLogCols = 64;
+// Batches of more than kSmallBatch tokens: a fp64 GEMM on the matrix cores
+// (v_mfma_f64_16x16x4_f64: exact fp64 products, fp64 sums).  A block = 32
+// tokens x 64 experts x one of kLogSplit column ranges, 4 waves of 16
+// experts x 32 tokens.  64-column chunks of x and of the router rows are
+// widened to fp64 into LDS, transposed to [column][token|expert] (so a lane's
+// MFMA operand is one 8-byte read), with the next chunk already loaded into
+// registers.  zp[s][t][e] is the partial sum over range s; k_topk adds the
+// ranges and the bias in a fixed order, so the result does not depend on
+// scheduling.
+constexpr int kLgT = 32;
+constexpr int kLgE = 64;
+constexpr int kLgC = 64;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int x_bf16, int T,
                                                 int d, int E, const float* __restrict__ Wr,
                                                 double* __restrict__ zp) {
-  __shared__ float s_w[256][kLogCols + 1];
-  __shared__ __attribute__((aligned(16))) double s_x[kLogCols][kLogTok];
-  const int t = threadIdx.x;
-  const int t0 = blockIdx.x * kLogTok;
-  const int nt = min(kLogTok, T - t0);
+  __shared__ double s_x[kLgC][kLgT + 1];
+  __shared__ double s_w[kLgC][kLgE + 1];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t0 = blockIdx.x * kLgT;
+  const int nt = min(kLgT, T - t0);
   const int split = blockIdx.y;
-  const int e0 = blockIdx.z * 256;
-  const int e = e0 + t;
-  const int nchunk = d / kLogCols;
+  const int e0 = blockIdx.z * kLgE;
+  const int nchunk = d / kLgC;
   const int c_begin = split * nchunk / kLogSplit, c_end = (split + 1) * nchunk / kLogSplit;
-  double acc[kLogTok];
+
+  // staging: x value q = i * 256 + t is token q / 64, column q % 64; router
+  // value q is expert q / 64, column q % 64 (coalesced along the columns)
+  constexpr int kXPer = kLgT * kLgC / 256, kWPer = kLgE * kLgC / 256;
+  float xv[kXPer], wv[kWPer];
+  auto fetch = [&](int c) {
+    const int col0 = c * kLgC;
 #pragma unroll
-  for (int j = 0; j < kLogTok; ++j) acc[j] = 0.0;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int col0 = c * kLogCols;
-    // 256 rows x 16 float4 of the router, coalesced along each row
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int q = i * 256 + t, row = q >> 4, c4 = q & 15;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + row < E)
-        v = *reinterpret_cast<const float4*>(Wr + (size_t)(e0 + row) * d + col0 + 4 * c4);
-      s_w[row][4 * c4] = v.x;
-      s_w[row][4 * c4 + 1] = v.y;
-      s_w[row][4 * c4 + 2] = v.z;
-      s_w[row][4 * c4 + 3] = v.w;
-    }
-    // kLogTok tokens x 64 columns of x, widened to fp64, stored [column][token]
-#pragma unroll
-    for (int i = 0; i < kLogTok * kLogCols / 256; ++i) {
-      const int q = i * 256 + t, tok = q / kLogCols, col = q % kLogCols;
-      double v = 0.0;
+    for (int i = 0; i < kXPer; ++i) {
+      const int q = i * 256 + t, tok = q / kLgC, col = q % kLgC;
+      float v = 0.0f;
       if (tok < nt) {
         const size_t at = (size_t)(t0 + tok) * d + col0 + col;
-        v = x_bf16 ? (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[at] << 16)
-                   : (double)static_cast<const float*>(x)[at];
+        v = x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[at] << 16)
+                   : static_cast<const float*>(x)[at];
       }
-      s_x[col][tok] = v;
+      xv[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int q = i * 256 + t, ex = q / kLgC, col = q % kLgC;
+      wv[i] = e0 + ex < E ? Wr[(size_t)(e0 + ex) * d + col0 + col] : 0.0f;
+    }
+  };
+
+  f64x4 acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+  if (c_begin < c_end) fetch(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int q = i * 256 + t;
+      s_x[q % kLgC][q / kLgC] = (double)xv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int q = i * 256 + t;
+      s_w[q % kLgC][q / kLgC] = (double)wv[i];
     }
     __syncthreads();
-#pragma unroll 4
-    for (int col = 0; col < kLogCols; ++col) {
-      const double w = (double)s_w[t][col];
+    if (c + 1 < c_end) fetch(c + 1);
+    // lane l: A = x[token 16 mt + l % 16][column k], B = Wr[expert 16 w + l % 16][column k],
+    // k = 4 ks + l / 16
 #pragma unroll
-      for (int j = 0; j < kLogTok; ++j) acc[j] += w * s_x[col][j];
+    for (int ks = 0; ks < kLgC / 4; ++ks) {
+      const int k = 4 * ks + (lane >> 4);
+      const double b = s_w[k][16 * wave + (lane & 15)];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(s_x[k][16 * mt + (lane & 15)], b, acc[mt], 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane l, element i: token 16 mt + l / 16 + 4 i, expert 16 w + l % 16
+  const int e = e0 + 16 * wave + (lane & 15);
   if (e < E) {
-    for (int j = 0; j < nt; ++j) zp[((size_t)split * T + t0 + j) * E + e] = acc[j];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * mt + (lane >> 4) + 4 * i;
+        if (tok < nt) zp[((size_t)split * T + t0 + tok) * E + e] = acc[mt][i];
+      }
   }
 }
 
@@ -316,7 +343,7 @@ hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hi
 
 hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const float* Wr,
                          double* zp, hipStream_t s) {
-  const dim3 grid((T + kLogTok - 1) / kLogTok, kLogSplit, (E + 255) / 256);
+  const dim3 grid((T + kLgT - 1) / kLgT, kLogSplit, (E + kLgE - 1) / kLgE);
   return launch(1, k_logits, grid, dim3(256), s, x, x_bf16, T, d, E, Wr, zp);
 }
 
