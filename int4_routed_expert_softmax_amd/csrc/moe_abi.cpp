@@ -30,7 +30,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   const size_t Tk = (size_t)T * k;
   const size_t cap = (size_t)(E < (long)Tk ? E : Tk);
   L.tickets = take(kTicketWords * sizeof(uint32_t));
-  L.z = take((size_t)T * E * (T > kSmallBatch ? kLogSplit : 1) * sizeof(double));
+  L.z = take((size_t)T * E * (small_batch(T, k) ? 1 : kLogSplit) * sizeof(double));
   L.xn = take((size_t)T * d * sizeof(float));
   L.xq = take((size_t)T * (d / kChunk) * kChunkDigitBytes);
   L.xsx = take((size_t)T * (d / kXGroup) * sizeof(int32_t));
@@ -264,7 +264,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.kdiv = k;
   const int maxU = E < T * k ? E : T * k;
 
-  if (T <= kSmallBatch && T * k <= kSmallPicks) {
+  if (small_batch(T, k)) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (recomputed per
     // block) and gate/up; 3: down + combine
     RouterArgs ra{};

@@ -95,6 +95,10 @@ constexpr int kSmallBatch = 8;
 // The small-batch path recomputes routing inside the gate/up kernel with one
 // wave for the union, so it needs T * k <= 64 picks.
 constexpr int kSmallPicks = 64;
+// Whether moe_layer_forward takes the three-launch small-batch path.  Every
+// other batch (more tokens, or more than kSmallPicks picks) has its logits
+// computed as kLogSplit partial sums, which the workspace must hold.
+inline bool small_batch(int T, int k) { return T <= kSmallBatch && T * k <= kSmallPicks; }
 
 // Routing results of a small batch: the gate/up kernel recomputes top-k and
 // the union from the logits at the start of every block (cheaper than a

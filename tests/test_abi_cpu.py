@@ -49,6 +49,16 @@ def test_blob_and_workspace_sizes():
     assert moe.workspace_bytes(GLM, 0) == 0
 
 
+@pytest.mark.parametrize("T,k", [(1, 32), (3, 32), (8, 9), (9, 1), (64, 8)])
+def test_workspace_holds_split_logits(T, k):
+    # Batches past the small-batch path (T > 8 or T * k > 64 picks) keep 8
+    # fp64 partial sums per logit; narrow d and f so nothing else hides it.
+    dims = moe.Dims(64, 64, 1024, k)
+    small = T <= 8 and T * k <= 64
+    need = T * 1024 * 8 * (1 if small else 8)
+    assert moe.workspace_bytes(dims, T) >= need
+
+
 def call_route(dims, x=FAKE, dtype=moe.MOE_F32, T=1, wr=FAKE, idx=FAKE, w=FAKE, ws=FAKE,
                ws_bytes=None):
     if ws_bytes is None:

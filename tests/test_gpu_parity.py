@@ -69,6 +69,12 @@ def test_tiny_layer():
     small("mfma_ragged", 1024, 512, 64, 8, 75),
     small("mfma_bf16", 512, 1024, 32, 4, 37, x_kind="bf16"),
     small("mfma_k1_hot", 512, 512, 8, 1, 70),
+    # the ABI's limits: 1024 experts, top-32 (a batch union beyond one wave)
+    small("maxE_k32", 256, 128, 1024, 32, 3),
+    small("maxE_k32_mfma", 512, 512, 1024, 32, 12, zipf=False),
+    # a long batch: 1500 tokens x 8 picks over 256 experts, uniform and skewed
+    small("long1500", 512, 512, 256, 8, 1500, zipf=False),
+    small("long1500_zipf", 512, 512, 256, 8, 1500),
 ], ids=lambda w: w.name)
 def test_edge_shapes(w):
     full_parity(w)
