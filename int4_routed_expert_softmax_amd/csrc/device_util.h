@@ -26,6 +26,8 @@ __device__ __forceinline__ float dpp(float v) {
 // After the first two every quad is uniform, so the mirrors pair whole quads
 // and then whole half-rows.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// quad_perm [3,2,1,0] (lane ^ 3) and row_ror:8 (lane ^ 8 inside a row of 16)
+constexpr int kDppXor3 = 0x1B, kDppRor8 = 0x128;
 
 // Sum over the 64 lanes, the same value in every lane, in a fixed order:
 // butterflies inside each row of 16 lanes (DPP quad permutes and mirrors),
@@ -68,10 +70,28 @@ __device__ __forceinline__ float reduce8(const float (&v)[8], int lane) {
   return c;
 }
 
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int hi = dpp_i<kCtrl>((int)(b >> 32)), lo = dpp_i<kCtrl>((int)b);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// fp64 sum over the 64 lanes in a fixed order, the same in every lane:
+// butterflies inside each row of 16 lanes, then the four row sums in order.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -113,6 +113,9 @@ struct SmallRoute {
   int32_t rows[kSmallPicks];
   int32_t sorted[kSmallPicks];
   int32_t n;
+  // per token, the best k of each 64-expert group (logit, id)
+  double cz[kSmallBatch][64];
+  int32_t ce[kSmallBatch][64];
 };
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
@@ -197,7 +200,34 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     // in LDS once the union is known
     __shared__ const uint8_t* s_tab[kMaxE];
     for (int e = threadIdx.x; e < E; e += 256 * C) s_tab[e] = L.table[e];
-    for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
+    const int G = (E + 63) / 64;
+    if (G * k <= 64) {
+      // each 64-expert group of each token sorted by its own wave, then the
+      // token's G * k survivors sorted by one wave: the top k of a token are
+      // among the top k of its groups
+      for (int task = wave; task < T * G; task += 4 * C) {
+        const int t = task / G, g = task - t * G;
+        const int e = g * 64 + lane;
+        double z = e < E ? ro.z[(size_t)t * E + e] : -INFINITY;
+        int id = e < E ? e : INT_MAX;
+        wave_sort64(z, id);
+        if (lane < k) {
+          sr.cz[t][g * k + lane] = z;
+          sr.ce[t][g * k + lane] = id;
+        }
+      }
+      __syncthreads();
+      for (int t = wave; t < T; t += 4 * C) {
+        double z = lane < G * k ? sr.cz[t][lane] : -INFINITY;
+        int id = lane < G * k ? sr.ce[t][lane] : INT_MAX;
+        if (G > 1) wave_sort64(z, id);
+        // k <= E puts k real experts first; the clamp only keeps a table
+        // lookup in bounds should that ever fail
+        topk_emit(z, (unsigned)id < (unsigned)E ? id : 0, k, sr.idx + t * k, sr.w + t * k);
+      }
+    } else {
+      for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
+    }
     __syncthreads();
     if (wave == 0) wave_union_small(sr.idx, n, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
     __syncthreads();

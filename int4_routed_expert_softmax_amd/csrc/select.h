@@ -22,10 +22,9 @@ namespace moe {
 // ---------------------------------------------------------------- top-k
 // Selection order: larger logit first, equal logits -> lower expert id.
 // e == INT_MAX marks "no candidate", ranked after everything.
+// (Bitwise, not short-circuit, so it compiles to compares and selects.)
 __device__ __forceinline__ bool ranks_before(double bz, int be, double az, int ae) {
-  if (be == INT_MAX) return false;
-  if (ae == INT_MAX) return true;
-  return bz > az || (bz == az && be < ae);
+  return (be != INT_MAX) & ((ae == INT_MAX) | (bz > az) | ((bz == az) & (be < ae)));
 }
 
 template <int kCtrl>
@@ -68,6 +67,72 @@ __device__ __forceinline__ void wave_argmax(double& z, int& e) {
   }
   z = bz;
   e = be;
+}
+
+// Lanes 0..k-1 hold the chosen (logit, id) pairs in selection order: write
+// the ids and the renormalised softmax weights exp(z_j - z_0) / sum over the
+// chosen of exp(z_j' - z_0) (fp64, rounded once to fp32).
+__device__ __forceinline__ void topk_emit(double my_z, int my_e, int k, int32_t* idx_out,
+                                          float* w_out) {
+  const int lane = threadIdx.x & 63;
+  const double z0 = readlane_f64(my_z, 0);
+  const double p = lane < k ? exp(my_z - z0) : 0.0;
+  const double den = wave_sum(p);
+  if (lane < k) {
+    idx_out[lane] = my_e;
+    w_out[lane] = (float)(p / den);
+  }
+}
+
+// ---------------------------------------------------------------- bitonic
+// The value of lane ^ J: DPP inside a row of 16 lanes (J = 4 as a quad
+// reversal followed by a half-row mirror: i ^ 3 ^ 7 = i ^ 4), a cross-lane
+// permute across rows.
+template <int J>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (J == 1) return dpp_i<kDppXor1>(v);
+  else if constexpr (J == 2) return dpp_i<kDppXor2>(v);
+  else if constexpr (J == 4) return dpp_i<kDppHalfMirror>(dpp_i<kDppXor3>(v));
+  else if constexpr (J == 8) return dpp_i<kDppRor8>(v);
+  else return __shfl_xor(v, J, 64);
+}
+
+// Selection order without branches: larger logit first, equal logits ->
+// lower id.  Padding is (-inf, INT_MAX), which every real pair precedes.
+__device__ __forceinline__ bool goes_first(double bz, int be, double az, int ae) {
+  return (bz > az) | ((bz == az) & (be < ae));
+}
+
+// One compare-exchange of a bitonic network: this lane and lane ^ J keep the
+// earlier (keep_first) or the later of their two pairs.  Two padding pairs
+// are equal, so exchanging them changes nothing.
+template <int J>
+__device__ __forceinline__ void bitonic_step(double& z, int& e, bool keep_first) {
+  const long long b = __double_as_longlong(z);
+  const int hi = lane_xor<J>((int)(b >> 32));
+  const int lo = lane_xor<J>((int)b);
+  const int oe = lane_xor<J>(e);
+  const double oz = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+  const bool take = goes_first(oz, oe, z, e) == keep_first;
+  z = take ? oz : z;
+  e = take ? oe : e;
+}
+
+// Sorts the wave's 64 (logit, id) pairs, one per lane, into selection order
+// (lane 0 first) with Batcher's bitonic network: in stage S, blocks of S
+// lanes alternate direction; step J compares lanes i and i ^ J.  Ids must be
+// distinct apart from the (-inf, INT_MAX) padding, so the order is total.
+__device__ __forceinline__ void wave_sort64(double& z, int& e) {
+  const int lane = threadIdx.x & 63;
+#define MOE_BSTEP(S, J) bitonic_step<J>(z, e, ((lane & (J)) == 0) == ((lane & (S)) == 0))
+  MOE_BSTEP(2, 1);
+  MOE_BSTEP(4, 2); MOE_BSTEP(4, 1);
+  MOE_BSTEP(8, 4); MOE_BSTEP(8, 2); MOE_BSTEP(8, 1);
+  MOE_BSTEP(16, 8); MOE_BSTEP(16, 4); MOE_BSTEP(16, 2); MOE_BSTEP(16, 1);
+  MOE_BSTEP(32, 16); MOE_BSTEP(32, 8); MOE_BSTEP(32, 4); MOE_BSTEP(32, 2); MOE_BSTEP(32, 1);
+  MOE_BSTEP(64, 32); MOE_BSTEP(64, 16); MOE_BSTEP(64, 8); MOE_BSTEP(64, 4); MOE_BSTEP(64, 2);
+  MOE_BSTEP(64, 1);
+#undef MOE_BSTEP
 }
 
 constexpr int kMaxPerLane = 16;  // E <= 1024
@@ -113,13 +178,7 @@ __device__ __forceinline__ void wave_topk_n(const double* zt, int E, int k, int3
       my_e = be;
     }
   }
-  const double z0 = readlane_f64(my_z, 0);
-  const double p = lane < k ? exp(my_z - z0) : 0.0;
-  const double den = wave_sum(p);
-  if (lane < k) {
-    idx_out[lane] = my_e;
-    w_out[lane] = (float)(p / den);
-  }
+  topk_emit(my_z, my_e, k, idx_out, w_out);
 }
 
 __device__ __forceinline__ void wave_topk(const double* zt, int E, int k, int32_t* idx_out,
