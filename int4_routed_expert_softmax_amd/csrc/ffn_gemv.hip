@@ -118,6 +118,42 @@ struct SmallRoute {
   int32_t ce[kSmallBatch][64];
 };
 
+// Top-k of a small batch by the block's waves (G * K2 <= 64, G = groups of
+// 64 experts, K2 = k rounded up to a power of two).  Stage 1: the best K2 of
+// every group of every token, one wave per group, stored as runs of K2 with
+// odd groups reversed.  Stage 2: one wave per token merges its runs; lanes
+// 0..k-1 are the token's top k (its best k are among its groups' best K2).
+template <int K2>
+__device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, int wave,
+                                           int nwaves) {
+  const int T = ro.T, E = ro.E, k = ro.k;
+  const int lane = threadIdx.x & 63;
+  const int G = (E + 63) / 64;
+  for (int task = wave; task < T * G; task += nwaves) {
+    const int t = task / G, g = task - t * G;
+    const int e = g * 64 + lane;
+    double z = e < E ? ro.z[(size_t)t * E + e] : -INFINITY;
+    int id = e < E ? e : INT_MAX;
+    wave_best<K2>(z, id);
+    if (lane < K2) {
+      const int at = g * K2 + ((g & 1) ? K2 - 1 - lane : lane);
+      sr.cz[t][at] = z;
+      sr.ce[t][at] = id;
+    }
+  }
+  __syncthreads();
+  int span = K2;
+  while (span < G * K2) span *= 2;
+  for (int t = wave; t < T; t += nwaves) {
+    double z = lane < G * K2 ? sr.cz[t][lane] : -INFINITY;
+    int id = lane < G * K2 ? sr.ce[t][lane] : INT_MAX;
+    merge_runs<K2, K2>(z, id, span);
+    // k <= E puts k real experts first; the clamp only keeps a table lookup
+    // in bounds should that ever fail
+    topk_emit(z, (unsigned)id < (unsigned)E ? id : 0, k, sr.idx + t * k, sr.w + t * k);
+  }
+}
+
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
 // of g and u, reduced over the wave, is left in s_g / s_u[j][row][slice].
 template <int C, int NT>
@@ -201,29 +237,15 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     __shared__ const uint8_t* s_tab[kMaxE];
     for (int e = threadIdx.x; e < E; e += 256 * C) s_tab[e] = L.table[e];
     const int G = (E + 63) / 64;
-    if (G * k <= 64) {
-      // each 64-expert group of each token sorted by its own wave, then the
-      // token's G * k survivors sorted by one wave: the top k of a token are
-      // among the top k of its groups
-      for (int task = wave; task < T * G; task += 4 * C) {
-        const int t = task / G, g = task - t * G;
-        const int e = g * 64 + lane;
-        double z = e < E ? ro.z[(size_t)t * E + e] : -INFINITY;
-        int id = e < E ? e : INT_MAX;
-        wave_sort64(z, id);
-        if (lane < k) {
-          sr.cz[t][g * k + lane] = z;
-          sr.ce[t][g * k + lane] = id;
-        }
-      }
-      __syncthreads();
-      for (int t = wave; t < T; t += 4 * C) {
-        double z = lane < G * k ? sr.cz[t][lane] : -INFINITY;
-        int id = lane < G * k ? sr.ce[t][lane] : INT_MAX;
-        if (G > 1) wave_sort64(z, id);
-        // k <= E puts k real experts first; the clamp only keeps a table
-        // lookup in bounds should that ever fail
-        topk_emit(z, (unsigned)id < (unsigned)E ? id : 0, k, sr.idx + t * k, sr.w + t * k);
+    const int K2 = k <= 1 ? 1 : 1 << (32 - __builtin_clz(k - 1));
+    if (G * K2 <= 64) {
+      switch (K2) {
+        case 1: small_topk<1>(ro, sr, wave, 4 * C); break;
+        case 2: small_topk<2>(ro, sr, wave, 4 * C); break;
+        case 4: small_topk<4>(ro, sr, wave, 4 * C); break;
+        case 8: small_topk<8>(ro, sr, wave, 4 * C); break;
+        case 16: small_topk<16>(ro, sr, wave, 4 * C); break;
+        default: small_topk<32>(ro, sr, wave, 4 * C); break;
       }
     } else {
       for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);

@@ -118,21 +118,63 @@ __device__ __forceinline__ void bitonic_step(double& z, int& e, bool keep_first)
   e = take ? oe : e;
 }
 
-// Sorts the wave's 64 (logit, id) pairs, one per lane, into selection order
-// (lane 0 first) with Batcher's bitonic network: in stage S, blocks of S
-// lanes alternate direction; step J compares lanes i and i ^ J.  Ids must be
-// distinct apart from the (-inf, INT_MAX) padding, so the order is total.
-__device__ __forceinline__ void wave_sort64(double& z, int& e) {
-  const int lane = threadIdx.x & 63;
-#define MOE_BSTEP(S, J) bitonic_step<J>(z, e, ((lane & (J)) == 0) == ((lane & (S)) == 0))
-  MOE_BSTEP(2, 1);
-  MOE_BSTEP(4, 2); MOE_BSTEP(4, 1);
-  MOE_BSTEP(8, 4); MOE_BSTEP(8, 2); MOE_BSTEP(8, 1);
-  MOE_BSTEP(16, 8); MOE_BSTEP(16, 4); MOE_BSTEP(16, 2); MOE_BSTEP(16, 1);
-  MOE_BSTEP(32, 16); MOE_BSTEP(32, 8); MOE_BSTEP(32, 4); MOE_BSTEP(32, 2); MOE_BSTEP(32, 1);
-  MOE_BSTEP(64, 32); MOE_BSTEP(64, 16); MOE_BSTEP(64, 8); MOE_BSTEP(64, 4); MOE_BSTEP(64, 2);
-  MOE_BSTEP(64, 1);
-#undef MOE_BSTEP
+// Keep, in both lanes, the earlier of this lane's pair and lane ^ J's.
+template <int J>
+__device__ __forceinline__ void keep_earlier(double& z, int& e) {
+  const long long b = __double_as_longlong(z);
+  const int hi = lane_xor<J>((int)(b >> 32));
+  const int lo = lane_xor<J>((int)b);
+  const int oe = lane_xor<J>(e);
+  const double oz = __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+  const bool take = goes_first(oz, oe, z, e);
+  z = take ? oz : z;
+  e = take ? oe : e;
+}
+
+// Half-cleaner steps J, J/2, ..., 1 of Batcher's bitonic network; blocks of
+// DIR lanes alternate direction (lanes with bit DIR clear put the earlier
+// pair first).
+template <int J, int DIR>
+__device__ __forceinline__ void half_clean(double& z, int& e) {
+  if constexpr (J >= 1) {
+    const int lane = threadIdx.x & 63;
+    bitonic_step<J>(z, e, ((lane & J) == 0) == ((lane & DIR) == 0));
+    half_clean<J / 2, DIR>(z, e);
+  }
+}
+
+// Bitonic sort of every run of K2 lanes (stages S = 2 .. K2), directions
+// alternating from run to run.
+template <int S, int K2>
+__device__ __forceinline__ void sort_runs(double& z, int& e) {
+  if constexpr (S <= K2) {
+    half_clean<S / 2, S>(z, e);
+    sort_runs<S * 2, K2>(z, e);
+  }
+}
+
+// Bitonic top-k merge levels L, 2L, ... below `span`: runs of K2 lanes, L
+// apart, sorted in opposite directions; keeping the earlier of lanes i and
+// i ^ L leaves the best K2 of each pair of runs as a bitonic sequence, which
+// the half-cleaner re-sorts, directions now alternating over 2L lanes.
+template <int L, int K2>
+__device__ __forceinline__ void merge_runs(double& z, int& e, int span) {
+  if constexpr (L <= 32) {
+    if (L < span) {
+      keep_earlier<L>(z, e);
+      half_clean<K2 / 2, 2 * L>(z, e);
+      merge_runs<2 * L, K2>(z, e, span);
+    }
+  }
+}
+
+// The best K2 (a power of two) of the wave's 64 (logit, id) pairs, one per
+// lane, into lanes 0..K2-1 in selection order.  Ids must be distinct apart
+// from the (-inf, INT_MAX) padding.
+template <int K2>
+__device__ __forceinline__ void wave_best(double& z, int& e) {
+  sort_runs<2, K2>(z, e);
+  merge_runs<K2, K2>(z, e, 64);
 }
 
 constexpr int kMaxPerLane = 16;  // E <= 1024
@@ -203,7 +245,7 @@ __device__ __forceinline__ void wave_union_small(const int32_t* idx, int n, int 
   const int id = valid ? idx[lane] : 0;
   const int key = valid ? id * 64 + lane : INT_MAX;
   int rank = 0;
-  for (int s = 0; s < 64; ++s) rank += __builtin_amdgcn_readlane(key, s) < key;
+  for (int s = 0; s < n; ++s) rank += __builtin_amdgcn_readlane(key, s) < key;  // lanes >= n: INT_MAX
   if (valid) {
     rows[rank] = lane;
     s_sorted[rank] = id;

@@ -69,6 +69,10 @@ def test_tiny_layer():
     small("mfma_ragged", 1024, 512, 64, 8, 75),
     small("mfma_bf16", 512, 1024, 32, 4, 37, x_kind="bf16"),
     small("mfma_k1_hot", 512, 512, 8, 1, 70),
+    # small batches whose top-k merges several 64-expert groups
+    small("small_E1024_k4", 256, 128, 1024, 4, 2),
+    small("small_E300_k5", 256, 128, 300, 5, 3),
+    small("small_E64_k32", 256, 128, 64, 32, 2, zipf=False),
     # the ABI's limits: 1024 experts, top-32 (a batch union beyond one wave)
     small("maxE_k32", 256, 128, 1024, 32, 3),
     small("maxE_k32_mfma", 512, 512, 1024, 32, 12, zipf=False),
@@ -96,6 +100,19 @@ def test_all_ties_choose_lowest_ids():
     idx, wts = L.route(L.x_device(x, False))
     assert np.array_equal(idx, np.tile(np.arange(4), (6, 1)))
     assert np.all(wts == np.float32(0.25))
+
+
+@pytest.mark.parametrize("E,k,T", [(300, 5, 3), (1024, 4, 2), (256, 8, 1), (64, 32, 2)])
+def test_small_batch_ties_across_groups(E, k, T):
+    # zero router rows: each logit is its bias, 1 for the last expert of
+    # every 64-expert group and 0 elsewhere, so the picks are those experts
+    # in id order, then the lowest ids: ties within and across groups, all
+    # decided by the lower-id rule, in the layer call's own top-k and in
+    # moe_route's
+    w = small(f"ties_E{E}_k{k}", 256, 128, E, k, T, zipf=False)
+    bias = (np.arange(E) % 64 == 63).astype(np.float32)
+    L = DeviceLayer(w, Wr=np.zeros((E, 256), np.float32), bias=bias)
+    full_parity(w, layer=L)
 
 
 def test_zero_down_with_residual_leaves_h_unchanged():
