@@ -265,6 +265,16 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
         if (i < cap) ro.uniq[i] = sr.uniq[i];
       }
       if (threadIdx.x == 0) *ro.n_uniq = sr.n;
+      if (threadIdx.x < sr.n) {
+        const int i = threadIdx.x, beg = sr.offsets[i], cnt = sr.offsets[i + 1] - beg;
+        DownPlan pl;
+        pl.blob = s_tab[sr.uniq[i]];
+        pl.n = cnt;
+#pragma unroll
+        for (int j = 0; j < kSmallBatch; ++j) pl.slot[j] = j < cnt ? sr.rows[beg + j] : 0;
+        pl.pad = 0;
+        ro.plan[i] = pl;
+      }
       if (ro.stats) {
         if (threadIdx.x == 0) ro.stats[0] = sr.n;
         for (int e = threadIdx.x; e < E; e += 256 * C) ro.stats[1 + e] = 0;
@@ -403,43 +413,49 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
 // [8 rb, 8 rb + 8) for every union expert (wave w takes experts w, w + 4,
 // ...), so each expert's down matrix is still read exactly once, and the
 // block forms out[t][rows] = (x[t][rows]) + sum_j w[t][j] y[t*k+j][rows] in
-// ascending j from its own results: no other block is involved.
+// ascending j from its own results: no other block is involved.  Everything
+// a wave needs of an expert is one DownPlan record, so a weight load waits
+// on a single dependent load; the router weights and the residual are
+// fetched at the start.
 constexpr int kDcRows = 8;
 constexpr int kDcWaves = 4;
 
 template <int NT>
-__global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(ExpertList L, int d, int f,
-                                                                 Digits ad, CombineArgs cb) {
+__global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* __restrict__ plan,
+                                                                 const int32_t* __restrict__ n_uniq,
+                                                                 int d, int f, Digits ad,
+                                                                 CombineArgs cb) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.x * kDcRows;
-  const int U = *L.n_uniq;
+  const int U = *n_uniq;
   const int nch = f / kChunk, nga = f / kGroup;
   const size_t fd = (size_t)f * d;
   __shared__ float s_y[kSmallPicks][kDcRows];
-  // union entries and their blob addresses, gathered once per block
-  __shared__ const uint8_t* s_blob[kSmallPicks];
-  for (int i = threadIdx.x; i < U; i += 64 * kDcWaves) s_blob[i] = L.table[L.uniq[i]];
-  __syncthreads();
+  __shared__ float s_w[kSmallPicks];
+  // epilogue operands first: thread i < T * 8 owns (token i / 8, row i % 8)
+  const int nk = cb.T * cb.k;
+  if (threadIdx.x < nk) s_w[threadIdx.x] = cb.w[threadIdx.x];
+  const bool owner = threadIdx.x < cb.T * kDcRows;
+  const size_t o = (size_t)(threadIdx.x / kDcRows) * d + r0 + threadIdx.x % kDcRows;
+  const float res = (owner && cb.resid) ? cb.resid[o] : 0.0f;
 
+  auto dcode = [&](const uint8_t* blob) { return blob + fd + (size_t)r0 * (f / 2); };
+  auto dscale = [&](const uint8_t* blob) {
+    return reinterpret_cast<const _Float16*>(blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+  };
   if constexpr (NT == 1) {
     // one token per expert: a wave takes two experts at a time and issues all
     // of both experts' loads before using any
     for (int u = wave; u < U; u += 2 * kDcWaves) {
       const int u2 = u + kDcWaves;
       const bool two = u2 < U;
-      ExpertRef e0, e1;
-      e0.blob = s_blob[u];
-      e0.beg = L.offsets[u];
-      e1.blob = s_blob[two ? u2 : u];
-      e1.beg = L.offsets[two ? u2 : u];
-      const int slot0 = L.list[e0.beg], slot1 = L.list[e1.beg];
-      const uint8_t* dc0 = e0.blob + fd + (size_t)r0 * (f / 2);
-      const uint8_t* dc1 = e1.blob + fd + (size_t)r0 * (f / 2);
-      const _Float16* ds0 = reinterpret_cast<const _Float16*>(e0.blob + 3 * fd / 2) +
-                            2 * (fd / kGroup) + (size_t)r0 * nga;
-      const _Float16* ds1 = reinterpret_cast<const _Float16*>(e1.blob + 3 * fd / 2) +
-                            2 * (fd / kGroup) + (size_t)r0 * nga;
+      const DownPlan p0 = plan[u], p1 = plan[two ? u2 : u];
+      const int slot0 = p0.slot[0], slot1 = p1.slot[0];
+      const uint8_t* dc0 = dcode(p0.blob);
+      const uint8_t* dc1 = dcode(p1.blob);
+      const _Float16* ds0 = dscale(p0.blob);
+      const _Float16* ds1 = dscale(p1.blob);
       for (int p = 0; p * 64 < nch; ++p) {
         const int c = p * 64 + lane;
         const bool act = c < nch;
@@ -474,34 +490,33 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(ExpertList L, in
     }
   } else {
     for (int u = wave; u < U; u += kDcWaves) {
-      const ExpertRef ex = expert_ref(L, u);
-      const uint8_t* dcode = ex.blob + fd + (size_t)r0 * (f / 2);
-      const _Float16* dsc =
-          reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+      const DownPlan pl = plan[u];
+      const uint8_t* dc = dcode(pl.blob);
+      const _Float16* ds = dscale(pl.blob);
       for (int p = 0; p * 64 < nch; ++p) {
         const int c = p * 64 + lane;
         const bool act = c < nch;
         const unsigned cl = act ? (unsigned)c : 0u;
         uint4 wd[kDcRows];
         float sd[kDcRows];
-  #pragma unroll
+#pragma unroll
         for (int b = 0; b < kDcRows; ++b) {
-          wd[b] = stream_load16(dcode + (size_t)b * (f / 2) + cl * 16u);
-          sd[b] = stream_scale(dsc + (size_t)b * nga + cl / 2u);
+          wd[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
+          sd[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
         }
-        for (int t0 = 0; t0 < ex.n; t0 += NT) {
-          const int nt = min(NT, ex.n - t0);
+        for (int t0 = 0; t0 < pl.n; t0 += NT) {
+          const int nt = min(NT, pl.n - t0);
           int slot[NT];
           ChunkAct aa[NT];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < NT; ++j) {
-            slot[j] = j < nt ? L.list[ex.beg + t0 + j] : 0;
+            slot[j] = j < nt ? pl.slot[t0 + j] : 0;
             aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
           }
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < NT; ++j) {
             float v[8];
-  #pragma unroll
+#pragma unroll
             for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
             const float tot = reduce8(v, lane);
             if ((lane & 7) == 0 && j < nt) {
@@ -514,12 +529,11 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(ExpertList L, in
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < cb.T * kDcRows; i += 64 * kDcWaves) {
-    const int t = i / kDcRows, b = i % kDcRows;
+  if (owner) {
+    const int t = threadIdx.x / kDcRows, b = threadIdx.x % kDcRows;
     float acc = 0.0f;
-    for (int j = 0; j < cb.k; ++j) acc += cb.w[t * cb.k + j] * s_y[t * cb.k + j][b];
-    const size_t o = (size_t)t * d + r0 + b;
-    if (cb.resid) acc = cb.resid[o] + acc;
+    for (int j = 0; j < cb.k; ++j) acc += s_w[t * cb.k + j] * s_y[t * cb.k + j][b];
+    if (cb.resid) acc = res + acc;
     cb.out[o] = acc;
   }
 }
@@ -574,12 +588,13 @@ hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digit
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
 }
 
-hipError_t launch_down_combine(const ExpertList& L, int d, int f, Digits ad,
-                               const CombineArgs& cb, int tokens_per_expert_max, hipStream_t s) {
+hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
+                               Digits ad, const CombineArgs& cb, int tokens_per_expert_max,
+                               hipStream_t s) {
   const dim3 grid(d / kDcRows);
   if (tokens_per_expert_max <= 1)
-    return launch(6, k_down_combine<1>, grid, dim3(64 * kDcWaves), s, L, d, f, ad, cb);
-  return launch(6, k_down_combine<2>, grid, dim3(64 * kDcWaves), s, L, d, f, ad, cb);
+    return launch(6, k_down_combine<1>, grid, dim3(64 * kDcWaves), s, plan, n_uniq, d, f, ad, cb);
+  return launch(6, k_down_combine<2>, grid, dim3(64 * kDcWaves), s, plan, n_uniq, d, f, ad, cb);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,

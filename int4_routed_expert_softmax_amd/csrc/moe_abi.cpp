@@ -52,6 +52,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.aunit = take(Tk * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
   L.blku = take((cap + Tk / mfma_mblock() + 1) * sizeof(int32_t));
+  L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
 }
@@ -281,10 +282,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     ra.z = z;
     ra.xd = xd;
     MOE_TRY(launch_router_front(ra, s));
-    RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats};
+    DownPlan* plan = at<DownPlan>(ws, L.plan);
+    RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, plan};
     MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, T, s));
     CombineArgs cb{w, resid, out, T, k};
-    MOE_TRY(launch_down_combine(EL, d, f, ad, cb, T, s));
+    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, T, s));
     return MOE_OK;
   }
 

@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, a32, ah, aunit, mbo, blku, total;
+  size_t xh, xunit, a32, ah, aunit, mbo, blku, plan, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -100,15 +100,27 @@ constexpr int kSmallPicks = 64;
 // computed as kLogSplit partial sums, which the workspace must hold.
 inline bool small_batch(int T, int k) { return T <= kSmallBatch && T * k <= kSmallPicks; }
 
+// What the down projection of a small batch needs of union expert u, in one
+// record: its blob and its slots (a token picks an expert at most once, so
+// an expert of a batch of at most kSmallBatch tokens has at most that many).
+struct DownPlan {
+  const uint8_t* blob;
+  int32_t n;
+  int32_t slot[kSmallBatch];
+  int32_t pad;
+};
+static_assert(sizeof(DownPlan) == 48, "DownPlan is three 16-byte pieces");
+
 // Routing results of a small batch: the gate/up kernel recomputes top-k and
 // the union from the logits at the start of every block (cheaper than a
-// separate launch) and block (0, 0) publishes them here.
+// separate launch) and block (0, 0) publishes them here, with the down plan.
 struct RouteOut {
   const double* z;
   int T, E, k;
   int32_t* idx;
   float* w;
   int32_t *uniq, *n_uniq, *offsets, *rows, *stats;
+  DownPlan* plan;  // [kSmallPicks]
 };
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
@@ -139,8 +151,9 @@ struct CombineArgs {
   float* out;          // [T][d]
   int T, k;
 };
-hipError_t launch_down_combine(const ExpertList& L, int d, int f, Digits ad,
-                               const CombineArgs& cb, int tokens_per_expert_max, hipStream_t s);
+hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
+                               Digits ad, const CombineArgs& cb, int tokens_per_expert_max,
+                               hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 
