@@ -352,17 +352,39 @@ def run_chain(a):
     U = stats[Wm:, :, 0].cpu().numpy().astype(np.float64)  # [K][L]
     weight_bytes_step = U.sum(axis=1).mean() * blob
 
-    # instrumented eager pass: HIP events around every gate/up and down launch
+    # instrumented eager pass: HIP events around every gate/up and down launch.
+    # Enqueuing a 48-layer step with events takes the host longer than the GPU
+    # takes to run it; a drained queue would stamp each start event while the
+    # GPU waits for the host.  So every step is enqueued behind a spin kernel
+    # that lasts longer than the enqueue, and its 144 launches run back to back.
+    t_enq = time.perf_counter()
+    step(Wm, cur.cuda_stream)
+    t_enq = time.perf_counter() - t_enq
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    spin_per_s = (1 << 20) / (e0.elapsed_time(e1) * 1e-3)
+    spin = int(min(3.0 * t_enq * spin_per_s, 1 << 34))
     n_launch = K * L
     ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(n_launch)],
               [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]) for k in ("gateup", "down")}
     arms = {k: moe.moe_timing_arm(k, *ev[k]) for k in ev}
     for s in range(Wm, Wm + K):
+        torch.cuda._sleep(spin)
         step(s, cur.cuda_stream)
     torch.cuda.synchronize()
     counts = {k: moe.moe_timing_disarm(arms[k]) for k in arms}
     assert all(c == n_launch for c in counts.values()), counts
     dur = {k: np.array([x.elapsed_time(y) for x, y in zip(*ev[k])]) * 1e-3 for k in ev}
+    for k in dur:
+        q = np.percentile(dur[k], [10, 50, 90, 99]) * 1e6
+        print(f"bench: chain48 {k} event us p10 {q[0]:.2f} p50 {q[1]:.2f} p90 {q[2]:.2f} "
+              f"p99 {q[3]:.2f}; by layer mean " +
+              " ".join(f"{v:.1f}" for v in dur[k].reshape(K, L).mean(axis=0)[:6] * 1e6) + " ...",
+              file=sys.stderr, flush=True)
     u_launch = U.reshape(-1)
     gu_gbps = float(np.mean(u_launch * nib_gu / dur["gateup"]) / 1e9)
     dn_gbps = float(np.mean(u_launch * nib_dn / dur["down"]) / 1e9)
