@@ -200,7 +200,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if w.T <= 8 else
+                  "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
                                f"top-{w.top_k}, T={w.T} tokens, gs64 int4 experts "
@@ -400,7 +401,8 @@ def run_chain(a):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if w.T <= 8 else
+                  "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts, 48 fresh layers)",
         "config": {"workload": f"chain48: {L} chained decode layers h <- h + MoE(RMSNorm(h)), T=1, "
                                f"d={w.d} f={w.f} E={w.n_experts} top-{w.top_k}, all "
