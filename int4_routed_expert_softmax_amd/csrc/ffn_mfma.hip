@@ -225,8 +225,10 @@ constexpr int kScaleWave = 2 * kWaveRows * 16;
 constexpr int kLdsBytes = kScaleOff + kGWaves * kScaleWave;
 static_assert(kLdsBytes <= 160 * 1024, "one block per CU");
 // copies per wave and stage: 4 (codes) + 2 (activations), plus 1 (scales) in
-// stages 0, 4, 8, ...  Activation rows past the block's tokens copy the last
-// token's row, so every wave issues the same copies.
+// stages 0, 4, 8, ...  Wave w copies activation rows 8 w .. 8 w + 7 (M-tile
+// w / 2), so waves past the block's last M-tile copy no activations (4 per
+// stage); inside a used M-tile, rows past the block's tokens copy the last
+// token's row.
 constexpr int kCopies = 6;
 
 // One block: 8 waves, each owning 64 weight rows, times one M-block of up to
@@ -312,15 +314,18 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
   uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
 
   const int nst = K / kSC;
+  const bool a_copy = wave < 2 * nmt;  // wave-uniform
   auto issue = [&](int st) {
     uint8_t* base = s_lds + (st % kRing) * kStage;
     const uint32_t so = (uint32_t)st * (kSC / 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dma16((i < 2 ? c0 : c1) + (i & 1) * b_half + so + b_off, base + wave * kBWave + i * 1024);
+    if (a_copy) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(g.a + a_off[i] + st * kSC, base + kStageB + (8 * wave + 4 * i) * (kSC * 2));
+      for (int i = 0; i < 2; ++i)
+        dma16(g.a + a_off[i] + st * kSC, base + kStageB + (8 * wave + 4 * i) * (kSC * 2));
+    }
     if ((st & 3) == 0)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
   };
@@ -370,8 +375,16 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
   issue(1);
   for (int st = 0; st < nst; ++st) {
     if (st + 1 < nst) {
-      if (((st + 1) & 3) == 0) MOE_WAIT_VM_LGKM0(kCopies + 1);
-      else MOE_WAIT_VM_LGKM0(kCopies);
+      // stage st has landed once at most this wave's copies of stage st + 1
+      // are in flight
+      const bool scales_next = ((st + 1) & 3) == 0;
+      if (a_copy) {
+        if (scales_next) MOE_WAIT_VM_LGKM0(kCopies + 1);
+        else MOE_WAIT_VM_LGKM0(kCopies);
+      } else {
+        if (scales_next) MOE_WAIT_VM_LGKM0(kCopies - 1);
+        else MOE_WAIT_VM_LGKM0(kCopies - 2);
+      }
     } else {
       MOE_WAIT_VM_LGKM0(0);
     }
