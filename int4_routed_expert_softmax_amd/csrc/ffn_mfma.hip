@@ -208,9 +208,9 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 
 // LDS: a ring of kRing stages, each covering 128 K-columns (two scale groups),
 //   B  [wave][64 rows][64 B]   codes; row r holds its 16-byte piece p at slot
-//                              p ^ ((r >> 1) & 3)
+//                              p ^ ((r >> 1) & 3) ^ ((r >> 3) & 1)
 //   A  [64 rows][256 B]        packed activations; piece p (8 columns) of row r
-//                              at slot p ^ (r & 7)
+//                              at slot p ^ (r & 15)
 // followed by per-wave scales, two buffers of [64 rows][8 groups] fp16 (8
 // groups = 4 stages), refilled every 4 stages.
 constexpr int kSC = 128;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
 
   // ---- per-lane copy sources
   // codes, copy i: lane l -> ring row 16 i + l / 4, slot l % 4 (piece slot ^ swizzle)
-  const uint32_t b_piece = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
+  const uint32_t b_piece = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1));
   const uint32_t b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + b_piece * 16u;
   const uint32_t b_half = 16u * (uint32_t)(K / 2);
   // activations, copy i of wave w: lane l -> row 8 w + 4 i + l / 16, slot l % 16
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 8 * wave + 4 * i + (lane >> 4);
-    a_off[i] = row_of(r) * (uint32_t)K + (uint32_t)((lane & 15) ^ (r & 7)) * 8u;
+    a_off[i] = row_of(r) * (uint32_t)K + (uint32_t)((lane & 15) ^ (r & 15)) * 8u;
   }
   // scales: lane l -> ring row l, 8 groups
   const _Float16* s_lane = (lane < 32 ? s0 : s1) + (size_t)(lane & 31) * ng;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int nt = 0; nt < kNt; ++nt) {
       const int r = 16 * nt + n;
-      const int slot = (2 * gg + (kg >> 1)) ^ ((r >> 1) & 3);
+      const int slot = (2 * gg + (kg >> 1)) ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
       const uint2 w = *reinterpret_cast<const uint2*>(base + wave * kBWave + r * (kSC / 2) +
                                                       slot * 16 + 8 * (kg & 1));
       const uint32_t h = *reinterpret_cast<const uint16_t*>(sc + r * 16);
@@ -360,8 +360,8 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
       if (mt < nmt) {
         const uint8_t* ar = base + kStageB + (16 * mt + n) * (kSC * 2);
         const int p0 = 8 * gg + 2 * kg;
-        const f16x8 a0 = *reinterpret_cast<const f16x8*>(ar + (p0 ^ (n & 7)) * 16);
-        const f16x8 a1 = *reinterpret_cast<const f16x8*>(ar + ((p0 + 1) ^ (n & 7)) * 16);
+        const f16x8 a0 = *reinterpret_cast<const f16x8*>(ar + (p0 ^ n) * 16);
+        const f16x8 a1 = *reinterpret_cast<const f16x8*>(ar + ((p0 + 1) ^ n) * 16);
 #pragma unroll
         for (int nt = 0; nt < kNt; ++nt) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0[nt], acc[mt][nt], 0, 0, 0);
