@@ -129,10 +129,18 @@ __device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, i
   const int T = ro.T, E = ro.E, k = ro.k;
   const int lane = threadIdx.x & 63;
   const int G = (E + 63) / 64;
-  for (int task = wave; task < T * G; task += nwaves) {
+  const int ntask = T * G;
+  auto zload = [&](int task) {
+    const int t = task / G, e = (task - t * G) * 64 + lane;
+    return e < E ? ro.z[(size_t)t * E + e] : -INFINITY;
+  };
+  // the next task's logits are requested before the current one is sorted
+  double znext = wave < ntask ? zload(wave) : -INFINITY;
+  for (int task = wave; task < ntask; task += nwaves) {
     const int t = task / G, g = task - t * G;
     const int e = g * 64 + lane;
-    double z = e < E ? ro.z[(size_t)t * E + e] : -INFINITY;
+    double z = znext;
+    if (task + nwaves < ntask) znext = zload(task + nwaves);
     int id = e < E ? e : INT_MAX;
     wave_best<K2>(z, id);
     if (lane < K2) {
@@ -152,6 +160,76 @@ __device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, i
     // in bounds should that ever fail
     topk_emit(z, (unsigned)id < (unsigned)E ? id : 0, k, sr.idx + t * k, sr.w + t * k);
   }
+}
+
+// Top-k and batch union of a small batch (T <= kSmallBatch, T * k <=
+// kSmallPicks) from its complete logits ro.z, into sr, by the block's nwaves
+// waves (every thread of the block takes part).
+__device__ __forceinline__ void small_route(const RouteOut& ro, SmallRoute& sr, int wave,
+                                            int nwaves) {
+  const int T = ro.T, E = ro.E, k = ro.k;
+  const int G = (E + 63) / 64;
+  const int K2 = k <= 1 ? 1 : 1 << (32 - __builtin_clz(k - 1));
+  if (G * K2 <= 64) {
+    switch (K2) {
+      case 1: small_topk<1>(ro, sr, wave, nwaves); break;
+      case 2: small_topk<2>(ro, sr, wave, nwaves); break;
+      case 4: small_topk<4>(ro, sr, wave, nwaves); break;
+      case 8: small_topk<8>(ro, sr, wave, nwaves); break;
+      case 16: small_topk<16>(ro, sr, wave, nwaves); break;
+      default: small_topk<32>(ro, sr, wave, nwaves); break;
+    }
+  } else {
+    for (int t = wave; t < T; t += nwaves) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
+  }
+  __syncthreads();
+  if (wave == 0) wave_union_small(sr.idx, T * k, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
+  __syncthreads();
+}
+
+// Writes a small batch's routing (ids, weights, union, slot lists, stats and,
+// with ro.plan, the down plan from the expert table tab).  Every thread of
+// the block calls it; nthreads = block size.
+__device__ __forceinline__ void publish_small_route(const RouteOut& ro, const SmallRoute& sr,
+                                                    const uint8_t* const* tab, int nthreads) {
+  const int E = ro.E, n = ro.T * ro.k;
+  const int cap = min(E, n);
+  for (int i = threadIdx.x; i < n; i += nthreads) {
+    ro.idx[i] = sr.idx[i];
+    ro.w[i] = sr.w[i];
+    ro.rows[i] = sr.rows[i];
+  }
+  for (int i = threadIdx.x; i <= cap; i += nthreads) {
+    ro.offsets[i] = sr.offsets[i];
+    if (i < cap) ro.uniq[i] = sr.uniq[i];
+  }
+  if (threadIdx.x == 0) *ro.n_uniq = sr.n;
+  if (ro.plan && threadIdx.x < sr.n) {
+    const int i = threadIdx.x, beg = sr.offsets[i], cnt = sr.offsets[i + 1] - beg;
+    DownPlan pl;
+    pl.blob = tab[sr.uniq[i]];
+    pl.n = cnt;
+#pragma unroll
+    for (int j = 0; j < kSmallBatch; ++j) pl.slot[j] = j < cnt ? sr.rows[beg + j] : 0;
+    pl.pad = 0;
+    ro.plan[i] = pl;
+  }
+  if (ro.stats) {
+    if (threadIdx.x == 0) ro.stats[0] = sr.n;
+    for (int e = threadIdx.x; e < E; e += nthreads) ro.stats[1 + e] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < sr.n; i += nthreads)
+      ro.stats[1 + sr.uniq[i]] = sr.offsets[i + 1] - sr.offsets[i];
+  }
+}
+
+// Routing of a small batch that takes the grouped GEMM: top-k and union in
+// one block (the gate/up kernel of the GEMV path does the same in its own
+// prologue).
+__global__ __launch_bounds__(1024) void k_route_small(RouteOut ro) {
+  __shared__ SmallRoute sr;
+  small_route(ro, sr, threadIdx.x >> 6, 16);
+  publish_small_route(ro, sr, nullptr, 1024);
 }
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
@@ -230,59 +308,13 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
   int kdiv;
   if constexpr (SMALL) {
     __shared__ SmallRoute sr;
-    const int T = ro.T, E = ro.E, k = ro.k;
-    const int n = T * k;
+    const int E = ro.E, k = ro.k;
     // the expert table travels alongside the routing, so the blob address is
     // in LDS once the union is known
     __shared__ const uint8_t* s_tab[kMaxE];
     for (int e = threadIdx.x; e < E; e += 256 * C) s_tab[e] = L.table[e];
-    const int G = (E + 63) / 64;
-    const int K2 = k <= 1 ? 1 : 1 << (32 - __builtin_clz(k - 1));
-    if (G * K2 <= 64) {
-      switch (K2) {
-        case 1: small_topk<1>(ro, sr, wave, 4 * C); break;
-        case 2: small_topk<2>(ro, sr, wave, 4 * C); break;
-        case 4: small_topk<4>(ro, sr, wave, 4 * C); break;
-        case 8: small_topk<8>(ro, sr, wave, 4 * C); break;
-        case 16: small_topk<16>(ro, sr, wave, 4 * C); break;
-        default: small_topk<32>(ro, sr, wave, 4 * C); break;
-      }
-    } else {
-      for (int t = wave; t < T; t += 4 * C) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
-    }
-    __syncthreads();
-    if (wave == 0) wave_union_small(sr.idx, n, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
-    __syncthreads();
-    if (rb == 0 && u == 0) {
-      const int cap = min(E, n);
-      for (int i = threadIdx.x; i < n; i += 256 * C) {
-        ro.idx[i] = sr.idx[i];
-        ro.w[i] = sr.w[i];
-        ro.rows[i] = sr.rows[i];
-      }
-      for (int i = threadIdx.x; i <= cap; i += 256 * C) {
-        ro.offsets[i] = sr.offsets[i];
-        if (i < cap) ro.uniq[i] = sr.uniq[i];
-      }
-      if (threadIdx.x == 0) *ro.n_uniq = sr.n;
-      if (threadIdx.x < sr.n) {
-        const int i = threadIdx.x, beg = sr.offsets[i], cnt = sr.offsets[i + 1] - beg;
-        DownPlan pl;
-        pl.blob = s_tab[sr.uniq[i]];
-        pl.n = cnt;
-#pragma unroll
-        for (int j = 0; j < kSmallBatch; ++j) pl.slot[j] = j < cnt ? sr.rows[beg + j] : 0;
-        pl.pad = 0;
-        ro.plan[i] = pl;
-      }
-      if (ro.stats) {
-        if (threadIdx.x == 0) ro.stats[0] = sr.n;
-        for (int e = threadIdx.x; e < E; e += 256 * C) ro.stats[1 + e] = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < sr.n; i += 256 * C)
-          ro.stats[1 + sr.uniq[i]] = sr.offsets[i + 1] - sr.offsets[i];
-      }
-    }
+    small_route(ro, sr, wave, 4 * C);
+    if (rb == 0 && u == 0) publish_small_route(ro, sr, s_tab, 256 * C);
     if (u >= sr.n) return;
     ex.blob = s_tab[sr.uniq[u]];
     ex.beg = sr.offsets[u];
@@ -586,6 +618,10 @@ hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digit
   const dim3 grid(d / kRowsPerBlock, max_experts);
   if (tokens_per_expert_max <= 1) return launch(6, k_down<1>, grid, dim3(256), s, L, d, f, ad, y);
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
+}
+
+hipError_t launch_route_small(const RouteOut& ro, hipStream_t s) {
+  return launch(3, k_route_small, dim3(1), dim3(1024), s, ro);
 }
 
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,

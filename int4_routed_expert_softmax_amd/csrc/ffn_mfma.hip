@@ -16,9 +16,10 @@
 // q * s stays a normal fp16 number for 2^-14 <= |s| <= 2^12; smaller scales
 // lose relative precision gradually (fp16 subnormals), larger ones overflow.
 //
-// Work unit: one block (8 waves) = one expert x one M-block of up to 64 of its
-// tokens x 512 weight rows (64 per wave; gate/up: 32 rows of gate and the same
-// 32 rows of up, so SwiGLU is local to the wave).  K is walked in 128-column
+// Work unit: one block (8 waves, or 2 for batches of up to 16 rows) = one
+// expert x one M-block of up to 64 (16) of its tokens x 512 (128) weight rows
+// (64 per wave; gate/up: 32 rows of gate and the same 32 rows of up, so
+// SwiGLU is local to the wave).  K is walked in 128-column
 // stages copied global -> LDS without passing through registers, into a ring
 // of 3 stages; the A and B fragments come from LDS.  d and f must be multiples
 // of 512.
@@ -28,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device_util.h"
 #include "moe_internal.h"
@@ -42,7 +44,6 @@ typedef __attribute__((address_space(1))) const u32x4* g_u32x4_ptr;
 
 constexpr int kNt = 4;                                  // 16-row N-tiles per wave
 constexpr int kWaveRows = kNt * 16;                     // weight rows per wave
-constexpr int kGWaves = 8;                              // waves per block
 constexpr int kPackExp = 14;                            // packed |x'| < 2^14
 constexpr float kBias = 1032.0f;
 
@@ -203,8 +204,12 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
 }
-// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt unconstrained)
-#define MOE_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70)
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70);
+}
 
 // LDS: a ring of kRing stages, each covering 128 K-columns (two scale groups),
 //   B  [wave][64 rows][64 B]   codes; row r holds its 16-byte piece p at slot
@@ -214,30 +219,55 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 // followed by per-wave scales, two buffers of [64 rows][8 groups] fp16 (8
 // groups = 4 stages), refilled every 4 stages.
 constexpr int kSC = 128;
-constexpr int kRing = 3;
-constexpr int kMBlock = 64;
-constexpr int kMT = kMBlock / 16;
 constexpr int kBWave = kWaveRows * (kSC / 2);
-constexpr int kStageB = kGWaves * kBWave;
-constexpr int kStage = kStageB + kMBlock * kSC * 2;
-constexpr int kScaleOff = kRing * kStage;
 constexpr int kScaleWave = 2 * kWaveRows * 16;
-constexpr int kLdsBytes = kScaleOff + kGWaves * kScaleWave;
-static_assert(kLdsBytes <= 160 * 1024, "one block per CU");
+// Block shapes: GW waves (GW x 64 weight rows) x an M-block of 8 GW tokens
+// (each wave copies 8 activation rows), over a ring of R stages (R - 1 in
+// flight).  GW = 8, R = 3: 64-token M-blocks, 160 KB, one block per CU
+// (prefill); GW = 2, R = 5: 16-token M-blocks, 64 KB, two blocks per CU, so a
+// batch of a few tokens over a dozen experts keeps enough bytes in flight.
+// The scale pieces are double-buffered (4 stages each): a piece is refilled
+// R - 1 stages before its first use, which must come after the last use of the
+// piece two back, so R <= 5.
+template <int GW, int R>
+struct RingShape {
+  static constexpr int kRing = R;
+  static constexpr int kMBlock = 8 * GW;
+  static constexpr int kMT = kMBlock / 16;
+  static constexpr int kStageB = GW * kBWave;
+  static constexpr int kStage = kStageB + kMBlock * kSC * 2;
+  static constexpr int kScaleOff = kRing * kStage;
+  static constexpr int kLdsBytes = kScaleOff + GW * kScaleWave;
+  static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
+  static_assert(R >= 3 && R <= 5, "ring depth");
+};
+
+// Copies a wave has in flight after issuing stages st + 1 .. st + R - 2, with
+// st % 4 == PH: 4 code copies, 2 activation copies when the wave copies
+// activations, and a scale copy in stages that are multiples of 4.
+template <int R, int PH, bool ACOPY>
+constexpr int copies_ahead() {
+  int c = 0;
+  for (int i = 1; i <= R - 2; ++i) c += 4 + (ACOPY ? 2 : 0) + (((PH + i) & 3) == 0 ? 1 : 0);
+  return c;
+}
 // copies per wave and stage: 4 (codes) + 2 (activations), plus 1 (scales) in
 // stages 0, 4, 8, ...  Wave w copies activation rows 8 w .. 8 w + 7 (M-tile
 // w / 2), so waves past the block's last M-tile copy no activations (4 per
 // stage); inside a used M-tile, rows past the block's tokens copy the last
 // token's row.
-constexpr int kCopies = 6;
 
 // One block: 8 waves, each owning 64 weight rows, times one M-block of up to
 // 64 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
-template <int MODE>
-__global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kLdsBytes];
+template <int MODE, int GW, int R>
+__global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
+  using Shape = RingShape<GW, R>;
+  constexpr int kRing = Shape::kRing;
+  constexpr int kMBlock = Shape::kMBlock, kMT = Shape::kMT, kStageB = Shape::kStageB;
+  constexpr int kStage = Shape::kStage, kScaleOff = Shape::kScaleOff;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[Shape::kLdsBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -276,7 +306,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
   // ---- this wave's weight rows (ring rows 0..31 and 32..63); waves past the
   // last row copy the last wave's rows and compute nothing
   const int nwaves = MODE == kGateUp ? f / 32 : d / kWaveRows;
-  const int wv = blockIdx.x * kGWaves + wave;
+  const int wv = blockIdx.x * GW + wave;
   const bool active = wv < nwaves;
   const int wc = min(wv, nwaves - 1);
   const size_t fd = (size_t)f * d;
@@ -371,32 +401,36 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
     }
   };
 
-  issue(0);
-  issue(1);
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) {
-      // stage st has landed once at most this wave's copies of stage st + 1
-      // are in flight
-      const bool scales_next = ((st + 1) & 3) == 0;
-      if (a_copy) {
-        if (scales_next) MOE_WAIT_VM_LGKM0(kCopies + 1);
-        else MOE_WAIT_VM_LGKM0(kCopies);
-      } else {
-        if (scales_next) MOE_WAIT_VM_LGKM0(kCopies - 1);
-        else MOE_WAIT_VM_LGKM0(kCopies - 2);
-      }
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) issue(i);
+  // one step: wait for stage st, barrier, refill the slot of stage st - 1,
+  // compute stage st.  Unrolled by the 4-stage scale period so that every
+  // wait count is a constant.
+  auto step = [&](int st, auto phase) {
+    constexpr int PH = decltype(phase)::value;
+    if (st + kRing - 2 < nst) {
+      // stage st has landed once at most the copies of stages st + 1 ..
+      // st + R - 2 are in flight
+      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, true>()>();
+      else wait_vm_lgkm0<copies_ahead<kRing, PH, false>()>();
     } else {
-      MOE_WAIT_VM_LGKM0(0);
+      wait_vm_lgkm0<0>();
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // every wave is past stage st - 1: its ring slot takes stage st + 2
-    if (st + 2 < nst) issue(st + 2);
+    // every wave is past stage st - 1: its ring slot takes stage st + R - 1
+    if (st + kRing - 1 < nst) issue(st + kRing - 1);
     if (active) {
       group(st, 0);
       group(st, 1);
     }
+  };
+  for (int st0 = 0; st0 < nst; st0 += 4) {  // nst is a multiple of 4
+    step(st0, std::integral_constant<int, 0>());
+    step(st0 + 1, std::integral_constant<int, 1>());
+    step(st0 + 2, std::integral_constant<int, 2>());
+    step(st0 + 3, std::integral_constant<int, 3>());
   }
   if (!active) return;
 
@@ -431,7 +465,9 @@ __global__ __launch_bounds__(64 * kGWaves) void k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------- launchers
 
-int mfma_mblock() { return kMBlock; }
+// Batches of up to 16 rows take the small block shape.
+static int gemm_waves(int rows) { return rows <= 16 ? 2 : 8; }
+int mfma_mblock(int rows) { return 8 * gemm_waves(rows); }
 
 bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 
@@ -452,17 +488,19 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     px.n_uniq = L.n_uniq;
     px.mbo = m.mbo;
     px.blk_u = m.blk_u;
-    px.mblock = kMBlock;
+    px.mblock = mfma_mblock(m.x_rows);
   }
   const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
   e = launch(4, k_pack, dim3(gx), dim3(256), s, px);
   if (e != hipSuccess) return e;
 
-  const unsigned mb = L.single ? (unsigned)((L.single_n + kMBlock - 1) / kMBlock)
+  const int gw = gemm_waves(m.x_rows), mblock = mfma_mblock(m.x_rows);
+  const unsigned mb = L.single ? (unsigned)((L.single_n + mblock - 1) / mblock)
                                : (unsigned)m.mb_bound;
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
-  const unsigned wg = (unsigned)((m.f / 32 + kGWaves - 1) / kGWaves);
-  e = launch(5, k_gemm<kGateUp>, dim3(wg, mb), dim3(64 * kGWaves), s, ga);
+  const unsigned wg = (unsigned)((m.f / 32 + gw - 1) / gw);
+  e = gw == 2 ? launch(5, k_gemm<kGateUp, 2, 5>, dim3(wg, mb), dim3(128), s, ga)
+              : launch(5, k_gemm<kGateUp, 8, 3>, dim3(wg, mb), dim3(512), s, ga);
   if (e != hipSuccess) return e;
 
   PackArgs pa{};
@@ -475,8 +513,9 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
-  const unsigned wd = (unsigned)((m.d / kWaveRows + kGWaves - 1) / kGWaves);
-  return launch(6, k_gemm<kDown>, dim3(wd, mb), dim3(64 * kGWaves), s, gd);
+  const unsigned wd = (unsigned)((m.d / kWaveRows + gw - 1) / gw);
+  return gw == 2 ? launch(6, k_gemm<kDown, 2, 4>, dim3(wd, mb), dim3(128), s, gd)
+                 : launch(6, k_gemm<kDown, 8, 3>, dim3(wd, mb), dim3(512), s, gd);
 }
 
 }  // namespace moe

@@ -30,7 +30,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   const size_t Tk = (size_t)T * k;
   const size_t cap = (size_t)(E < (long)Tk ? E : Tk);
   L.tickets = take(kTicketWords * sizeof(uint32_t));
-  L.z = take((size_t)T * E * (small_batch(T, k) ? 1 : kLogSplit) * sizeof(double));
+  L.z = take((size_t)T * E * (gemv_small_path(T, k, d, f) ? 1 : kLogSplit) * sizeof(double));
   L.xn = take((size_t)T * d * sizeof(float));
   L.xq = take((size_t)T * (d / kChunk) * kChunkDigitBytes);
   L.xsx = take((size_t)T * (d / kXGroup) * sizeof(int32_t));
@@ -51,7 +51,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.ah = take(Tk * f * sizeof(uint16_t));
   L.aunit = take(Tk * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
-  L.blku = take((cap + Tk / mfma_mblock() + 1) * sizeof(int32_t));
+  L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
   L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
@@ -208,7 +208,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   EL.single = static_cast<const uint8_t*>(expert_blob);
   EL.single_n = n;
   EL.kdiv = 1;
-  if (n > kSmallBatch && mfma_shape_ok(dm->d, dm->f)) {
+  if (n >= kMfmaMinTokens && mfma_shape_ok(dm->d, dm->f)) {
     MfmaArgs m = mfma_args(ws, L, dm->d, dm->f);
     m.L = EL;
     m.x = x;
@@ -265,7 +265,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.kdiv = k;
   const int maxU = E < T * k ? E : T * k;
 
-  if (small_batch(T, k)) {
+  if (gemv_small_path(T, k, d, f)) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (recomputed per
     // block) and gate/up; 3: down + combine
     RouterArgs ra{};
@@ -298,9 +298,27 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     xr = xn;
     xr_bf16 = 0;
   }
-  MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, z, s));
-  MOE_TRY(launch_topk(z, kLogSplit, bias, T, E, k, idx, w, s));
-  MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
+  if (small_batch(T, k)) {
+    // a few tokens on the grouped GEMM: logits (+ bias) by the small-batch
+    // router front end, top-k and union in one block
+    RouterArgs ra{};
+    ra.x = xr;
+    ra.x_bf16 = xr_bf16;
+    ra.T = T;
+    ra.d = d;
+    ra.E = E;
+    ra.k = k;
+    ra.Wr = w_router;
+    ra.bias = bias;
+    ra.z = z;
+    MOE_TRY(launch_router_front(ra, s));
+    RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, nullptr};
+    MOE_TRY(launch_route_small(ro, s));
+  } else {
+    MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, z, s));
+    MOE_TRY(launch_topk(z, kLogSplit, bias, T, E, k, idx, w, s));
+    MOE_TRY(launch_union(idx, T, E, k, uniq, nuniq, offs, rows, stats, s));
+  }
   if (mfma_shape_ok(d, f)) {
     MfmaArgs m = mfma_args(ws, L, d, f);
     m.L = EL;
@@ -308,7 +326,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.x_bf16 = xr_bf16;
     m.x_rows = T;
     m.slots = T * k;
-    m.mb_bound = maxU + (T * k + mfma_mblock() - 1) / mfma_mblock();
+    m.mb_bound = maxU + (T * k + mfma_mblock(T) - 1) / mfma_mblock(T);
     m.y = y;
     MOE_TRY(launch_ffn_mfma(m, s));
   } else {

@@ -99,6 +99,7 @@ constexpr int kSmallPicks = 64;
 // other batch (more tokens, or more than kSmallPicks picks) has its logits
 // computed as kLogSplit partial sums, which the workspace must hold.
 inline bool small_batch(int T, int k) { return T <= kSmallBatch && T * k <= kSmallPicks; }
+bool mfma_shape_ok(int d, int f);
 
 // What the down projection of a small batch needs of union expert u, in one
 // record: its blob and its slots (a token picks an expert at most once, so
@@ -124,6 +125,9 @@ struct RouteOut {
 };
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
+// Top-k and union of a small batch from complete logits (ro.z), written to
+// ro's outputs (ro.plan may be null).
+hipError_t launch_route_small(const RouteOut& ro, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
 // Logits of batches above kSmallBatch tokens: kLogSplit partial sums per
 // logit, zp[s][t][e] (no bias); launch_topk(nsplit = kLogSplit, bias) adds
@@ -180,9 +184,18 @@ struct MfmaArgs {
   int32_t* blk_u;            // [mb_bound]
   float* y;
 };
-int mfma_mblock();
+// M-block (tokens per GEMM block) for a batch of `rows` activation rows.
+int mfma_mblock(int rows);
+constexpr int kMinMBlock = 16;
 // The grouped GEMM needs d and f to be multiples of 512.
 bool mfma_shape_ok(int d, int f);
+// Batches from this many tokens on take the grouped GEMM when the shape
+// allows it, also within the small-batch limits: its dequantisation work per
+// weight does not grow with the tokens an expert serves, the GEMV's does.
+constexpr int kMfmaMinTokens = 2;
+inline bool gemv_small_path(int T, int k, int d, int f) {
+  return small_batch(T, k) && !(T >= kMfmaMinTokens && mfma_shape_ok(d, f));
+}
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s);
 
 }  // namespace moe

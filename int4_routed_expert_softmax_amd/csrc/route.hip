@@ -231,13 +231,15 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
         }
       }
     } else {
+      // every row is read unconditionally (rows past the batch repeat the
+      // last one and their sums are never used), so the loads of all rows
+      // are in flight together
       for (int i = tid; i < d; i += 256)
 #pragma unroll
-        for (int j = 0; j < TB; ++j)
-          if (j < T) {
-            const double h = xval(j, i);
-            ss[j] += h * h;
-          }
+        for (int j = 0; j < TB; ++j) {
+          const double h = xval(j < T ? j : T - 1, i);
+          ss[j] += h * h;
+        }
     }
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
@@ -277,13 +279,14 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
         const float4 w = wr[m];
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-          if (j < T) {
-            const float4 v = TB == 1 ? xr[m] : xval4(j, i4);
-            acc[j] += (double)w.x * (double)norm(j, v.x);
-            acc[j] += (double)w.y * (double)norm(j, v.y);
-            acc[j] += (double)w.z * (double)norm(j, v.z);
-            acc[j] += (double)w.w * (double)norm(j, v.w);
-          }
+          // unconditional loads (rows past the batch repeat the last one,
+          // their sums are never stored): all rows' loads go out together
+          const int jj = j < T ? j : T - 1;
+          const float4 v = TB == 1 ? xr[m] : xval4(jj, i4);
+          acc[j] += (double)w.x * (double)norm(jj, v.x);
+          acc[j] += (double)w.y * (double)norm(jj, v.y);
+          acc[j] += (double)w.z * (double)norm(jj, v.z);
+          acc[j] += (double)w.w * (double)norm(jj, v.w);
         }
       }
     }

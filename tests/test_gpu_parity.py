@@ -69,6 +69,10 @@ def test_tiny_layer():
     small("mfma_ragged", 1024, 512, 64, 8, 75),
     small("mfma_bf16", 512, 1024, 32, 4, 37, x_kind="bf16"),
     small("mfma_k1_hot", 512, 512, 8, 1, 70),
+    # batches of 2..16 tokens on the grouped GEMM's small block shape
+    small("mfma_T2", 512, 512, 16, 4, 2),
+    small("mfma_T5_bf16", 512, 1024, 32, 8, 5, x_kind="bf16"),
+    small("mfma_T16", 1024, 512, 64, 8, 16, zipf=False),
     # small batches whose top-k merges several 64-expert groups
     small("small_E1024_k4", 256, 128, 1024, 4, 2),
     small("small_E300_k5", 256, 128, 300, 5, 3),
@@ -85,7 +89,8 @@ def test_edge_shapes(w):
 
 
 @pytest.mark.parametrize("w", [small("chainlike", 256, 128, 16, 2, 5),
-                               small("chainlike_mfma", 512, 512, 16, 4, 24)],
+                               small("chainlike_mfma", 512, 512, 16, 4, 24),
+                               small("chainlike_mfma_T4", 512, 512, 16, 4, 4)],
                          ids=lambda w: w.name)
 def test_prenorm_residual(w):
     full_parity(w, flags=moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL)
@@ -129,7 +134,8 @@ def test_zero_down_with_residual_leaves_h_unchanged():
 
 
 @pytest.mark.parametrize("w", [small("inplace", 256, 128, 16, 2, 4),
-                               small("inplace_mfma", 512, 512, 16, 4, 20)],
+                               small("inplace_mfma", 512, 512, 16, 4, 20),
+                               small("inplace_mfma_T3", 512, 512, 16, 2, 3)],
                          ids=lambda w: w.name)
 def test_in_place_residual(w):
     L = DeviceLayer(w)
@@ -213,14 +219,15 @@ def test_glm_expert_ffn_device_and_host_mapped(decode_layer):
 
 
 def test_glm_expert_ffn_batched_mfma(decode_layer):
-    """Single expert over many rows (the grouped-GEMM path): a gathered fp32
-    batch spanning three M-blocks with a ragged tail, and a bf16 batch."""
+    """Single expert over several rows (the grouped-GEMM path): gathered fp32
+    batches spanning three 64-token M-blocks with a ragged tail, one and two
+    16-token M-blocks (the small block shape), and a bf16 batch."""
     w = W["decode1"]
     L = decode_layer
     xb, _ = configs.tokens(W["prefill512"])          # bf16 bits [512][d]
     xf = configs.bf16_bits_to_f32(xb)
     rng = np.random.default_rng(5)
-    for e, n in [(0, 150), (77, 21)]:
+    for e, n in [(0, 150), (77, 21), (3, 2), (200, 13)]:
         sel = rng.choice(xf.shape[0], size=n, replace=False).astype(np.int32)
         xd = torch.from_numpy(np.ascontiguousarray(xf * 1.5)).to(DEV)
         rows = torch.from_numpy(sel).to(DEV)
