@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
       for (int i = tid; i < d; i += 256)
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-          const double h = xval(j < T ? j : T - 1, i);
+          const double h = xval(TB == 1 ? 0 : (j < T ? j : T - 1), i);
           ss[j] += h * h;
         }
     }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
         for (int j = 0; j < TB; ++j) {
           // unconditional loads (rows past the batch repeat the last one,
           // their sums are never stored): all rows' loads go out together
-          const int jj = j < T ? j : T - 1;
+          const int jj = TB == 1 ? 0 : (j < T ? j : T - 1);
           const float4 v = TB == 1 ? xr[m] : xval4(jj, i4);
           acc[j] += (double)w.x * (double)norm(jj, v.x);
           acc[j] += (double)w.y * (double)norm(jj, v.y);
