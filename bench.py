@@ -236,8 +236,8 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
     (useful flops 2 * T*k * d * 2f over its measured launches), and for one
     expert alone at M = 512 tokens and at the token count of the hottest
     expert of the batch (moe_expert_ffn, same kernels), each timed with HIP
-    events over 20 launches.  One expert fills 8 x ceil(M/64) blocks of 8
-    waves, one per CU, so its figure is also given per occupied CU."""
+    events over 20 launches.  Its blocks may not fill every CU, so the
+    figure is also given per occupied CU."""
     import oracle
     from synth import configs
 
@@ -270,7 +270,10 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
         assert moe.moe_timing_disarm(h) == reps
         t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
         flops = 2.0 * n * w.d * 2 * w.f
-        blocks = (w.f // 32 // 8) * ((n + 63) // 64)
+        # the library's block shape for one expert: 2 waves x 64 tokens from 128
+        # rows on, else 8 waves x 64 tokens (2 x 16 at up to 16 rows)
+        gw = 2 if n >= 128 or n <= 16 else 8
+        blocks = (w.f // 32 // gw) * ((n + 63) // 64)
         tf = flops / t / 1e12
         out[label] = {"expert": e, "M": n, "gateup_us": round(t * 1e6, 2), "tflops": round(tf, 1),
                       "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "blocks": blocks,

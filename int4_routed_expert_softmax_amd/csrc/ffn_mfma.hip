@@ -223,16 +223,20 @@ constexpr int kBWave = kWaveRows * (kSC / 2);
 constexpr int kScaleWave = 2 * kWaveRows * 16;
 // Block shapes: GW waves (GW x 64 weight rows) x an M-block of 8 GW tokens
 // (each wave copies 8 activation rows), over a ring of R stages (R - 1 in
-// flight).  GW = 8, R = 3: 64-token M-blocks, 160 KB, one block per CU
-// (prefill); GW = 2, R = 5: 16-token M-blocks, 64 KB, two blocks per CU, so a
-// batch of a few tokens over a dozen experts keeps enough bytes in flight.
+// flight).  GW = 8, R = 3, MB = 64: 160 KB, one block per CU (prefill); GW =
+// 2, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB, two or three blocks per
+// CU, so a batch of a few tokens over a dozen experts keeps enough bytes in
+// flight; GW = 2, MB = 64, R = 3: 76 KB, one expert over many tokens spread
+// over four times as many blocks as the 8-wave shape gives it.
 // The scale pieces are double-buffered (4 stages each): a piece is refilled
 // R - 1 stages before its first use, which must come after the last use of the
 // piece two back, so R <= 5.
-template <int GW, int R>
+template <int GW, int R, int MB>
 struct RingShape {
   static constexpr int kRing = R;
-  static constexpr int kMBlock = 8 * GW;
+  static constexpr int kMBlock = MB;
+  static constexpr int kARows = MB / GW;       // activation rows copied per wave
+  static constexpr int kACopies = kARows / 4;  // 1 KB copies (4 rows) per wave and stage
   static constexpr int kMT = kMBlock / 16;
   static constexpr int kStageB = GW * kBWave;
   static constexpr int kStage = kStageB + kMBlock * kSC * 2;
@@ -240,30 +244,31 @@ struct RingShape {
   static constexpr int kLdsBytes = kScaleOff + GW * kScaleWave;
   static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
   static_assert(R >= 3 && R <= 5, "ring depth");
+  static_assert(MB % 16 == 0 && kARows % 8 == 0, "whole M-tiles, whole copies");
 };
 
 // Copies a wave has in flight after issuing stages st + 1 .. st + R - 2, with
-// st % 4 == PH: 4 code copies, 2 activation copies when the wave copies
-// activations, and a scale copy in stages that are multiples of 4.
-template <int R, int PH, bool ACOPY>
+// st % 4 == PH: 4 code copies, NA activation copies, and a scale copy in
+// stages that are multiples of 4.
+template <int R, int PH, int NA>
 constexpr int copies_ahead() {
   int c = 0;
-  for (int i = 1; i <= R - 2; ++i) c += 4 + (ACOPY ? 2 : 0) + (((PH + i) & 3) == 0 ? 1 : 0);
+  for (int i = 1; i <= R - 2; ++i) c += 4 + NA + (((PH + i) & 3) == 0 ? 1 : 0);
   return c;
 }
-// copies per wave and stage: 4 (codes) + 2 (activations), plus 1 (scales) in
-// stages 0, 4, 8, ...  Wave w copies activation rows 8 w .. 8 w + 7 (M-tile
-// w / 2), so waves past the block's last M-tile copy no activations (4 per
-// stage); inside a used M-tile, rows past the block's tokens copy the last
-// token's row.
+// copies per wave and stage: 4 (codes) + kACopies (activations: wave w copies
+// rows kARows w .. kARows (w + 1) - 1), plus 1 (scales) in stages 0, 4, 8, ...
+// A wave whose first row lies past the block's last M-tile copies no
+// activations; rows past the block's tokens copy the last token's row.
 
 // One block: 8 waves, each owning 64 weight rows, times one M-block of up to
 // 64 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
-template <int MODE, int GW, int R>
+template <int MODE, int GW, int R, int MB>
 __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
-  using Shape = RingShape<GW, R>;
+  using Shape = RingShape<GW, R, MB>;
+  constexpr int kARows = Shape::kARows, kACopies = Shape::kACopies;
   constexpr int kRing = Shape::kRing;
   constexpr int kMBlock = Shape::kMBlock, kMT = Shape::kMT, kStageB = Shape::kStageB;
   constexpr int kStage = Shape::kStage, kScaleOff = Shape::kScaleOff;
@@ -333,10 +338,10 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   const uint32_t b_half = 16u * (uint32_t)(K / 2);
   // activations, copy i of wave w: lane l -> row 8 w + 4 i + l / 16, slot l % 16
   // (M-tile w / 2)
-  uint32_t a_off[2];
+  uint32_t a_off[kACopies];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < kACopies; ++i) {
+    const int r = kARows * wave + 4 * i + (lane >> 4);
     a_off[i] = row_of(r) * (uint32_t)K + (uint32_t)((lane & 15) ^ (r & 15)) * 8u;
   }
   // scales: lane l -> ring row l, 8 groups
@@ -344,7 +349,9 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
 
   const int nst = K / kSC;
-  const bool a_copy = wave < 2 * nmt;  // wave-uniform
+  // a wave copies its activation rows only when the first lies in a used
+  // M-tile (wave-uniform)
+  const bool a_copy = kARows * wave < 16 * nmt;
   auto issue = [&](int st) {
     uint8_t* base = s_lds + (st % kRing) * kStage;
     const uint32_t so = (uint32_t)st * (kSC / 2);
@@ -353,8 +360,8 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
       dma16((i < 2 ? c0 : c1) + (i & 1) * b_half + so + b_off, base + wave * kBWave + i * 1024);
     if (a_copy) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma16(g.a + a_off[i] + st * kSC, base + kStageB + (8 * wave + 4 * i) * (kSC * 2));
+      for (int i = 0; i < kACopies; ++i)
+        dma16(g.a + a_off[i] + st * kSC, base + kStageB + (kARows * wave + 4 * i) * (kSC * 2));
     }
     if ((st & 3) == 0)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
@@ -411,8 +418,8 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
     if (st + kRing - 2 < nst) {
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
-      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, true>()>();
-      else wait_vm_lgkm0<copies_ahead<kRing, PH, false>()>();
+      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, kACopies>()>();
+      else wait_vm_lgkm0<copies_ahead<kRing, PH, 0>()>();
     } else {
       wait_vm_lgkm0<0>();
     }
@@ -465,9 +472,19 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------- launchers
 
-// Batches of up to 16 rows take the small block shape.
-static int gemm_waves(int rows) { return rows <= 16 ? 2 : 8; }
-int mfma_mblock(int rows) { return 8 * gemm_waves(rows); }
+// Block shape of a call: batches of up to 16 rows take 2-wave blocks with
+// 16-token M-blocks; one expert over 128 rows or more (the compute-bound case)
+// takes 2-wave blocks with 64-token M-blocks, four times as many blocks as the
+// 8-wave shape; everything else 8-wave blocks with 64-token M-blocks.
+struct GemmShape {
+  int gw, mblock;
+};
+static GemmShape gemm_shape(int rows, bool single) {
+  if (rows <= 16) return {2, 16};
+  if (single && rows >= 128) return {2, 64};
+  return {8, 64};
+}
+int mfma_mblock(int rows) { return gemm_shape(rows, false).mblock; }
 
 bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 
@@ -488,19 +505,21 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     px.n_uniq = L.n_uniq;
     px.mbo = m.mbo;
     px.blk_u = m.blk_u;
-    px.mblock = mfma_mblock(m.x_rows);
+    px.mblock = gemm_shape(m.x_rows, false).mblock;
   }
   const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
   e = launch(4, k_pack, dim3(gx), dim3(256), s, px);
   if (e != hipSuccess) return e;
 
-  const int gw = gemm_waves(m.x_rows), mblock = mfma_mblock(m.x_rows);
+  const GemmShape sh = gemm_shape(m.x_rows, L.single != nullptr);
+  const int gw = sh.gw, mblock = sh.mblock;
   const unsigned mb = L.single ? (unsigned)((L.single_n + mblock - 1) / mblock)
                                : (unsigned)m.mb_bound;
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
   const unsigned wg = (unsigned)((m.f / 32 + gw - 1) / gw);
-  e = gw == 2 ? launch(5, k_gemm<kGateUp, 2, 5>, dim3(wg, mb), dim3(128), s, ga)
-              : launch(5, k_gemm<kGateUp, 8, 3>, dim3(wg, mb), dim3(512), s, ga);
+  if (gw == 2 && mblock == 16) e = launch(5, k_gemm<kGateUp, 2, 5, 16>, dim3(wg, mb), dim3(128), s, ga);
+  else if (gw == 2) e = launch(5, k_gemm<kGateUp, 2, 3, 64>, dim3(wg, mb), dim3(128), s, ga);
+  else e = launch(5, k_gemm<kGateUp, 8, 3, 64>, dim3(wg, mb), dim3(512), s, ga);
   if (e != hipSuccess) return e;
 
   PackArgs pa{};
@@ -514,8 +533,9 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
 
   GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
   const unsigned wd = (unsigned)((m.d / kWaveRows + gw - 1) / gw);
-  return gw == 2 ? launch(6, k_gemm<kDown, 2, 4>, dim3(wd, mb), dim3(128), s, gd)
-                 : launch(6, k_gemm<kDown, 8, 3>, dim3(wd, mb), dim3(512), s, gd);
+  if (gw == 2 && mblock == 16) return launch(6, k_gemm<kDown, 2, 4, 16>, dim3(wd, mb), dim3(128), s, gd);
+  if (gw == 2) return launch(6, k_gemm<kDown, 2, 3, 64>, dim3(wd, mb), dim3(128), s, gd);
+  return launch(6, k_gemm<kDown, 8, 3, 64>, dim3(wd, mb), dim3(512), s, gd);
 }
 
 }  // namespace moe
