@@ -570,6 +570,71 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
   }
 }
 
+// Down projection and combine for one token (its k picks are k distinct
+// union experts).  Block rb owns output rows [R rb, R rb + R); wave w takes
+// experts w, w + 8, ... over all R rows, so an expert's activation digits are
+// loaded once per R rows and each lane has R weight loads in flight.
+constexpr int kD1Waves = 8;
+
+template <int R>
+__global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPlan* __restrict__ plan,
+                                                                     const int32_t* __restrict__ n_uniq,
+                                                                     int d, int f, Digits ad,
+                                                                     CombineArgs cb) {
+  static_assert(R % 8 == 0, "rows in groups of 8 (one DPP reduction each)");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = blockIdx.x * R;
+  const int U = *n_uniq;
+  const int nch = f / kChunk, nga = f / kGroup;
+  const size_t fd = (size_t)f * d;
+  __shared__ float s_y[kSmallPicks][R];
+  __shared__ float s_w[kSmallPicks];
+  // epilogue operands first: thread t < R owns output row r0 + t
+  if (threadIdx.x < cb.k) s_w[threadIdx.x] = cb.w[threadIdx.x];
+  const bool owner = threadIdx.x < R;
+  const float res = (owner && cb.resid) ? cb.resid[r0 + threadIdx.x] : 0.0f;
+
+  for (int u = wave; u < U; u += kD1Waves) {
+    const DownPlan pl = plan[u];
+    const int slot = pl.slot[0];
+    const uint8_t* dc = pl.blob + fd + (size_t)r0 * (f / 2);
+    const _Float16* ds =
+        reinterpret_cast<const _Float16*>(pl.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+    for (int p = 0; p * 64 < nch; ++p) {
+      const int c = p * 64 + lane;
+      const bool act = c < nch;
+      const unsigned cl = act ? (unsigned)c : 0u;
+      uint4 wv[R];
+      float sv[R];
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        wv[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
+        sv[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
+      }
+      const ChunkAct a = load_act(ad, slot, nch, c, act);
+#pragma unroll
+      for (int g = 0; g < R / 8; ++g) {
+        float v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) v[b] = chunk_term(wv[8 * g + b], sv[8 * g + b], a);
+        const float tot = reduce8(v, lane);
+        if ((lane & 7) == 0) {
+          float* dst = &s_y[slot][8 * g + (lane >> 3)];
+          *dst = p == 0 ? tot : *dst + tot;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (owner) {
+    float acc = 0.0f;
+    for (int j = 0; j < cb.k; ++j) acc += s_w[j] * s_y[j][threadIdx.x];
+    if (cb.resid) acc = res + acc;
+    cb.out[r0 + threadIdx.x] = acc;
+  }
+}
+
 // out[t][c] = (x[t][c] if resid) + sum_j w[t][j] * y[t*k + j][c], ascending j.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
                                                  const float* __restrict__ w, const float* resid,
@@ -627,6 +692,13 @@ hipError_t launch_route_small(const RouteOut& ro, hipStream_t s) {
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
                                Digits ad, const CombineArgs& cb, int tokens_per_expert_max,
                                hipStream_t s) {
+  if (tokens_per_expert_max <= 1 && cb.T == 1) {
+    if (d % 24 == 0)
+      return launch(6, k_down_combine_t1<24>, dim3(d / 24), dim3(64 * kD1Waves), s, plan, n_uniq, d,
+                    f, ad, cb);
+    return launch(6, k_down_combine_t1<16>, dim3(d / 16), dim3(64 * kD1Waves), s, plan, n_uniq, d,
+                  f, ad, cb);
+  }
   const dim3 grid(d / kDcRows);
   if (tokens_per_expert_max <= 1)
     return launch(6, k_down_combine<1>, grid, dim3(64 * kDcWaves), s, plan, n_uniq, d, f, ad, cb);
