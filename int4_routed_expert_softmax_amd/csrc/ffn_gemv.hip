@@ -648,6 +648,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   out[(size_t)t * d + c] = acc;
 }
 
+// The same with four columns per thread (16-byte loads and stores), for a
+// 16-byte aligned out (and residual); d is a multiple of 64.
+__global__ __launch_bounds__(256) void k_combine4(const float* __restrict__ y,
+                                                  const float* __restrict__ w, const float* resid,
+                                                  float* out, int d, int k) {
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * 256 + threadIdx.x;
+  if (4 * c4 >= d) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * d)[c4];
+    acc.x += wj * v.x;
+    acc.y += wj * v.y;
+    acc.z += wj * v.z;
+    acc.w += wj * v.w;
+  }
+  if (resid) {
+    const float4 r = reinterpret_cast<const float4*>(resid + (size_t)t * d)[c4];
+    acc = make_float4(r.x + acc.x, r.y + acc.y, r.z + acc.z, r.w + acc.w);
+  }
+  reinterpret_cast<float4*>(out + (size_t)t * d)[c4] = acc;
+}
+
 // Column slices: ceil(chunks per row / 64), at most 4 (wider rows take passes).
 static int slices(int K) {
   const int c = (K / kChunk + 63) / 64;
@@ -707,6 +731,9 @@ hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int 
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s) {
+  const bool wide = ((uintptr_t)out % 16 == 0) && ((uintptr_t)resid % 16 == 0) && d % 4 == 0;
+  if (wide)
+    return launch(7, k_combine4, dim3((d / 4 + 255) / 256, T), dim3(256), s, y, w, resid, out, d, k);
   return launch(7, k_combine, dim3((d + 255) / 256, T), dim3(256), s, y, w, resid, out, d, k);
 }
 

@@ -120,6 +120,20 @@ def test_small_batch_ties_across_groups(E, k, T):
     full_parity(w, layer=L)
 
 
+def test_output_aligned_to_4_bytes_only():
+    # out starts one float into its allocation: the combine takes its scalar
+    # form (the 16-byte one needs an aligned out)
+    w = small("unaligned_out", 512, 512, 16, 4, 20)
+    L = DeviceLayer(w)
+    x, bf = configs.tokens(w)
+    buf = torch.full((w.T * w.d + 1,), -7.0, dtype=torch.float32, device=DEV)
+    out = buf[1:].view(w.T, w.d)
+    L.forward(L.x_device(x, bf), out=out)
+    ref = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=bf)
+    assert_close(out.cpu().numpy(), ref["out"])
+    assert buf[0].item() == -7.0
+
+
 def test_zero_down_with_residual_leaves_h_unchanged():
     w = small("zerodown", 256, 128, 16, 2, 3)
     blobs = configs.experts(w).copy()
