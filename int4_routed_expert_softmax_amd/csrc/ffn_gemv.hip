@@ -441,7 +441,8 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
   }
 }
 
-// Down projection and combine for small batches.  Block rb owns output rows
+// Down projection and combine for small batches of 2 or more tokens (one
+// token: k_down_combine_t1).  Block rb owns output rows
 // [8 rb, 8 rb + 8) for every union expert (wave w takes experts w, w + 4,
 // ...), so each expert's down matrix is still read exactly once, and the
 // block forms out[t][rows] = (x[t][rows]) + sum_j w[t][j] y[t*k+j][rows] in
@@ -476,85 +477,39 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
   auto dscale = [&](const uint8_t* blob) {
     return reinterpret_cast<const _Float16*>(blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
   };
-  if constexpr (NT == 1) {
-    // one token per expert: a wave takes two experts at a time and issues all
-    // of both experts' loads before using any
-    for (int u = wave; u < U; u += 2 * kDcWaves) {
-      const int u2 = u + kDcWaves;
-      const bool two = u2 < U;
-      const DownPlan p0 = plan[u], p1 = plan[two ? u2 : u];
-      const int slot0 = p0.slot[0], slot1 = p1.slot[0];
-      const uint8_t* dc0 = dcode(p0.blob);
-      const uint8_t* dc1 = dcode(p1.blob);
-      const _Float16* ds0 = dscale(p0.blob);
-      const _Float16* ds1 = dscale(p1.blob);
-      for (int p = 0; p * 64 < nch; ++p) {
-        const int c = p * 64 + lane;
-        const bool act = c < nch;
-        const unsigned cl = act ? (unsigned)c : 0u;
-        uint4 w0[kDcRows], w1[kDcRows];
-        float s0[kDcRows], s1[kDcRows];
+  for (int u = wave; u < U; u += kDcWaves) {
+    const DownPlan pl = plan[u];
+    const uint8_t* dc = dcode(pl.blob);
+    const _Float16* ds = dscale(pl.blob);
+    for (int p = 0; p * 64 < nch; ++p) {
+      const int c = p * 64 + lane;
+      const bool act = c < nch;
+      const unsigned cl = act ? (unsigned)c : 0u;
+      uint4 wd[kDcRows];
+      float sd[kDcRows];
 #pragma unroll
-        for (int b = 0; b < kDcRows; ++b) {
-          w0[b] = stream_load16(dc0 + (size_t)b * (f / 2) + cl * 16u);
-          w1[b] = stream_load16(dc1 + (size_t)b * (f / 2) + cl * 16u);
-          s0[b] = stream_scale(ds0 + (size_t)b * nga + cl / 2u);
-          s1[b] = stream_scale(ds1 + (size_t)b * nga + cl / 2u);
-        }
-        const ChunkAct a0 = load_act(ad, slot0, nch, c, act);
-        const ChunkAct a1 = load_act(ad, slot1, nch, c, act && two);
-        float v[8];
-#pragma unroll
-        for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(w0[b], s0[b], a0);
-        float tot = reduce8(v, lane);
-        if ((lane & 7) == 0) {
-          float* dst = &s_y[slot0][lane >> 3];
-          *dst = p == 0 ? tot : *dst + tot;
-        }
-#pragma unroll
-        for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(w1[b], s1[b], a1);
-        tot = reduce8(v, lane);
-        if (two && (lane & 7) == 0) {
-          float* dst = &s_y[slot1][lane >> 3];
-          *dst = p == 0 ? tot : *dst + tot;
-        }
+      for (int b = 0; b < kDcRows; ++b) {
+        wd[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
+        sd[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
       }
-    }
-  } else {
-    for (int u = wave; u < U; u += kDcWaves) {
-      const DownPlan pl = plan[u];
-      const uint8_t* dc = dcode(pl.blob);
-      const _Float16* ds = dscale(pl.blob);
-      for (int p = 0; p * 64 < nch; ++p) {
-        const int c = p * 64 + lane;
-        const bool act = c < nch;
-        const unsigned cl = act ? (unsigned)c : 0u;
-        uint4 wd[kDcRows];
-        float sd[kDcRows];
+      for (int t0 = 0; t0 < pl.n; t0 += NT) {
+        const int nt = min(NT, pl.n - t0);
+        int slot[NT];
+        ChunkAct aa[NT];
 #pragma unroll
-        for (int b = 0; b < kDcRows; ++b) {
-          wd[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
-          sd[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
+        for (int j = 0; j < NT; ++j) {
+          slot[j] = j < nt ? pl.slot[t0 + j] : 0;
+          aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
         }
-        for (int t0 = 0; t0 < pl.n; t0 += NT) {
-          const int nt = min(NT, pl.n - t0);
-          int slot[NT];
-          ChunkAct aa[NT];
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            slot[j] = j < nt ? pl.slot[t0 + j] : 0;
-            aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
-          }
+        for (int j = 0; j < NT; ++j) {
+          float v[8];
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            float v[8];
-#pragma unroll
-            for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
-            const float tot = reduce8(v, lane);
-            if ((lane & 7) == 0 && j < nt) {
-              float* dst = &s_y[slot[j]][lane >> 3];
-              *dst = p == 0 ? tot : *dst + tot;
-            }
+          for (int b = 0; b < kDcRows; ++b) v[b] = chunk_term(wd[b], sd[b], aa[j]);
+          const float tot = reduce8(v, lane);
+          if ((lane & 7) == 0 && j < nt) {
+            float* dst = &s_y[slot[j]][lane >> 3];
+            *dst = p == 0 ? tot : *dst + tot;
           }
         }
       }
@@ -714,19 +669,16 @@ hipError_t launch_route_small(const RouteOut& ro, hipStream_t s) {
 }
 
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, int tokens_per_expert_max,
-                               hipStream_t s) {
-  if (tokens_per_expert_max <= 1 && cb.T == 1) {
+                               Digits ad, const CombineArgs& cb, hipStream_t s) {
+  if (cb.T == 1) {
     if (d % 24 == 0)
       return launch(6, k_down_combine_t1<24>, dim3(d / 24), dim3(64 * kD1Waves), s, plan, n_uniq, d,
                     f, ad, cb);
     return launch(6, k_down_combine_t1<16>, dim3(d / 16), dim3(64 * kD1Waves), s, plan, n_uniq, d,
                   f, ad, cb);
   }
-  const dim3 grid(d / kDcRows);
-  if (tokens_per_expert_max <= 1)
-    return launch(6, k_down_combine<1>, grid, dim3(64 * kDcWaves), s, plan, n_uniq, d, f, ad, cb);
-  return launch(6, k_down_combine<2>, grid, dim3(64 * kDcWaves), s, plan, n_uniq, d, f, ad, cb);
+  return launch(6, k_down_combine<2>, dim3(d / kDcRows), dim3(64 * kDcWaves), s, plan, n_uniq, d,
+                f, ad, cb);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,

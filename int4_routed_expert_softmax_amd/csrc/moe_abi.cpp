@@ -286,7 +286,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, plan};
     MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, T, s));
     CombineArgs cb{w, resid, out, T, k};
-    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, T, s));
+    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, s));
     return MOE_OK;
   }
 

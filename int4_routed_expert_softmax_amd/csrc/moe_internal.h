@@ -156,8 +156,7 @@ struct CombineArgs {
   int T, k;
 };
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, int tokens_per_expert_max,
-                               hipStream_t s);
+                               Digits ad, const CombineArgs& cb, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 
