@@ -95,9 +95,10 @@ constexpr int kSmallBatch = 8;
 // The small-batch path recomputes routing inside the gate/up kernel with one
 // wave for the union, so it needs T * k <= 64 picks.
 constexpr int kSmallPicks = 64;
-// Whether moe_layer_forward takes the three-launch small-batch path.  Every
-// other batch (more tokens, or more than kSmallPicks picks) has its logits
-// computed as kLogSplit partial sums, which the workspace must hold.
+// A small batch (at most kSmallBatch tokens and kSmallPicks picks) takes its
+// logits, bias added, from the router front end and its top-k and union from
+// one workgroup (the gate/up kernel of the GEMV path, or k_route_small).
+// Larger batches have their logits computed as kLogSplit partial sums.
 inline bool small_batch(int T, int k) { return T <= kSmallBatch && T * k <= kSmallPicks; }
 bool mfma_shape_ok(int d, int f);
 
@@ -129,7 +130,7 @@ hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
 // ro's outputs (ro.plan may be null).
 hipError_t launch_route_small(const RouteOut& ro, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
-// Logits of batches above kSmallBatch tokens: kLogSplit partial sums per
+// Logits of batches past the small-batch limits: kLogSplit partial sums per
 // logit, zp[s][t][e] (no bias); launch_topk(nsplit = kLogSplit, bias) adds
 // them.  The small-batch front end writes complete logits (nsplit = 1, bias
 // already added).

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h,
 // (fp64) summation order differs from a sequential sum: ~1e-16 relative, far
 // below the gap between neighbouring logits.
 //
-// Batches of more than kSmallBatch tokens: a fp64 GEMM on the matrix cores
+// Batches past the small-batch limits: a fp64 GEMM on the matrix cores
 // (v_mfma_f64_16x16x4_f64: exact fp64 products, fp64 sums).  A block = 32
 // tokens x 64 experts x one of kLogSplit column ranges, 4 waves of 16
 // experts x 32 tokens.  64-column chunks of x and of the router rows are
@@ -172,13 +172,14 @@ __global__ __launch_bounds__(kUnionThreads) void k_union(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------- router front end
-// For batches of up to kSmallBatch tokens, one launch computes every logit and
-// the activations' digit form: one workgroup per expert computes that
-// expert's logits for every token, and extra workgroups after them make the
-// digit split in parallel (RMSNorm first if asked, recomputed in the same
+// For small batches, one launch computes every logit (bias added) and, for the
+// GEMV path, the activations' digit form: one workgroup per expert computes
+// that expert's logits for every token, and extra workgroups after them make
+// the digit split in parallel (RMSNorm first if asked, recomputed in the same
 // order in every workgroup so all agree bit for bit).  Top-k and the union
-// run at the start of the next kernel (the gate/up projection), which needs
-// them first; nothing here waits on another workgroup.
+// run next in one workgroup: at the start of the gate/up kernel (GEMV path)
+// or in k_route_small (grouped GEMM); nothing here waits on another
+// workgroup.
 template <int TB>
 __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
   const int e = blockIdx.x;
