@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--batch-invariant", action="store_true",
+                   help="verify8: run the batch with MOE_BATCH_INVARIANT (each token computed "
+                        "exactly as in a one-token call)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 20 plain device-to-device copies of this many MiB (the known-size "
                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -147,9 +150,18 @@ def main():
     ws = moe.make_workspace(dims, w.T, dev)
     stream = torch.cuda.current_stream()
 
+    inv = a.batch_invariant
+    if inv and (w.T > 8 or w.T * w.top_k > 64):
+        sys.exit(f"--batch-invariant: {w.name} has T={w.T}, past the single-token family's "
+                 "batch limits (T <= 8, T * k <= 64)")
+    flags = moe.MOE_BATCH_INVARIANT if inv else 0
+    # the library's choice: one token (or the flag) takes the int8-digit GEMV
+    # kernels; 2+ tokens with d, f multiples of 512 the fp16 MFMA grouped GEMM
+    gemv = w.T == 1 or inv or w.d % 512 or w.f % 512
+
     def step(i):
         L = layers[i % a.layers]
-        moe.moe_layer_forward(dims, L["x"], L["Wr"], L["bias"], L["table"], out,
+        moe.moe_layer_forward(dims, L["x"], L["Wr"], L["bias"], L["table"], out, flags=flags,
                               stats=stats[i % a.layers], ws=ws, stream=stream.cuda_stream)
 
     for i in range(a.warmup):
@@ -200,12 +212,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if w.T <= 8 else
+        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if gemv else
                   "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
                                f"top-{w.top_k}, T={w.T} tokens, gs64 int4 experts "
-                               f"({blob} B each), {a.layers} rotating HBM-resident layers",
+                               f"({blob} B each), {a.layers} rotating HBM-resident layers"
+                               + (", MOE_BATCH_INVARIANT" if inv else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "layers_rotated": a.layers, "distinct_experts_per_step": float(u_steps.mean())},
         "expert_weight_GBps": round(weight_bytes_step / sec / 1e9, 1),

@@ -75,15 +75,17 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
 /* moe_layer_forward flags. */
 enum {
-  MOE_PRENORM_RMS = 1u, /* route and run experts on RMSNorm(x), unit gain (x must be f32) */
-  MOE_RESIDUAL = 2u     /* out = x + MoE(...) (x must be f32) */
+  MOE_PRENORM_RMS = 1u,    /* route and run experts on RMSNorm(x), unit gain (x must be f32) */
+  MOE_RESIDUAL = 2u,       /* out = x + MoE(...) (x must be f32) */
+  MOE_BATCH_INVARIANT = 4u /* each token's result as if it were alone in the call (see below) */
 };
 
 /* Return codes. */
 enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* null or inconsistent argument, T < 1 */
-  MOE_EUNSUPPORTED = -2, /* group_size != 64, d/f not multiples of 64, k > 32, E > 1024, bad dtype/flags */
+  MOE_EUNSUPPORTED = -2, /* group_size != 64, d/f not multiples of 64, k > 32, E > 1024, bad dtype/flags,
+                            MOE_BATCH_INVARIANT with T > 8 or T * k > 64 */
   MOE_ENOSPC = -3,       /* ws_bytes smaller than moe_workspace_bytes() */
   MOE_EHIP = -4          /* a kernel launch failed; moe_strerror() names the HIP error */
 };
@@ -165,6 +167,20 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 (+ x[t] with MOE_RESIDUAL), summed in ascending slot j, where
  *                 x' = RMSNorm(x) with MOE_PRENORM_RMS, else x.  out may alias x.
  *   flags         MOE_PRENORM_RMS | MOE_RESIDUAL (both need x_dtype MOE_F32)
+ *                 | MOE_BATCH_INVARIANT (any dtype; T <= 8 and T * k <= 64):
+ *                 token t's out[t] and its counts in stats are bit-identical
+ *                 to those of a call with x[t] alone (T = 1, same flags,
+ *                 table and weights), so a batched verify of drafted tokens
+ *                 computes exactly the function that produced them one at a
+ *                 time.  The batch runs the single-token kernel family with
+ *                 every token's arithmetic in the single-token order; each
+ *                 distinct expert is still streamed once per call.  Without
+ *                 the flag, batches of 2 or more tokens may take the matrix-
+ *                 core path, whose rounding differs from the single-token
+ *                 path within the output tolerance.
+ *                 Source: drafts and their batched verification must compute
+ *                 the same function, pinned to one kernel family — README
+ *                 工作原理 › 诚实的推测解码; 技术解读, "精度与语义：速度可以牺牲，语义不能".
  *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
  *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]
  *                 = number of tokens that picked expert e

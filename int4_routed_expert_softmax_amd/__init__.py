@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_PRENORM_RMS, MOE_RESIDUAL = 1, 2
+MOE_PRENORM_RMS, MOE_RESIDUAL, MOE_BATCH_INVARIANT = 1, 2, 4
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 
 # Every function include/moe.h declares.

@@ -223,13 +223,14 @@ __device__ __forceinline__ void publish_small_route(const RouteOut& ro, const Sm
   }
 }
 
-// Routing of a small batch that takes the grouped GEMM: top-k and union in
-// one block (the gate/up kernel of the GEMV path does the same in its own
-// prologue).
-__global__ __launch_bounds__(1024) void k_route_small(RouteOut ro) {
+// Routing of a small batch in one block: top-k and union (the single-token
+// gate/up kernel does the same in its own prologue, with the same per-token
+// arithmetic), and the down plan when ro.plan is set (table: the expert
+// table, read only then).
+__global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t* const* table) {
   __shared__ SmallRoute sr;
   small_route(ro, sr, threadIdx.x >> 6, 16);
-  publish_small_route(ro, sr, nullptr, 1024);
+  publish_small_route(ro, sr, table, 1024);
 }
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
@@ -301,7 +302,19 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay scalar
   const int stream = wave / C, slice = wave % C;
-  const int u = blockIdx.y, rb = blockIdx.x;
+  int u = blockIdx.y, rb = blockIdx.x, grp = blockIdx.z;
+  const int G = gridDim.z, npairs = gridDim.x * gridDim.y;
+  if (G > 1 && npairs % 8 == 0) {
+    // token groups of one (row block, expert) pair on one XCD, dispatched
+    // back to back: blocks go to the 8 XCDs in turn, so flat index F maps to
+    // pair 8 (F / 8 / G) + F % 8, group (F / 8) % G, and the groups' re-reads
+    // of the pair's rows meet in that XCD's L2
+    const int F = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int hi = F >> 3, pair = (hi / G) * 8 + (F & 7);
+    grp = hi % G;
+    rb = pair % gridDim.x;
+    u = pair / gridDim.x;
+  }
   __shared__ float s_g[NT][kRowsPerBlock][C], s_u[NT][kRowsPerBlock][C];
   ExpertRef ex;
   const int32_t* list;
@@ -336,7 +349,9 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
   const int r0 = rb * kRowsPerBlock + rl0;
   auto slot_at = [&](int i) { return list ? list[ex.beg + i] : i; };
 
-  for (int t0 = 0; t0 < ex.n; t0 += NT) {
+  // grid z splits an expert's tokens: group grp takes tokens grp NT, then
+  // every G NT further on
+  for (int t0 = grp * NT; t0 < ex.n; t0 += NT * G) {
     const int nt = min(NT, ex.n - t0);
     int xrow[NT];
 #pragma unroll
@@ -635,8 +650,8 @@ static int slices(int K) {
 
 template <bool SMALL, int NT>
 static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, int d, int f,
-                           Digits xd, Digits ad, hipStream_t s) {
-  const dim3 grid(f / kRowsPerBlock, maxU);
+                           Digits xd, Digits ad, int groups, hipStream_t s) {
+  const dim3 grid(f / kRowsPerBlock, maxU, groups);
   switch (slices(d)) {
     case 1: return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
     case 2: return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
@@ -645,16 +660,20 @@ static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, in
   }
 }
 
-// tokens_per_expert_max: an upper bound on any expert's token count (1 selects
-// the single-token kernels).
+// tokens_per_expert_max: 1 selects the single-token kernels (each block takes
+// one token at a time), else two at a time.  token_groups: blocks per (row
+// block, expert), each taking every token_groups-th one (or pair) of the
+// expert's tokens; 1 with a small route (its prologue).
 hipError_t launch_gateup(const ExpertList& L, const RouteOut* ro, int max_experts, int d, int f,
-                         Digits xd, Digits ad, int tokens_per_expert_max, hipStream_t s) {
+                         Digits xd, Digits ad, int tokens_per_expert_max, int token_groups,
+                         hipStream_t s) {
+  if (token_groups < 1 || (ro && token_groups != 1)) return hipErrorInvalidValue;
   if (tokens_per_expert_max <= 1) {
-    if (ro) return gateup_c<true, 1>(L, *ro, max_experts, d, f, xd, ad, s);
-    return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, s);
+    if (ro) return gateup_c<true, 1>(L, *ro, max_experts, d, f, xd, ad, 1, s);
+    return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
   }
-  if (ro) return gateup_c<true, 2>(L, *ro, max_experts, d, f, xd, ad, s);
-  return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, s);
+  if (ro) return gateup_c<true, 2>(L, *ro, max_experts, d, f, xd, ad, 1, s);
+  return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
 }
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
@@ -664,8 +683,9 @@ hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digit
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
 }
 
-hipError_t launch_route_small(const RouteOut& ro, hipStream_t s) {
-  return launch(3, k_route_small, dim3(1), dim3(1024), s, ro);
+hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s) {
+  if (ro.plan && !table) return hipErrorInvalidValue;
+  return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table);
 }
 
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,

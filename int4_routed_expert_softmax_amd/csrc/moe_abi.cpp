@@ -222,7 +222,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   }
   const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
   MOE_TRY(launch_digitize(x, x_dtype == MOE_BF16, rows, n, dm->d, xd, s));
-  MOE_TRY(launch_gateup(EL, nullptr, 1, dm->d, dm->f, xd, ad, n, s));
+  MOE_TRY(launch_gateup(EL, nullptr, 1, dm->d, dm->f, xd, ad, n, 1, s));
   MOE_TRY(launch_down(EL, 1, dm->d, dm->f, ad, y, n, s));
   return MOE_OK;
 }
@@ -235,8 +235,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   int st = dims_status(dm);
   if (st != MOE_OK) return st;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL)) return MOE_EUNSUPPORTED;
-  if (flags && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
+  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT))
+    return MOE_EUNSUPPORTED;
+  if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
+  const bool invariant = (flags & MOE_BATCH_INVARIANT) != 0;
+  if (invariant && T >= 1 && !small_batch(T, dm->top_k)) return MOE_EUNSUPPORTED;
   if (T < 1 || !x || !w_router || !expert_table || !out || !ws) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4)) return MOE_EINVAL;
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
@@ -265,9 +268,13 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.kdiv = k;
   const int maxU = E < T * k ? E : T * k;
 
-  if (gemv_small_path(T, k, d, f)) {
-    // 1: [RMSNorm], logits, digit split; 2: top-k + union (recomputed per
-    // block) and gate/up; 3: down + combine
+  if (invariant || gemv_small_path(T, k, d, f)) {
+    // 1: [RMSNorm], logits, digit split; 2: top-k + union (one token: in
+    // every gate/up block's prologue; 2+: one k_route_small block) and
+    // gate/up; 3: down + combine.  Every step keeps one order of
+    // arithmetic per token whatever the batch (the kernels for 1 and for 2+
+    // tokens accumulate a token's terms alike), which MOE_BATCH_INVARIANT
+    // relies on.
     RouterArgs ra{};
     ra.x = x;
     ra.x_bf16 = x_dtype == MOE_BF16;
@@ -284,7 +291,17 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     MOE_TRY(launch_router_front(ra, s));
     DownPlan* plan = at<DownPlan>(ws, L.plan);
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, plan};
-    MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, T, s));
+    if (T == 1) {
+      MOE_TRY(launch_gateup(EL, &ro, maxU, d, f, xd, ad, 1, 1, s));
+    } else {
+      // 2+ tokens: routing once, in one block; then one gate/up block per
+      // (row block, expert, token) running the single-token kernel (the
+      // two-token one runs out of registers at 12 waves a block), the
+      // blocks of one expert's rows back to back on one XCD so its rows
+      // come from HBM once
+      MOE_TRY(launch_route_small(ro, EL.table, s));
+      MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, 1, T, s));
+    }
     CombineArgs cb{w, resid, out, T, k};
     MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, s));
     return MOE_OK;
@@ -313,7 +330,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     ra.z = z;
     MOE_TRY(launch_router_front(ra, s));
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, nullptr};
-    MOE_TRY(launch_route_small(ro, s));
+    MOE_TRY(launch_route_small(ro, nullptr, s));
   } else {
     MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, z, s));
     MOE_TRY(launch_topk(z, kLogSplit, bias, T, E, k, idx, w, s));
@@ -331,7 +348,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     MOE_TRY(launch_ffn_mfma(m, s));
   } else {
     MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
-    MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, s));
+    MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, 1, s));
     MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
   }
   MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));

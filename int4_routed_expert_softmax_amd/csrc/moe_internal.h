@@ -127,8 +127,9 @@ struct RouteOut {
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
 // Top-k and union of a small batch from complete logits (ro.z), written to
-// ro's outputs (ro.plan may be null).
-hipError_t launch_route_small(const RouteOut& ro, hipStream_t s);
+// ro's outputs; with ro.plan set, also the down plan, whose blob addresses
+// come from the expert table (else table may be null).
+hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
 // Logits of batches past the small-batch limits: kLogSplit partial sums per
 // logit, zp[s][t][e] (no bias); launch_topk(nsplit = kLogSplit, bias) adds
@@ -144,7 +145,8 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
                            Digits out, hipStream_t s);
 hipError_t launch_gateup(const ExpertList& L, const RouteOut* small_route, int max_experts, int d,
-                         int f, Digits xd, Digits ad, int tokens_per_expert_max, hipStream_t s);
+                         int f, Digits xd, Digits ad, int tokens_per_expert_max, int token_groups,
+                         hipStream_t s);
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
                        int tokens_per_expert_max, hipStream_t s);

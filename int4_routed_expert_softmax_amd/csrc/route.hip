@@ -232,14 +232,19 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
         }
       }
     } else {
-      // every row is read unconditionally (rows past the batch repeat the
+      // the same partition and order as above (float4 i4 = tid + 256 m, its
+      // four values in turn), so a token's sum does not depend on the batch.
+      // Every row is read unconditionally (rows past the batch repeat the
       // last one and their sums are never used), so the loads of all rows
-      // are in flight together
-      for (int i = tid; i < d; i += 256)
+      // are in flight together.
+      for (int i4 = tid; i4 < n4; i4 += 256)
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
-          const double h = xval(TB == 1 ? 0 : (j < T ? j : T - 1), i);
-          ss[j] += h * h;
+          const float4 v = xval4(TB == 1 ? 0 : (j < T ? j : T - 1), i4);
+          ss[j] += (double)v.x * (double)v.x;
+          ss[j] += (double)v.y * (double)v.y;
+          ss[j] += (double)v.z * (double)v.z;
+          ss[j] += (double)v.w * (double)v.w;
         }
     }
 #pragma unroll

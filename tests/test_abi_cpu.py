@@ -123,7 +123,14 @@ def test_layer_forward_rejects_bad_arguments():
     assert call(table=None) == moe.MOE_EINVAL
     assert call(out=None) == moe.MOE_EINVAL
     assert call(T=-1) == moe.MOE_EINVAL
-    assert call(flags=4) == moe.MOE_EUNSUPPORTED
+    assert call(flags=8) == moe.MOE_EUNSUPPORTED
+    # batch invariance covers the single-token family's batch limits only
+    ws9 = moe.workspace_bytes(GLM, 9)
+    assert call(flags=moe.MOE_BATCH_INVARIANT, T=9, wsb=ws9) == moe.MOE_EUNSUPPORTED
+    d32 = moe.Dims(6144, 2048, 256, 32).c()
+    assert f(ctypes.byref(d32), FAKE, moe.MOE_F32, 3, FAKE, None, FAKE, FAKE,
+             moe.MOE_BATCH_INVARIANT, 1e-6, None, FAKE,
+             moe.workspace_bytes(moe.Dims(6144, 2048, 256, 32), 3), None) == moe.MOE_EUNSUPPORTED
     assert call(flags=moe.MOE_RESIDUAL, dt=moe.MOE_BF16) == moe.MOE_EUNSUPPORTED
     assert call(flags=moe.MOE_PRENORM_RMS, eps=-1.0) == moe.MOE_EINVAL
     assert call(wsb=ws - 256) == moe.MOE_ENOSPC
