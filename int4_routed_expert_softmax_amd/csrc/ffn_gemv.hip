@@ -642,10 +642,12 @@ __global__ __launch_bounds__(256) void k_combine4(const float* __restrict__ y,
   reinterpret_cast<float4*>(out + (size_t)t * d)[c4] = acc;
 }
 
-// Column slices: ceil(chunks per row / 64), at most 4 (wider rows take passes).
+// Column slices: ceil(chunks per row / 64), at most 3 (wider rows take
+// passes): four would make 16-wave blocks, whose 128-register cap the gate/up
+// loop does not fit in without spilling.
 static int slices(int K) {
   const int c = (K / kChunk + 63) / 64;
-  return c < 1 ? 1 : (c > 4 ? 4 : c);
+  return c < 1 ? 1 : (c > 3 ? 3 : c);
 }
 
 template <bool SMALL, int NT>
@@ -655,8 +657,7 @@ static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, in
   switch (slices(d)) {
     case 1: return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
     case 2: return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
-    case 3: return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
-    default: return launch(5, k_gateup<4, SMALL, NT>, grid, dim3(1024), s, L, ro, d, f, xd, ad);
+    default: return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
   }
 }
 

@@ -103,6 +103,9 @@ def test_in_place_with_residual(verify8):
     configs.Workload("inv_d320_E300", d=320, f=192, n_experts=300, top_k=5, T=7, seed=32),
     # the batch limit T * k = 64
     configs.Workload("inv_k32_T2", d=256, f=128, n_experts=96, top_k=32, T=2, seed=33),
+    # rows past 8192 columns: the router's streamed (not register-held) rows
+    # and two column passes in gate/up
+    configs.Workload("inv_d10240", d=10240, f=192, n_experts=16, top_k=2, T=3, seed=34),
 ], ids=lambda w: w.name)
 def test_small_shapes(w):
     L = DeviceLayer(w)

@@ -63,6 +63,11 @@ def test_tiny_layer():
     small("k1", 256, 128, 16, 1, 9),
     small("kE", 128, 64, 16, 16, 3, zipf=False),
     small("wide", 2112, 704, 64, 8, 70),
+    # rows wider than one pass of the gate/up blocks (192 chunks of 32)
+    small("wide8192_t1", 8192, 256, 16, 2, 1),
+    small("wide8192_T3", 8192, 320, 16, 2, 3),
+    small("wide10240", 10240, 192, 16, 2, 20),
+    small("wide10240_t1", 10240, 192, 16, 2, 1),  # router rows past 8192 columns
     small("bf16", 256, 128, 32, 4, 33, x_kind="bf16"),
     # multi-token batches on the grouped-GEMM path (d, f multiples of 512)
     small("mfma", 512, 512, 16, 4, 40),
