@@ -654,27 +654,32 @@ template <bool SMALL, int NT>
 static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, int d, int f,
                            Digits xd, Digits ad, int groups, hipStream_t s) {
   const dim3 grid(f / kRowsPerBlock, maxU, groups);
-  switch (slices(d)) {
-    case 1: return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
-    case 2: return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
-    default: return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
-  }
+  const int c = slices(d);
+  if (c == 1) return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
+  if (c == 2) return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
+  // two tokens at a time fit a block's registers only up to 2 slices
+  if constexpr (NT == 1)
+    return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
+  return hipErrorInvalidValue;
 }
 
 // tokens_per_expert_max: 1 selects the single-token kernels (each block takes
-// one token at a time), else two at a time.  token_groups: blocks per (row
-// block, expert), each taking every token_groups-th one (or pair) of the
-// expert's tokens; 1 with a small route (its prologue).
+// one token at a time), else two at a time where the block's registers allow
+// (rows of up to 128 chunks).  token_groups: blocks per (row block, expert),
+// each taking every token_groups-th one (or pair) of the expert's tokens.
+// A small route (the routing prologue) takes one token and one group.
 hipError_t launch_gateup(const ExpertList& L, const RouteOut* ro, int max_experts, int d, int f,
                          Digits xd, Digits ad, int tokens_per_expert_max, int token_groups,
                          hipStream_t s) {
-  if (token_groups < 1 || (ro && token_groups != 1)) return hipErrorInvalidValue;
-  if (tokens_per_expert_max <= 1) {
-    if (ro) return gateup_c<true, 1>(L, *ro, max_experts, d, f, xd, ad, 1, s);
-    return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
+  if (token_groups < 1) return hipErrorInvalidValue;
+  if (ro) {
+    // the routing prologue serves single tokens only
+    if (token_groups != 1 || tokens_per_expert_max > 1) return hipErrorInvalidValue;
+    return gateup_c<true, 1>(L, *ro, max_experts, d, f, xd, ad, 1, s);
   }
-  if (ro) return gateup_c<true, 2>(L, *ro, max_experts, d, f, xd, ad, 1, s);
-  return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
+  if (tokens_per_expert_max > 1 && slices(d) < 3)
+    return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
+  return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
 }
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
