@@ -124,6 +124,9 @@ def main():
     from synth import configs
 
     w = configs.WORKLOADS[a.workload]
+    if a.batch_invariant and (w.T > 8 or w.T * w.top_k > 64):
+        sys.exit(f"--batch-invariant: {w.name} has T={w.T}, past the single-token family's "
+                 "batch limits (T <= 8, T * k <= 64)")
     dev = torch.device("cuda:0")
     dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
     blob = w.blob_bytes
@@ -151,9 +154,6 @@ def main():
     stream = torch.cuda.current_stream()
 
     inv = a.batch_invariant
-    if inv and (w.T > 8 or w.T * w.top_k > 64):
-        sys.exit(f"--batch-invariant: {w.name} has T={w.T}, past the single-token family's "
-                 "batch limits (T <= 8, T * k <= 64)")
     flags = moe.MOE_BATCH_INVARIANT if inv else 0
     # the library's choice: one token (or the flag) takes the int8-digit GEMV
     # kernels; 2+ tokens with d, f multiples of 512 the fp16 MFMA grouped GEMM
