@@ -197,6 +197,59 @@ int moe_layer_forward(const moe_dims* dims, const void* x, int x_dtype, int32_t 
                       size_t ws_bytes, void* stream);
 
 /*
+ * HBM slot cache in front of the experts' home memory.
+ *
+ * moe_cache_state_bytes — bytes of the cache state for n_slots slots; 0 for
+ * invalid dims or n_slots outside [1, E].  The state lives in caller device
+ * memory, zero-filled once before its first use (every slot empty), and is
+ * then owned by the calls that take it.  Layout (32-bit words):
+ *   header: clock (calls so far), hits, misses (union experts found in a
+ *           slot / copied into one, over all calls), last_hits, last_misses,
+ *           3 reserved
+ *   slot_of[E]   slot + 1 holding expert e, 0 if none
+ *   expert_of[S] expert + 1 held by slot s, 0 if empty
+ *   stamp[S]     clock value of slot s's last use
+ */
+size_t moe_cache_state_bytes(const moe_dims* dims, int32_t n_slots);
+
+/*
+ * moe_layer_forward_cached — the layer for a small batch (T <= 8, T * k <= 64)
+ * whose experts live in home memory (pinned host memory mapped into the device
+ * address space, or any device-readable memory) behind an HBM cache of
+ * n_slots expert slots.
+ *   home_table  device array of E pointers to the experts' blobs in their home
+ *               memory (16-byte aligned); only missed experts are read there
+ *   slots       device memory of n_slots * moe_expert_blob_bytes() bytes,
+ *               256-byte aligned, owned by the cache
+ *   n_slots     min(E, T * k) <= n_slots <= E
+ *   cache_state device buffer of moe_cache_state_bytes(dims, n_slots)
+ *   other arguments as moe_layer_forward (all three flags accepted).
+ * Per call, on the device: the router and the union; placement in one
+ * workgroup (experts of the union found in a slot keep it and count as hits;
+ * each other one, in ascending id, takes the least recently used slot not
+ * used by this call, ties to the lower slot, and evicts its expert); the
+ * missed blobs are copied from home into their slots; the expert kernels
+ * read every union expert from its slot.  The batch runs the single-token
+ * kernel family, so out (and stats) are bit-identical to moe_layer_forward
+ * with MOE_BATCH_INVARIANT (for one token: with any flags) and the blobs
+ * resident, for any cache contents: where an expert's bytes come from
+ * decides only the speed.  Calls sharing one
+ * cache state must be ordered (one stream); the clock wraps after 2^32 calls.
+ * Errors as moe_layer_forward; MOE_EUNSUPPORTED also for T or n_slots out of
+ * range.
+ * Source: an expert is fetched once per batch from wherever it lives and
+ * resident experts are served from the faster tier, the placement following
+ * each token's routing — README 工作原理 › 绝不为同一次磁盘读取等待两遍 (place,
+ * overlap); colibri 技术解读, "引擎结构：一个 C 文件，五步 token 路径"
+ * (route → union → place → overlap → learn).
+ */
+int moe_layer_forward_cached(const moe_dims* dims, const void* x, int x_dtype, int32_t T,
+                             const float* w_router, const float* bias,
+                             const void* const* home_table, void* slots, int32_t n_slots,
+                             void* cache_state, float* out, uint32_t flags, float rms_eps,
+                             int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing — instrumentation, not part of the layer's computation.
  * Kernels of the library, by name:                                          */
 enum {

@@ -22,7 +22,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 
 # Every function include/moe.h declares.
 EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_route",
-           "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_timing_arm")
+           "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_cache_state_bytes",
+           "moe_layer_forward_cached", "moe_timing_arm")
 
 # Kernel ids for moe_timing_arm.
 KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
@@ -90,6 +91,11 @@ def _load():
     L.moe_layer_forward.restype = ctypes.c_int
     L.moe_layer_forward.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, u32,
                                     ctypes.c_float, vp, vp, sz, vp]
+    L.moe_cache_state_bytes.restype = sz
+    L.moe_cache_state_bytes.argtypes = [dp, i32]
+    L.moe_layer_forward_cached.restype = ctypes.c_int
+    L.moe_layer_forward_cached.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, vp, vp,
+                                           u32, ctypes.c_float, vp, vp, sz, vp]
     L.moe_timing_arm.restype = ctypes.c_int
     L.moe_timing_arm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int]
     rt = _hip_runtimes()
@@ -172,6 +178,37 @@ def moe_layer_forward(dims: Dims, x, w_router, bias, expert_table, out, flags=0,
                                  _ptr(bias), _ptr(expert_table), _ptr(out), flags, rms_eps,
                                  _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+
+
+def cache_state_bytes(dims: Dims, n_slots: int) -> int:
+    return lib.moe_cache_state_bytes(ctypes.byref(dims.c()), n_slots)
+
+
+def make_cache_state(dims: Dims, n_slots: int, device="cuda"):
+    """A zero-filled cache state (every slot empty)."""
+    import torch
+    n = cache_state_bytes(dims, n_slots)
+    if n == 0:
+        raise ValueError(f"no cache state for {n_slots} slots of {dims}")
+    return torch.zeros(n // 4, dtype=torch.int32, device=device)
+
+
+def cache_header(state) -> dict:
+    """The state's header counters (reads the device buffer)."""
+    h = state[:5].cpu().tolist()
+    return dict(zip(("clock", "hits", "misses", "last_hits", "last_misses"), h))
+
+
+def moe_layer_forward_cached(dims: Dims, x, w_router, bias, home_table, slots, n_slots,
+                             cache_state, out, flags=0, rms_eps=1e-6, stats=None, ws=None,
+                             stream=None):
+    """home_table: int64 device tensor of E blob addresses (e.g. host-mapped
+    pinned memory); slots: device memory for n_slots blobs."""
+    T = x.shape[0]
+    _check(lib.moe_layer_forward_cached(
+        ctypes.byref(dims.c()), _ptr(x), _xdtype(x), T, _ptr(w_router), _ptr(bias),
+        _ptr(home_table), _ptr(slots), n_slots, _ptr(cache_state), _ptr(out), flags, rms_eps,
+        _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)), "moe_layer_forward_cached")
 
 
 def moe_timing_arm(kernel: str, start_events, stop_events):

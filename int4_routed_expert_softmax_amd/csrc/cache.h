@@ -1,0 +1,51 @@
+// HBM slot cache for expert blobs whose home is host memory (or any memory the
+// device can read): placement of a call's union experts into slots, on the
+// device, and the copy of the missed blobs into their slots.  Internal; the
+// entry point is moe_layer_forward_cached (include/moe.h).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Cache state, in caller memory, zero-filled once (= every slot empty):
+//   CacheHeader (32 B)
+//   | slot_of[E]   int32: slot + 1 of a resident expert, 0 = not resident
+//   | expert_of[S] int32: expert + 1 a slot holds, 0 = empty
+//   | stamp[S]     uint32: clock value of the slot's last use
+struct CacheHeader {
+  uint32_t clock;        // calls so far
+  uint32_t hits, misses; // union experts found resident / copied in, over all calls
+  uint32_t last_hits, last_misses;
+  uint32_t pad[3];
+};
+static_assert(sizeof(CacheHeader) == 32, "header layout is part of the ABI");
+
+inline size_t cache_state_bytes(int E, int S) {
+  return sizeof(CacheHeader) + 4 * (size_t)E + 8 * (size_t)S;
+}
+
+// Largest slot count the placement block handles (one thread per slot); no
+// more slots than experts are ever useful, and E <= 1024.
+constexpr int kMaxSlots = 1024;
+
+struct CacheArgs {
+  uint8_t* state;
+  int E, S;
+  uint8_t* slots;            // S slots of blob_bytes each
+  size_t blob_bytes;
+  const uint8_t* const* home;  // [E] every expert's blob where it lives
+  const int32_t* uniq;       // this call's union (ascending ids) and its size
+  const int32_t* n_uniq;
+  DownPlan* plan;            // [U] blob pointers rewritten to the slots
+  const uint8_t** eff;       // [E] this call's expert table (union entries written)
+  const uint8_t** fill_src;  // [min(E, T k)] blobs to copy in, and their slots
+  uint8_t** fill_dst;
+  int32_t* n_fill;
+};
+
+hipError_t launch_cache_place(const CacheArgs& a, hipStream_t s);
+// max_fill: an upper bound on the number of misses (the union's capacity).
+hipError_t launch_cache_fill(const CacheArgs& a, int max_fill, hipStream_t s);
+
+}  // namespace moe

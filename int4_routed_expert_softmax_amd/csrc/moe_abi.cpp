@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "cache.h"
 #include "moe_internal.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -79,6 +80,15 @@ int dims_status(const moe_dims* dm) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The cached layer's table and copy list follow the layout: [E] table
+// pointers, [cap] sources, [cap] destinations, the copy count.
+size_t cache_ws_bytes(int E) {
+  return align_up(8 * (size_t)E) + 2 * align_up(8 * (size_t)kSmallPicks) + align_up(4);
+}
+
+// What every entry point requires of ws_bytes: moe_workspace_bytes(dims, T).
+size_t ws_need(const Layout& L, int E) { return L.total + cache_ws_bytes(E); }
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error: %s", hipGetErrorString(e));
@@ -134,7 +144,12 @@ MOE_API size_t moe_expert_blob_bytes(const moe_dims* dm) {
 
 MOE_API size_t moe_workspace_bytes(const moe_dims* dm, int32_t T_max) {
   if (dims_status(dm) != MOE_OK || T_max < 1) return 0;
-  return layout(dm->d, dm->f, dm->n_experts, dm->top_k, T_max).total;
+  return ws_need(layout(dm->d, dm->f, dm->n_experts, dm->top_k, T_max), dm->n_experts);
+}
+
+MOE_API size_t moe_cache_state_bytes(const moe_dims* dm, int32_t n_slots) {
+  if (dims_status(dm) != MOE_OK || n_slots < 1 || n_slots > dm->n_experts) return 0;
+  return align_up(cache_state_bytes(dm->n_experts, n_slots));
 }
 
 MOE_API const char* moe_strerror(int code) {
@@ -159,7 +174,7 @@ MOE_API int moe_route(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
   if (T < 1 || !x || !w_router || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_EINVAL;
   const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, T);
-  if (ws_bytes < L.total) return MOE_ENOSPC;
+  if (ws_bytes < ws_need(L, dm->n_experts)) return MOE_ENOSPC;
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* z = at<double>(ws, L.z);
   if (T <= kSmallBatch) {
@@ -201,7 +216,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   if (n < 1 || !expert_blob || !x || !y || !ws) return MOE_EINVAL;
   if (!aligned(expert_blob, 16) || !aligned(x, 4) || !aligned(y, 4)) return MOE_EINVAL;
   const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, n);
-  if (ws_bytes < L.total) return MOE_ENOSPC;
+  if (ws_bytes < ws_need(L, dm->n_experts)) return MOE_ENOSPC;
   if (!rows_fit((size_t)n * dm->top_k, dm)) return MOE_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   ExpertList EL{};
@@ -245,7 +260,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
   const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
   const Layout L = layout(d, f, E, k, T);
-  if (ws_bytes < L.total) return MOE_ENOSPC;
+  if (ws_bytes < ws_need(L, dm->n_experts)) return MOE_ENOSPC;
   if (!rows_fit((size_t)T * k, dm)) return MOE_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -352,6 +367,100 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
   }
   MOE_TRY(launch_combine(y, w, resid, out, T, d, k, s));
+  return MOE_OK;
+}
+
+MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
+                                     const float* w_router, const float* bias,
+                                     const void* const* home_table, void* slots, int32_t n_slots,
+                                     void* cache_state, float* out, uint32_t flags, float rms_eps,
+                                     int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+  int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT))
+    return MOE_EUNSUPPORTED;
+  if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
+  if (T < 1 || !x || !w_router || !home_table || !slots || !cache_state || !out || !ws)
+    return MOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4) || !aligned(slots, 256) ||
+      !aligned(cache_state, 4))
+    return MOE_EINVAL;
+  if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
+  const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
+  if (!small_batch(T, k)) return MOE_EUNSUPPORTED;
+  const int cap = E < T * k ? E : T * k;
+  if (n_slots < cap || n_slots > E) return MOE_EUNSUPPORTED;
+  const Layout L = layout(d, f, E, k, T);
+  if (ws_bytes < ws_need(L, E)) return MOE_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  double* z = at<double>(ws, L.z);
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* w = at<float>(ws, L.w);
+  int32_t* uniq = at<int32_t>(ws, L.uniq);
+  int32_t* offs = at<int32_t>(ws, L.offs);
+  int32_t* nuniq = at<int32_t>(ws, L.nuniq);
+  int32_t* rows = at<int32_t>(ws, L.rows);
+  DownPlan* plan = at<DownPlan>(ws, L.plan);
+  const Digits xd = x_digits(ws, L), ad = a_digits(ws, L);
+  size_t o = L.total;
+  const uint8_t** eff = at<const uint8_t*>(ws, o);
+  o += align_up(8 * (size_t)E);
+  const uint8_t** fill_src = at<const uint8_t*>(ws, o);
+  o += align_up(8 * (size_t)kSmallPicks);
+  uint8_t** fill_dst = at<uint8_t*>(ws, o);
+  o += align_up(8 * (size_t)kSmallPicks);
+  int32_t* n_fill = at<int32_t>(ws, o);
+
+  // 1: [RMSNorm], logits, digit split
+  RouterArgs ra{};
+  ra.x = x;
+  ra.x_bf16 = x_dtype == MOE_BF16;
+  ra.T = T;
+  ra.d = d;
+  ra.E = E;
+  ra.k = k;
+  ra.prenorm = (flags & MOE_PRENORM_RMS) != 0;
+  ra.eps = rms_eps;
+  ra.Wr = w_router;
+  ra.bias = bias;
+  ra.z = z;
+  ra.xd = xd;
+  MOE_TRY(launch_router_front(ra, s));
+  // 2: top-k, union and the down plan (blobs at home for now)
+  const uint8_t* const* home = reinterpret_cast<const uint8_t* const*>(home_table);
+  RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, plan};
+  MOE_TRY(launch_route_small(ro, home, s));
+  // 3: placement (the table and the down plan now point at slots), 4: copies
+  CacheArgs ca{};
+  ca.state = static_cast<uint8_t*>(cache_state);
+  ca.E = E;
+  ca.S = n_slots;
+  ca.slots = static_cast<uint8_t*>(slots);
+  ca.blob_bytes = moe_expert_blob_bytes(dm);
+  ca.home = home;
+  ca.uniq = uniq;
+  ca.n_uniq = nuniq;
+  ca.plan = plan;
+  ca.eff = eff;
+  ca.fill_src = fill_src;
+  ca.fill_dst = fill_dst;
+  ca.n_fill = n_fill;
+  MOE_TRY(launch_cache_place(ca, s));
+  MOE_TRY(launch_cache_fill(ca, cap, s));
+  // 5: the single-token kernels on the slots (one gate/up block per row
+  // block, expert and token; each token's arithmetic as in a resident call)
+  ExpertList EL{};
+  EL.table = eff;
+  EL.uniq = uniq;
+  EL.n_uniq = nuniq;
+  EL.offsets = offs;
+  EL.list = rows;
+  EL.kdiv = k;
+  MOE_TRY(launch_gateup(EL, nullptr, cap, d, f, xd, ad, 1, T, s));
+  CombineArgs cb{w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out, T, k};
+  MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, s));
   return MOE_OK;
 }
 

@@ -136,6 +136,38 @@ def test_layer_forward_rejects_bad_arguments():
     assert call(wsb=ws - 256) == moe.MOE_ENOSPC
 
 
+def test_cache_state_sizes():
+    # header (8 words) + slot_of[E] + expert_of[S] + stamp[S], rounded to 256 B
+    assert moe.cache_state_bytes(GLM, 8) == (32 + 4 * 256 + 8 * 8 + 255) // 256 * 256
+    assert moe.cache_state_bytes(GLM, 256) == (32 + 4 * 256 + 8 * 256 + 255) // 256 * 256
+    assert moe.cache_state_bytes(GLM, 0) == 0
+    assert moe.cache_state_bytes(GLM, 257) == 0  # more slots than experts
+
+
+def test_cached_layer_rejects_bad_arguments():
+    d = GLM.c()
+    f = moe.lib.moe_layer_forward_cached
+    ws = moe.workspace_bytes(GLM, 1)
+
+    def call(**kw):
+        a = dict(x=FAKE, dt=moe.MOE_F32, T=1, wr=FAKE, home=FAKE, slots=FAKE, S=8, state=FAKE,
+                 out=FAKE, flags=0, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(ctypes.byref(d), a["x"], a["dt"], a["T"], a["wr"], None, a["home"], a["slots"],
+                 a["S"], a["state"], a["out"], a["flags"], 1e-6, None, a["ws"], a["wsb"], None)
+
+    assert call(home=None) == moe.MOE_EINVAL
+    assert call(slots=None) == moe.MOE_EINVAL
+    assert call(state=None) == moe.MOE_EINVAL
+    assert call(slots=FAKE + 16) == moe.MOE_EINVAL       # slots must be 256-byte aligned
+    assert call(S=7) == moe.MOE_EUNSUPPORTED               # fewer slots than a union can hold
+    assert call(T=2, S=15, wsb=moe.workspace_bytes(GLM, 2)) == moe.MOE_EUNSUPPORTED
+    assert call(S=257) == moe.MOE_EUNSUPPORTED             # more slots than experts
+    assert call(T=9, S=72, wsb=moe.workspace_bytes(GLM, 9)) == moe.MOE_EUNSUPPORTED  # past the small-batch limits
+    assert call(flags=8) == moe.MOE_EUNSUPPORTED
+    assert call(wsb=ws - 256) == moe.MOE_ENOSPC
+
+
 def test_strerror():
     for c in (0, -1, -2, -3, -4, 99):
         assert isinstance(moe.strerror(c), str) and moe.strerror(c)
