@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--host-tier", type=int, default=0, metavar="SLOTS",
+                   help="decode1 / verify8 with one layer's experts in pinned host memory behind an "
+                        "HBM cache of SLOTS expert slots (moe_layer_forward_cached); each step is "
+                        "a new batch of tokens")
     p.add_argument("--batch-invariant", action="store_true",
                    help="verify8: run the batch with MOE_BATCH_INVARIANT (each token computed "
                         "exactly as in a one-token call)")
@@ -117,6 +121,8 @@ def main():
         return run_chain(a)
     a.steps = 200 if a.steps is None else a.steps
     a.warmup = 10 if a.warmup is None else a.warmup
+    if a.host_tier:
+        return run_host_tier(a)
 
     import torch
 
@@ -292,6 +298,99 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
                       "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "blocks": blocks,
                       "frac_per_occupied_cu": round(tf / (MFMA_PEAK_TFLOPS * min(blocks, 256) / 256), 4)}
     return out
+
+
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction, published
+
+
+def run_host_tier(a):
+    """One layer's 256 experts at home in pinned host memory mapped into the
+    device, behind an HBM cache of --host-tier slots.  Every step is a new
+    batch of tokens (warm-up steps fill the cache); misses are copied from
+    host memory by the library's fill kernel, hits are read from HBM.  The
+    step rate includes the copies: what the layer costs when the experts
+    do not all fit in HBM."""
+    import ctypes
+
+    import torch
+
+    import int4_routed_expert_softmax_amd as moe
+    from synth import configs
+
+    w = configs.WORKLOADS[a.workload]
+    if w.T > 8 or w.T * w.top_k > 64:
+        sys.exit(f"--host-tier: {w.name} has T={w.T}, past the cached layer's batch limits")
+    S = a.host_tier
+    dev = torch.device("cuda:0")
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    blob = w.blob_bytes
+    if not (min(w.n_experts, w.T * w.top_k) <= S <= w.n_experts):
+        sys.exit(f"--host-tier {S}: slots must lie in [{min(w.n_experts, w.T * w.top_k)}, "
+                 f"{w.n_experts}]")
+    print(f"bench: {w.name} host tier, pinning {w.n_experts * blob / 1e9:.1f} GB of experts",
+          file=sys.stderr, flush=True)
+    blobs = configs.experts(w, 0)
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    hptr, dptr = ctypes.c_void_p(), ctypes.c_void_p()
+    if hip.hipHostMalloc(ctypes.byref(hptr), ctypes.c_size_t(blobs.nbytes), ctypes.c_uint(2)) != 0:
+        sys.exit("hipHostMalloc failed")
+    try:
+        ctypes.memmove(hptr, blobs.ctypes.data, blobs.nbytes)
+        del blobs
+        if hip.hipHostGetDevicePointer(ctypes.byref(dptr), hptr, ctypes.c_uint(0)) != 0:
+            sys.exit("hipHostGetDevicePointer failed")
+        home = torch.tensor([dptr.value + e * blob for e in range(w.n_experts)], dtype=torch.int64,
+                            device=dev)
+        Wr, bias = configs.router(w, 0)
+        Wr, bias = torch.from_numpy(Wr).to(dev), torch.from_numpy(bias).to(dev)
+        n = a.warmup + a.steps
+        xs = [configs.tokens(w, s)[0] for s in range(n)]
+        x = torch.from_numpy(np.stack(xs)).to(dev)  # [n][T][d]
+        slots = torch.empty(S * blob, dtype=torch.uint8, device=dev)
+        state = moe.make_cache_state(dims, S, dev)
+        out = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+        ws = moe.make_workspace(dims, w.T, dev)
+
+        def step(i):
+            moe.moe_layer_forward_cached(dims, x[i], Wr, bias, home, slots, S, state, out, ws=ws)
+
+        for i in range(a.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        h0 = moe.cache_header(state)
+        t0 = time.perf_counter()
+        for i in range(a.warmup, n):
+            step(i)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / a.steps
+        h1 = moe.cache_header(state)
+    finally:
+        torch.cuda.synchronize()
+        hip.hipHostFree(hptr)
+    hits, misses = h1["hits"] - h0["hits"], h1["misses"] - h0["misses"]
+    host_bytes = misses * blob / a.steps
+    host_gbps = host_bytes / sec / 1e9
+    res = {
+        "metric": METRIC, "value": round(w.T / sec, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
+        "config": {"workload": f"{w.name} host tier: one layer, d={w.d} f={w.f} E={w.n_experts} "
+                               f"top-{w.top_k}, T={w.T}, experts in pinned host memory behind "
+                               f"{S} HBM slots, a new batch of tokens per step",
+                   "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
+                   "slots": S},
+        "cache": {"hit_rate": round(hits / max(hits + misses, 1), 4),
+                  "hits_per_step": round(hits / a.steps, 3),
+                  "misses_per_step": round(misses / a.steps, 3),
+                  "host_bytes_per_step": round(host_bytes),
+                  # copied bytes over the whole step time (copies and compute):
+                  # a lower bound on the link rate the copy kernel reaches
+                  "host_GBps_over_step": round(host_gbps, 2),
+                  "host_link_peak_GBps": HOST_LINK_PEAK_GBPS},
+    }
+    print(json.dumps(res), flush=True)
 
 
 def run_chain(a):
