@@ -26,6 +26,7 @@
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "pack.h"
 #include "select.h"
 
 namespace moe {
@@ -226,10 +227,14 @@ __device__ __forceinline__ void publish_small_route(const RouteOut& ro, const Sm
 // Routing of a small batch in one block: top-k and union (the single-token
 // gate/up kernel does the same in its own prologue, with the same per-token
 // arithmetic), and the down plan when ro.plan is set (table: the expert
-// table, read only then).
-__global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t* const* table) {
+// table, read only then).  With px.mbo set, wave 15 also writes the union's
+// M-block map for the grouped GEMM.
+__global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t* const* table,
+                                                      PackArgs px) {
   __shared__ SmallRoute sr;
-  small_route(ro, sr, threadIdx.x >> 6, 16);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  small_route(ro, sr, wave, 16);
+  if (px.mbo && wave == 15) mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, lane);
   publish_small_route(ro, sr, table, 1024);
 }
 
@@ -689,9 +694,19 @@ hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digit
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
 }
 
-hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s) {
+hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s,
+                              const PackArgs* map) {
   if (ro.plan && !table) return hipErrorInvalidValue;
-  return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table);
+  PackArgs px{};
+  if (map) {
+    // one wave maps a union of at most 64 experts
+    if (!map->mbo || !map->blk_u || map->mblock < 1 || ro.T * ro.k > 64)
+      return hipErrorInvalidValue;
+    px.mbo = map->mbo;
+    px.blk_u = map->blk_u;
+    px.mblock = map->mblock;
+  }
+  return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table, px);
 }
 
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,

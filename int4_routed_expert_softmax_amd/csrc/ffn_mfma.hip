@@ -33,6 +33,7 @@
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "pack.h"
 
 namespace moe {
 
@@ -44,10 +45,7 @@ typedef __attribute__((address_space(1))) const u32x4* g_u32x4_ptr;
 
 constexpr int kNt = 4;                                  // 16-row N-tiles per wave
 constexpr int kWaveRows = kNt * 16;                     // weight rows per wave
-constexpr int kPackExp = 14;                            // packed |x'| < 2^14
 constexpr float kBias = 1032.0f;
-
-__device__ __forceinline__ int slot_of_col(int e) { return 2 * (e & 3) + (e >> 2); }
 
 __device__ __forceinline__ u32x4 nt_load16(const uint8_t* p) {
   return __builtin_nontemporal_load((g_u32x4_ptr)(p));
@@ -81,40 +79,9 @@ __device__ __forceinline__ int find_bucket(const int32_t* p, int n, int j) {
 }
 
 // ---------------------------------------------------------------- packing
-// One wave per row: max |v| over the row, then x' = fp16(v * 2^(14 - e)) with
-// max|v| < 2^e, columns permuted within blocks of 8; unit[r] = 2^(e - 14).
-// With mbo set, the last block instead writes the union's M-block prefix: mbo[u] = sum over u' < u of
-// ceil(count(u') / mblock), u = 0..U.
-struct PackArgs {
-  const void* src;
-  int src_bf16, K, rows;
-  const int32_t* gather;  // source row of row r (nullptr: r)
-  _Float16* dst;          // [rows][K]
-  float* unit;            // [rows]
-  const int32_t* offsets;
-  const int32_t* n_uniq;
-  int32_t* mbo;
-  int32_t* blk_u;
-  int mblock;
-};
-
-__device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float (&v)[8]) {
-  if (bf16) {
-    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
-    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(w[j] << 16);
-      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
-    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
-    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
-    v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
-  }
-}
-
+// One wave per row (pack.h); with mbo set, the last block instead writes the
+// union's M-block prefix: mbo[u] = sum over u' < u of ceil(count(u') /
+// mblock), u = 0..U.
 __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   if (p.mbo && blockIdx.x == gridDim.x - 1) {
     __shared__ int s_tot[4];
@@ -150,30 +117,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   }
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= p.rows) return;
-  const int lane = threadIdx.x & 63;
-  const size_t src_row = p.gather ? (size_t)p.gather[r] : (size_t)r;
-  const size_t base = src_row * p.K;
-  float m = 0.0f;
-  for (int c = lane * 8; c < p.K; c += 512) {
-    float v[8];
-    load8(p.src, p.src_bf16, base + c, v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-  }
-  m = wave_max(m);
-  int e = 0;
-  if (m > 0.0f) frexpf(m, &e);  // m < 2^e
-  const float up = m > 0.0f ? ldexpf(1.0f, kPackExp - e) : 1.0f;
-  _Float16* drow = p.dst + (size_t)r * p.K;
-  for (int c = lane * 8; c < p.K; c += 512) {
-    float v[8];
-    load8(p.src, p.src_bf16, base + c, v);
-    f16x8 h;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[slot_of_col(j)] = (_Float16)(v[j] * up);
-    *reinterpret_cast<f16x8*>(drow + c) = h;
-  }
-  if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
+  pack_row(p, r, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------- projection
@@ -258,8 +202,10 @@ constexpr int copies_ahead() {
 }
 // copies per wave and stage: 4 (codes) + kACopies (activations: wave w copies
 // rows kARows w .. kARows (w + 1) - 1), plus 1 (scales) in stages 0, 4, 8, ...
-// A wave whose first row lies past the block's last M-tile copies no
-// activations; rows past the block's tokens copy the last token's row.
+// A wave whose first row lies past the block's last token copies no
+// activations (the A rows it would fill only feed output rows that are never
+// stored: an MFMA output row depends on its own A row alone); rows past the
+// block's tokens in a wave that does copy take the last token's row.
 
 // One block: 8 waves, each owning 64 weight rows, times one M-block of up to
 // 64 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
@@ -349,9 +295,9 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
 
   const int nst = K / kSC;
-  // a wave copies its activation rows only when the first lies in a used
-  // M-tile (wave-uniform)
-  const bool a_copy = kARows * wave < 16 * nmt;
+  // a wave copies its activation rows only when the first is one of the
+  // block's tokens (wave-uniform)
+  const bool a_copy = kARows * wave < min(kMBlock, cnt - tok0);
   auto issue = [&](int st) {
     uint8_t* base = s_lds + (st % kRing) * kStage;
     const uint32_t so = (uint32_t)st * (kSC / 2);
@@ -488,10 +434,8 @@ int mfma_mblock(int rows) { return gemm_shape(rows, false).mblock; }
 
 bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 
-hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
+PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   const ExpertList& L = m.L;
-  hipError_t e;
-  // x rows -> fp16 (and the union's M-block map)
   PackArgs px{};
   px.src = m.x;
   px.src_bf16 = m.x_bf16;
@@ -507,9 +451,19 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     px.blk_u = m.blk_u;
     px.mblock = gemm_shape(m.x_rows, false).mblock;
   }
-  const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
-  e = launch(4, k_pack, dim3(gx), dim3(256), s, px);
-  if (e != hipSuccess) return e;
+  return px;
+}
+
+hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
+  const ExpertList& L = m.L;
+  hipError_t e;
+  if (!m.x_packed) {
+    // x rows -> fp16 (and the union's M-block map)
+    const PackArgs px = mfma_x_pack_args(m);
+    const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
+    e = launch(4, k_pack, dim3(gx), dim3(256), s, px);
+    if (e != hipSuccess) return e;
+  }
 
   const GemmShape sh = gemm_shape(m.x_rows, L.single != nullptr);
   const int gw = sh.gw, mblock = sh.mblock;

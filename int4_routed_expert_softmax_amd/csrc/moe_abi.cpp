@@ -330,6 +330,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     xr = xn;
     xr_bf16 = 0;
   }
+  int x_packed = 0;
   if (small_batch(T, k)) {
     // a few tokens on the grouped GEMM: logits (+ bias) by the small-batch
     // router front end, top-k and union in one block
@@ -343,9 +344,24 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     ra.Wr = w_router;
     ra.bias = bias;
     ra.z = z;
-    MOE_TRY(launch_router_front(ra, s));
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, nullptr};
-    MOE_TRY(launch_route_small(ro, nullptr, s));
+    if (mfma_shape_ok(d, f)) {
+      // the grouped GEMM's x pack runs in extra workgroups of the router
+      // front end and its M-block map in the routing block: two launches
+      // fewer than the pack kernel's
+      MfmaArgs m = mfma_args(ws, L, d, f);
+      m.L = EL;
+      m.x = xr;
+      m.x_bf16 = xr_bf16;
+      m.x_rows = T;
+      ra.px = mfma_x_pack_args(m);
+      MOE_TRY(launch_router_front(ra, s));
+      MOE_TRY(launch_route_small(ro, nullptr, s, &ra.px));
+      x_packed = 1;
+    } else {
+      MOE_TRY(launch_router_front(ra, s));
+      MOE_TRY(launch_route_small(ro, nullptr, s));
+    }
   } else {
     MOE_TRY(launch_logits(xr, xr_bf16, T, d, E, w_router, z, s));
     MOE_TRY(launch_topk(z, kLogSplit, bias, T, E, k, idx, w, s));
@@ -360,6 +376,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.slots = T * k;
     m.mb_bound = maxU + (T * k + mfma_mblock(T) - 1) / mfma_mblock(T);
     m.y = y;
+    m.x_packed = x_packed;
     MOE_TRY(launch_ffn_mfma(m, s));
   } else {
     MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));

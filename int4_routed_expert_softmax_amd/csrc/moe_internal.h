@@ -82,6 +82,21 @@ hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s,
 
 // Arguments of the small-batch router front end (optional RMSNorm, logits and
 // digit split in one launch; xd.q == nullptr skips the digit split).
+// Rows of activations to pack into the grouped GEMM's fp16 A operand (one
+// power of two per row), and optionally the union's M-block map.
+struct PackArgs {
+  const void* src;
+  int src_bf16, K, rows;
+  const int32_t* gather;  // source row of row r (nullptr: r)
+  _Float16* dst;          // [rows][K]
+  float* unit;            // [rows]
+  const int32_t* offsets;
+  const int32_t* n_uniq;
+  int32_t* mbo;
+  int32_t* blk_u;
+  int mblock;
+};
+
 struct RouterArgs {
   const void* x;
   int x_bf16, T, d, E, k, prenorm;
@@ -90,6 +105,7 @@ struct RouterArgs {
   const float* bias;
   double* z;
   Digits xd;
+  PackArgs px;  // px.dst set: workgroups past the logits and digit split pack px.rows rows
 };
 constexpr int kSmallBatch = 8;
 // The small-batch path recomputes routing inside the gate/up kernel with one
@@ -128,8 +144,11 @@ struct RouteOut {
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s);
 // Top-k and union of a small batch from complete logits (ro.z), written to
 // ro's outputs; with ro.plan set, also the down plan, whose blob addresses
-// come from the expert table (else table may be null).
-hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s);
+// come from the expert table (else table may be null).  With map (not null),
+// the same block also writes the union's M-block map for the grouped GEMM
+// (map->mbo, map->blk_u, in M-blocks of map->mblock tokens).
+hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, hipStream_t s,
+                              const PackArgs* map = nullptr);
 hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hipStream_t s);
 // Logits of batches past the small-batch limits: kLogSplit partial sums per
 // logit, zp[s][t][e] (no bias); launch_topk(nsplit = kLogSplit, bias) adds
@@ -185,7 +204,10 @@ struct MfmaArgs {
   int32_t* mbo;              // [n_experts + 1]
   int32_t* blk_u;            // [mb_bound]
   float* y;
+  int x_packed;              // xh, xunit and the M-block map are already written
 };
+// The x pack (and M-block map) launch_ffn_mfma would run for m.
+PackArgs mfma_x_pack_args(const MfmaArgs& m);
 // M-block (tokens per GEMM block) for a batch of `rows` activation rows.
 int mfma_mblock(int rows);
 constexpr int kMinMBlock = 16;

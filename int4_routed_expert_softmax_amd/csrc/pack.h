@@ -1,0 +1,93 @@
+// Activation rows -> the grouped GEMM's fp16 A operand, and the union's
+// M-block map.  Used by k_pack (any batch) and by the one-block small-batch
+// routing kernel, which packs the batch's rows after routing it.
+//
+// A row is scaled by a power of two so that max|v| < 2^14 and rounded to fp16
+// (relative 2^-12): x' = fp16(v * 2^(14 - e)) with max|v| < 2^e, and
+// unit[r] = 2^(e - 14), so x = x' * unit.  Within every block of 8 columns,
+// position p holds column (p >> 1) + 4 (p & 1): the order in which the GEMM's
+// dequantisation splits a 32-bit word of 8 codes into fp16 pairs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kPackExp = 14;  // packed |x'| < 2^14
+
+__device__ __forceinline__ int slot_of_col(int e) { return 2 * (e & 3) + (e >> 2); }
+
+__device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float (&v)[8]) {
+  if (bf16) {
+    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + i);
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + i + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
+    v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  }
+}
+
+// Row r of p, by one whole wave (lane = its lane).
+__device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
+  const size_t src_row = p.gather ? (size_t)p.gather[r] : (size_t)r;
+  const size_t base = src_row * p.K;
+  float m = 0.0f;
+  for (int c = lane * 8; c < p.K; c += 512) {
+    float v[8];
+    load8(p.src, p.src_bf16, base + c, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  int e = 0;
+  if (m > 0.0f) frexpf(m, &e);  // m < 2^e
+  const float up = m > 0.0f ? ldexpf(1.0f, kPackExp - e) : 1.0f;
+  _Float16* drow = p.dst + (size_t)r * p.K;
+  for (int c = lane * 8; c < p.K; c += 512) {
+    float v[8];
+    load8(p.src, p.src_bf16, base + c, v);
+    _Float16 h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[slot_of_col(j)] = (_Float16)(v[j] * up);
+    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+    f16x8_t hv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hv[j] = h[j];
+    *reinterpret_cast<f16x8_t*>(drow + c) = hv;
+  }
+  if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
+}
+
+// M-block map of a union of at most 64 experts (offs[0..U]), by one whole
+// wave: mbo[u] = sum over u' < u of ceil(count(u') / mblock), mbo[U] the
+// total, and blk_u[j] = the expert of M-block j.
+__device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int mblock,
+                                                int32_t* mbo, int32_t* blk_u, int lane) {
+  const int c = lane < U ? (offs[lane + 1] - offs[lane] + mblock - 1) / mblock : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int nb = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += nb;
+  }
+  const int run = incl - c;
+  if (lane < U) {
+    mbo[lane] = run;
+    for (int j = 0; j < c; ++j) blk_u[run + j] = lane;
+  }
+  if (lane == 63) mbo[U] = incl;
+}
+
+}  // namespace moe

@@ -13,6 +13,7 @@
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "pack.h"
 #include "select.h"
 
 namespace moe {
@@ -185,6 +186,17 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, d = a.d, E = a.E;
+  // the last (rows + 3) / 4 workgroups pack the rows for the grouped GEMM,
+  // one wave per row, alongside the logits
+  const int pack_blocks = a.px.dst ? (a.px.rows + 3) / 4 : 0;
+  if (pack_blocks) {
+    const int pb = (int)gridDim.x - pack_blocks;
+    if (e >= pb) {
+      const int r = (e - pb) * 4 + wave;
+      if (r < a.px.rows) pack_row(a.px, r, lane);
+      return;
+    }
+  }
   __shared__ double part[TB][4];
   __shared__ double s_r[TB];
 
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     // workgroups past the last expert: the digit split, one wave per 64
     // columns of a token
     const int nb = d / 64, nch = d / kChunk, ng = d / kXGroup;
-    for (int it = (e - E) * 4 + wave; it < T * nb; it += (gridDim.x - E) * 4) {
+    for (int it = (e - E) * 4 + wave; it < T * nb; it += ((int)gridDim.x - E - pack_blocks) * 4) {
       const int t = it / nb, col = (it % nb) * 64 + lane;
       digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
                  a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
@@ -369,7 +381,9 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s) {
   const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + 3) / 4 : 0;
-  const dim3 grid(a.E + dig_blocks);
+  if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1)) return hipErrorInvalidValue;
+  const int pack_blocks = a.px.dst ? (a.px.rows + 3) / 4 : 0;
+  const dim3 grid(a.E + dig_blocks + pack_blocks);
   if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(256), s, a);
   if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(256), s, a);
   if (a.T <= 4) return launch(1, k_router_front<4>, grid, dim3(256), s, a);
