@@ -71,7 +71,7 @@ def calibrate_copy(mib):
 
 
 # Sources the decode gate/up kernel is built from.
-GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "select.h")
+GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h")
 
 
 def kernel_source_hash():
@@ -198,6 +198,17 @@ def main():
     assert all(c == K for c in counts.values()), counts
     dur = {k: np.array([s.elapsed_time(e) for s, e in zip(*ev[k])]) * 1e-3 for k in ev}  # seconds
 
+    # and once more with an event pair around every step (their spread)
+    sev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+           [torch.cuda.Event(enable_timing=True) for _ in range(K)])
+    torch.cuda.synchronize()
+    for i in range(K):
+        sev[0][i].record()
+        step(i)
+        sev[1][i].record()
+    torch.cuda.synchronize()
+    step_us = np.array([s_.elapsed_time(e_) for s_, e_ in zip(*sev)]) * 1e3
+
     sec = (t1 - t0) / K
     u_steps = np.array([U[i % a.layers] for i in range(K)])
     tok_s = w.T / sec
@@ -227,6 +238,7 @@ def main():
                                + (", MOE_BATCH_INVARIANT" if inv else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "layers_rotated": a.layers, "distinct_experts_per_step": float(u_steps.mean())},
+        "step_us_p10_p50_p90": [round(float(v), 2) for v in np.percentile(step_us, [10, 50, 90])],
         "expert_weight_GBps": round(weight_bytes_step / sec / 1e9, 1),
         "expert_weight_frac_hbm_peak": round(weight_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gateup (gate+up projections, SwiGLU)",
@@ -234,12 +246,18 @@ def main():
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": committed_traffic(w.name),
                      "bytes_per_launch": float(gu_bytes.mean()),
-                     "avg_launch_us": round(float(dur["gateup"].mean() * 1e6), 3)},
+                     "avg_launch_us": round(float(dur["gateup"].mean() * 1e6), 3),
+                     "launch_us_p10_p50_p90": [round(float(v) * 1e6, 3) for v in
+                                               np.percentile(dur["gateup"], [10, 50, 90])]},
         "roofline_down": {"bound": "hbm", "achieved": round(dn_gbps, 1), "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "bytes_per_launch": float(dn_bytes.mean()),
                           "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
     }
+    ceil = hbm_ceiling(moe, torch)
+    res["hbm_read_ceiling"] = ceil
+    res["roofline"]["frac_of_read_ceiling"] = round(gu_gbps / ceil["GBps"], 4)
+    res["roofline_down"]["frac_of_read_ceiling"] = round(dn_gbps / ceil["GBps"], 4)
     if w.T > 8:
         res["mfma"] = mfma_figures(moe, torch, w, layers[0], dims, gu_bytes, dur, U)
     if not a.no_cpu:
@@ -248,6 +266,36 @@ def main():
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+
+
+def hbm_ceiling(moe, torch, gib=4):
+    """Read bandwidth of a plain streaming kernel (moe_hbm_read_probe) over
+    `gib` GiB, far past the 256 MB Infinity Cache: the best of a few grid
+    sizes, each timed with HIP events over 5 launches after one untimed."""
+    n = gib << 30
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+        moe.moe_hbm_read_probe(buf, sink, blocks)
+        reps = 5
+        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(reps)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(reps)])
+        h = moe.moe_timing_arm("read_probe", *ev)
+        for _ in range(reps):
+            moe.moe_hbm_read_probe(buf, sink, blocks)
+        torch.cuda.synchronize()
+        assert moe.moe_timing_disarm(h) == reps
+        t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
+        gbps = n / t / 1e9
+        if best is None or gbps > best["GBps"]:
+            best = {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "bytes": n, "blocks": blocks}
+    del buf
+    torch.cuda.empty_cache()
+    best["kind"] = ("plain streaming read kernel (16-byte non-temporal loads, 8 in flight per "
+                    "lane), best grid of 1024/2048/4096/8192 blocks x 256 threads")
+    return best
 
 
 def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):

@@ -261,7 +261,8 @@ enum {
   MOE_KERNEL_GATEUP = 5, /* gate/up projections + SwiGLU (the largest byte stream) */
   MOE_KERNEL_DOWN = 6,   /* down projection */
   MOE_KERNEL_COMBINE = 7,
-  MOE_KERNEL_COUNT = 8
+  MOE_KERNEL_READ_PROBE = 8, /* moe_hbm_read_probe */
+  MOE_KERNEL_COUNT = 9
 };
 /*
  * moe_timing_arm — the next n launches of `kernel` record start_events[i]
@@ -274,6 +275,24 @@ enum {
  * Process-wide state: not for concurrent use from several threads.
  */
 int moe_timing_arm(int kernel, void* const* start_events, void* const* stop_events, int n);
+
+/*
+ * moe_hbm_read_probe — measurement helper, not part of the layer: one kernel
+ * that streams `bytes` bytes of device memory at `buf` (16-byte aligned,
+ * bytes a multiple of 16) through non-temporal 16-byte loads, eight in
+ * flight per lane, over `blocks` workgroups of 256 threads.  Timed over a
+ * buffer far larger than the 256 MB Infinity Cache, it gives the read
+ * bandwidth a plain kernel reaches on the device, the ceiling against which
+ * the expert kernels' achieved GB/s is also read (besides the published peak).
+ * `sink` is device memory of blocks * 256 uint32 words; the kernel writes a
+ * word only when its XOR of the data equals a fixed key (so the loads
+ * cannot be elided), which callers must not rely on either way.  Enqueued on
+ * `stream`; never synchronises.  MOE_EINVAL for null pointers, a misaligned
+ * buffer, bytes == 0 or not a multiple of 16, or blocks < 1; MOE_EHIP when
+ * the launch fails.
+ */
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,11 +23,11 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 # Every function include/moe.h declares.
 EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_route",
            "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_cache_state_bytes",
-           "moe_layer_forward_cached", "moe_timing_arm")
+           "moe_layer_forward_cached", "moe_timing_arm", "moe_hbm_read_probe")
 
 # Kernel ids for moe_timing_arm.
 KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
-           "down": 6, "combine": 7}
+           "down": 6, "combine": 7, "read_probe": 8}
 
 
 class MoeError(RuntimeError):
@@ -98,6 +98,8 @@ def _load():
                                            u32, ctypes.c_float, vp, vp, sz, vp]
     L.moe_timing_arm.restype = ctypes.c_int
     L.moe_timing_arm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int]
+    L.moe_hbm_read_probe.restype = ctypes.c_int
+    L.moe_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     rt = _hip_runtimes()
     if len(rt) > 1:
         raise ImportError(f"more than one HIP runtime is loaded: {rt}")
@@ -234,3 +236,11 @@ def moe_timing_arm(kernel: str, start_events, stop_events):
 def moe_timing_disarm(handle) -> int:
     """Disarm; returns how many launches were recorded."""
     return lib.moe_timing_arm(handle[0], None, None, 0)
+
+
+def moe_hbm_read_probe(buf, sink, blocks: int, stream=None):
+    """Stream all bytes of the device tensor buf (a plain read kernel: the
+    measured HBM ceiling); sink: int32 device tensor of blocks * 256 words."""
+    assert sink.numel() * sink.element_size() >= blocks * 256 * 4
+    _check(lib.moe_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), blocks,
+                                  _stream(stream)), "moe_hbm_read_probe")

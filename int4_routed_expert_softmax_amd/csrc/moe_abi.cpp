@@ -58,7 +58,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   return L;
 }
 
-TimingSlot g_timing[8];
+TimingSlot g_timing[MOE_KERNEL_COUNT];
 
 }  // namespace moe
 
@@ -491,4 +491,13 @@ MOE_API int moe_timing_arm(int kernel, void* const* start_events, void* const* s
   t.n = n;
   t.next = 0;
   return recorded;
+}
+
+MOE_API int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                               void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || blocks < 1) return MOE_EINVAL;
+  if (!aligned(buf, 16)) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(launch_read_probe(buf, bytes, sink, blocks, s));
+  return MOE_OK;
 }

@@ -66,7 +66,7 @@ struct TimingSlot {
   hipEvent_t const* stop = nullptr;
   int n = 0, next = 0;
 };
-extern TimingSlot g_timing[8];
+extern TimingSlot g_timing[9];
 
 template <typename K, typename... Args>
 hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
@@ -80,8 +80,6 @@ hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s,
   return hipGetLastError();
 }
 
-// Arguments of the small-batch router front end (optional RMSNorm, logits and
-// digit split in one launch; xd.q == nullptr skips the digit split).
 // Rows of activations to pack into the grouped GEMM's fp16 A operand (one
 // power of two per row), and optionally the union's M-block map.
 struct PackArgs {
@@ -97,6 +95,8 @@ struct PackArgs {
   int mblock;
 };
 
+// Arguments of the small-batch router front end (optional RMSNorm, logits and
+// digit split in one launch; xd.q == nullptr skips the digit split).
 struct RouterArgs {
   const void* x;
   int x_bf16, T, d, E, k, prenorm;
@@ -221,5 +221,9 @@ inline bool gemv_small_path(int T, int k, int d, int f) {
   return small_batch(T, k) && !(T >= kMfmaMinTokens && mfma_shape_ok(d, f));
 }
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s);
+// Streaming read of bytes (a multiple of 16) with `blocks` workgroups of 256
+// threads; sink holds blocks * 256 words and is written only in practice never.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t s);
 
 }  // namespace moe

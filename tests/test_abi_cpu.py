@@ -168,6 +168,17 @@ def test_cached_layer_rejects_bad_arguments():
     assert call(wsb=ws - 256) == moe.MOE_ENOSPC
 
 
+def test_read_probe_rejects_bad_arguments():
+    # validation happens before anything touches a device
+    L = moe.lib
+    assert L.moe_hbm_read_probe(None, 1 << 20, 16, 4, None) == moe.MOE_EINVAL
+    assert L.moe_hbm_read_probe(64, 1 << 20, None, 4, None) == moe.MOE_EINVAL
+    assert L.moe_hbm_read_probe(64, 0, 16, 4, None) == moe.MOE_EINVAL
+    assert L.moe_hbm_read_probe(64, 1000, 16, 4, None) == moe.MOE_EINVAL
+    assert L.moe_hbm_read_probe(64, 1 << 20, 16, 0, None) == moe.MOE_EINVAL
+    assert L.moe_hbm_read_probe(72, 1 << 20, 16, 4, None) == moe.MOE_EINVAL
+
+
 def test_strerror():
     for c in (0, -1, -2, -3, -4, 99):
         assert isinstance(moe.strerror(c), str) and moe.strerror(c)
