@@ -613,9 +613,9 @@ def cpu_baseline_chain(w, seconds):
                                  eps=1e-6)["out"].astype(np.float32)
         t_ffn += time.perf_counter() - t1
         n += 1
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle.omp_threads()
     return {"value": round(n / t_ffn / w.layers, 5), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n} chained layers of step 0 (fp64 C oracle, OpenMP over output rows; "
                       f"expert generation excluded), {t_ffn:.1f} s"}
 
@@ -629,19 +629,40 @@ def cpu_baseline(w, seconds):
     Wr, bias = configs.router(w, 0)
     table = list(configs.experts(w, 0))
     x, bf = configs.tokens(w, 0)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        t = n % x.shape[0]
-        oracle.layer_forward(x[t:t + 1], Wr, bias, table, w.d, w.f, w.top_k, x_bf16=bf)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(secs):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            t = n % x.shape[0]
+            oracle.layer_forward(x[t:t + 1], Wr, bias, table, w.d, w.f, w.top_k, x_bf16=bf)
+            n += 1
+            if time.perf_counter() - t0 >= secs:
+                break
+        return n, time.perf_counter() - t0
+
+    cores = oracle.omp_threads()
+    n, dt = run(seconds)
+    # the same oracle on one thread, over a quarter of the time
+    oracle.omp_threads(1)
+    n1, dt1 = run(seconds / 4)
+    oracle.omp_threads(cores)
     return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} single-token forwards of {w.name} layer 0 (fp64 C oracle, OpenMP over "
-                      f"output rows), {dt:.1f} s"}
+                      f"output rows), {dt:.1f} s",
+            "value_1thread": round(n1 / dt1, 4),
+            "sample_1thread": f"{n1} forwards on 1 thread, {dt1:.1f} s",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

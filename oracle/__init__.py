@@ -31,6 +31,16 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def omp_threads(n: int | None = None) -> int:
+    """Threads the oracle's OpenMP loops use (the process's libgomp, which
+    the oracle library links); with n, set them first."""
+    lib()
+    gomp = ctypes.CDLL("libgomp.so.1")
+    if n is not None:
+        gomp.omp_set_num_threads(int(n))
+    return int(gomp.omp_get_max_threads())
+
+
 def lib():
     global _lib
     if _lib is None:
