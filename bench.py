@@ -337,10 +337,11 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
         assert moe.moe_timing_disarm(h) == reps
         t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
         flops = 2.0 * n * w.d * 2 * w.f
-        # the library's block shape for one expert: 2 waves x 64 tokens from 128
-        # rows on, else 8 waves x 64 tokens (2 x 16 at up to 16 rows)
-        gw = 2 if n >= 128 or n <= 16 else 8
-        blocks = (w.f // 32 // gw) * ((n + 63) // 64)
+        # the library's block shape for one expert: 2 waves x 64 rows x 64 tokens
+        # from 128 rows on (2 x 64 x 16 at up to 16 rows), else 16 waves x 32
+        # rows x 64 tokens: 128 or 512 weight rows a block
+        a_cols = 64 if n >= 128 or n <= 16 else 256
+        blocks = (w.f // a_cols) * ((n + 63) // 64)
         tf = flops / t / 1e12
         out[label] = {"expert": e, "M": n, "gateup_us": round(t * 1e6, 2), "tflops": round(tf, 1),
                       "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "blocks": blocks,

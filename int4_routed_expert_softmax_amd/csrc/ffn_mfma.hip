@@ -16,10 +16,11 @@
 // q * s stays a normal fp16 number for 2^-14 <= |s| <= 2^12; smaller scales
 // lose relative precision gradually (fp16 subnormals), larger ones overflow.
 //
-// Work unit: one block (8 waves, or 2 for batches of up to 16 rows) = one
-// expert x one M-block of up to 64 (16) of its tokens x 512 (128) weight rows
-// (64 per wave; gate/up: 32 rows of gate and the same 32 rows of up, so
-// SwiGLU is local to the wave).  K is walked in 128-column
+// Work unit: one block (16 waves of 32 weight rows, or 2 waves of 64 rows for
+// batches of up to 16 rows and for one expert over many tokens) = one expert x
+// one M-block of up to 64 (16) of its tokens x 512 (128) weight rows (gate/up:
+// a wave's rows are half gate rows and the same rows of up, so SwiGLU is
+// local to the wave).  K is walked in 128-column
 // stages copied global -> LDS without passing through registers, into a ring
 // of 3 stages; the A and B fragments come from LDS.  d and f must be multiples
 // of 512.
@@ -43,8 +44,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4* g_u32x4_ptr;
 
-constexpr int kNt = 4;                                  // 16-row N-tiles per wave
-constexpr int kWaveRows = kNt * 16;                     // weight rows per wave
 constexpr float kBias = 1032.0f;
 
 __device__ __forceinline__ u32x4 nt_load16(const uint8_t* p) {
@@ -160,23 +159,27 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 //                              p ^ ((r >> 1) & 3) ^ ((r >> 3) & 1)
 //   A  [64 rows][256 B]        packed activations; piece p (8 columns) of row r
 //                              at slot p ^ (r & 15)
-// followed by per-wave scales, two buffers of [64 rows][8 groups] fp16 (8
+// followed by per-wave scales, two buffers of [wave rows][8 groups] fp16 (8
 // groups = 4 stages), refilled every 4 stages.
 constexpr int kSC = 128;
-constexpr int kBWave = kWaveRows * (kSC / 2);
-constexpr int kScaleWave = 2 * kWaveRows * 16;
-// Block shapes: GW waves (GW x 64 weight rows) x an M-block of 8 GW tokens
-// (each wave copies 8 activation rows), over a ring of R stages (R - 1 in
-// flight).  GW = 8, R = 3, MB = 64: 160 KB, one block per CU (prefill); GW =
-// 2, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB, two or three blocks per
-// CU, so a batch of a few tokens over a dozen experts keeps enough bytes in
-// flight; GW = 2, MB = 64, R = 3: 76 KB, one expert over many tokens spread
-// over four times as many blocks as the 8-wave shape gives it.
+// Block shapes: GW waves (GW x 16 NTW weight rows) x an M-block of MB tokens
+// (each wave copies MB / GW activation rows), over a ring of R stages (R - 1
+// in flight).  GW = 16, NTW = 2, R = 3, MB = 64: 160 KB, one block per CU,
+// four waves per SIMD (prefill; 8 waves of 64 rows in the same LDS were 2%
+// slower); GW = 2, NTW = 4, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB,
+// two or three blocks per CU, so a batch of a few tokens over a dozen experts
+// keeps enough bytes in flight; GW = 2, NTW = 4, MB = 64, R = 3: 76 KB, one
+// expert over many tokens spread over more blocks than the 16-wave shape
+// gives it.
 // The scale pieces are double-buffered (4 stages each): a piece is refilled
 // R - 1 stages before its first use, which must come after the last use of the
 // piece two back, so R <= 5.
-template <int GW, int R, int MB>
+template <int GW, int R, int MB, int NTW>
 struct RingShape {
+  static constexpr int kNt = NTW;                 // 16-row N-tiles per wave
+  static constexpr int kWaveRows = 16 * NTW;      // weight rows per wave
+  static constexpr int kBWave = kWaveRows * (kSC / 2);
+  static constexpr int kScaleWave = 2 * kWaveRows * 16;  // two buffers of [rows][8 groups]
   static constexpr int kRing = R;
   static constexpr int kMBlock = MB;
   static constexpr int kARows = MB / GW;       // activation rows copied per wave
@@ -188,32 +191,36 @@ struct RingShape {
   static constexpr int kLdsBytes = kScaleOff + GW * kScaleWave;
   static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
   static_assert(R >= 3 && R <= 5, "ring depth");
-  static_assert(MB % 16 == 0 && kARows % 8 == 0, "whole M-tiles, whole copies");
+  static_assert(MB % 16 == 0 && kARows % 4 == 0, "whole M-tiles, whole copies");
+  static_assert(NTW == 2 || NTW == 4, "gate/up rows split evenly into gate and up");
 };
 
 // Copies a wave has in flight after issuing stages st + 1 .. st + R - 2, with
 // st % 4 == PH: 4 code copies, NA activation copies, and a scale copy in
 // stages that are multiples of 4.
-template <int R, int PH, int NA>
+template <int R, int PH, int NB, int NA>
 constexpr int copies_ahead() {
   int c = 0;
-  for (int i = 1; i <= R - 2; ++i) c += 4 + NA + (((PH + i) & 3) == 0 ? 1 : 0);
+  for (int i = 1; i <= R - 2; ++i) c += NB + NA + (((PH + i) & 3) == 0 ? 1 : 0);
   return c;
 }
-// copies per wave and stage: 4 (codes) + kACopies (activations: wave w copies
+// copies per wave and stage: NTW (codes, 16 rows each) + kACopies (activations: wave w copies
 // rows kARows w .. kARows (w + 1) - 1), plus 1 (scales) in stages 0, 4, 8, ...
 // A wave whose first row lies past the block's last token copies no
 // activations (the A rows it would fill only feed output rows that are never
 // stored: an MFMA output row depends on its own A row alone); rows past the
 // block's tokens in a wave that does copy take the last token's row.
 
-// One block: 8 waves, each owning 64 weight rows, times one M-block of up to
-// 64 tokens of one expert.  Stage st is copied while stage st - 2 is computed;
+// One block: GW waves, each owning 16 NTW weight rows, times one M-block of up
+// to MB tokens of one expert.  Stage st is copied while stage st - 2 is computed;
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
-template <int MODE, int GW, int R, int MB>
+template <int MODE, int GW, int R, int MB, int NTW>
 __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
-  using Shape = RingShape<GW, R, MB>;
+  using Shape = RingShape<GW, R, MB, NTW>;
+  constexpr int kNt = Shape::kNt, kWaveRows = Shape::kWaveRows, kBWave = Shape::kBWave;
+  constexpr int kScaleWave = Shape::kScaleWave;
+  constexpr int kHalf = kWaveRows / 2;
   constexpr int kARows = Shape::kARows, kACopies = Shape::kACopies;
   constexpr int kRing = Shape::kRing;
   constexpr int kMBlock = Shape::kMBlock, kMT = Shape::kMT, kStageB = Shape::kStageB;
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 
   // ---- this wave's weight rows (ring rows 0..31 and 32..63); waves past the
   // last row copy the last wave's rows and compute nothing
-  const int nwaves = MODE == kGateUp ? f / 32 : d / kWaveRows;
+  const int nwaves = MODE == kGateUp ? f / kHalf : d / kWaveRows;
   const int wv = blockIdx.x * GW + wave;
   const bool active = wv < nwaves;
   const int wc = min(wv, nwaves - 1);
@@ -265,15 +272,15 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   const uint8_t *c0, *c1;
   const _Float16 *s0, *s1;
   if (MODE == kGateUp) {
-    c0 = blob + (size_t)(32 * wc) * (K / 2);
+    c0 = blob + (size_t)(kHalf * wc) * (K / 2);
     c1 = c0 + fd / 2;
-    s0 = sbase + (size_t)(32 * wc) * ng;
+    s0 = sbase + (size_t)(kHalf * wc) * ng;
     s1 = s0 + fd / 64;
   } else {
-    c0 = blob + fd + (size_t)(64 * wc) * (K / 2);
-    c1 = c0 + (size_t)32 * (K / 2);
-    s0 = sbase + 2 * (fd / 64) + (size_t)(64 * wc) * ng;
-    s1 = s0 + (size_t)32 * ng;
+    c0 = blob + fd + (size_t)(kWaveRows * wc) * (K / 2);
+    c1 = c0 + (size_t)kHalf * (K / 2);
+    s0 = sbase + 2 * (fd / 64) + (size_t)(kWaveRows * wc) * ng;
+    s1 = s0 + (size_t)kHalf * ng;
   }
   const int n = lane & 15, kg = lane >> 4;
 
@@ -290,8 +297,10 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
     const int r = kARows * wave + 4 * i + (lane >> 4);
     a_off[i] = row_of(r) * (uint32_t)K + (uint32_t)((lane & 15) ^ (r & 15)) * 8u;
   }
-  // scales: lane l -> ring row l, 8 groups
-  const _Float16* s_lane = (lane < 32 ? s0 : s1) + (size_t)(lane & 31) * ng;
+  // scales: lane l < kWaveRows -> ring row l, 8 groups (the other lanes copy
+  // nothing)
+  const int srow = lane % kWaveRows;
+  const _Float16* s_lane = (srow < kHalf ? s0 : s1) + (size_t)(srow % kHalf) * ng;
   uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
 
   const int nst = K / kSC;
@@ -302,14 +311,15 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
     uint8_t* base = s_lds + (st % kRing) * kStage;
     const uint32_t so = (uint32_t)st * (kSC / 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma16((i < 2 ? c0 : c1) + (i & 1) * b_half + so + b_off, base + wave * kBWave + i * 1024);
+    for (int i = 0; i < kNt; ++i)
+      dma16((i < kNt / 2 ? c0 : c1) + (i % (kNt / 2)) * b_half + so + b_off,
+            base + wave * kBWave + i * 1024);
     if (a_copy) {
 #pragma unroll
       for (int i = 0; i < kACopies; ++i)
         dma16(g.a + a_off[i] + st * kSC, base + kStageB + (kARows * wave + 4 * i) * (kSC * 2));
     }
-    if ((st & 3) == 0)
+    if ((st & 3) == 0 && lane < kWaveRows)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
   };
 
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
     if (st + kRing - 2 < nst) {
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
-      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, kACopies>()>();
-      else wait_vm_lgkm0<copies_ahead<kRing, PH, 0>()>();
+      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, kACopies>()>();
+      else wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, 0>()>();
     } else {
       wait_vm_lgkm0<0>();
     }
@@ -400,10 +410,10 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
       if (MODE == kGateUp) {
         const int xr = L.single ? ti : slot / L.kdiv;
         const float us = g.unit[xr];
-        float* orow = g.out + (size_t)slot * f + 32 * wv;
+        float* orow = g.out + (size_t)slot * f + kHalf * wv;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float gv = acc[mt][h][i] * us, uv = acc[mt][h + 2][i] * us;
+        for (int h = 0; h < kNt / 2; ++h) {
+          const float gv = acc[mt][h][i] * us, uv = acc[mt][h + kNt / 2][i] * us;
           orow[16 * h + n] = silu(gv) * uv;
         }
       } else {
@@ -421,14 +431,15 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 // Block shape of a call: batches of up to 16 rows take 2-wave blocks with
 // 16-token M-blocks; one expert over 128 rows or more (the compute-bound case)
 // takes 2-wave blocks with 64-token M-blocks, four times as many blocks as the
-// 8-wave shape; everything else 8-wave blocks with 64-token M-blocks.
+// 16-wave shape; everything else 16-wave blocks (32 rows a wave) with 64-token
+// M-blocks.
 struct GemmShape {
-  int gw, mblock;
+  int gw, mblock, ntw;
 };
 static GemmShape gemm_shape(int rows, bool single) {
-  if (rows <= 16) return {2, 16};
-  if (single && rows >= 128) return {2, 64};
-  return {8, 64};
+  if (rows <= 16) return {2, 16, 4};
+  if (single && rows >= 128) return {2, 64, 4};
+  return {16, 64, 2};
 }
 int mfma_mblock(int rows) { return gemm_shape(rows, false).mblock; }
 
@@ -466,14 +477,14 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   }
 
   const GemmShape sh = gemm_shape(m.x_rows, L.single != nullptr);
-  const int gw = sh.gw, mblock = sh.mblock;
+  const int gw = sh.gw, mblock = sh.mblock, ntw = sh.ntw;
   const unsigned mb = L.single ? (unsigned)((L.single_n + mblock - 1) / mblock)
                                : (unsigned)m.mb_bound;
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
-  const unsigned wg = (unsigned)((m.f / 32 + gw - 1) / gw);
-  if (gw == 2 && mblock == 16) e = launch(5, k_gemm<kGateUp, 2, 5, 16>, dim3(wg, mb), dim3(128), s, ga);
-  else if (gw == 2) e = launch(5, k_gemm<kGateUp, 2, 3, 64>, dim3(wg, mb), dim3(128), s, ga);
-  else e = launch(5, k_gemm<kGateUp, 8, 3, 64>, dim3(wg, mb), dim3(512), s, ga);
+  const unsigned wg = (unsigned)((m.f / (8 * ntw) + gw - 1) / gw);
+  if (gw == 2 && mblock == 16) e = launch(5, k_gemm<kGateUp, 2, 5, 16, 4>, dim3(wg, mb), dim3(128), s, ga);
+  else if (gw == 2) e = launch(5, k_gemm<kGateUp, 2, 3, 64, 4>, dim3(wg, mb), dim3(128), s, ga);
+  else e = launch(5, k_gemm<kGateUp, 16, 3, 64, 2>, dim3(wg, mb), dim3(1024), s, ga);
   if (e != hipSuccess) return e;
 
   PackArgs pa{};
@@ -486,10 +497,10 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
-  const unsigned wd = (unsigned)((m.d / kWaveRows + gw - 1) / gw);
-  if (gw == 2 && mblock == 16) return launch(6, k_gemm<kDown, 2, 4, 16>, dim3(wd, mb), dim3(128), s, gd);
-  if (gw == 2) return launch(6, k_gemm<kDown, 2, 3, 64>, dim3(wd, mb), dim3(128), s, gd);
-  return launch(6, k_gemm<kDown, 8, 3, 64>, dim3(wd, mb), dim3(512), s, gd);
+  const unsigned wd = (unsigned)((m.d / (16 * ntw) + gw - 1) / gw);
+  if (gw == 2 && mblock == 16) return launch(6, k_gemm<kDown, 2, 4, 16, 4>, dim3(wd, mb), dim3(128), s, gd);
+  if (gw == 2) return launch(6, k_gemm<kDown, 2, 3, 64, 4>, dim3(wd, mb), dim3(128), s, gd);
+  return launch(6, k_gemm<kDown, 16, 3, 64, 2>, dim3(wd, mb), dim3(1024), s, gd);
 }
 
 }  // namespace moe
