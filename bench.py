@@ -337,9 +337,9 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
         assert moe.moe_timing_disarm(h) == reps
         t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
         flops = 2.0 * n * w.d * 2 * w.f
-        # the library's block shape for one expert: 2 waves x 64 rows x 64 tokens
-        # from 128 rows on (2 x 64 x 16 at up to 16 rows), else 16 waves x 32
-        # rows x 64 tokens: 128 or 512 weight rows a block
+        # the library's block shape for one expert: 4 waves x 32 rows x 64 tokens
+        # from 128 rows on (2 waves x 64 rows x 16 tokens at up to 16 rows), else
+        # 16 waves x 32 rows x 64 tokens: 128 or 512 weight rows a block
         a_cols = 64 if n >= 128 or n <= 16 else 256
         blocks = (w.f // a_cols) * ((n + 63) // 64)
         tf = flops / t / 1e12
