@@ -55,18 +55,18 @@ def lib():
         L.ref_bf16.restype = dbl
         L.ref_bf16.argtypes = [ctypes.c_uint16]
         L.ref_blob_bytes.restype = i64
-        L.ref_blob_bytes.argtypes = [i32, i32]
-        L.ref_dequant.argtypes = [vp, i32, i32, i32, vp]
+        L.ref_blob_bytes.argtypes = [i32, i32, i32]
+        L.ref_dequant.argtypes = [vp, i32, i32, i32, i32, vp]
         L.ref_silu.restype = dbl
         L.ref_silu.argtypes = [dbl]
-        L.ref_expert_ffn.argtypes = [i32, i32, vp, vp, i32, vp]
+        L.ref_expert_ffn.argtypes = [i32, i32, i32, vp, vp, i32, vp]
         L.ref_route.argtypes = [i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
         L.ref_union.restype = i32
         L.ref_union.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.ref_rmsnorm.argtypes = [i32, vp, dbl, vp]
         L.ref_layer_forward.restype = i32
-        L.ref_layer_forward.argtypes = [i32, i32, i32, i32, vp, i32, i32, vp, vp, vp, u32, dbl,
-                                        vp, vp, vp, vp, vp, vp, vp]
+        L.ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, vp, u32,
+                                        dbl, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -90,14 +90,16 @@ def bf16(bits: int) -> float:
     return lib().ref_bf16(bits)
 
 
-def blob_bytes(d: int, f: int) -> int:
-    return lib().ref_blob_bytes(d, f)
+# group: 64 (one fp16 scale per 64 consecutive weights of a row) or 0 (one
+# scale per row)
+def blob_bytes(d: int, f: int, group: int = 64) -> int:
+    return lib().ref_blob_bytes(d, f, group)
 
 
-def dequant(blob: np.ndarray, d: int, f: int, which: int) -> np.ndarray:
+def dequant(blob: np.ndarray, d: int, f: int, which: int, group: int = 64) -> np.ndarray:
     rows, cols = (d, f) if which == 2 else (f, d)
     W = np.empty((rows, cols), dtype=np.float64)
-    lib().ref_dequant(_p(blob), d, f, which, _p(W))
+    lib().ref_dequant(_p(blob), d, f, group, which, _p(W))
     return W
 
 
@@ -105,11 +107,11 @@ def silu(v: float) -> float:
     return lib().ref_silu(v)
 
 
-def expert_ffn(blob: np.ndarray, x: np.ndarray, d: int, f: int) -> np.ndarray:
+def expert_ffn(blob: np.ndarray, x: np.ndarray, d: int, f: int, group: int = 64) -> np.ndarray:
     x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
     n = x.shape[0]
     y = np.empty((n, d), dtype=np.float64)
-    lib().ref_expert_ffn(d, f, _p(blob), _p(x), n, _p(y))
+    lib().ref_expert_ffn(d, f, group, _p(blob), _p(x), n, _p(y))
     return y
 
 
@@ -152,7 +154,7 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return xn
 
 
-def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6):
+def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6, group=64):
     """table: sequence of E uint8 blobs (or None for experts nobody picks).
     -> dict(out [T][d] f64, idx, w, uniq, offsets, rows, reads [E])."""
     x = _xarg(x, x_bf16)
@@ -169,7 +171,7 @@ def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6):
     offsets = np.empty(cap + 1, dtype=np.int32)
     rows = np.empty(T * k, dtype=np.int32)
     reads = np.zeros(E, dtype=np.int32)
-    U = lib().ref_layer_forward(d, f, E, k, _p(x), int(x_bf16), T, _p(Wr), _p(b),
+    U = lib().ref_layer_forward(d, f, group, E, k, _p(x), int(x_bf16), T, _p(Wr), _p(b),
                                 ctypes.cast(ptrs, ctypes.c_void_p), flags, eps, _p(out),
                                 _p(idx), _p(w), _p(uniq), _p(offsets), _p(rows), _p(reads))
     if U < 0:

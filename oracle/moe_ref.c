@@ -36,14 +36,17 @@
  * an expert: README 工作原理 › 绝不为同一次磁盘读取等待两遍):
  *   gate codes [f][d/2] | up codes [f][d/2] | down codes [d][f/2]
  *   | gate scales [f][d/64] | up scales [f][d/64] | down scales [d][f/64]
- * codes are bytes holding two 4-bit weights, scales are IEEE binary16.
+ * codes are bytes holding two 4-bit weights, scales are IEEE binary16.  The
+ * functions that read a blob take gs, the scale group: 64 for the layout
+ * above (gs64, README 开始使用 › 获取模型), or 0 for one scale per row (the
+ * per-row scaling of the nxmr blog, «纯C语言»): gate scales [f], up scales
+ * [f], down scales [d], each weight w[r][c] = q[r][c] * s[r].
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-#define REF_GROUP 64
 #define REF_PRENORM 1u
 #define REF_RESIDUAL 2u
 
@@ -82,32 +85,39 @@ double ref_bf16(uint16_t b) {
 
 /* ---- expert blob ----------------------------------------------------------- */
 
-int64_t ref_blob_bytes(int d, int f) { return 3LL * f * d / 2 + 2LL * (3LL * f * d / REF_GROUP); }
+/* Scales of one row of `cols` weights: cols / gs (gs = 64), or 1 (gs = 0). */
+static int64_t row_scales(int cols, int gs) { return gs ? cols / gs : 1; }
+
+int64_t ref_blob_bytes(int d, int f, int gs) {
+  return 3LL * f * d / 2 + 2LL * (2LL * f * row_scales(d, gs) + (int64_t)d * row_scales(f, gs));
+}
 
 /* which: 0 gate [f x d], 1 up [f x d], 2 down [d x f]. */
-static void mat_view(const uint8_t* blob, int d, int f, int which, const uint8_t** codes,
+static void mat_view(const uint8_t* blob, int d, int f, int gs, int which, const uint8_t** codes,
                      const uint16_t** scales, int* rows, int* cols) {
   int64_t fd = (int64_t)f * d;
   *codes = blob + which * (fd / 2);
-  *scales = (const uint16_t*)(blob + 3 * (fd / 2)) + which * (fd / REF_GROUP);
+  *scales = (const uint16_t*)(blob + 3 * (fd / 2)) + which * (f * row_scales(d, gs));
   *rows = which == 2 ? d : f;
   *cols = which == 2 ? f : d;
 }
 
-/* Row r of a matrix, dequantised: w[c] = q[r,c] * s[r, c/64] (exact in fp64). */
-static void dequant_row(const uint8_t* codes, const uint16_t* scales, int cols, int r, double* w) {
+/* Row r of a matrix, dequantised: w[c] = q[r,c] * s[r, c/gs] (gs64) or
+ * q[r,c] * s[r] (per row), exact in fp64. */
+static void dequant_row(const uint8_t* codes, const uint16_t* scales, int cols, int gs, int r,
+                        double* w) {
   const uint8_t* rc = codes + (int64_t)r * (cols / 2);
-  const uint16_t* rs = scales + (int64_t)r * (cols / REF_GROUP);
-  for (int c = 0; c < cols; ++c) w[c] = (double)ref_nibble(rc, c) * ref_f16(rs[c / REF_GROUP]);
+  const uint16_t* rs = scales + (int64_t)r * row_scales(cols, gs);
+  for (int c = 0; c < cols; ++c) w[c] = (double)ref_nibble(rc, c) * ref_f16(rs[gs ? c / gs : 0]);
 }
 
 /* Dense dequantised matrix (rows x cols doubles), for tests on small shapes. */
-void ref_dequant(const uint8_t* blob, int d, int f, int which, double* W) {
+void ref_dequant(const uint8_t* blob, int d, int f, int gs, int which, double* W) {
   const uint8_t* codes;
   const uint16_t* scales;
   int rows, cols;
-  mat_view(blob, d, f, which, &codes, &scales, &rows, &cols);
-  for (int r = 0; r < rows; ++r) dequant_row(codes, scales, cols, r, W + (int64_t)r * cols);
+  mat_view(blob, d, f, gs, which, &codes, &scales, &rows, &cols);
+  for (int r = 0; r < rows; ++r) dequant_row(codes, scales, cols, gs, r, W + (int64_t)r * cols);
 }
 
 double ref_silu(double v) { return v / (1.0 + exp(-v)); }
@@ -116,13 +126,13 @@ double ref_silu(double v) { return v / (1.0 + exp(-v)); }
  *   g = Wg x, u = Wu x, a = silu(g) * u, y = Wd a.
  * The pages only say the chosen experts run their feed-forward computation
  * (colibri 技术解读, "集群模式与开放问题清单"); SwiGLU is the reading taken. */
-void ref_expert_ffn(int d, int f, const uint8_t* blob, const double* x, int n, double* y) {
+void ref_expert_ffn(int d, int f, int gs, const uint8_t* blob, const double* x, int n, double* y) {
   const uint8_t *gc, *uc, *dc;
-  const uint16_t *gs, *us, *ds;
+  const uint16_t *gsc, *usc, *dsc;
   int rows, cols;
-  mat_view(blob, d, f, 0, &gc, &gs, &rows, &cols);
-  mat_view(blob, d, f, 1, &uc, &us, &rows, &cols);
-  mat_view(blob, d, f, 2, &dc, &ds, &rows, &cols);
+  mat_view(blob, d, f, gs, 0, &gc, &gsc, &rows, &cols);
+  mat_view(blob, d, f, gs, 1, &uc, &usc, &rows, &cols);
+  mat_view(blob, d, f, gs, 2, &dc, &dsc, &rows, &cols);
   double* a = (double*)malloc(sizeof(double) * (size_t)n * f);
 #pragma omp parallel
   {
@@ -130,8 +140,8 @@ void ref_expert_ffn(int d, int f, const uint8_t* blob, const double* x, int n, d
     double* wu = (double*)malloc(sizeof(double) * d);
 #pragma omp for schedule(static)
     for (int r = 0; r < f; ++r) {
-      dequant_row(gc, gs, d, r, wg);
-      dequant_row(uc, us, d, r, wu);
+      dequant_row(gc, gsc, d, gs, r, wg);
+      dequant_row(uc, usc, d, gs, r, wu);
       for (int t = 0; t < n; ++t) {
         const double* xt = x + (int64_t)t * d;
         double g = 0.0, u = 0.0;
@@ -147,7 +157,7 @@ void ref_expert_ffn(int d, int f, const uint8_t* blob, const double* x, int n, d
     double* wd = (double*)malloc(sizeof(double) * f);
 #pragma omp for schedule(static)
     for (int c = 0; c < d; ++c) {
-      dequant_row(dc, ds, f, c, wd);
+      dequant_row(dc, dsc, f, gs, c, wd);
       for (int t = 0; t < n; ++t) {
         const double* at = a + (int64_t)t * f;
         double acc = 0.0;
@@ -269,7 +279,7 @@ void ref_rmsnorm(int d, const float* h, double eps, float* xn) {
  * Outputs: out[T][d] (fp64), idx/w [T][k], uniq/offsets/rows as ref_union,
  * reads[E] += 1 for every time an expert's blob is read.  Returns U, or -1 if
  * a selected expert has no blob. */
-int ref_layer_forward(int d, int f, int E, int k, const void* x, int x_is_bf16, int T,
+int ref_layer_forward(int d, int f, int gs, int E, int k, const void* x, int x_is_bf16, int T,
                       const float* Wr, const float* bias, const uint8_t* const* table,
                       uint32_t flags, double eps, double* out, int32_t* idx, double* w,
                       int32_t* uniq, int32_t* offsets, int32_t* rows, int32_t* reads) {
@@ -300,7 +310,7 @@ int ref_layer_forward(int d, int f, int E, int k, const void* x, int x_is_bf16, 
       int t = rows[offsets[u] + i] / k;
       for (int c = 0; c < d; ++c) xs[(int64_t)i * d + c] = x_at(xin, xin_bf16, (int64_t)t * d + c);
     }
-    ref_expert_ffn(d, f, table[e], xs, n, ys); /* the one read of expert e */
+    ref_expert_ffn(d, f, gs, table[e], xs, n, ys); /* the one read of expert e */
     reads[e] += 1;
     for (int i = 0; i < n; ++i)
       memcpy(yslot + (int64_t)rows[offsets[u] + i] * d, ys + (int64_t)i * d, sizeof(double) * d);

@@ -37,10 +37,11 @@ class Workload:
     zipf: bool = True
     layers: int = 1
     steps: int = 1
+    group: int = 64             # scale group: 64, or 0 for one scale per row
 
     @property
     def blob_bytes(self) -> int:
-        nib, nsc = blob_sizes(self.d, self.f)
+        nib, nsc = blob_sizes(self.d, self.f, self.group)
         return nib + 2 * nsc
 
     @property
@@ -57,6 +58,13 @@ WORKLOADS = {
                            seed=1003, x_kind="bf16"),
     "chain48": Workload("chain48", d=6144, f=2048, n_experts=256, top_k=8, T=1, seed=1004,
                         layers=48, steps=64),
+    # the same layer with per-row int4 experts (one fp16 scale per weight row)
+    "decode1_perrow": Workload("decode1_perrow", d=6144, f=2048, n_experts=256, top_k=8, T=1,
+                               seed=1005, group=0),
+    "verify8_perrow": Workload("verify8_perrow", d=6144, f=2048, n_experts=256, top_k=8, T=8,
+                               seed=1006, x_kind="shared_base", group=0),
+    "prefill512_perrow": Workload("prefill512_perrow", d=6144, f=2048, n_experts=256, top_k=8,
+                                  T=512, seed=1007, x_kind="bf16", group=0),
 }
 
 
@@ -86,11 +94,11 @@ def tokens(w: Workload, step: int = 0, T: int | None = None):
 def experts(w: Workload, layer: int = 0, e0: int = 0, ne: int | None = None):
     """Expert blobs [ne][blob_bytes] uint8 of one layer."""
     ne = w.n_experts - e0 if ne is None else ne
-    return layer_blobs(w.seed, layer, ne, w.d, w.f, e0=e0)
+    return layer_blobs(w.seed, layer, ne, w.d, w.f, e0=e0, group=w.group)
 
 
 def one_expert(w: Workload, layer: int, e: int):
-    return expert_blob(w.seed, layer, e, w.d, w.f)
+    return expert_blob(w.seed, layer, e, w.d, w.f, group=w.group)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

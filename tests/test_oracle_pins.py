@@ -136,6 +136,76 @@ def test_ffn_brute_force(d, f, n):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+# ------------------------------------------------------ per-row scale format
+
+
+def np_dequant_perrow(blob, d, f, which):
+    """Independent dense dequantisation of a per-row blob: codes as for gs64,
+    then the scales gate [f], up [f], down [d], one per row."""
+    fd = f * d
+    rows, cols = (d, f) if which == 2 else (f, d)
+    codes = blob[which * fd // 2:(which + 1) * fd // 2].reshape(rows, cols // 2)
+    q = np.empty((rows, cols), dtype=np.int64)
+    q[:, 0::2] = ((codes & 15).astype(np.int64) ^ 8) - 8
+    q[:, 1::2] = ((codes >> 4).astype(np.int64) ^ 8) - 8
+    s_all = blob[3 * fd // 2:].view(np.float16).astype(np.float64)
+    beg = [0, f, 2 * f][which]
+    return q * s_all[beg:beg + rows][:, None]
+
+
+def perrow_as_gs64(blob, d, f):
+    """The gs64 blob with the same codes whose every 64-weight group carries
+    its row's scale."""
+    fd = f * d
+    s_all = blob[3 * fd // 2:].view(np.float16)
+    sg, su, sdn = s_all[:f], s_all[f:2 * f], s_all[2 * f:]
+    sc = np.concatenate([np.repeat(sg, d // 64), np.repeat(su, d // 64), np.repeat(sdn, f // 64)])
+    return np.concatenate([blob[:3 * fd // 2], sc.view(np.uint8)])
+
+
+def test_perrow_blob_size_closed_form():
+    for d, f in [(256, 128), (6144, 2048)]:
+        assert oracle.blob_bytes(d, f, group=0) == 3 * f * d // 2 + 2 * (2 * f + d)
+        assert synth.expert_blob(1, 0, 0, d, f, group=0).size == oracle.blob_bytes(d, f, group=0)
+    assert oracle.blob_bytes(6144, 2048) == 20054016
+
+
+@pytest.mark.parametrize("d,f", [(256, 128), (128, 192)])
+def test_perrow_dequant_brute_force(d, f):
+    blob = synth.expert_blob(3, 0, 1, d, f, group=0)
+    for which in range(3):
+        assert np.array_equal(oracle.dequant(blob, d, f, which, group=0),
+                              np_dequant_perrow(blob, d, f, which))
+
+
+def test_perrow_is_gs64_with_the_row_scale_in_every_group():
+    """A per-row expert computes exactly what the gs64 expert with its row
+    scale repeated over the row's groups computes (each weight q * s is the
+    same exact number), through the FFN and the whole layer."""
+    d, f, E, k, T = 256, 128, 16, 2, 5
+    blobs = synth.layer_blobs(9, 0, E, d, f, group=0)
+    g64 = [perrow_as_gs64(b, d, f) for b in blobs]
+    x = np.random.default_rng(4).normal(size=(T, d))
+    for e in (0, 7):
+        assert np.array_equal(oracle.expert_ffn(blobs[e], x, d, f, group=0),
+                              oracle.expert_ffn(g64[e], x, d, f))
+    Wr = (np.random.default_rng(5).normal(size=(E, d)) * 0.02).astype(np.float32)
+    xs = x.astype(np.float32)
+    a = oracle.layer_forward(xs, Wr, None, list(blobs), d, f, k, group=0)
+    b = oracle.layer_forward(xs, Wr, None, g64, d, f, k)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["idx"], b["idx"])
+
+
+def test_perrow_ffn_brute_force():
+    d, f, n = 192, 128, 3
+    blob = synth.expert_blob(4, 1, 2, d, f, group=0)
+    x = np.random.default_rng(3).normal(size=(n, d))
+    Wg, Wu, Wd = (np_dequant_perrow(blob, d, f, i) for i in range(3))
+    ref = (np_silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    y = oracle.expert_ffn(blob, x, d, f, group=0)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 def _set_scales(blob, d, f, which, value, group=None, row=None):
     b = blob.copy()
     fd = f * d
