@@ -33,6 +33,11 @@
  *   gate codes [f][d/2] | up codes [f][d/2] | down codes [d][f/2]
  *   | gate scales [f][d/64] | up scales [f][d/64] | down scales [d][f/64]
  * Size: moe_expert_blob_bytes(); 20,054,016 bytes at d = 6144, f = 2048.
+ * Per-row variant (dims.group_size = 0; the per-row scaling the nxmr blog
+ * names, «纯C语言»): the same codes, then one scale per row,
+ *   | gate scales [f] | up scales [f] | down scales [d]
+ * so w[r][c] = q[r][c] * s[r]; 18,894,848 bytes at d = 6144, f = 2048.  Every
+ * entry point takes both layouts and computes the same way on them.
  *
  * Conventions for every entry point:
  *  - Pointers are device pointers (or host memory mapped into the device
@@ -67,7 +72,7 @@ typedef struct moe_dims {
   int32_t f;          /* expert FFN width; multiple of 64, 64..65536 */
   int32_t n_experts;  /* E; 1..1024 */
   int32_t top_k;      /* k; 1..min(E, 32) */
-  int32_t group_size; /* weights per fp16 scale; must be 64 */
+  int32_t group_size; /* weights per fp16 scale: 64, or 0 for one scale per row */
 } moe_dims;
 
 /* Activation dtypes (x_dtype). */
@@ -84,7 +89,8 @@ enum {
 enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* null or inconsistent argument, T < 1 */
-  MOE_EUNSUPPORTED = -2, /* group_size != 64, d/f not multiples of 64, k > 32, E > 1024, bad dtype/flags,
+  MOE_EUNSUPPORTED = -2, /* group_size not 64 or 0, d/f not multiples of 64, k > 32, E > 1024,
+                            bad dtype/flags,
                             MOE_BATCH_INVARIANT with T > 8 or T * k > 64 */
   MOE_ENOSPC = -3,       /* ws_bytes smaller than moe_workspace_bytes() */
   MOE_EHIP = -4          /* a kernel launch failed; moe_strerror() names the HIP error */

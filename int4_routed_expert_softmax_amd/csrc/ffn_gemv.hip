@@ -246,8 +246,8 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t*
                                             int r0, int rl0, int slice, int lane,
                                             const Digits& xd, const int (&xrow)[NT], int nt,
                                             float (*s_g)[kRowsPerBlock][C],
-                                            float (*s_u)[kRowsPerBlock][C]) {
-  const int nch = d / kChunk, ngx = d / kGroup;
+                                            float (*s_u)[kRowsPerBlock][C], int pr) {
+  const int nch = d / kChunk, ngx = srow(d, pr);
   constexpr int kB = kGUBatch, kNB = kRowsPerStream / kGUBatch;
   for (int p = 0; p * 64 * C < nch; ++p) {
     const int c = (p * C + slice) * 64 + lane;
@@ -263,8 +263,8 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t*
         const size_t r = (size_t)r0 + rb0 + b;
         wg[buf][b] = stream_load16(gcode + r * (d / 2) + (unsigned)cl * 16u);
         wu[buf][b] = stream_load16(ucode + r * (d / 2) + (unsigned)cl * 16u);
-        sg[buf][b] = stream_scale(gsc + r * ngx + (unsigned)cl / 2u);
-        su[buf][b] = stream_scale(usc + r * ngx + (unsigned)cl / 2u);
+        sg[buf][b] = stream_scale(gsc + r * ngx + scol((unsigned)cl, pr));
+        su[buf][b] = stream_scale(usc + r * ngx + scol((unsigned)cl, pr));
       }
     };
     issue(0, 0);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
   const uint8_t* gcode = ex.blob;
   const uint8_t* ucode = ex.blob + fd / 2;
   const _Float16* gsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2);
-  const _Float16* usc = gsc + fd / kGroup;
+  const _Float16* usc = gsc + (size_t)f * srow(d, L.per_row);
   const int rl0 = stream * kRowsPerStream;
   const int r0 = rb * kRowsPerBlock + rl0;
   auto slot_at = [&](int i) { return list ? list[ex.beg + i] : i; };
@@ -361,7 +361,8 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     int xrow[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) xrow[j] = j < nt ? slot_at(t0 + j) / kdiv : 0;
-    gateup_rows<C, NT>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u);
+    gateup_rows<C, NT>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u,
+                       L.per_row);
     __syncthreads();
     if (wave < nt) {
       // wave j: token j, the block's 64 rows (four 16-wide groups of a)
@@ -387,8 +388,8 @@ template <int NT>
 __device__ __forceinline__ void down_rows(const uint8_t* dcode, const _Float16* dsc, int f, int r0,
                                           int rl0, int lane, const Digits& ad,
                                           const int (&slot)[NT], int nt,
-                                          float (*s_y)[kRowsPerBlock]) {
-  const int nch = f / kChunk, nga = f / kGroup;
+                                          float (*s_y)[kRowsPerBlock], int pr) {
+  const int nch = f / kChunk, nga = srow(f, pr);
   constexpr int kB = kDnBatch, kNB = kRowsPerStream / kDnBatch;
   for (int p = 0; p * 64 < nch; ++p) {
     const int c = p * 64 + lane;
@@ -401,7 +402,7 @@ __device__ __forceinline__ void down_rows(const uint8_t* dcode, const _Float16* 
       for (int b = 0; b < kB; ++b) {
         const size_t r = (size_t)r0 + rb0 + b;
         wd[buf][b] = stream_load16(dcode + r * (f / 2) + (unsigned)cl * 16u);
-        sd[buf][b] = stream_scale(dsc + r * nga + (unsigned)cl / 2u);
+        sd[buf][b] = stream_scale(dsc + r * nga + scol((unsigned)cl, pr));
       }
     };
     issue(0, 0);
@@ -440,7 +441,8 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
   const int rb = blockIdx.x;
   const size_t fd = (size_t)f * d;
   const uint8_t* dcode = ex.blob + fd;
-  const _Float16* dsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (fd / kGroup);
+  const _Float16* dsc =
+      reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2) + 2 * (size_t)f * srow(d, L.per_row);
   const int rl0 = wave * kRowsPerStream;
   const int r0 = rb * kRowsPerBlock + rl0;
   __shared__ float s_y[NT][kRowsPerBlock];
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
     int slot[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) slot[j] = j < nt ? slot_at(t0 + j) : 0;
-    down_rows<NT>(dcode, dsc, f, r0, rl0, lane, ad, slot, nt, s_y);
+    down_rows<NT>(dcode, dsc, f, r0, rl0, lane, ad, slot, nt, s_y, L.per_row);
     __syncthreads();
     for (int i = threadIdx.x; i < nt * kRowsPerBlock; i += 256) {
       const int j = i / kRowsPerBlock, row = i % kRowsPerBlock;
@@ -477,12 +479,12 @@ template <int NT>
 __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* __restrict__ plan,
                                                                  const int32_t* __restrict__ n_uniq,
                                                                  int d, int f, Digits ad,
-                                                                 CombineArgs cb) {
+                                                                 CombineArgs cb, int pr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.x * kDcRows;
   const int U = *n_uniq;
-  const int nch = f / kChunk, nga = f / kGroup;
+  const int nch = f / kChunk, nga = srow(f, pr);
   const size_t fd = (size_t)f * d;
   __shared__ float s_y[kSmallPicks][kDcRows];
   __shared__ float s_w[kSmallPicks];
@@ -495,7 +497,8 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
 
   auto dcode = [&](const uint8_t* blob) { return blob + fd + (size_t)r0 * (f / 2); };
   auto dscale = [&](const uint8_t* blob) {
-    return reinterpret_cast<const _Float16*>(blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+    return reinterpret_cast<const _Float16*>(blob + 3 * fd / 2) + 2 * (size_t)f * srow(d, pr) +
+           (size_t)r0 * nga;
   };
   for (int u = wave; u < U; u += kDcWaves) {
     const DownPlan pl = plan[u];
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
 #pragma unroll
       for (int b = 0; b < kDcRows; ++b) {
         wd[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
-        sd[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
+        sd[b] = stream_scale(ds + (size_t)b * nga + scol(cl, pr));
       }
       for (int t0 = 0; t0 < pl.n; t0 += NT) {
         const int nt = min(NT, pl.n - t0);
@@ -555,13 +558,13 @@ template <int R>
 __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPlan* __restrict__ plan,
                                                                      const int32_t* __restrict__ n_uniq,
                                                                      int d, int f, Digits ad,
-                                                                     CombineArgs cb) {
+                                                                     CombineArgs cb, int pr) {
   static_assert(R % 8 == 0, "rows in groups of 8 (one DPP reduction each)");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.x * R;
   const int U = *n_uniq;
-  const int nch = f / kChunk, nga = f / kGroup;
+  const int nch = f / kChunk, nga = srow(f, pr);
   const size_t fd = (size_t)f * d;
   __shared__ float s_y[kSmallPicks][R];
   __shared__ float s_w[kSmallPicks];
@@ -575,7 +578,8 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
     const int slot = pl.slot[0];
     const uint8_t* dc = pl.blob + fd + (size_t)r0 * (f / 2);
     const _Float16* ds =
-        reinterpret_cast<const _Float16*>(pl.blob + 3 * fd / 2) + 2 * (fd / kGroup) + (size_t)r0 * nga;
+        reinterpret_cast<const _Float16*>(pl.blob + 3 * fd / 2) + 2 * (size_t)f * srow(d, pr) +
+        (size_t)r0 * nga;
     for (int p = 0; p * 64 < nch; ++p) {
       const int c = p * 64 + lane;
       const bool act = c < nch;
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
 #pragma unroll
       for (int b = 0; b < R; ++b) {
         wv[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
-        sv[b] = stream_scale(ds + (size_t)b * nga + cl / 2u);
+        sv[b] = stream_scale(ds + (size_t)b * nga + scol(cl, pr));
       }
       const ChunkAct a = load_act(ad, slot, nch, c, act);
 #pragma unroll
@@ -710,16 +714,16 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
 }
 
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, hipStream_t s) {
+                               Digits ad, const CombineArgs& cb, int per_row, hipStream_t s) {
   if (cb.T == 1) {
     if (d % 24 == 0)
       return launch(6, k_down_combine_t1<24>, dim3(d / 24), dim3(64 * kD1Waves), s, plan, n_uniq, d,
-                    f, ad, cb);
+                    f, ad, cb, per_row);
     return launch(6, k_down_combine_t1<16>, dim3(d / 16), dim3(64 * kD1Waves), s, plan, n_uniq, d,
-                  f, ad, cb);
+                  f, ad, cb, per_row);
   }
   return launch(6, k_down_combine<2>, dim3(d / kDcRows), dim3(64 * kDcWaves), s, plan, n_uniq, d,
-                f, ad, cb);
+                f, ad, cb, per_row);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,

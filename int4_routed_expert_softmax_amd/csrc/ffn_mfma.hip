@@ -198,12 +198,12 @@ struct RingShape {
 };
 
 // Copies a wave has in flight after issuing stages st + 1 .. st + R - 2, with
-// st % 4 == PH: 4 code copies, NA activation copies, and a scale copy in
-// stages that are multiples of 4.
-template <int R, int PH, int NB, int NA>
+// st % 4 == PH: NB code copies, NA activation copies, and (NS = 1) a scale
+// copy in stages that are multiples of 4.
+template <int R, int PH, int NB, int NA, int NS>
 constexpr int copies_ahead() {
   int c = 0;
-  for (int i = 1; i <= R - 2; ++i) c += NB + NA + (((PH + i) & 3) == 0 ? 1 : 0);
+  for (int i = 1; i <= R - 2; ++i) c += NB + NA + (NS && ((PH + i) & 3) == 0 ? 1 : 0);
   return c;
 }
 // copies per wave and stage: NTW (codes, 16 rows each) + kACopies (activations: wave w copies
@@ -233,7 +233,8 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int d = g.d, f = g.f;
   const int K = MODE == kGateUp ? d : f;
-  const int ng = K / 64;
+  const int pr = g.L.per_row;
+  const int ng = srow(K, pr);  // scales per weight row
 
   // ---- the block's expert and tokens
   const ExpertList& L = g.L;
@@ -271,17 +272,18 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   const int wc = min(wv, nwaves - 1);
   const size_t fd = (size_t)f * d;
   const _Float16* sbase = reinterpret_cast<const _Float16*>(blob + 3 * (fd / 2));
+  const size_t gate_sc = (size_t)f * srow(d, pr);  // scales of the gate (and of the up) matrix
   const uint8_t *c0, *c1;
   const _Float16 *s0, *s1;
   if (MODE == kGateUp) {
     c0 = blob + (size_t)(kHalf * wc) * (K / 2);
     c1 = c0 + fd / 2;
     s0 = sbase + (size_t)(kHalf * wc) * ng;
-    s1 = s0 + fd / 64;
+    s1 = s0 + gate_sc;
   } else {
     c0 = blob + fd + (size_t)(kWaveRows * wc) * (K / 2);
     c1 = c0 + (size_t)kHalf * (K / 2);
-    s0 = sbase + 2 * (fd / 64) + (size_t)(kWaveRows * wc) * ng;
+    s0 = sbase + 2 * gate_sc + (size_t)(kWaveRows * wc) * ng;
     s1 = s0 + (size_t)kHalf * ng;
   }
   const int n = lane & 15, kg = lane >> 4;
@@ -301,9 +303,18 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   }
   // scales: lane l < kWaveRows -> ring row l, 8 groups (the other lanes copy
   // nothing)
-  const int srow = lane % kWaveRows;
-  const _Float16* s_lane = (srow < kHalf ? s0 : s1) + (size_t)(srow % kHalf) * ng;
+  const int sr_lane = lane % kWaveRows;
+  const _Float16* s_lane = (sr_lane < kHalf ? s0 : s1) + (size_t)(sr_lane % kHalf) * ng;
   uint8_t* s_scales = s_lds + kScaleOff + wave * kScaleWave;
+  if (pr && lane < kWaveRows) {
+    // one scale per row: put in every group of both buffers, once (this
+    // wave's own LDS; the first stage's wait covers the writes)
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(s_lane);
+    const uint32_t hh = h | (h << 16);
+    const uint4 v = make_uint4(hh, hh, hh, hh);
+    *reinterpret_cast<uint4*>(s_scales + lane * 16) = v;
+    *reinterpret_cast<uint4*>(s_scales + kWaveRows * 16 + lane * 16) = v;
+  }
 
   const int nst = K / kSC;
   // a wave copies its activation rows only when the first is one of the
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
       for (int i = 0; i < kACopies; ++i)
         dma16(g.a + a_off[i] + st * kSC, base + kStageB + (kARows * wave + 4 * i) * (kSC * 2));
     }
-    if ((st & 3) == 0 && lane < kWaveRows)
+    if ((st & 3) == 0 && !pr && lane < kWaveRows)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * (kWaveRows * 16));
   };
 
@@ -376,8 +387,11 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
     if (st + kRing - 2 < nst) {
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
-      if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, kACopies>()>();
-      else wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, 0>()>();
+      // (per-row scales: no scale copies)
+      if (a_copy && !pr) wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, kACopies, 1>()>();
+      else if (a_copy) wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, kACopies, 0>()>();
+      else if (!pr) wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, 0, 1>()>();
+      else wait_vm_lgkm0<copies_ahead<kRing, PH, kNt, 0, 0>()>();
     } else {
       wait_vm_lgkm0<0>();
     }

@@ -72,7 +72,7 @@ int dims_status(const moe_dims* dm) {
   if (!dm) return MOE_EINVAL;
   if (dm->d <= 0 || dm->f <= 0 || dm->n_experts <= 0 || dm->top_k <= 0) return MOE_EINVAL;
   if (dm->top_k > dm->n_experts) return MOE_EINVAL;
-  if (dm->group_size != kGroup) return MOE_EUNSUPPORTED;
+  if (dm->group_size != kGroup && dm->group_size != 0) return MOE_EUNSUPPORTED;
   if (dm->d % kGroup || dm->f % kGroup || dm->d > 65536 || dm->f > 65536) return MOE_EUNSUPPORTED;
   if (dm->n_experts > 1024 || dm->top_k > 32) return MOE_EUNSUPPORTED;
   return MOE_OK;
@@ -139,7 +139,8 @@ bool rows_fit(size_t rows, const moe_dims* dm) {
 MOE_API size_t moe_expert_blob_bytes(const moe_dims* dm) {
   if (dims_status(dm) != MOE_OK) return 0;
   const size_t fd = (size_t)dm->f * dm->d;
-  return 3 * fd / 2 + 2 * (3 * fd / kGroup);
+  const int pr = dm->group_size == 0;
+  return 3 * fd / 2 + 2 * (2 * (size_t)dm->f * srow(dm->d, pr) + (size_t)dm->d * srow(dm->f, pr));
 }
 
 MOE_API size_t moe_workspace_bytes(const moe_dims* dm, int32_t T_max) {
@@ -223,6 +224,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   EL.single = static_cast<const uint8_t*>(expert_blob);
   EL.single_n = n;
   EL.kdiv = 1;
+  EL.per_row = dm->group_size == 0;
   if (n >= kMfmaMinTokens && mfma_shape_ok(dm->d, dm->f)) {
     MfmaArgs m = mfma_args(ws, L, dm->d, dm->f);
     m.L = EL;
@@ -281,6 +283,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.offsets = offs;
   EL.list = rows;
   EL.kdiv = k;
+  EL.per_row = dm->group_size == 0;
   const int maxU = E < T * k ? E : T * k;
 
   if (invariant || gemv_small_path(T, k, d, f)) {
@@ -318,7 +321,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
       MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, 1, T, s));
     }
     CombineArgs cb{w, resid, out, T, k};
-    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, s));
+    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));
     return MOE_OK;
   }
 
@@ -475,9 +478,10 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   EL.offsets = offs;
   EL.list = rows;
   EL.kdiv = k;
+  EL.per_row = dm->group_size == 0;
   MOE_TRY(launch_gateup(EL, nullptr, cap, d, f, xd, ad, 1, T, s));
   CombineArgs cb{w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out, T, k};
-  MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, s));
+  MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));
   return MOE_OK;
 }
 

@@ -57,7 +57,15 @@ struct ExpertList {
   const int32_t* offsets;
   const int32_t* list;
   int kdiv;
+  int per_row;  // blobs carry one scale per row (else one per kGroup weights)
 };
+
+// Scales of one row of K weights in a blob: K / kGroup, or 1 with per-row
+// scales.  A blob's scales follow its codes: gate [f][srow(d)], up
+// [f][srow(d)], down [d][srow(f)].
+__host__ __device__ inline int srow(int K, int per_row) { return per_row ? 1 : K / kGroup; }
+// Scale of 32-weight chunk c within its row.
+__host__ __device__ inline unsigned scol(unsigned c, int per_row) { return per_row ? 0u : c / 2u; }
 
 // Opt-in kernel timing (moe_timing_arm): launches of an armed kernel record
 // caller-provided start/stop events around their execution.
@@ -178,7 +186,7 @@ struct CombineArgs {
   int T, k;
 };
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, hipStream_t s);
+                               Digits ad, const CombineArgs& cb, int per_row, hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 

@@ -8,6 +8,7 @@ import re
 import pytest
 
 import int4_routed_expert_softmax_amd as moe
+import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -43,6 +44,10 @@ def test_blob_and_workspace_sizes():
     assert moe.expert_blob_bytes(GLM) == 20054016
     assert moe.expert_blob_bytes(TINY) == 52224
     assert moe.expert_blob_bytes(moe.Dims(6144, 2048, 256, 8, group_size=32)) == 0
+    # per-row scales: the codes, then 2f + d scales
+    assert moe.expert_blob_bytes(moe.Dims(6144, 2048, 256, 8, group_size=0)) == 18894848
+    assert moe.expert_blob_bytes(moe.Dims(256, 128, 16, 2, group_size=0)) == \
+        oracle.blob_bytes(256, 128, group=0)
     w1 = moe.workspace_bytes(GLM, 1)
     w512 = moe.workspace_bytes(GLM, 512)
     assert 0 < w1 < 4 << 20 and w512 > w1
