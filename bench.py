@@ -41,7 +41,8 @@ def parse():
                    help="timed steps (default 200; chain48: 64)")
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; chain48: 2)")
     p.add_argument("--workload", default="decode1",
-                   choices=["decode1", "verify8", "prefill512", "chain48"])
+                   choices=["decode1", "verify8", "prefill512", "chain48", "decode1_perrow",
+                            "verify8_perrow", "prefill512_perrow"])
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
@@ -72,6 +73,14 @@ def calibrate_copy(mib):
 
 # Sources the decode gate/up kernel is built from.
 GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h")
+
+
+def matrix_bytes(w):
+    """(gate + up, down) bytes of one expert: codes and fp16 scales (one per
+    64 weights of a row, or one per row)."""
+    sg = w.d // 64 if w.group else 1
+    sd = w.f // 64 if w.group else 1
+    return 2 * (w.f * w.d // 2 + 2 * w.f * sg), w.f * w.d // 2 + 2 * w.d * sd
 
 
 def kernel_source_hash():
@@ -134,10 +143,9 @@ def main():
         sys.exit(f"--batch-invariant: {w.name} has T={w.T}, past the single-token family's "
                  "batch limits (T <= 8, T * k <= 64)")
     dev = torch.device("cuda:0")
-    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
     blob = w.blob_bytes
-    nib_gu = 2 * (w.f * w.d // 2 + 2 * (w.f * w.d // 64))   # gate + up codes and scales
-    nib_dn = w.f * w.d // 2 + 2 * (w.f * w.d // 64)
+    nib_gu, nib_dn = matrix_bytes(w)
 
     print(f"bench: {w.name} T={w.T} layers={a.layers} generating + uploading "
           f"{a.layers * w.n_experts * blob / 1e9:.1f} GB", file=sys.stderr, flush=True)
@@ -233,7 +241,8 @@ def main():
                   "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
-                               f"top-{w.top_k}, T={w.T} tokens, gs64 int4 experts "
+                               f"top-{w.top_k}, T={w.T} tokens, "
+                               f"{'gs64' if w.group else 'per-row'} int4 experts "
                                f"({blob} B each), {a.layers} rotating HBM-resident layers"
                                + (", MOE_BATCH_INVARIANT" if inv else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
@@ -371,7 +380,7 @@ def run_host_tier(a):
         sys.exit(f"--host-tier: {w.name} has T={w.T}, past the cached layer's batch limits")
     S = a.host_tier
     dev = torch.device("cuda:0")
-    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
     blob = w.blob_bytes
     if not (min(w.n_experts, w.T * w.top_k) <= S <= w.n_experts):
         sys.exit(f"--host-tier {S}: slots must lie in [{min(w.n_experts, w.T * w.top_k)}, "
@@ -454,10 +463,9 @@ def run_chain(a):
 
     w = configs.WORKLOADS["chain48"]
     dev = torch.device("cuda:0")
-    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k)
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
     blob = w.blob_bytes
-    nib_gu = 2 * (w.f * w.d // 2 + 2 * (w.f * w.d // 64))
-    nib_dn = w.f * w.d // 2 + 2 * (w.f * w.d // 64)
+    nib_gu, nib_dn = matrix_bytes(w)
     L = w.layers
     K, Wm = a.steps, a.warmup
     eps = 1e-6
@@ -636,7 +644,8 @@ def cpu_baseline(w, seconds):
         t0 = time.perf_counter()
         while True:
             t = n % x.shape[0]
-            oracle.layer_forward(x[t:t + 1], Wr, bias, table, w.d, w.f, w.top_k, x_bf16=bf)
+            oracle.layer_forward(x[t:t + 1], Wr, bias, table, w.d, w.f, w.top_k, x_bf16=bf,
+                                 group=w.group)
             n += 1
             if time.perf_counter() - t0 >= secs:
                 break
