@@ -54,7 +54,6 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h,
 constexpr int kLgT = 32;
 constexpr int kLgE = 64;
 constexpr int kLgC = 64;
-constexpr int kLgChains = 2;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
@@ -95,13 +94,7 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int 
     }
   };
 
-  // kLgChains accumulators per M-tile (k-step ks goes to chain ks % kLgChains):
-  // 2 kLgChains independent MFMA chains per wave
-  f64x4 acc[2][kLgChains];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int c = 0; c < kLgChains; ++c) acc[mt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  f64x4 acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
   if (c_begin < c_end) fetch(c_begin);
   for (int c = c_begin; c < c_end; ++c) {
 #pragma unroll
@@ -124,8 +117,7 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int 
       const double b = s_w[k][16 * wave + (lane & 15)];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        acc[mt][ks % kLgChains] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-            s_x[k][16 * mt + (lane & 15)], b, acc[mt][ks % kLgChains], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(s_x[k][16 * mt + (lane & 15)], b, acc[mt], 0, 0, 0);
     }
     __syncthreads();
   }
@@ -137,12 +129,7 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * mt + (lane >> 4) + 4 * i;
-        if (tok < nt) {
-          double z = acc[mt][0][i];
-#pragma unroll
-          for (int c = 1; c < kLgChains; ++c) z += acc[mt][c][i];
-          zp[((size_t)split * T + t0 + tok) * E + e] = z;
-        }
+        if (tok < nt) zp[((size_t)split * T + t0 + tok) * E + e] = acc[mt][i];
       }
   }
 }
