@@ -181,23 +181,33 @@ __global__ __launch_bounds__(kUnionThreads) void k_union(const int32_t* __restri
 // run next in one workgroup: at the start of the gate/up kernel (GEMV path)
 // or in k_route_small (grouped GEMM); nothing here waits on another
 // workgroup.
+// Router front end blocks: kRF threads, kRFW waves.  A token's logit is the
+// same sum for any batch size: thread tid takes float4 columns tid + kRF m,
+// then a wave reduction and sum_waves over the waves.
+constexpr int kRF = 512;
+constexpr int kRFW = kRF / 64;
+static_assert(kRFW == 8, "sum_waves adds 8 wave sums");
+__device__ __forceinline__ double sum_waves(const double (&p)[kRFW]) {
+  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
 template <int TB>
-__global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
+__global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, d = a.d, E = a.E;
-  // the last (rows + 3) / 4 workgroups pack the rows for the grouped GEMM,
-  // one wave per row, alongside the logits
-  const int pack_blocks = a.px.dst ? (a.px.rows + 3) / 4 : 0;
+  // the last (rows + kRFW - 1) / kRFW workgroups pack the rows for the
+  // grouped GEMM, one wave per row, alongside the logits
+  const int pack_blocks = a.px.dst ? (a.px.rows + kRFW - 1) / kRFW : 0;
   if (pack_blocks) {
     const int pb = (int)gridDim.x - pack_blocks;
     if (e >= pb) {
-      const int r = (e - pb) * 4 + wave;
+      const int r = (e - pb) * kRFW + wave;
       if (r < a.px.rows) pack_row(a.px, r, lane);
       return;
     }
   }
-  __shared__ double part[TB][4];
+  __shared__ double part[TB][kRFW];
   __shared__ double s_r[TB];
 
   auto xval = [&](int t, size_t i) -> float {
@@ -212,17 +222,17 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     }
     return reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * d)[i4];
   };
-  // Rows of up to 8192 columns stay in registers (8 float4 per thread): the
+  // Rows of up to 8192 columns stay in registers (4 float4 per thread): the
   // router row is requested before the RMSNorm reduction so the two overlap,
   // and a single token's x is read once.
-  constexpr int kReg = 8;
+  constexpr int kReg = 8192 / 4 / kRF;
   const int n4 = d >> 2;
-  const bool in_regs = n4 <= 256 * kReg;
+  const bool in_regs = n4 <= kRF * kReg;
   float4 wr[kReg], xr[kReg];
   if (in_regs) {
 #pragma unroll
     for (int m = 0; m < kReg; ++m) {
-      const int i4 = tid + 256 * m;
+      const int i4 = tid + kRF * m;
       if (e < E && i4 < n4) wr[m] = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d)[i4];
       if (TB == 1 && i4 < n4) xr[m] = xval4(0, i4);
     }
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     if (TB == 1 && in_regs) {
 #pragma unroll
       for (int m = 0; m < kReg; ++m) {
-        if (tid + 256 * m < n4) {
+        if (tid + kRF * m < n4) {
           const float4 v = xr[m];
           ss[0] += (double)v.x * (double)v.x;
           ss[0] += (double)v.y * (double)v.y;
@@ -244,12 +254,12 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
         }
       }
     } else {
-      // the same partition and order as above (float4 i4 = tid + 256 m, its
+      // the same partition and order as above (float4 i4 = tid + kRF m, its
       // four values in turn), so a token's sum does not depend on the batch.
       // Every row is read unconditionally (rows past the batch repeat the
       // last one and their sums are never used), so the loads of all rows
       // are in flight together.
-      for (int i4 = tid; i4 < n4; i4 += 256)
+      for (int i4 = tid; i4 < n4; i4 += kRF)
 #pragma unroll
         for (int j = 0; j < TB; ++j) {
           const float4 v = xval4(TB == 1 ? 0 : (j < T ? j : T - 1), i4);
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     }
     __syncthreads();
     if (tid < T) {
-      const double tot = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+      const double tot = sum_waves(part[tid]);
       s_r[tid] = 1.0 / sqrt(tot / d + (double)a.eps);
     }
     __syncthreads();
@@ -279,7 +289,8 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     // workgroups past the last expert: the digit split, one wave per 64
     // columns of a token
     const int nb = d / 64, nch = d / kChunk, ng = d / kXGroup;
-    for (int it = (e - E) * 4 + wave; it < T * nb; it += ((int)gridDim.x - E - pack_blocks) * 4) {
+    for (int it = (e - E) * kRFW + wave; it < T * nb;
+         it += ((int)gridDim.x - E - pack_blocks) * kRFW) {
       const int t = it / nb, col = (it % nb) * 64 + lane;
       digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
                  a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
@@ -292,7 +303,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
   if (in_regs) {
 #pragma unroll
     for (int m = 0; m < kReg; ++m) {
-      const int i4 = tid + 256 * m;
+      const int i4 = tid + kRF * m;
       if (i4 < n4) {
         const float4 w = wr[m];
 #pragma unroll
@@ -310,7 +321,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
     }
   } else {
     const float4* w4 = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d);
-    for (int i = tid; i < n4; i += 256) {
+    for (int i = tid; i < n4; i += kRF) {
       const float4 w = w4[i];
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(256) void k_router_front(RouterArgs a) {
   }
   __syncthreads();
   if (tid < T) {
-    const double sj = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+    const double sj = sum_waves(part[tid]);
     a.z[(size_t)tid * E + e] = sj + (a.bias ? (double)a.bias[e] : 0.0);
   }
 }
@@ -380,14 +391,14 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 }
 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s) {
-  const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + 3) / 4 : 0;
+  const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + kRFW - 1) / kRFW : 0;
   if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1)) return hipErrorInvalidValue;
-  const int pack_blocks = a.px.dst ? (a.px.rows + 3) / 4 : 0;
+  const int pack_blocks = a.px.dst ? (a.px.rows + kRFW - 1) / kRFW : 0;
   const dim3 grid(a.E + dig_blocks + pack_blocks);
-  if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(256), s, a);
-  if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(256), s, a);
-  if (a.T <= 4) return launch(1, k_router_front<4>, grid, dim3(256), s, a);
-  return launch(1, k_router_front<8>, grid, dim3(256), s, a);
+  if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(kRF), s, a);
+  if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(kRF), s, a);
+  if (a.T <= 4) return launch(1, k_router_front<4>, grid, dim3(kRF), s, a);
+  return launch(1, k_router_front<8>, grid, dim3(kRF), s, a);
 }
 
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
