@@ -137,26 +137,89 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int 
 // ---------------------------------------------------------------- top-k
 // One wave per token.  With nsplit > 1 the logits are the fixed-order sum of
 // the per-range partials plus the bias, formed in LDS first.
-__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ z, int nsplit,
-                                              const float* __restrict__ bias, int T, int E, int k,
-                                              int32_t* __restrict__ idx, float* __restrict__ w) {
-  __shared__ double s_z[4][kMaxE];
+// Bitonic top-k of one token by one wave, when every group of 64 experts'
+// best K2 (k rounded up to a power of two) fit in the wave together (G K2 <=
+// 64): each group is sorted into a run of its best K2 (odd groups reversed)
+// in LDS, then the runs are merged pairwise, keeping the better half, down
+// to the best K2.  cz, ce: this wave's 64-entry LDS scratch.
+template <int K2>
+__device__ __forceinline__ void wave_topk_bitonic(const double* zt, int E, int k, int32_t* idx_out,
+                                                  float* w_out, double* cz, int* ce) {
+  const int lane = threadIdx.x & 63;
+  const int G = (E + 63) / 64;
+  for (int g = 0; g < G; ++g) {
+    const int e = g * 64 + lane;
+    double z = e < E ? zt[e] : -INFINITY;
+    int id = e < E ? e : INT_MAX;
+    wave_best<K2>(z, id);
+    if (lane < K2) {
+      const int at = g * K2 + ((g & 1) ? K2 - 1 - lane : lane);
+      cz[at] = z;
+      ce[at] = id;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int span = K2;
+  while (span < G * K2) span *= 2;
+  double z = lane < G * K2 ? cz[lane] : -INFINITY;
+  int id = lane < G * K2 ? ce[lane] : INT_MAX;
+  merge_runs<K2, K2>(z, id, span);
+  // k <= E puts k real experts first; the clamp only keeps a lookup in bounds
+  topk_emit(z, (unsigned)id < (unsigned)E ? id : 0, k, idx_out, w_out);
+}
+
+// One token per wave, kTopkWaves waves per block.
+constexpr int kTopkWaves = 1;
+__global__ __launch_bounds__(64 * kTopkWaves) void k_topk(const double* __restrict__ z, int nsplit,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int k, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w) {
+  __shared__ double s_z[kTopkWaves][kMaxE];
+  __shared__ double s_cz[kTopkWaves][64];
+  __shared__ int s_ce[kTopkWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * kTopkWaves + wave;
   if (t >= T) return;
   const double* zt = z + (size_t)t * E;
   if (nsplit > 1) {
+    // the kLogSplit partial sums of two experts are requested before any is
+    // added (then added in range order, as before)
+#pragma unroll 2
     for (int e = lane; e < E; e += 64) {
+      double p[kLogSplit];
+#pragma unroll
+      for (int s = 0; s < kLogSplit; ++s) p[s] = z[((size_t)s * T + t) * E + e];
+      const double b = bias ? (double)bias[e] : 0.0;
       double v = 0.0;
-      for (int s = 0; s < nsplit; ++s) v += z[((size_t)s * T + t) * E + e];
-      s_z[wave][e] = v + (bias ? (double)bias[e] : 0.0);
+#pragma unroll
+      for (int s = 0; s < kLogSplit; ++s) v += p[s];
+      s_z[wave][e] = v + b;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     zt = s_z[wave];
   }
-  wave_topk(zt, E, k, idx + (size_t)t * k, w + (size_t)t * k);
+  const int G = (E + 63) / 64;
+  const int K2 = k <= 1 ? 1 : 1 << (32 - __builtin_clz(k - 1));
+  int32_t* io = idx + (size_t)t * k;
+  float* wo = w + (size_t)t * k;
+  if (G * K2 <= 64) {
+    double* cz = s_cz[wave];
+    int* ce = s_ce[wave];
+    switch (K2) {
+      case 1: wave_topk_bitonic<1>(zt, E, k, io, wo, cz, ce); break;
+      case 2: wave_topk_bitonic<2>(zt, E, k, io, wo, cz, ce); break;
+      case 4: wave_topk_bitonic<4>(zt, E, k, io, wo, cz, ce); break;
+      case 8: wave_topk_bitonic<8>(zt, E, k, io, wo, cz, ce); break;
+      case 16: wave_topk_bitonic<16>(zt, E, k, io, wo, cz, ce); break;
+      default: wave_topk_bitonic<32>(zt, E, k, io, wo, cz, ce); break;
+    }
+  } else {
+    wave_topk(zt, E, k, io, wo);
+  }
 }
 
 // ---------------------------------------------------------------- union
@@ -381,7 +444,9 @@ hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const f
 
 hipError_t launch_topk(const double* z, int nsplit, const float* bias, int T, int E, int k,
                        int32_t* idx, float* w, hipStream_t s) {
-  return launch(2, k_topk, dim3((T + 3) / 4), dim3(256), s, z, nsplit, bias, T, E, k, idx, w);
+  if (nsplit != 1 && nsplit != kLogSplit) return hipErrorInvalidValue;
+  return launch(2, k_topk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), s, z,
+                nsplit, bias, T, E, k, idx, w);
 }
 
 hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, int32_t* n_uniq,
