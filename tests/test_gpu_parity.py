@@ -112,7 +112,10 @@ def test_all_ties_choose_lowest_ids():
     assert np.all(wts == np.float32(0.25))
 
 
-@pytest.mark.parametrize("E,k,T", [(300, 5, 3), (1024, 4, 2), (256, 8, 1), (64, 32, 2)])
+@pytest.mark.parametrize("E,k,T", [(300, 5, 3), (1024, 4, 2), (256, 8, 1), (64, 32, 2),
+                                   # batches past the small limits: summed logit ranges,
+                                   # then one wave's bitonic top-k per token
+                                   (300, 5, 20), (1024, 4, 17)])
 def test_small_batch_ties_across_groups(E, k, T):
     # zero router rows: each logit is its bias, 1 for the last expert of
     # every 64-expert group and 0 elsewhere, so the picks are those experts
