@@ -16,10 +16,10 @@
 // q * s stays a normal fp16 number for 2^-14 <= |s| <= 2^12; smaller scales
 // lose relative precision gradually (fp16 subnormals), larger ones overflow.
 //
-// Work unit: one block (16 waves of 32 weight rows; 2 waves of 64 rows for
-// batches of up to 16 rows; 4 waves of 32 rows for one expert over many
-// tokens) = one expert x one M-block of up to 64 (16) of its tokens x 512
-// (128) weight rows (gate/up:
+// Work unit: one block (16 waves of 32 weight rows; 4 waves of 32 rows for
+// batches of up to 16 rows and for one expert over many tokens) = one expert
+// x one M-block of up to 64 (16) of its tokens x 512 (128) weight rows
+// (gate/up:
 // a wave's rows are half gate rows and the same rows of up, so SwiGLU is
 // local to the wave).  K is walked in 128-column
 // stages copied global -> LDS without passing through registers, into a ring
@@ -167,9 +167,10 @@ constexpr int kSC = 128;
 // (each wave copies MB / GW activation rows), over a ring of R stages (R - 1
 // in flight).  GW = 16, NTW = 2, R = 3, MB = 64: 160 KB, one block per CU,
 // four waves per SIMD (prefill; 8 waves of 64 rows in the same LDS were 2%
-// slower); GW = 2, NTW = 4, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB,
+// slower); GW = 4, NTW = 2, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB,
 // two or three blocks per CU, so a batch of a few tokens over a dozen experts
-// keeps enough bytes in flight; GW = 4, NTW = 2, MB = 64, R = 3: 76 KB, one
+// keeps enough bytes in flight (2 waves of 64 rows: 8 tokens over 13 experts
+// took 54 us for gate/up and 29 us for down instead of 50 and 26); GW = 4, NTW = 2, MB = 64, R = 3: 76 KB, one
 // expert over many tokens: 128 rows a block, as many blocks as CUs at 512
 // tokens, every SIMD busy (2 waves of 64 rows left half of them idle: one
 // expert at M = 512 took 84 us instead of 56).
@@ -444,8 +445,8 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------- launchers
 
-// Block shape of a call: batches of up to 16 rows take 2-wave blocks with
-// 16-token M-blocks; one expert over 128 rows or more (the compute-bound case)
+// Block shape of a call: batches of up to 16 rows take 4-wave blocks of 128
+// rows with 16-token M-blocks; one expert over 128 rows or more (the compute-bound case)
 // takes 4-wave blocks of 128 rows with 64-token M-blocks, four times as many
 // blocks as the 16-wave shape; everything else 16-wave blocks (32 rows a
 // wave) with 64-token M-blocks.
@@ -453,7 +454,7 @@ struct GemmShape {
   int gw, mblock, ntw;
 };
 static GemmShape gemm_shape(int rows, bool single) {
-  if (rows <= 16) return {2, 16, 4};
+  if (rows <= 16) return {4, 16, 2};
   if (single && rows >= 128) return {4, 64, 2};
   return {16, 64, 2};
 }
@@ -498,7 +499,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
                                : (unsigned)m.mb_bound;
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
   const unsigned wg = (unsigned)((m.f / (8 * ntw) + gw - 1) / gw);
-  if (gw == 2 && mblock == 16) e = launch(5, k_gemm<kGateUp, 2, 5, 16, 4>, dim3(wg, mb), dim3(128), s, ga);
+  if (gw == 4 && mblock == 16) e = launch(5, k_gemm<kGateUp, 4, 5, 16, 2>, dim3(wg, mb), dim3(256), s, ga);
   else if (gw == 4) e = launch(5, k_gemm<kGateUp, 4, 3, 64, 2>, dim3(wg, mb), dim3(256), s, ga);
   else e = launch(5, k_gemm<kGateUp, 16, 3, 64, 2>, dim3(wg, mb), dim3(1024), s, ga);
   if (e != hipSuccess) return e;
@@ -514,7 +515,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
 
   GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
   const unsigned wd = (unsigned)((m.d / (16 * ntw) + gw - 1) / gw);
-  if (gw == 2 && mblock == 16) return launch(6, k_gemm<kDown, 2, 4, 16, 4>, dim3(wd, mb), dim3(128), s, gd);
+  if (gw == 4 && mblock == 16) return launch(6, k_gemm<kDown, 4, 4, 16, 2>, dim3(wd, mb), dim3(256), s, gd);
   if (gw == 4) return launch(6, k_gemm<kDown, 4, 3, 64, 2>, dim3(wd, mb), dim3(256), s, gd);
   return launch(6, k_gemm<kDown, 16, 3, 64, 2>, dim3(wd, mb), dim3(1024), s, gd);
 }
