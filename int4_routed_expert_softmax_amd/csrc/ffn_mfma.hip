@@ -167,10 +167,11 @@ constexpr int kSC = 128;
 // (each wave copies MB / GW activation rows), over a ring of R stages (R - 1
 // in flight).  GW = 16, NTW = 2, R = 3, MB = 64: 160 KB, one block per CU,
 // four waves per SIMD (prefill; 8 waves of 64 rows in the same LDS were 2%
-// slower); GW = 4, NTW = 2, MB = 16, R = 5 (gate/up) or 4 (down): 64 / 52 KB,
-// two or three blocks per CU, so a batch of a few tokens over a dozen experts
-// keeps enough bytes in flight (2 waves of 64 rows: 8 tokens over 13 experts
-// took 54 us for gate/up and 29 us for down instead of 50 and 26); GW = 4, NTW = 2, MB = 64, R = 3: 76 KB, one
+// slower); GW = 4, NTW = 2, MB = 16, R = 3: 40 KB, several blocks per CU, so a
+// batch of a few tokens over a dozen experts keeps enough waves and bytes in
+// flight (8 tokens over 13 experts: gate/up 48 us, down 25 us; 2 waves of 64
+// rows with 5- and 4-stage rings took 54 and 29 us, 4 waves with them 50 and
+// 26 us); GW = 4, NTW = 2, MB = 64, R = 3: 76 KB, one
 // expert over many tokens: 128 rows a block, as many blocks as CUs at 512
 // tokens, every SIMD busy (2 waves of 64 rows left half of them idle: one
 // expert at M = 512 took 84 us instead of 56).
@@ -499,7 +500,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
                                : (unsigned)m.mb_bound;
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
   const unsigned wg = (unsigned)((m.f / (8 * ntw) + gw - 1) / gw);
-  if (gw == 4 && mblock == 16) e = launch(5, k_gemm<kGateUp, 4, 5, 16, 2>, dim3(wg, mb), dim3(256), s, ga);
+  if (gw == 4 && mblock == 16) e = launch(5, k_gemm<kGateUp, 4, 3, 16, 2>, dim3(wg, mb), dim3(256), s, ga);
   else if (gw == 4) e = launch(5, k_gemm<kGateUp, 4, 3, 64, 2>, dim3(wg, mb), dim3(256), s, ga);
   else e = launch(5, k_gemm<kGateUp, 16, 3, 64, 2>, dim3(wg, mb), dim3(1024), s, ga);
   if (e != hipSuccess) return e;
@@ -515,7 +516,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
 
   GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
   const unsigned wd = (unsigned)((m.d / (16 * ntw) + gw - 1) / gw);
-  if (gw == 4 && mblock == 16) return launch(6, k_gemm<kDown, 4, 4, 16, 2>, dim3(wd, mb), dim3(256), s, gd);
+  if (gw == 4 && mblock == 16) return launch(6, k_gemm<kDown, 4, 3, 16, 2>, dim3(wd, mb), dim3(256), s, gd);
   if (gw == 4) return launch(6, k_gemm<kDown, 4, 3, 64, 2>, dim3(wd, mb), dim3(256), s, gd);
   return launch(6, k_gemm<kDown, 16, 3, 64, 2>, dim3(wd, mb), dim3(1024), s, gd);
 }
