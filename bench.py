@@ -72,7 +72,8 @@ def calibrate_copy(mib):
 
 
 # Sources the decode gate/up kernel is built from.
-GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h")
+GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h",
+                  "small_route.h")
 
 
 def matrix_bytes(w):
