@@ -39,10 +39,51 @@ __device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float
   }
 }
 
+// Rows of up to kPackRegCols columns are read once into registers (every
+// load of the row in flight together), longer ones twice (max, then convert).
+constexpr int kPackRegChunks = 8;                    // 8-column chunks per lane
+constexpr int kPackRegCols = 64 * 8 * kPackRegChunks;  // 4096
+
+__device__ __forceinline__ void store8(_Float16* drow, int c, const float (&v)[8], float up) {
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  _Float16 h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[slot_of_col(j)] = (_Float16)(v[j] * up);
+  f16x8_t hv;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) hv[j] = h[j];
+  *reinterpret_cast<f16x8_t*>(drow + c) = hv;
+}
+
 // Row r of p, by one whole wave (lane = its lane).
 __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
   const size_t src_row = p.gather ? (size_t)p.gather[r] : (size_t)r;
   const size_t base = src_row * p.K;
+  if (p.K <= kPackRegCols) {
+    float v[kPackRegChunks][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPackRegChunks; ++i) {
+      const int c = (i * 64 + lane) * 8;
+      if (c < p.K) {
+        load8(p.src, p.src_bf16, base + c, v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+      }
+    }
+    m = wave_max(m);
+    int e = 0;
+    if (m > 0.0f) frexpf(m, &e);  // m < 2^e
+    const float up = m > 0.0f ? ldexpf(1.0f, kPackExp - e) : 1.0f;
+    _Float16* drow = p.dst + (size_t)r * p.K;
+#pragma unroll
+    for (int i = 0; i < kPackRegChunks; ++i) {
+      const int c = (i * 64 + lane) * 8;
+      if (c < p.K) store8(drow, c, v[i], up);
+    }
+    if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
+    return;
+  }
   float m = 0.0f;
   for (int c = lane * 8; c < p.K; c += 512) {
     float v[8];
