@@ -163,6 +163,9 @@ def test_batches_from_device_home(glm):
     (configs.Workload("cache_all", d=256, f=128, n_experts=16, top_k=4, T=3, seed=42), 16, 3, False),
     (configs.Workload("cache_bf16", d=512, f=512, n_experts=32, top_k=4, T=1, seed=43,
                       x_kind="bf16"), 6, 1, True),
+    # per-row int4 experts (one scale per row): slots of their own blob size
+    (configs.Workload("cache_perrow", d=512, f=512, n_experts=64, top_k=8, T=2, seed=44,
+                      group=0), 16, 2, False),
 ], ids=lambda v: v.name if hasattr(v, "name") else str(v))
 def test_small_layers(w, S, T, bf16):
     L = DeviceLayer(w)
@@ -178,3 +181,11 @@ def test_small_layers(w, S, T, bf16):
             assert after["misses"] == before["misses"], "a repeated sequence missed with every expert resident"
     finally:
         home.free()
+
+
+def test_glm_perrow_decode_from_device_home():
+    """The GLM-shaped layer with per-row experts, a new token per call, 12 slots."""
+    L = DeviceLayer(configs.WORKLOADS["decode1_perrow"])
+    cache = Cache(L, L.table, 12)
+    run_sequence(L, cache, range(6), 1, 0)
+    cache.check_slots()
