@@ -71,9 +71,11 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 20}), flush=True)
 
 
-# Sources the decode gate/up kernel is built from.
+# Sources the gate/up kernel of each path is built from: the one-token
+# GEMV path (decode, chain) and the grouped GEMM (batches of 2+ tokens).
 GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h",
                   "small_route.h")
+GEMM_SOURCES = ("device_util.h", "ffn_mfma.hip", "moe_internal.h", "pack.h", "small_route.h")
 
 
 def matrix_bytes(w):
@@ -84,13 +86,17 @@ def matrix_bytes(w):
     return 2 * (w.f * w.d // 2 + 2 * w.f * sg), w.f * w.d // 2 + 2 * w.d * sd
 
 
-def kernel_source_hash():
-    """sha256 of the gate/up kernel's sources: a counter summary is only
-    reused while it matches."""
+def gateup_sources(workload):
+    return GATEUP_SOURCES if workload.startswith(("decode1", "chain48")) else GEMM_SOURCES
+
+
+def kernel_source_hash(workload="decode1"):
+    """sha256 of the gate/up kernel's sources for this workload: a counter
+    summary is only reused while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_routed_expert_softmax_amd", "csrc")
-    for name in GATEUP_SOURCES:
+    for name in gateup_sources(workload):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -107,7 +113,7 @@ def committed_traffic(workload):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha") != kernel_source_hash():
+    if vals.get("kernel_source_sha") != kernel_source_hash(workload):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -179,6 +185,7 @@ def main():
         moe.moe_layer_forward(dims, L["x"], L["Wr"], L["bias"], L["table"], out, flags=flags,
                               stats=stats[i % a.layers], ws=ws, stream=stream.cuda_stream)
 
+    a.warmup = max(a.warmup, a.layers)  # every layer once, so its stats are known
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()

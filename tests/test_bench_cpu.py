@@ -27,3 +27,18 @@ def test_batch_invariant_past_its_limits_is_refused():
     r = run("--workload", "prefill512", "--batch-invariant", "--no-cpu")
     assert r.returncode != 0
     assert "batch limits" in r.stderr
+
+
+def test_per_launch_bytes_and_source_hashes():
+    # the algorithmic bytes bench.py divides by, and the counter-summary
+    # hashes, for every workload it offers
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import configs
+    for name in ("decode1", "verify8", "prefill512", "chain48", "decode1_perrow",
+                 "verify8_perrow", "prefill512_perrow"):
+        w = configs.WORKLOADS[name]
+        gu, dn = bench.matrix_bytes(w)
+        assert gu + dn == w.blob_bytes
+        assert len(bench.kernel_source_hash(name)) == 16
+    assert bench.matrix_bytes(configs.WORKLOADS["decode1"]) == (13369344, 6684672)
