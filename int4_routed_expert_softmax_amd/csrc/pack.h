@@ -41,8 +41,8 @@ __device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float
 
 // Rows of up to kPackRegCols columns are read once into registers (every
 // load of the row in flight together), longer ones twice (max, then convert).
-constexpr int kPackRegChunks = 8;                    // 8-column chunks per lane
-constexpr int kPackRegCols = 64 * 8 * kPackRegChunks;  // 4096
+constexpr int kPackRegChunks = 12;                   // 8-column chunks per lane
+constexpr int kPackRegCols = 64 * 8 * kPackRegChunks;  // 6144
 
 __device__ __forceinline__ void store8(_Float16* drow, int c, const float (&v)[8], float up) {
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
