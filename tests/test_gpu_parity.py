@@ -78,6 +78,11 @@ def test_tiny_layer():
     small("mfma_T2", 512, 512, 16, 4, 2),
     small("mfma_T5_bf16", 512, 1024, 32, 8, 5, x_kind="bf16"),
     small("mfma_T16", 1024, 512, 64, 8, 16, zipf=False),
+    # rows past the pack's 6144-column register path (max, then convert): x
+    # packed beside the router (small batch) and by the pack kernel, and a
+    small("mfma_x7168_T5", 7168, 512, 16, 4, 5),
+    small("mfma_x7168", 7168, 512, 16, 4, 40),
+    small("mfma_a7168", 512, 7168, 16, 4, 12),
     # small batches whose top-k merges several 64-expert groups
     small("small_E1024_k4", 256, 128, 1024, 4, 2),
     small("small_E300_k5", 256, 128, 300, 5, 3),
