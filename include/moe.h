@@ -108,6 +108,29 @@ size_t moe_workspace_bytes(const moe_dims* dims, int32_t T_max);
 const char* moe_strerror(int code);
 
 /*
+ * Where a call leaves its routing in the workspace: byte offsets from ws of
+ * the routing results of the last moe_layer_forward or
+ * moe_layer_forward_cached call for T tokens on that workspace (the layout
+ * depends on the call's T, not on the T_max the workspace was sized for):
+ *   topk_idx  int32 [T][k]   chosen ids in slot order (as moe_route)
+ *   topk_w    f32   [T][k]   renormalised router weights (as moe_route)
+ *   uniq      int32 [min(E, T*k)]      distinct ids ascending, then -1 (as moe_union)
+ *   n_uniq    int32 [1]                U
+ *   offsets   int32 [min(E, T*k) + 1]  per-expert slot ranges (as moe_union)
+ *   rows      int32 [T*k]              slot ids grouped by expert, ascending t
+ * These are the lists the call's expert kernels walked, so a caller can check
+ * or reuse them (they are valid once the call's work on its stream has
+ * completed and until the next call on the workspace).  Returns MOE_OK, or
+ * MOE_EINVAL / MOE_EUNSUPPORTED for invalid dims, T < 1 or a NULL `out`.
+ * Source: route, then union, per token and layer — colibri 技术解读,
+ * "引擎结构：一个 C 文件，五步 token 路径"; README 工作原理 › 绝不为同一次磁盘读取等待两遍.
+ */
+typedef struct moe_routing_offsets {
+  size_t topk_idx, topk_w, uniq, n_uniq, offsets, rows;
+} moe_routing_offsets;
+int moe_workspace_routing(const moe_dims* dims, int32_t T, moe_routing_offsets* out);
+
+/*
  * moe_route — router logits, top-k and renormalised weights.
  *   x          [T][d] activations, f32 or bf16 (x_dtype), row-major
  *   w_router   [E][d] f32 router matrix, row-major

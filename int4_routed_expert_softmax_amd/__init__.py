@@ -21,7 +21,8 @@ MOE_PRENORM_RMS, MOE_RESIDUAL, MOE_BATCH_INVARIANT = 1, 2, 4
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 
 # Every function include/moe.h declares.
-EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_route",
+EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_workspace_routing",
+           "moe_strerror", "moe_route",
            "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_cache_state_bytes",
            "moe_layer_forward_cached", "moe_timing_arm", "moe_hbm_read_probe")
 
@@ -34,6 +35,11 @@ class MoeError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: {strerror(code)} (code {code})")
         self.code = code
+
+
+class moe_routing_offsets(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("topk_idx", "topk_w", "uniq", "n_uniq", "offsets", "rows")]
 
 
 class moe_dims(ctypes.Structure):
@@ -80,6 +86,8 @@ def _load():
     L.moe_expert_blob_bytes.argtypes = [dp]
     L.moe_workspace_bytes.restype = sz
     L.moe_workspace_bytes.argtypes = [dp, i32]
+    L.moe_workspace_routing.restype = ctypes.c_int
+    L.moe_workspace_routing.argtypes = [dp, i32, ctypes.POINTER(moe_routing_offsets)]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_route.restype = ctypes.c_int
@@ -150,6 +158,36 @@ def make_workspace(dims: Dims, T_max: int, device="cuda"):
     """A zero-filled workspace (the library keeps its counters at zero)."""
     import torch
     return torch.zeros(workspace_bytes(dims, T_max), dtype=torch.uint8, device=device)
+
+
+def moe_workspace_routing(dims: Dims, T: int) -> dict:
+    """Byte offsets in a workspace of the routing results a layer call on T
+    tokens leaves there."""
+    o = moe_routing_offsets()
+    _check(lib.moe_workspace_routing(ctypes.byref(dims.c()), T, ctypes.byref(o)),
+           "moe_workspace_routing")
+    return {n: getattr(o, n) for n, _ in moe_routing_offsets._fields_}
+
+
+def workspace_routing(dims: Dims, T: int, ws) -> dict:
+    """Views into the workspace ws (uint8 device tensor) of the routing of
+    the last layer call on T tokens: topk_idx [T][k] int32, topk_w [T][k]
+    f32, uniq [cap] int32, n_uniq [1] int32, offsets [cap + 1] int32, rows
+    [T*k] int32, cap = min(E, T*k)."""
+    import torch
+    off = moe_workspace_routing(dims, T)
+    k, cap = dims.top_k, min(dims.n_experts, T * dims.top_k)
+
+    def view(name, n, dt):
+        nb = n * 4
+        return ws[off[name]:off[name] + nb].view(dt)
+
+    return {"topk_idx": view("topk_idx", T * k, torch.int32).view(T, k),
+            "topk_w": view("topk_w", T * k, torch.float32).view(T, k),
+            "uniq": view("uniq", cap, torch.int32),
+            "n_uniq": view("n_uniq", 1, torch.int32),
+            "offsets": view("offsets", cap + 1, torch.int32),
+            "rows": view("rows", T * k, torch.int32)}
 
 
 def moe_route(dims: Dims, x, w_router, bias, topk_idx, topk_w, ws, stream=None):

@@ -148,6 +148,20 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dm, int32_t T_max) {
   return ws_need(layout(dm->d, dm->f, dm->n_experts, dm->top_k, T_max), dm->n_experts);
 }
 
+MOE_API int moe_workspace_routing(const moe_dims* dm, int32_t T, moe_routing_offsets* out) {
+  const int st = dims_status(dm);
+  if (st != MOE_OK) return st;
+  if (T < 1 || !out) return MOE_EINVAL;
+  const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, T);
+  out->topk_idx = L.idx;
+  out->topk_w = L.w;
+  out->uniq = L.uniq;
+  out->n_uniq = L.nuniq;
+  out->offsets = L.offs;
+  out->rows = L.rows;
+  return MOE_OK;
+}
+
 MOE_API size_t moe_cache_state_bytes(const moe_dims* dm, int32_t n_slots) {
   if (dims_status(dm) != MOE_OK || n_slots < 1 || n_slots > dm->n_experts) return 0;
   return align_up(cache_state_bytes(dm->n_experts, n_slots));

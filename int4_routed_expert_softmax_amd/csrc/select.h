@@ -264,12 +264,19 @@ __device__ __forceinline__ void wave_union_small(const int32_t* idx, int n, int 
     uniq[u] = sid;
     offsets[u] = lane;
   }
+  // offsets[U .. cap] = n and uniq[U .. cap - 1] = -1.  offsets has cap + 1
+  // <= 65 entries, one more than the wave has lanes: lane l writes entry
+  // l + 1 and lane 0 entry U (U itself can be 64, every pick a different
+  // expert).
   const int cap = min(E, n);
-  if (lane >= U && lane <= cap) {
-    offsets[lane] = n;
-    if (lane < cap) uniq[lane] = -1;
+  if (lane >= U && lane < cap) {
+    offsets[lane + 1] = n;
+    uniq[lane] = -1;
   }
-  if (lane == 0) *n_uniq = U;
+  if (lane == 0) {
+    offsets[U] = n;
+    *n_uniq = U;
+  }
 }
 
 // ---------------------------------------------------------------- union

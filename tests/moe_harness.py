@@ -2,6 +2,9 @@
 entry points through the C ABI, compare with the CPU oracle."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -76,18 +79,54 @@ class DeviceLayer:
         moe.moe_layer_forward(self.dims, xd, self.Wr_d, self.bias_d, self.table, out, flags=flags,
                               rms_eps=eps, stats=stats, ws=ws)
         torch.cuda.synchronize()
+        self.last_ws = ws
         return out, stats
 
     def oracle_table(self):
         return [self.blobs[e] for e in range(self.w.n_experts)]
 
 
-def assert_close(got, ref, what="output"):
+def record_margin(case: str, rel: float, **extra):
+    """Append a case's measured max-abs-error / max|ref| to the file named by
+    MOE_PARITY_LOG (one JSON object a line), when that variable is set."""
+    path = os.environ.get("MOE_PARITY_LOG")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as fh:
+        fh.write(json.dumps({"case": case, "rel_err": float(rel), "tol": REL_TOL, **extra}) + "\n")
+
+
+def assert_close(got, ref, what="output", case=None):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref).max()
     tol = REL_TOL * np.abs(ref).max()
     assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.3e}"
-    return err / max(np.abs(ref).max(), 1e-300)
+    rel = err / max(np.abs(ref).max(), 1e-300)
+    if case is not None:
+        record_margin(case, rel, what=what)
+    return rel
+
+
+def check_layer_routing(dims, ws, T: int, ref: dict, what: str = "layer call"):
+    """The routing a layer call left in its workspace (the lists its expert
+    kernels walked) against the oracle's: ids, union, offsets and slot lists
+    bit-exact, weights within 1e-6 relative."""
+    r = moe.workspace_routing(dims, T, ws)
+    torch.cuda.synchronize()
+    k = dims.top_k
+    idx = r["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx, ref["idx"]), f"{what}: routing indices differ from the oracle"
+    np.testing.assert_allclose(r["topk_w"].cpu().numpy(), ref["w"], rtol=1e-6, atol=1e-7,
+                               err_msg=f"{what}: router weights")
+    U = int(r["n_uniq"].item())
+    assert U == ref["U"], f"{what}: U {U} != {ref['U']}"
+    uniq, offs, rows = (r[n].cpu().numpy() for n in ("uniq", "offsets", "rows"))
+    assert np.array_equal(uniq[:U], ref["uniq"]) and np.all(uniq[U:] == -1), f"{what}: union"
+    assert np.array_equal(offs[:U + 1], ref["offsets"]), f"{what}: offsets"
+    assert np.all(offs[U + 1:] == T * k), f"{what}: offsets past U"
+    assert np.array_equal(rows, ref["rows"]), f"{what}: per-expert slot lists"
+    return U
 
 
 def check_union(layer: DeviceLayer, idx: np.ndarray):

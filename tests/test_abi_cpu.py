@@ -191,3 +191,30 @@ def test_strerror():
 
 def test_one_hip_runtime_in_process():
     assert len(moe._hip_runtimes()) == 1
+
+
+@pytest.mark.parametrize("dims,T", [(GLM, 1), (GLM, 8), (GLM, 512), (TINY, 4),
+                                    (moe.Dims(256, 128, 1024, 32), 2)])
+def test_workspace_routing_offsets_lie_inside_the_workspace(dims, T):
+    off = moe.moe_workspace_routing(dims, T)
+    k, cap = dims.top_k, min(dims.n_experts, T * dims.top_k)
+    sizes = {"topk_idx": 4 * T * k, "topk_w": 4 * T * k, "uniq": 4 * cap, "n_uniq": 4,
+             "offsets": 4 * (cap + 1), "rows": 4 * T * k}
+    total = moe.workspace_bytes(dims, T)
+    spans = sorted((off[n], off[n] + sizes[n]) for n in sizes)
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0, "routing arrays overlap"
+    assert spans[-1][1] <= total
+    assert all(off[n] % 4 == 0 for n in off)
+    # a smaller call on a larger workspace: offsets of its own T, still inside
+    if T > 1:
+        assert moe.moe_workspace_routing(dims, 1)["rows"] < total
+
+
+def test_workspace_routing_rejects_bad_arguments():
+    o = moe.moe_routing_offsets()
+    assert moe.lib.moe_workspace_routing(ctypes.byref(GLM.c()), 0, ctypes.byref(o)) == moe.MOE_EINVAL
+    assert moe.lib.moe_workspace_routing(ctypes.byref(GLM.c()), 1, None) == moe.MOE_EINVAL
+    bad = moe.Dims(6144, 2048, 256, 8, 32)
+    assert moe.lib.moe_workspace_routing(ctypes.byref(bad.c()), 1, ctypes.byref(o)) == \
+        moe.MOE_EUNSUPPORTED

@@ -19,7 +19,7 @@ import int4_routed_expert_softmax_amd as moe
 import oracle
 from synth import configs
 
-from moe_harness import DEV, DeviceLayer, assert_close, say
+from moe_harness import DEV, DeviceLayer, assert_close, check_layer_routing, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,7 @@ def check(L: DeviceLayer, x: np.ndarray, bf: bool, flags: int, in_place=False, r
     solo, cnt = one_by_one(L, xd, flags, in_place)
     xb = xd.clone()
     out, st = L.forward(xb, flags=flags | INV, out=xb if in_place else None)
+    inv_ws = L.last_ws
     got = bits(out)
     for t in range(x.shape[0]):
         assert np.array_equal(got[t], solo[t]), (
@@ -69,7 +70,8 @@ def check(L: DeviceLayer, x: np.ndarray, bf: bool, flags: int, in_place=False, r
         r = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=bf,
                                  flags=flags)
         assert s[0] == r["U"]
-        assert_close(out.cpu().numpy(), r["out"])
+        check_layer_routing(L.dims, inv_ws, x.shape[0], r, f"{w.name} batch-invariant call")
+        assert_close(out.cpu().numpy(), r["out"], case=f"{w.name} INV flags={flags}")
 
 
 @pytest.fixture(scope="module")

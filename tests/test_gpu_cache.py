@@ -10,7 +10,9 @@ for one token, with MOE_BATCH_INVARIANT for batches.  The placement policy is
 pinned exactly: after every call the whole device state (clock, hit and miss
 counters, slot of every expert, expert of every slot, last-use stamps) must
 equal a host replay of the rule written out below, and a slot must hold its
-expert's blob byte for byte.
+expert's blob byte for byte.  Every cached call is also held to the oracle
+directly: its routing and union lists (as the call left them in its
+workspace) bit-exact, its output within 2e-3 * max|ref|.
 """
 import ctypes
 
@@ -19,9 +21,10 @@ import pytest
 import torch
 
 import int4_routed_expert_softmax_amd as moe
+import oracle
 from synth import configs
 
-from moe_harness import DEV, DeviceLayer, say
+from moe_harness import DEV, DeviceLayer, assert_close, check_layer_routing, say
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +99,7 @@ class Cache:
         moe.moe_layer_forward_cached(L.dims, xd, L.Wr_d, L.bias_d, self.home, self.slots, self.S,
                                      self.state, out, flags=flags, stats=stats, ws=ws)
         torch.cuda.synchronize()
+        self.last_ws = ws
         return out, stats
 
     def check_state(self, union):
@@ -116,10 +120,16 @@ def run_sequence(L: DeviceLayer, cache: Cache, steps, T, flags, bf16=False, in_p
     w = L.w
     for step in steps:
         x, bf = configs.tokens(w, step=step, T=T)
-        xd = L.x_device(np.ascontiguousarray(x), bf)
+        x = np.ascontiguousarray(x)
+        xd = L.x_device(x, bf)
         ref, rst = L.forward(xd.clone(), flags=flags | (INV if T > 1 else 0))
         xc = xd.clone()
         out, st = cache.forward(xc, flags, out=xc if in_place else None)
+        orc = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k,
+                                   x_bf16=bf, flags=flags, group=w.group)
+        check_layer_routing(L.dims, cache.last_ws, T, orc, f"{w.name} cached step {step}")
+        assert_close(out.cpu().numpy(), orc["out"], f"{w.name} cached step {step}",
+                     case=f"{w.name} cached T={T} S={cache.S} flags={flags}")
         assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32)), \
             f"step {step}: cached output differs from the resident one"
         s, r = st.cpu().numpy(), rst.cpu().numpy()

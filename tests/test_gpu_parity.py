@@ -1,11 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Bit-exact: routing indices, union lists and per-expert slot lists (ties to the
-lower expert id).  Floating point: layer and expert outputs within
+lower expert id), both from moe_route / moe_union and as the layer call itself
+left them in its workspace (the lists its expert kernels walked: the
+single-token gate/up prologue, the small-batch routing block, or the large-batch
+top-k and union kernels).  Floating point: layer and expert outputs within
 max-abs-error <= 2e-3 * max|ref| (the oracle is fp64); router weights within
 1e-6 relative.  Full-size GLM-5.2-shaped layers (d=6144, f=2048, 256 experts,
-top-8) run at batch 1, 8 and 512; the 512-token prefill chunk is compared in
-full for routing and union and on sampled tokens for outputs.
+top-8) run at batch 1, 8 and 512, each compared in full.
 """
 import ctypes
 
@@ -18,7 +20,8 @@ import oracle
 import synth
 from synth import configs
 
-from moe_harness import DEV, DeviceLayer, assert_close, check_union, say
+from moe_harness import (DEV, DeviceLayer, assert_close, check_layer_routing, check_union,
+                         record_margin, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +51,8 @@ def full_parity(w: configs.Workload, flags=0, layer=None):
     cnt = np.zeros(w.n_experts, np.int64)
     np.add.at(cnt, ref["idx"].reshape(-1), 1)
     assert np.array_equal(st[1:], cnt)
-    rel = assert_close(out.cpu().numpy(), ref["out"])
+    check_layer_routing(L.dims, L.last_ws, w.T, ref, f"{w.name} layer call")
+    rel = assert_close(out.cpu().numpy(), ref["out"], case=f"{w.name} flags={flags}")
     say(f"parity: {w.name} U={ref['U']} rel err {rel:.2e}")
     return L, ref, out
 
@@ -281,7 +285,10 @@ def test_glm_verify_batch8():
     say(f"verify8: union of {ref['U']} distinct experts for 64 picks")
 
 
-def test_glm_prefill512_routing_union_and_sampled_outputs():
+def test_glm_prefill512_every_token():
+    """The 512-token prefill chunk in full: routing and union through
+    moe_route / moe_union and as the layer call left them, and every output
+    value of all 512 tokens against one batched oracle layer."""
     w = W["prefill512"]
     L = DeviceLayer(w)
     x, bf = configs.tokens(w)
@@ -292,12 +299,54 @@ def test_glm_prefill512_routing_union_and_sampled_outputs():
     assert np.array_equal(idx, ridx)
     np.testing.assert_allclose(wts, rw, rtol=1e-6, atol=1e-7)
     U = check_union(L, idx)
-    say(f"prefill512: U = {U}")
+    say(f"prefill512: U = {U}; layer call")
     out, stats = L.forward(xd)
     assert stats[0].item() == U
     out = out.cpu().numpy()
-    for t in [0, 1, 137, 255, 400, 511]:
-        r = oracle.layer_forward(x[t:t + 1], L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k,
-                                 x_bf16=True)
-        rel = assert_close(out[t:t + 1], r["out"], f"prefill token {t}")
-        say(f"prefill512: token {t} rel err {rel:.2e}")
+    say("prefill512: oracle layer over all 512 tokens")
+    ref = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=True)
+    check_layer_routing(L.dims, L.last_ws, w.T, ref, "prefill512 layer call")
+    rel = assert_close(out, ref["out"], "prefill512 all tokens", case="prefill512 flags=0")
+    # per-token margins too: the worst token against its own max|ref|
+    per_tok = np.abs(out - ref["out"]).max(axis=1) / np.abs(ref["out"]).max(axis=1)
+    record_margin("prefill512 worst token (own max|ref|)", float(per_tok.max()))
+    say(f"prefill512: U={U} rel err {rel:.2e} (worst token against its own max: "
+        f"{per_tok.max():.2e})")
+
+
+def _disjoint_layer(name, d, f, E, k, T):
+    """Router rows and tokens that send token t to experts k t .. k t + k - 1
+    (every logit of those is 10, every other 0, so the ties inside a token are
+    decided by the lower id): T * k distinct picks."""
+    w = small(name, d, f, E, k, T, zipf=False)
+    Wr = np.zeros((E, d), np.float32)
+    for e in range(T * k):
+        Wr[e, e // k] = 1.0
+    L = DeviceLayer(w, Wr=Wr, bias=None)
+    x = np.zeros((T, d), np.float32)
+    x[np.arange(T), np.arange(T)] = 10.0
+    return w, L, x
+
+
+@pytest.mark.parametrize("d,f,E,k,T", [
+    (256, 128, 64, 8, 8),      # GEMV path, 8 tokens x 8 picks, every pick distinct
+    (256, 128, 1024, 32, 2),   # GEMV path, top-32 of 1024
+    (512, 512, 64, 8, 8),      # grouped-GEMM path (routing block + M-block map)
+    (512, 512, 1024, 32, 2),
+])
+def test_union_of_64_distinct_picks(d, f, E, k, T):
+    """A small batch whose T * k = 64 picks are all different experts (U = 64,
+    one past the last lane of the union wave) with and without the
+    batch-invariant flag: the layer's own union lists bit-exact, outputs in
+    tolerance."""
+    w, L, x = _disjoint_layer(f"disjoint_d{d}_E{E}_k{k}_T{T}", d, f, E, k, T)
+    say(f"parity: {w.name}")
+    ref = oracle.layer_forward(x, L.Wr, None, L.oracle_table(), d, f, k)
+    assert ref["U"] == 64
+    xd = L.x_device(x, False)
+    for flags in (0, moe.MOE_BATCH_INVARIANT):
+        out, st = L.forward(xd, flags=flags)
+        assert st[0].item() == 64
+        check_layer_routing(L.dims, L.last_ws, T, ref, f"{w.name} flags={flags}")
+        rel = assert_close(out.cpu().numpy(), ref["out"], case=f"{w.name} flags={flags}")
+        say(f"parity: {w.name} flags={flags} U=64 rel err {rel:.2e}")
