@@ -50,8 +50,8 @@
  *    Calls enqueue only kernels (no memset/memcpy), so they may be captured in
  *    a HIP graph.
  *  - `ws` is a caller-provided device workspace of at least
- *    moe_workspace_bytes(dims, T) bytes.  It must be zero-filled before its
- *    first use; every call leaves its internal counters at zero again.  Calls
+ *    moe_workspace_bytes(dims, T) bytes.  Its contents need not be
+ *    initialised: every call writes each word of it before reading it.  Calls
  *    that share a workspace must not overlap in time.
  *  - All arguments are validated before anything is enqueued; on error the
  *    call returns a negative code and enqueues nothing.  Device-side faults
@@ -277,6 +277,35 @@ int moe_layer_forward_cached(const moe_dims* dims, const void* x, int x_dtype, i
                              const void* const* home_table, void* slots, int32_t n_slots,
                              void* cache_state, float* out, uint32_t flags, float rms_eps,
                              int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward_noalloc — moe_layer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The arguments and results are those of
+ * moe_layer_forward without ws / ws_bytes: the workspace is instead a fixed
+ * array of MOE_NOALLOC_SCRATCH_BYTES in the library's own device memory,
+ * one per GPU, held from the first call on that GPU until the process ends.
+ * The call allocates and frees nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks up that device's copy of the
+ * array, with the device current.  The caller still owns x, the router, the
+ * expert table, out and stats.
+ *   - A call needs moe_workspace_bytes(dims, T) <= MOE_NOALLOC_SCRATCH_BYTES
+ *     (GLM-5.2-shaped layers, d = 6144, f = 2048, 256 experts, top-8: up to
+ *     T = 64 tokens); larger calls return MOE_ENOSPC and enqueue nothing.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's contents (no part of it needs to start at zero: every call
+ *     writes each word before it reads it).  Calls that overlap in time on
+ *     one GPU (other streams, other threads) race on it and must not be made.
+ *   - moe_workspace_routing applies to the array as to a workspace, but the
+ *     array is not addressable by the caller.
+ * Errors as moe_layer_forward, plus MOE_ENOSPC for a call past the limit and
+ * MOE_EHIP when the array's address cannot be looked up.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_forward_noalloc(const moe_dims* dims, const void* x, int x_dtype, int32_t T,
+                              const float* w_router, const float* bias,
+                              const void* const* expert_table, float* out, uint32_t flags,
+                              float rms_eps, int32_t* stats, void* stream);
 
 /*
  * Kernel timing — instrumentation, not part of the layer's computation.

@@ -24,7 +24,11 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_workspace_routing",
            "moe_strerror", "moe_route",
            "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_cache_state_bytes",
-           "moe_layer_forward_cached", "moe_timing_arm", "moe_hbm_read_probe")
+           "moe_layer_forward_cached", "moe_layer_forward_noalloc", "moe_timing_arm",
+           "moe_hbm_read_probe")
+
+# Bytes of the library's own per-GPU workspace behind moe_layer_forward_noalloc.
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Kernel ids for moe_timing_arm.
 KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
@@ -104,6 +108,9 @@ def _load():
     L.moe_layer_forward_cached.restype = ctypes.c_int
     L.moe_layer_forward_cached.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, i32, vp, vp,
                                            u32, ctypes.c_float, vp, vp, sz, vp]
+    L.moe_layer_forward_noalloc.restype = ctypes.c_int
+    L.moe_layer_forward_noalloc.argtypes = [dp, vp, ctypes.c_int, i32, vp, vp, vp, vp, u32,
+                                            ctypes.c_float, vp, vp]
     L.moe_timing_arm.restype = ctypes.c_int
     L.moe_timing_arm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int]
     L.moe_hbm_read_probe.restype = ctypes.c_int
@@ -218,6 +225,18 @@ def moe_layer_forward(dims: Dims, x, w_router, bias, expert_table, out, flags=0,
                                  _ptr(bias), _ptr(expert_table), _ptr(out), flags, rms_eps,
                                  _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(dims: Dims, x, w_router, bias, expert_table, out, flags=0,
+                              rms_eps=1e-6, stats=None, stream=None):
+    """moe_layer_forward on the library's own per-GPU workspace (no ws
+    argument; nothing is allocated).  Calls needing more than
+    NOALLOC_SCRATCH_BYTES of workspace raise MoeError (MOE_ENOSPC)."""
+    T = x.shape[0]
+    _check(lib.moe_layer_forward_noalloc(ctypes.byref(dims.c()), _ptr(x), _xdtype(x), T,
+                                         _ptr(w_router), _ptr(bias), _ptr(expert_table), _ptr(out),
+                                         flags, rms_eps, _ptr(stats), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def cache_state_bytes(dims: Dims, n_slots: int) -> int:

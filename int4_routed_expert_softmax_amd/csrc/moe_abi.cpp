@@ -95,6 +95,12 @@ int hip_status(hipError_t e) {
   return MOE_EHIP;
 }
 
+}  // namespace
+
+int moe::hip_error_status(hipError_t e) { return hip_status(e); }
+
+namespace {
+
 #define MOE_TRY(call)                       \
   do {                                      \
     const int _st = hip_status(call);       \

@@ -45,6 +45,9 @@ struct Layout {
 
 Layout layout(int d, int f, int E, int k, int T);
 
+// MOE_OK for hipSuccess, else MOE_EHIP with the error kept for moe_strerror.
+int hip_error_status(hipError_t e);
+
 // Expert list handed to the FFN kernels.  Either a device union (uniq, n_uniq,
 // offsets, list of slot ids; x row of a slot = slot / kdiv) read from the
 // device, or one expert (`single` blob, single_n rows, slot i = x row i).
