@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="decode1: skip the verify8 and prefill512 figures on the same layers")
     p.add_argument("--host-tier", type=int, default=0, metavar="SLOTS",
                    help="decode1 / verify8 with one layer's experts in pinned host memory behind an "
                         "HBM cache of SLOTS expert slots (moe_layer_forward_cached); each step is "
@@ -150,56 +152,102 @@ def main():
         sys.exit(f"--batch-invariant: {w.name} has T={w.T}, past the single-token family's "
                  "batch limits (T <= 8, T * k <= 64)")
     dev = torch.device("cuda:0")
-    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
-    blob = w.blob_bytes
-    nib_gu, nib_dn = matrix_bytes(w)
 
     print(f"bench: {w.name} T={w.T} layers={a.layers} generating + uploading "
-          f"{a.layers * w.n_experts * blob / 1e9:.1f} GB", file=sys.stderr, flush=True)
+          f"{a.layers * w.n_experts * w.blob_bytes / 1e9:.1f} GB", file=sys.stderr, flush=True)
     layers = []
     for l in range(a.layers):
         Wr, bias = configs.router(w, l)
         blobs = torch.from_numpy(configs.experts(w, l)).to(dev)
         table = torch.tensor([blobs[e].data_ptr() for e in range(w.n_experts)], dtype=torch.int64,
                              device=dev)
-        x, bf = configs.tokens(w, l)
-        xd = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if bf
-              else torch.from_numpy(x).to(dev))
         layers.append(dict(Wr=torch.from_numpy(Wr).to(dev),
                            bias=None if bias is None else torch.from_numpy(bias).to(dev),
-                           blobs=blobs, table=table, x=xd))
+                           blobs=blobs, table=table))
         print(f"bench: layer {l} resident", file=sys.stderr, flush=True)
+
+    res = measure(moe, torch, w, layers, a.steps, a.warmup, a.batch_invariant,
+                  lambda l: configs.tokens(w, l))
+    res["config"]["workload"] += f", {a.layers} rotating HBM-resident layers"
+    ceil = hbm_ceiling(moe, torch)
+    res["hbm_read_ceiling"] = ceil
+    for key in ("roofline", "roofline_down"):
+        res[key]["frac_of_read_ceiling"] = round(res[key]["achieved"] / ceil["GBps"], 4)
+    if w.T > 8:
+        res["mfma"] = mfma_figures(moe, torch, w, layers[0], res.pop("_gateup"))
+    res.pop("_gateup", None)
+    if a.workload == "decode1" and not a.no_extra:
+        # the other two single-layer workloads, measured on the same resident
+        # layers (same shape and weight distributions; their own token recipes)
+        extra = {}
+        for name in ("verify8", "prefill512"):
+            wx = configs.WORKLOADS[name]
+            K = min(a.steps, 50 if wx.T > 8 else a.steps)
+            r = measure(moe, torch, wx, layers, K, a.warmup, False,
+                        lambda l, wx=wx: configs.tokens(wx, l))
+            r["config"]["workload"] += (f", on the {a.layers} rotating layers of this run "
+                                        f"(decode1's seeded experts)")
+            if wx.T > 8:
+                r["mfma"] = mfma_figures(moe, torch, wx, layers[0], r.pop("_gateup"))
+            r.pop("_gateup", None)
+            for key in ("roofline", "roofline_down"):
+                r[key]["frac_of_read_ceiling"] = round(r[key]["achieved"] / ceil["GBps"], 4)
+            for k_ in ("metric", "unit", "n_gpus", "higher_is_better", "scaling", "vs_baseline",
+                       "data"):
+                r.pop(k_, None)
+            extra[name] = r
+            print(f"bench: {name} {r['value']} tokens/s, gate/up {r['roofline']['achieved']} GB/s",
+                  file=sys.stderr, flush=True)
+        res["other_workloads"] = extra
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def measure(moe, torch, w, layers, K, warmup, inv, tokens):
+    """One workload on resident layers: `warmup` untimed steps, then K steps
+    timed as one HIP graph replay (step i on layer i mod len(layers), each
+    layer with its own seeded tokens), K eager steps for comparison, K more
+    with HIP events around every gate/up and down launch (the roofline), and
+    K with an event pair around each step (the spread)."""
+    dev = torch.device("cuda:0")
+    R = len(layers)
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
+    blob = w.blob_bytes
+    nib_gu, nib_dn = matrix_bytes(w)
+    xs = []
+    for l in range(R):
+        x, bf = tokens(l)
+        xs.append(torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if bf
+                  else torch.from_numpy(np.ascontiguousarray(x)).to(dev))
     out = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
-    stats = torch.zeros(a.layers, 1 + w.n_experts, dtype=torch.int32, device=dev)
+    stats = torch.zeros(R, 1 + w.n_experts, dtype=torch.int32, device=dev)
     ws = moe.make_workspace(dims, w.T, dev)
     stream = torch.cuda.current_stream()
-
-    inv = a.batch_invariant
     flags = moe.MOE_BATCH_INVARIANT if inv else 0
     # the library's choice: one token (or the flag) takes the int8-digit GEMV
     # kernels; 2+ tokens with d, f multiples of 512 the fp16 MFMA grouped GEMM
     gemv = w.T == 1 or inv or w.d % 512 or w.f % 512
 
     def step(i, s=None):
-        L = layers[i % a.layers]
-        moe.moe_layer_forward(dims, L["x"], L["Wr"], L["bias"], L["table"], out, flags=flags,
-                              stats=stats[i % a.layers], ws=ws,
+        L = layers[i % R]
+        moe.moe_layer_forward(dims, xs[i % R], L["Wr"], L["bias"], L["table"], out, flags=flags,
+                              stats=stats[i % R], ws=ws,
                               stream=stream.cuda_stream if s is None else s)
 
-    a.warmup = max(a.warmup, a.layers)  # every layer once, so its stats are known
-    for i in range(a.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    U = stats[:, 0].cpu().numpy().astype(np.float64)  # distinct experts per layer
 
     # K steps with plain launches (Python enqueues every call)
-    K = a.steps
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i)
     torch.cuda.synchronize()
     eager = (time.perf_counter() - t0) / K
+    # the distinct experts of each layer, from the layer calls' own counts
+    U = stats[:, 0].cpu().numpy().astype(np.float64)
+    hot = stats[0, 1:].cpu().numpy()
 
     # the timed region: the same K steps as one HIP graph (the library only
     # enqueues kernels and allocates nothing), replayed once after a warm
@@ -217,6 +265,7 @@ def main():
     graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    del graph
 
     # the same K steps again with every launch of the two FFN kernels recording
     # HIP events on the launch stream (recording adds launch overhead, so the
@@ -244,21 +293,22 @@ def main():
     step_us = np.array([s_.elapsed_time(e_) for s_, e_ in zip(*sev)]) * 1e3
 
     sec = (t1 - t0) / K
-    u_steps = np.array([U[i % a.layers] for i in range(K)])
+    u_steps = np.array([U[i % R] for i in range(K)])
     tok_s = w.T / sec
     weight_bytes_step = u_steps.mean() * blob
     gu_bytes = u_steps * nib_gu
     dn_bytes = u_steps * nib_dn
     gu_gbps = float(np.mean(gu_bytes / dur["gateup"]) / 1e9)
     dn_gbps = float(np.mean(dn_bytes / dur["down"]) / 1e9)
-
-    res = {
+    del ws
+    torch.cuda.empty_cache()
+    return {
         "metric": METRIC,
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": a.warmup,
+        "warmup": warmup,
         "ms_per_step": round(sec * 1e3, 5),
         "ms_per_step_eager": round(eager * 1e3, 5),
         "higher_is_better": True,
@@ -268,12 +318,12 @@ def main():
                   "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
-                               f"top-{w.top_k}, T={w.T} tokens, "
+                               f"top-{w.top_k}, T={w.T} tokens "
+                               f"({'bf16' if w.x_bf16 else 'fp32'} x), "
                                f"{'gs64' if w.group else 'per-row'} int4 experts "
-                               f"({blob} B each), {a.layers} rotating HBM-resident layers"
-                               + (", MOE_BATCH_INVARIANT" if inv else ""),
+                               f"({blob} B each)" + (", MOE_BATCH_INVARIANT" if inv else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
-                   "layers_rotated": a.layers, "distinct_experts_per_step": float(u_steps.mean())},
+                   "layers_rotated": R, "distinct_experts_per_step": float(u_steps.mean())},
         "step_us_p10_p50_p90": [round(float(v), 2) for v in np.percentile(step_us, [10, 50, 90])],
         "expert_weight_GBps": round(weight_bytes_step / sec / 1e9, 1),
         "expert_weight_frac_hbm_peak": round(weight_bytes_step / sec / 1e9 / HBM_PEAK_GBPS, 4),
@@ -289,16 +339,8 @@ def main():
                           "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "bytes_per_launch": float(dn_bytes.mean()),
                           "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
+        "_gateup": {"dur": dur["gateup"], "hot_counts": hot, "x0": xs[0], "dims": dims},
     }
-    ceil = hbm_ceiling(moe, torch)
-    res["hbm_read_ceiling"] = ceil
-    res["roofline"]["frac_of_read_ceiling"] = round(gu_gbps / ceil["GBps"], 4)
-    res["roofline_down"]["frac_of_read_ceiling"] = round(dn_gbps / ceil["GBps"], 4)
-    if w.T > 8:
-        res["mfma"] = mfma_figures(moe, torch, w, layers[0], dims, gu_bytes, dur, U)
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
@@ -334,29 +376,24 @@ def hbm_ceiling(moe, torch, gib=4):
     return best
 
 
-def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
+def mfma_figures(moe, torch, w, L0, g):
     """fp16 MFMA throughput of the grouped gate/up GEMM: for the whole layer
     (useful flops 2 * T*k * d * 2f over its measured launches), and for one
-    expert alone at M = 512 tokens and at the token count of the hottest
-    expert of the batch (moe_expert_ffn, same kernels), each timed with HIP
-    events over 20 launches.  Its blocks may not fill every CU, so the
-    figure is also given per occupied CU."""
-    import oracle
-    from synth import configs
-
+    expert alone at M = 512 tokens and at the token count of layer 0's hottest
+    expert (from the layer call's own per-expert counts), each through
+    moe_expert_ffn (same kernels) timed with HIP events over 20 launches."""
     dev = torch.device("cuda:0")
+    dims = g["dims"]
     layer_flops = 2.0 * w.T * w.top_k * w.d * 2 * w.f
-    layer_tflops = layer_flops / float(dur["gateup"].mean()) / 1e12
-    x, bf = configs.tokens(w, 0)
-    Wr, bias = configs.router(w, 0)
-    idx, _, _ = oracle.route(x, Wr, bias, w.top_k, x_bf16=bf)
-    cnt = np.bincount(idx.reshape(-1), minlength=w.n_experts)
+    layer_tflops = layer_flops / float(g["dur"].mean()) / 1e12
+    cnt = g["hot_counts"]
     hot_e = int(np.argmax(cnt))
-    xd = L0["x"]
+    xd = g["x0"]
     out = {"layer_gateup_tflops": round(layer_tflops, 1),
            "layer_gateup_frac": round(layer_tflops / MFMA_PEAK_TFLOPS, 4),
            "peak_tflops": MFMA_PEAK_TFLOPS, "dtype": "fp16 x fp16 -> fp32 (v_mfma_f32_16x16x32_f16)"}
     for label, e, n in (("m512", 0, 512), ("hot", hot_e, int(cnt[hot_e]))):
+        n = min(n, xd.shape[0])
         blob = L0["blobs"][e]
         y = torch.empty(n, w.d, dtype=torch.float32, device=dev)
         ws = moe.make_workspace(dims, n, dev)
@@ -373,15 +410,9 @@ def mfma_figures(moe, torch, w, L0, dims, gu_bytes, dur, U):
         assert moe.moe_timing_disarm(h) == reps
         t = float(np.mean([s_.elapsed_time(e_) for s_, e_ in zip(*ev)])) * 1e-3
         flops = 2.0 * n * w.d * 2 * w.f
-        # the library's block shape for one expert: 4 waves x 32 rows x 64 tokens
-        # from 128 rows on (2 waves x 64 rows x 16 tokens at up to 16 rows), else
-        # 16 waves x 32 rows x 64 tokens: 128 or 512 weight rows a block
-        a_cols = 64 if n >= 128 or n <= 16 else 256
-        blocks = (w.f // a_cols) * ((n + 63) // 64)
         tf = flops / t / 1e12
         out[label] = {"expert": e, "M": n, "gateup_us": round(t * 1e6, 2), "tflops": round(tf, 1),
-                      "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "blocks": blocks,
-                      "frac_per_occupied_cu": round(tf / (MFMA_PEAK_TFLOPS * min(blocks, 256) / 256), 4)}
+                      "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}
     return out
 
 

@@ -56,6 +56,14 @@
  *  - All arguments are validated before anything is enqueued; on error the
  *    call returns a negative code and enqueues nothing.  Device-side faults
  *    surface at the caller's next synchronisation.  There is no CPU fallback.
+ *  - Scale range.  Calls on 2 or more tokens (rows) with d and f multiples of
+ *    512, without MOE_BATCH_INVARIANT, run the matrix-core path, which forms
+ *    each weight q * s as one IEEE binary16 number.  That is exact-to-rounding
+ *    for 2^-14 <= |s| <= 2^12 (2^-12 relative); smaller scales lose relative
+ *    precision gradually (binary16 subnormals) and |s| > 8188 overflows
+ *    (8 * |s| > 65504).  Every other path (one token, other shapes,
+ *    MOE_BATCH_INVARIANT, the cached layer) applies s in fp32 and takes any
+ *    finite scale; experts with scales outside the range belong there.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -81,7 +89,10 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 /* moe_layer_forward flags. */
 enum {
   MOE_PRENORM_RMS = 1u,    /* route and run experts on RMSNorm(x), unit gain (x must be f32) */
-  MOE_RESIDUAL = 2u,       /* out = x + MoE(...) (x must be f32) */
+  MOE_RESIDUAL = 2u,       /* out = x + MoE(...) (x must be f32).  The residual is the
+                              layer input itself (h_{l+1} = h_l + MoE(RMSNorm(h_l))): no
+                              separate residual pointer is taken, so a residual other than
+                              x cannot be expressed; callers with one add it themselves */
   MOE_BATCH_INVARIANT = 4u /* each token's result as if it were alone in the call (see below) */
 };
 

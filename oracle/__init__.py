@@ -31,6 +31,18 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def build_sanitized(out_dir: str) -> str:
+    """Build moe_ref.c with sanitize_check.c under AddressSanitizer and
+    UndefinedBehaviorSanitizer (every report fatal) into an executable in
+    out_dir; returns its path."""
+    exe = os.path.join(out_dir, "moe_ref_sanitized")
+    subprocess.check_call(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fopenmp", "-std=c11",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-o", exe, os.path.join(_HERE, "moe_ref.c"),
+                           os.path.join(_HERE, "sanitize_check.c"), "-lm"])
+    return exe
+
+
 def omp_threads(n: int | None = None) -> int:
     """Threads the oracle's OpenMP loops use (the process's libgomp, which
     the oracle library links); with n, set them first."""
