@@ -267,19 +267,11 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
     t1 = time.perf_counter()
     del graph
 
-    # the same K steps again with every launch of the two FFN kernels recording
+    # the same K steps again with every launch of the FFN kernels recording
     # HIP events on the launch stream (recording adds launch overhead, so the
-    # step rate above is measured without it)
-    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
-              [torch.cuda.Event(enable_timing=True) for _ in range(K)]) for k in ("gateup", "down")}
-    arms = {k: moe.moe_timing_arm(k, *ev[k]) for k in ev}
-    torch.cuda.synchronize()
-    for i in range(K):
-        step(i)
-    torch.cuda.synchronize()
-    counts = {k: moe.moe_timing_disarm(arms[k]) for k in arms}
-    assert all(c == K for c in counts.values()), counts
-    dur = {k: np.array([s.elapsed_time(e) for s, e in zip(*ev[k])]) * 1e-3 for k in ev}  # seconds
+    # step rate above is measured without it); a projection may run as a thin
+    # and an M-blocked launch, whose durations add up per step
+    dur = ffn_launch_durations(moe, torch, K, step)
 
     # and once more with an event pair around every step (their spread)
     sev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
@@ -376,6 +368,32 @@ def hbm_ceiling(moe, torch, gib=4):
     return best
 
 
+def ffn_launch_durations(moe, torch, K, step):
+    """Per-step seconds of the gate/up and the down projection over K steps:
+    HIP events around every launch of each kernel (the single-token GEMV, or
+    the grouped GEMM's thin and M-blocked launches, summed per step)."""
+    kinds = {"gateup": ("gateup", "gateup_thin"), "down": ("down", "down_thin")}
+    names = [n for v in kinds.values() for n in v]
+    ev = {n: ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(K)]) for n in names}
+    arms = {n: moe.moe_timing_arm(n, *ev[n]) for n in names}
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    counts = {n: moe.moe_timing_disarm(arms[n]) for n in names}
+    out = {}
+    for kind, parts in kinds.items():
+        tot = np.zeros(K)
+        for n in parts:
+            assert counts[n] in (0, K), counts
+            if counts[n] == K:
+                tot += np.array([s.elapsed_time(e) for s, e in zip(*ev[n])]) * 1e-3
+        assert tot.min() > 0, (kind, counts)
+        out[kind] = tot
+    return out
+
+
 def mfma_figures(moe, torch, w, L0, g):
     """fp16 MFMA throughput of the grouped gate/up GEMM: for the whole layer
     (useful flops 2 * T*k * d * 2f over its measured launches), and for one
@@ -402,7 +420,8 @@ def mfma_figures(moe, torch, w, L0, g):
         reps = 20
         ev = ([torch.cuda.Event(enable_timing=True) for _ in range(reps)],
               [torch.cuda.Event(enable_timing=True) for _ in range(reps)])
-        h = moe.moe_timing_arm("gateup", *ev)
+        kname = "gateup" if n > 16 else "gateup_thin"
+        h = moe.moe_timing_arm(kname, *ev)
         torch.cuda.synchronize()
         for _ in range(reps):
             moe.moe_expert_ffn(dims, blob, xd[:n], None, n, y, ws)

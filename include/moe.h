@@ -331,7 +331,9 @@ enum {
   MOE_KERNEL_DOWN = 6,   /* down projection */
   MOE_KERNEL_COMBINE = 7,
   MOE_KERNEL_READ_PROBE = 8, /* moe_hbm_read_probe */
-  MOE_KERNEL_COUNT = 9
+  MOE_KERNEL_GATEUP_THIN = 9, /* gate/up of experts with at most 16 tokens (batches of 2+) */
+  MOE_KERNEL_DOWN_THIN = 10,  /* down of those experts */
+  MOE_KERNEL_COUNT = 11
 };
 /*
  * moe_timing_arm — the next n launches of `kernel` record start_events[i]

@@ -32,7 +32,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Kernel ids for moe_timing_arm.
 KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
-           "down": 6, "combine": 7, "read_probe": 8}
+           "down": 6, "combine": 7, "read_probe": 8, "gateup_thin": 9, "down_thin": 10}
 
 
 class MoeError(RuntimeError):

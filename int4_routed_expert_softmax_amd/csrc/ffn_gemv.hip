@@ -110,13 +110,14 @@ constexpr int kDnBatch = 4;
 // gate/up kernel does the same in its own prologue, with the same per-token
 // arithmetic), and the down plan when ro.plan is set (table: the expert
 // table, read only then).  With px.mbo set, wave 15 also writes the union's
-// M-block map for the grouped GEMM.
+// M-block maps for the grouped GEMMs.
 __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t* const* table,
                                                       PackArgs px) {
   __shared__ SmallRoute sr;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   small_route(ro, sr, wave, 16);
-  if (px.mbo && wave == 15) mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, lane);
+  if (px.mbo && wave == 15)
+    mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t, lane);
   publish_small_route(ro, sr, table, 1024);
 }
 
@@ -586,10 +587,13 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
   PackArgs px{};
   if (map) {
     // one wave maps a union of at most 64 experts
-    if (!map->mbo || !map->blk_u || map->mblock < 1 || ro.T * ro.k > 64)
+    if (!map->mbo || !map->blk_u || !map->mbo_t || !map->blk_t || map->mblock < 1 ||
+        ro.T * ro.k > 64)
       return hipErrorInvalidValue;
     px.mbo = map->mbo;
     px.blk_u = map->blk_u;
+    px.mbo_t = map->mbo_t;
+    px.blk_t = map->blk_t;
     px.mblock = map->mblock;
   }
   return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table, px);

@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "moe.h"
 #include "moe_internal.h"
 #include "pack.h"
 
@@ -84,35 +85,56 @@ __device__ __forceinline__ int find_bucket(const int32_t* p, int n, int j) {
 // mblock), u = 0..U.
 __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   if (p.mbo && blockIdx.x == gridDim.x - 1) {
-    __shared__ int s_tot[4];
+    // thread t maps experts 4t .. 4t + 3: thin ones (at most kThinTokens
+    // tokens) take one thin block each, the others ceil(count / mblock)
+    // M-blocks; two block-wide exclusive scans place them
+    __shared__ int s_tot[2][4];
     const int U = *p.n_uniq, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int c[4], sum = 0;
+    int c[4], th[4], sum = 0, sum_t = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
-      c[i] = u < U ? (p.offsets[u + 1] - p.offsets[u] + p.mblock - 1) / p.mblock : 0;
+      const int n = u < U ? p.offsets[u + 1] - p.offsets[u] : 0;
+      th[i] = u < U && n <= kThinTokens;
+      c[i] = u < U && !th[i] ? (n + p.mblock - 1) / p.mblock : 0;
       sum += c[i];
+      sum_t += th[i];
     }
-    int incl = sum;
+    int incl = sum, incl_t = sum_t;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int nb = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += nb;
+      const int nb = __shfl_up(incl, o, 64), nt = __shfl_up(incl_t, o, 64);
+      if (lane >= o) {
+        incl += nb;
+        incl_t += nt;
+      }
     }
-    if (lane == 63) s_tot[wave] = incl;
+    if (lane == 63) {
+      s_tot[0][wave] = incl;
+      s_tot[1][wave] = incl_t;
+    }
     __syncthreads();
-    int run = incl - sum;
-    for (int w = 0; w < wave; ++w) run += s_tot[w];
+    int run = incl - sum, run_t = incl_t - sum_t;
+    for (int w = 0; w < wave; ++w) {
+      run += s_tot[0][w];
+      run_t += s_tot[1][w];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
       if (u < U) {
         p.mbo[u] = run;
+        p.mbo_t[u] = run_t;
         for (int j = 0; j < c[i]; ++j) p.blk_u[run + j] = u;
+        if (th[i]) p.blk_t[run_t] = u;
       }
       run += c[i];
+      run_t += th[i];
     }
-    if (t == 0) p.mbo[U] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+    if (t == 0) {
+      p.mbo[U] = s_tot[0][0] + s_tot[0][1] + s_tot[0][2] + s_tot[0][3];
+      p.mbo_t[U] = s_tot[1][0] + s_tot[1][1] + s_tot[1][2] + s_tot[1][3];
+    }
     return;
   }
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -131,6 +153,10 @@ struct GemmArgs {
   const _Float16* a;     // packed A rows [rows][K]
   const float* unit;     // [rows]
   float* out;            // gate/up: silu(g) * u [slots][f]; down: y [slots][d]
+  const float* corr;     // thin: [rows][K / 64] group corrections of A
+  const int32_t* mbo_t;  // thin union: number of thin experts at [n_uniq]
+  const int32_t* blk_t;  // thin union: the j-th thin expert
+  int thick_blocks;      // mixed launch: M-blocked blocks before the thin ones
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -219,8 +245,11 @@ constexpr int copies_ahead() {
 // to MB tokens of one expert.  Stage st is copied while stage st - 2 is computed;
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
+//
+// The body takes the block's LDS and its index along the M-blocks (jy), so the
+// mixed launch below can run it beside thin blocks.
 template <int MODE, int GW, int R, int MB, int NTW>
-__global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
   using Shape = RingShape<GW, R, MB, NTW>;
   constexpr int kNt = Shape::kNt, kWaveRows = Shape::kWaveRows, kBWave = Shape::kBWave;
   constexpr int kScaleWave = Shape::kScaleWave;
@@ -229,7 +258,6 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   constexpr int kRing = Shape::kRing;
   constexpr int kMBlock = Shape::kMBlock, kMT = Shape::kMT, kStageB = Shape::kStageB;
   constexpr int kStage = Shape::kStage, kScaleOff = Shape::kScaleOff;
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[Shape::kLdsBytes];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -245,11 +273,11 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   if (L.single) {
     off = 0;
     cnt = L.single_n;
-    tok0 = blockIdx.y * kMBlock;
+    tok0 = jy * kMBlock;
     if (tok0 >= cnt) return;
     blob = L.single;
   } else {
-    const int j = blockIdx.y;
+    const int j = jy;
     if (j >= g.mbo[*L.n_uniq]) return;
     const int u = g.blk_u[j];
     off = L.offsets[u];
@@ -444,24 +472,301 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   }
 }
 
+template <int MODE, int GW, int R, int MB, int NTW>
+__global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[RingShape<GW, R, MB, NTW>::kLdsBytes];
+  gemm_body<MODE, GW, R, MB, NTW>(g, s_lds, blockIdx.y);
+}
+
+// ---------------------------------------------------------------- thin GEMM
+// Experts of at most kThinTokens tokens (most of a prefill chunk's union and
+// every expert of a small batch): one block = one such expert (a single
+// 16-row M-tile) x GW waves of 32 weight rows.  The weights' per-64-column
+// scales multiply the fp32 partial sum of each group instead of every weight:
+// the codes enter the MFMA as the exact fp16 subnormals (q + 8) * 2^-24 (a
+// shift and one AND/XOR per two codes), each group's partial starts from the
+// group's correction -8 * 2^-24 * sum(x') (written by k_pack), so it ends as
+// 2^-24 * sum(x' q), and partial times scale is added to the accumulator.  With
+// one M-tile per block that is about half the VALU work of scaling every
+// weight before the MFMA, and the weights stay exact (only x' is rounded).
+// A stage (128 columns: two scale groups) holds, for every wave, its 32 rows
+// of codes, and for the block the M-tile's activation rows (copied by waves
+// 0..3) and group corrections (wave 0); the ring has R stages, R - 1 in
+// flight.  Each wave copies its rows' scales 16 bytes (8 groups, 4 stages) at
+// a time into two buffers of its own.
+constexpr int kThinWaveRows = 32;
+
+template <int GW, int R>
+struct ThinShape {
+  static constexpr int kBWave = kThinWaveRows * (kSC / 2);  // 2 KB: 32 rows x 64 B
+  static constexpr int kStageB = GW * kBWave;
+  static constexpr int kStageA = kThinTokens * kSC * 2;    // 16 rows x 256 B
+  static constexpr int kStageC = 32 * 4;                   // [2 groups][16 tokens] f32
+  static constexpr int kStage = kStageB + kStageA + kStageC;
+  static constexpr int kScalePiece = kThinWaveRows * 16;   // [32 rows][8 groups] fp16
+  static constexpr int kScaleOff = R * kStage;
+  static constexpr int kLdsBytes = kScaleOff + GW * 2 * kScalePiece;
+  static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
+  // a scale piece is copied R - 1 stages before its first use, which must
+  // come after the last use of the piece two back
+  static_assert(R >= 3 && R <= 5, "ring depth");
+  static_assert(GW >= 4, "waves 0..3 copy the 16 activation rows");
+  static_assert(kThinTokens == 16, "one M-tile");
+};
+
+// 8 codes (column j in bits 4j..4j+3) -> the fp16 subnormals (q + 8) * 2^-24
+// in slot order (col 0, 4, 1, 5, 2, 6, 3, 7): q + 8 is the code with its sign
+// bit flipped.
+__device__ __forceinline__ f16x8 raw8(uint32_t w) {
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h = ((w >> (4 * j)) & 0x000F000Fu) ^ 0x00080008u;
+    const f16x2 q = __builtin_bit_cast(f16x2, h);
+    r[2 * j] = q[0];
+    r[2 * j + 1] = q[1];
+  }
+  return r;
+}
+
+// 4-byte global -> LDS copy: lane l's word lands at lds + 4 l.
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
+}
+
+template <int MODE, int GW, int R>
+__device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
+  using Shape = ThinShape<GW, R>;
+  constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB;
+  constexpr int kStageA = Shape::kStageA, kStage = Shape::kStage, kScalePiece = Shape::kScalePiece;
+  constexpr int kHalf = kThinWaveRows / 2;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int d = g.d, f = g.f;
+  const int K = MODE == kGateUp ? d : f;
+  const int pr = g.L.per_row;
+  const int ng = srow(K, pr);  // scales per weight row
+  const int ngc = K / kGroup;  // correction groups per activation row
+
+  // ---- the block's expert (at most kThinTokens tokens)
+  const ExpertList& L = g.L;
+  int off, cnt;
+  const uint8_t* blob;
+  if (L.single) {
+    if (jy > 0) return;
+    off = 0;
+    cnt = L.single_n;
+    blob = L.single;
+  } else {
+    if (jy >= g.mbo_t[*L.n_uniq]) return;
+    const int u = g.blk_t[jy];
+    off = L.offsets[u];
+    cnt = L.offsets[u + 1] - off;
+    blob = L.table[L.uniq[u]];
+  }
+  // packed row of the block's token i (past the last token: the last one)
+  auto row_of = [&](int i) -> uint32_t {
+    const int ti = min(i, cnt - 1);
+    if (L.single) return (uint32_t)ti;
+    const int slot = L.list[off + ti];
+    return (uint32_t)(MODE == kGateUp ? slot / L.kdiv : slot);
+  };
+
+  // ---- this wave's 32 weight rows (gate/up: 16 gate rows and the same 16 up
+  // rows); waves past the last row copy the last wave's rows, compute nothing
+  const int nwaves = MODE == kGateUp ? f / kHalf : d / kThinWaveRows;
+  const int wv = blockIdx.x * GW + wave;
+  const bool active = wv < nwaves;
+  const int wc = min(wv, nwaves - 1);
+  const size_t fd = (size_t)f * d;
+  const _Float16* sbase = reinterpret_cast<const _Float16*>(blob + 3 * (fd / 2));
+  const size_t gate_sc = (size_t)f * srow(d, pr);
+  const uint8_t *c0, *c1;
+  const _Float16 *s0, *s1;
+  if (MODE == kGateUp) {
+    c0 = blob + (size_t)(kHalf * wc) * (K / 2);
+    c1 = c0 + fd / 2;
+    s0 = sbase + (size_t)(kHalf * wc) * ng;
+    s1 = s0 + gate_sc;
+  } else {
+    c0 = blob + fd + (size_t)(kThinWaveRows * wc) * (K / 2);
+    c1 = c0 + (size_t)kHalf * (K / 2);
+    s0 = sbase + 2 * gate_sc + (size_t)(kThinWaveRows * wc) * ng;
+    s1 = s0 + (size_t)kHalf * ng;
+  }
+  const int n = lane & 15, kg = lane >> 4;
+
+  // ---- per-lane copy sources (codes and activations as in k_gemm)
+  const uint32_t b_piece = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1));
+  const uint32_t b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + b_piece * 16u;
+  const bool a_copy = wave < 4 && 4 * wave < cnt;  // wave-uniform
+  const int a_row = 4 * (wave & 3) + (lane >> 4);
+  const uint32_t a_off = row_of(a_row) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
+  // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1)
+  const float* c_lane = g.corr + (size_t)row_of(lane & 15) * ngc + ((lane >> 4) & 1);
+  // scales: lane l < 32 -> row l of the wave, 16 bytes (8 groups) every 4 stages
+  const int sr_lane = lane % kThinWaveRows;
+  const _Float16* s_lane = (sr_lane < kHalf ? s0 : s1) + (size_t)(sr_lane % kHalf) * ng;
+  uint8_t* s_scales = s_lds + Shape::kScaleOff + wave * (2 * kScalePiece);
+  if (pr && lane < kThinWaveRows) {
+    // one scale per row: put in every group of both buffers, once (this
+    // wave's own LDS; the first stage's wait covers the writes)
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(s_lane);
+    const uint32_t hh = h | (h << 16);
+    const uint4 v = make_uint4(hh, hh, hh, hh);
+    *reinterpret_cast<uint4*>(s_scales + lane * 16) = v;
+    *reinterpret_cast<uint4*>(s_scales + kScalePiece + lane * 16) = v;
+  }
+
+  const int nst = K / kSC;
+  auto issue = [&](int st) {
+    uint8_t* base = s_lds + (st % R) * kStage;
+    const uint32_t so = (uint32_t)st * (kSC / 2);
+    dma16(c0 + b_off + so, base + wave * kBWave);
+    dma16(c1 + b_off + so, base + wave * kBWave + 1024);
+    if (a_copy) dma16(g.a + a_off + st * kSC, base + kStageB + 4 * wave * (kSC * 2));
+    // the correction copy fills 32 x 4 bytes: lanes 32..63 stay out of it
+    if (wave == 0 && lane < 32) dma4(c_lane + 2 * st, base + kStageB + kStageA);
+    if ((st & 3) == 0 && !pr && lane < kThinWaveRows)
+      dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * kScalePiece);
+  };
+
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // group 2 st + gg of a landed stage: lane (n, kg) takes, for MFMA step j,
+  // columns 16 kg + 8 j .. + 8 of the group
+  auto group = [&](int st, int gg) {
+    const uint8_t* base = s_lds + (st % R) * kStage;
+    const int gi = 2 * st + gg;
+    const uint8_t* sc = s_scales + ((gi >> 3) & 1) * kScalePiece + (gi & 7) * 2;
+    const uint8_t* ar = base + kStageB + n * (kSC * 2);
+    const int p0 = 8 * gg + 2 * kg;
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(ar + (p0 ^ n) * 16);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(ar + ((p0 + 1) ^ n) * 16);
+    const f32x4 c4 =
+        *reinterpret_cast<const f32x4*>(base + kStageB + kStageA + (16 * gg + 4 * kg) * 4);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = 16 * nt + n;
+      const int slot = (2 * gg + (kg >> 1)) ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
+      const uint2 w = *reinterpret_cast<const uint2*>(base + wave * kBWave + r * (kSC / 2) +
+                                                      slot * 16 + 8 * (kg & 1));
+      f32x4 pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, raw8(w.x), c4, 0, 0, 0);
+      pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, raw8(w.y), pg, 0, 0, 0);
+      const float sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sv, pg[i], acc[nt][i]);
+    }
+  };
+
+  // copies a wave issues per stage besides its scale pieces: 2 of codes, 1 of
+  // activations (waves 0..3 with tokens), 1 of corrections (wave 0)
+  const int per_stage = 2 + (a_copy ? 1 : 0) + (wave == 0 ? 1 : 0);
+#pragma unroll
+  for (int i = 0; i < R - 1; ++i)
+    if (i < nst) issue(i);
+  auto step = [&](int st, auto phase) {
+    constexpr int PH = decltype(phase)::value;
+    if (st + R - 2 < nst) {
+      // stage st has landed once at most the copies of stages st + 1 ..
+      // st + R - 2 are in flight
+      if (pr) {
+        if (per_stage == 2) wait_vm_lgkm0<copies_ahead<R, PH, 2, 0, 0>()>();
+        else if (per_stage == 3) wait_vm_lgkm0<copies_ahead<R, PH, 3, 0, 0>()>();
+        else wait_vm_lgkm0<copies_ahead<R, PH, 4, 0, 0>()>();
+      } else {
+        if (per_stage == 2) wait_vm_lgkm0<copies_ahead<R, PH, 2, 0, 1>()>();
+        else if (per_stage == 3) wait_vm_lgkm0<copies_ahead<R, PH, 3, 0, 1>()>();
+        else wait_vm_lgkm0<copies_ahead<R, PH, 4, 0, 1>()>();
+      }
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // every wave is past stage st - 1: its ring slot takes stage st + R - 1
+    if (st + R - 1 < nst) issue(st + R - 1);
+    if (active) {
+      group(st, 0);
+      group(st, 1);
+    }
+  };
+  for (int st0 = 0; st0 < nst; st0 += 4) {  // nst is a multiple of 4
+    step(st0, std::integral_constant<int, 0>());
+    step(st0 + 1, std::integral_constant<int, 1>());
+    step(st0 + 2, std::integral_constant<int, 2>());
+    step(st0 + 3, std::integral_constant<int, 3>());
+  }
+  if (!active) return;
+
+  // epilogue: lane (n, kg) holds tokens 4 kg + i for weight rows 16 nt + n;
+  // the partials were in units of 2^-24
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ti = 4 * kg + i;
+    if (ti >= cnt) continue;
+    const int slot = L.single ? ti : L.list[off + ti];
+    if (MODE == kGateUp) {
+      const int xr = L.single ? ti : slot / L.kdiv;
+      const float us = g.unit[xr] * 0x1p24f;
+      const float gv = acc[0][i] * us, uv = acc[1][i] * us;
+      g.out[(size_t)slot * f + kHalf * wv + n] = silu(gv) * uv;
+    } else {
+      const float us = g.unit[slot] * 0x1p24f;
+      float* orow = g.out + (size_t)slot * d + kThinWaveRows * wv;
+      orow[n] = acc[0][i] * us;
+      orow[16 + n] = acc[1][i] * us;
+    }
+  }
+}
+
+template <int MODE, int GW, int R>
+__global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R>::kLdsBytes];
+  thin_body<MODE, GW, R>(g, s_lds, blockIdx.y);
+}
+
+// One launch for a batch's whole union: blocks with y < g.thick_blocks run
+// the M-blocked GEMM (16 waves, 64-token M-blocks: the hot experts, whose
+// matrix-core and dequantisation work is the longest, dispatched first), the
+// others the thin GEMM (16 waves) over the experts of at most kThinTokens
+// tokens, so the streaming of the many small experts overlaps the compute of
+// the few large ones.  Both cover 512 weight rows a block.
+constexpr int kMixedThinRing = 3;
+template <int MODE>
+__global__ __launch_bounds__(1024) void k_gemm_mixed(GemmArgs g) {
+  constexpr int kA = RingShape<16, 3, 64, 2>::kLdsBytes;
+  constexpr int kB = ThinShape<16, kMixedThinRing>::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[kA > kB ? kA : kB];
+  if ((int)blockIdx.y < g.thick_blocks) gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, blockIdx.y);
+  else thin_body<MODE, 16, kMixedThinRing>(g, s_lds, blockIdx.y - g.thick_blocks);
+}
+
 // ---------------------------------------------------------------- launchers
 
-// Block shape of a call: batches of up to 16 rows take 4-wave blocks of 128
-// rows with 16-token M-blocks; one expert over 128 rows or more (the compute-bound case)
-// takes 4-wave blocks of 128 rows with 64-token M-blocks, four times as many
-// blocks as the 16-wave shape; everything else 16-wave blocks (32 rows a
-// wave) with 64-token M-blocks.
+// Block shape of the M-blocked GEMM (experts of more than kThinTokens tokens):
+// one expert over 128 rows or more (the compute-bound case) takes 4-wave
+// blocks of 128 rows with 64-token M-blocks, four times as many blocks as the
+// 16-wave shape; everything else 16-wave blocks (32 rows a wave) with 64-token
+// M-blocks.
 struct GemmShape {
   int gw, mblock, ntw;
 };
 static GemmShape gemm_shape(int rows, bool single) {
-  if (rows <= 16) return {4, 16, 2};
   if (single && rows >= 128) return {4, 64, 2};
   return {16, 64, 2};
 }
-int mfma_mblock(int rows) { return gemm_shape(rows, false).mblock; }
+int mfma_mblock(int) { return 64; }
 
 bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
+
+// Thin GEMM on its own (batches of at most kThinTokens rows, one expert of
+// that many): 4 waves of 32 rows, a ring of 4 stages, several blocks a CU, so
+// a dozen experts still give hundreds of blocks.
+constexpr int kThinGW = 4;
+constexpr int kThinRing = 4;
 
 PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   const ExpertList& L = m.L;
@@ -473,36 +778,60 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   px.gather = m.x_gather;
   px.dst = m.xh;
   px.unit = m.xunit;
+  px.corr = m.xcorr;
   if (!L.single) {
     px.offsets = L.offsets;
     px.n_uniq = L.n_uniq;
     px.mbo = m.mbo;
     px.blk_u = m.blk_u;
-    px.mblock = gemm_shape(m.x_rows, false).mblock;
+    px.mbo_t = m.mbo_t;
+    px.blk_t = m.blk_t;
+    px.mblock = mfma_mblock(m.x_rows);
   }
   return px;
+}
+
+// A projection: batches of at most kThinTokens rows (every expert thin) and a
+// single expert of that many run the thin GEMM alone; a single larger expert
+// the M-blocked GEMM; larger batches the mixed launch (M-blocked blocks for
+// the experts past kThinTokens tokens, then thin blocks for the others).
+template <int MODE>
+static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
+  const ExpertList& L = m.L;
+  const int rows = L.single ? L.single_n : m.x_rows;
+  const int kid = MODE == kGateUp ? MOE_KERNEL_GATEUP : MOE_KERNEL_DOWN;
+  const int kid_thin = MODE == kGateUp ? MOE_KERNEL_GATEUP_THIN : MOE_KERNEL_DOWN_THIN;
+  const int N = MODE == kGateUp ? m.f : m.d;  // weight rows (gate/up: gate rows; up alike)
+  const int wrows = MODE == kGateUp ? 16 : 32;  // of N a wave covers
+  const int nw = N / wrows;
+  if (rows <= kThinTokens) {
+    const dim3 grid((unsigned)((nw + kThinGW - 1) / kThinGW), L.single ? 1u : (unsigned)m.thin_bound);
+    return launch(kid_thin, k_gemm_thin<MODE, kThinGW, kThinRing>, grid, dim3(64 * kThinGW), s, ga);
+  }
+  if (L.single) {
+    const GemmShape sh = gemm_shape(rows, true);
+    const unsigned mb = (unsigned)((L.single_n + sh.mblock - 1) / sh.mblock);
+    const unsigned gx = (unsigned)((nw + sh.gw - 1) / sh.gw);
+    if (sh.gw == 4) return launch(kid, k_gemm<MODE, 4, 3, 64, 2>, dim3(gx, mb), dim3(256), s, ga);
+    return launch(kid, k_gemm<MODE, 16, 3, 64, 2>, dim3(gx, mb), dim3(1024), s, ga);
+  }
+  ga.thick_blocks = m.mb_bound;
+  const dim3 grid((unsigned)((nw + 15) / 16), (unsigned)(m.mb_bound + m.thin_bound));
+  return launch(kid, k_gemm_mixed<MODE>, grid, dim3(1024), s, ga);
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   const ExpertList& L = m.L;
   hipError_t e;
   if (!m.x_packed) {
-    // x rows -> fp16 (and the union's M-block map)
+    // x rows -> fp16 with their group corrections (and the union's M-block maps)
     const PackArgs px = mfma_x_pack_args(m);
     const unsigned gx = (unsigned)((m.x_rows + 3) / 4) + (L.single ? 0u : 1u);
-    e = launch(4, k_pack, dim3(gx), dim3(256), s, px);
+    e = launch(MOE_KERNEL_DIGITIZE, k_pack, dim3(gx), dim3(256), s, px);
     if (e != hipSuccess) return e;
   }
-
-  const GemmShape sh = gemm_shape(m.x_rows, L.single != nullptr);
-  const int gw = sh.gw, mblock = sh.mblock, ntw = sh.ntw;
-  const unsigned mb = L.single ? (unsigned)((L.single_n + mblock - 1) / mblock)
-                               : (unsigned)m.mb_bound;
-  GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32};
-  const unsigned wg = (unsigned)((m.f / (8 * ntw) + gw - 1) / gw);
-  if (gw == 4 && mblock == 16) e = launch(5, k_gemm<kGateUp, 4, 3, 16, 2>, dim3(wg, mb), dim3(256), s, ga);
-  else if (gw == 4) e = launch(5, k_gemm<kGateUp, 4, 3, 64, 2>, dim3(wg, mb), dim3(256), s, ga);
-  else e = launch(5, k_gemm<kGateUp, 16, 3, 64, 2>, dim3(wg, mb), dim3(1024), s, ga);
+  GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32, m.xcorr, m.mbo_t, m.blk_t, 0};
+  e = project<kGateUp>(m, ga, s);
   if (e != hipSuccess) return e;
 
   PackArgs pa{};
@@ -511,14 +840,12 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   pa.rows = m.slots;
   pa.dst = m.ah;
   pa.unit = m.aunit;
-  e = launch(4, k_pack, dim3((unsigned)((m.slots + 3) / 4)), dim3(256), s, pa);
+  pa.corr = m.acorr;
+  e = launch(MOE_KERNEL_DIGITIZE, k_pack, dim3((unsigned)((m.slots + 3) / 4)), dim3(256), s, pa);
   if (e != hipSuccess) return e;
 
-  GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y};
-  const unsigned wd = (unsigned)((m.d / (16 * ntw) + gw - 1) / gw);
-  if (gw == 4 && mblock == 16) return launch(6, k_gemm<kDown, 4, 3, 16, 2>, dim3(wd, mb), dim3(256), s, gd);
-  if (gw == 4) return launch(6, k_gemm<kDown, 4, 3, 64, 2>, dim3(wd, mb), dim3(256), s, gd);
-  return launch(6, k_gemm<kDown, 16, 3, 64, 2>, dim3(wd, mb), dim3(1024), s, gd);
+  GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y, m.acorr, m.mbo_t, m.blk_t, 0};
+  return project<kDown>(m, gd, s);
 }
 
 }  // namespace moe

@@ -48,11 +48,15 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.y = take(Tk * d * sizeof(float));
   L.xh = take((size_t)T * d * sizeof(uint16_t));
   L.xunit = take((size_t)T * sizeof(float));
+  L.xcorr = take((size_t)T * (d / kGroup) * sizeof(float));
   L.a32 = take(Tk * f * sizeof(float));
   L.ah = take(Tk * f * sizeof(uint16_t));
   L.aunit = take(Tk * sizeof(float));
+  L.acorr = take(Tk * (f / kGroup) * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
   L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
+  L.mbot = take((cap + 1) * sizeof(int32_t));
+  L.blkt = take(cap * sizeof(int32_t));
   L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
@@ -126,11 +130,15 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.f = f;
   m.xh = at<_Float16>(ws, L.xh);
   m.xunit = at<float>(ws, L.xunit);
+  m.xcorr = at<float>(ws, L.xcorr);
   m.a32 = at<float>(ws, L.a32);
   m.ah = at<_Float16>(ws, L.ah);
   m.aunit = at<float>(ws, L.aunit);
+  m.acorr = at<float>(ws, L.acorr);
   m.mbo = at<int32_t>(ws, L.mbo);
   m.blk_u = at<int32_t>(ws, L.blku);
+  m.mbo_t = at<int32_t>(ws, L.mbot);
+  m.blk_t = at<int32_t>(ws, L.blkt);
   return m;
 }
 
@@ -397,7 +405,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.x_bf16 = xr_bf16;
     m.x_rows = T;
     m.slots = T * k;
-    m.mb_bound = maxU + (T * k + mfma_mblock(T) - 1) / mfma_mblock(T);
+    // experts past kThinTokens tokens: fewer than T k / (kThinTokens + 1) of
+    // them, each with ceil(count / 64) < count / 64 + 1 M-blocks
+    const int nthick = T * k / (kThinTokens + 1) < maxU ? T * k / (kThinTokens + 1) : maxU;
+    m.mb_bound = (T * k + mfma_mblock(T) - 1) / mfma_mblock(T) + nthick;
+    m.thin_bound = maxU;
     m.y = y;
     m.x_packed = x_packed;
     MOE_TRY(launch_ffn_mfma(m, s));

@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, a32, ah, aunit, mbo, blku, plan, total;
+  size_t xh, xunit, xcorr, a32, ah, aunit, acorr, mbo, blku, mbot, blkt, plan, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -77,7 +77,7 @@ struct TimingSlot {
   hipEvent_t const* stop = nullptr;
   int n = 0, next = 0;
 };
-extern TimingSlot g_timing[9];
+extern TimingSlot g_timing[11];
 
 template <typename K, typename... Args>
 hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
@@ -91,18 +91,29 @@ hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s,
   return hipGetLastError();
 }
 
+// Experts with at most this many tokens in a batch run on the thin grouped
+// GEMM (one 16-row M-tile per block); the others on the M-blocked one.
+constexpr int kThinTokens = 16;
+
 // Rows of activations to pack into the grouped GEMM's fp16 A operand (one
-// power of two per row), and optionally the union's M-block map.
+// power of two per row), their per-64-column group sums for the thin GEMM,
+// and optionally the union's M-block maps.
 struct PackArgs {
   const void* src;
   int src_bf16, K, rows;
   const int32_t* gather;  // source row of row r (nullptr: r)
   _Float16* dst;          // [rows][K]
   float* unit;            // [rows]
+  float* corr;            // [rows][K / 64]: -8 * 2^-24 * (sum of the group's packed values)
   const int32_t* offsets;
   const int32_t* n_uniq;
+  // with mbo set: experts of at most kThinTokens tokens get one thin block
+  // each (mbo_t[u] = thin experts before u, blk_t[j] = the j-th), the others
+  // ceil(count / mblock) M-blocks (mbo[u] prefix, blk_u[j] = expert of M-block j)
   int32_t* mbo;
   int32_t* blk_u;
+  int32_t* mbo_t;
+  int32_t* blk_t;
   int mblock;
 };
 
@@ -206,16 +217,21 @@ struct MfmaArgs {
   int x_rows;                // rows to pack (T tokens, or n rows of a single expert)
   const int32_t* x_gather;   // source row of packed row r (nullptr: r)
   int slots;                 // rows of a32 / ah / y
-  int mb_bound;              // union: upper bound on the number of M-blocks
+  int mb_bound;              // union: upper bound on the M-blocked GEMM's M-blocks
+  int thin_bound;            // union: upper bound on the number of thin experts
   _Float16* xh;
   float* xunit;
+  float* xcorr;              // [x_rows][d / 64]
   float* a32;
   _Float16* ah;
   float* aunit;
+  float* acorr;              // [slots][f / 64]
   int32_t* mbo;              // [n_experts + 1]
   int32_t* blk_u;            // [mb_bound]
+  int32_t* mbo_t;            // [n_experts + 1]
+  int32_t* blk_t;            // [n_experts]
   float* y;
-  int x_packed;              // xh, xunit and the M-block map are already written
+  int x_packed;              // xh, xunit, xcorr and the M-block maps are already written
 };
 // The x pack (and M-block map) launch_ffn_mfma would run for m.
 PackArgs mfma_x_pack_args(const MfmaArgs& m);

@@ -39,6 +39,25 @@ __device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float
   }
 }
 
+// The thin grouped GEMM feeds the codes to the matrix cores as the fp16
+// subnormals (q + 8) * 2^-24 and starts each 64-column group's partial sum at
+// -8 * 2^-24 * (sum of the group's packed values), which makes the partial
+// 2^-24 * sum of q * x'.  corr_of8 sums a lane's 8 packed values (as stored,
+// in fp64), the 8 lanes of a 64-column group add theirs, and the group's
+// first lane writes the correction (rounded once to fp32).
+__device__ __forceinline__ double corr_of8(const float (&v)[8], float up) {
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += (double)(float)(_Float16)(v[j] * up);
+  return s;
+}
+__device__ __forceinline__ void store_corr(const PackArgs& p, int r, int c, double s, int lane) {
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = (float)(-8.0 * 0x1p-24 * s);
+}
+
 // Rows of up to kPackRegCols columns are read once into registers (every
 // load of the row in flight together), longer ones twice (max, then convert).
 constexpr int kPackRegChunks = 12;                   // 8-column chunks per lane
@@ -80,6 +99,8 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
     for (int i = 0; i < kPackRegChunks; ++i) {
       const int c = (i * 64 + lane) * 8;
       if (c < p.K) store8(drow, c, v[i], up);
+      // K is a multiple of 512: a chunk's 64 lanes are all in or all out
+      if (p.corr && i * 512 < p.K) store_corr(p, r, c, corr_of8(v[i], up), lane);
     }
     if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
     return;
@@ -107,28 +128,45 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) hv[j] = h[j];
     *reinterpret_cast<f16x8_t*>(drow + c) = hv;
+    if (p.corr) store_corr(p, r, c, corr_of8(v, up), lane);
   }
   if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
 }
 
-// M-block map of a union of at most 64 experts (offs[0..U]), by one whole
-// wave: mbo[u] = sum over u' < u of ceil(count(u') / mblock), mbo[U] the
-// total, and blk_u[j] = the expert of M-block j.
-__device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int mblock,
-                                                int32_t* mbo, int32_t* blk_u, int lane) {
-  const int c = lane < U ? (offs[lane + 1] - offs[lane] + mblock - 1) / mblock : 0;
+// M-block maps of a union of at most 64 experts (offs[0..U]), by one whole
+// wave: experts of at most kThinTokens tokens are listed in blk_t (mbo_t[u] =
+// thin experts before u, mbo_t[U] their number); each other expert gets
+// ceil(count / mblock) M-blocks (mbo[u] = M-blocks before u, mbo[U] the total,
+// blk_u[j] = the expert of M-block j).
+__device__ __forceinline__ int wave_excl_scan(int c, int lane, int& total) {
   int incl = c;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int nb = __shfl_up(incl, o, 64);
     if (lane >= o) incl += nb;
   }
-  const int run = incl - c;
+  total = __shfl(incl, 63, 64);
+  return incl - c;
+}
+__device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int mblock,
+                                                int32_t* mbo, int32_t* blk_u, int32_t* mbo_t,
+                                                int32_t* blk_t, int lane) {
+  const int n = lane < U ? offs[lane + 1] - offs[lane] : 0;
+  const bool thin = lane < U && n <= kThinTokens;
+  const int c = lane < U && !thin ? (n + mblock - 1) / mblock : 0;
+  int tot, tot_t;
+  const int run = wave_excl_scan(c, lane, tot);
+  const int run_t = wave_excl_scan(thin ? 1 : 0, lane, tot_t);
   if (lane < U) {
     mbo[lane] = run;
+    mbo_t[lane] = run_t;
     for (int j = 0; j < c; ++j) blk_u[run + j] = lane;
+    if (thin) blk_t[run_t] = lane;
   }
-  if (lane == 63) mbo[U] = incl;
+  if (lane == 0) {
+    mbo[U] = tot;
+    mbo_t[U] = tot_t;
+  }
 }
 
 }  // namespace moe

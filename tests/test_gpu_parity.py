@@ -350,3 +350,33 @@ def test_union_of_64_distinct_picks(d, f, E, k, T):
         check_layer_routing(L.dims, L.last_ws, T, ref, f"{w.name} flags={flags}")
         rel = assert_close(out.cpu().numpy(), ref["out"], case=f"{w.name} flags={flags}")
         say(f"parity: {w.name} flags={flags} U=64 rel err {rel:.2e}")
+
+
+@pytest.mark.parametrize("counts,x_kind", [
+    ((16, 17, 1, 64, 65), "normal"),  # both sides of the thin limit and of a 64-token M-block
+    ((3, 16, 2, 40), "bf16"),
+])
+def test_thin_and_mblocked_experts_side_by_side(counts, x_kind):
+    """Token counts chosen per expert (top-1, every token of expert e sends
+    its logit to e alone): experts of at most 16 tokens run on the thin
+    grouped GEMM, larger ones on the M-blocked GEMM, in the same call."""
+    E, d, f = len(counts), 512, 1024
+    T = sum(counts)
+    w = small(f"counts_{'_'.join(map(str, counts))}", d, f, E, 1, T, zipf=False, x_kind=x_kind)
+    Wr = np.zeros((E, d), np.float32)
+    Wr[np.arange(E), np.arange(E)] = 1.0
+    L = DeviceLayer(w, Wr=Wr, bias=None)
+    x = configs.tokens(w)[0]
+    xf = configs.bf16_bits_to_f32(x) if x_kind == "bf16" else x.copy()
+    owner = np.repeat(np.arange(E), counts)
+    xf[:, :E] = 0.0
+    xf[np.arange(T), owner] = 10.0
+    xin = synth.to_bf16_bits(xf) if x_kind == "bf16" else xf
+    say(f"parity: {w.name} T={T}")
+    ref = oracle.layer_forward(xin, Wr, None, L.oracle_table(), d, f, 1, x_bf16=x_kind == "bf16")
+    assert np.array_equal(np.bincount(ref["idx"].reshape(-1), minlength=E), counts)
+    out, st = L.forward(L.x_device(xin, x_kind == "bf16"))
+    assert np.array_equal(st.cpu().numpy()[1:], counts)
+    check_layer_routing(L.dims, L.last_ws, T, ref, f"{w.name} layer call")
+    rel = assert_close(out.cpu().numpy(), ref["out"], case=f"{w.name} flags=0")
+    say(f"parity: {w.name} rel err {rel:.2e}")
