@@ -42,20 +42,22 @@ __device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float
 // The thin grouped GEMM feeds the codes to the matrix cores as the fp16
 // subnormals (q + 8) * 2^-24 and starts each 64-column group's partial sum at
 // -8 * 2^-24 * (sum of the group's packed values), which makes the partial
-// 2^-24 * sum of q * x'.  corr_of8 sums a lane's 8 packed values (as stored,
-// in fp64), the 8 lanes of a 64-column group add theirs, and the group's
-// first lane writes the correction (rounded once to fp32).
-__device__ __forceinline__ double corr_of8(const float (&v)[8], float up) {
-  double s = 0.0;
+// 2^-24 * sum of q * x'.  corr_of8 sums a lane's 8 packed values (as stored),
+// the 8 lanes of a 64-column group add theirs with a DPP butterfly (quad
+// swaps, then the half-row mirror pairs the two quads), and the group's first
+// lane writes the correction.  fp32 in a fixed order: its rounding (about
+// 2^-24 of 8 |sum x'|) is some 2^-18 of a group's partial.
+__device__ __forceinline__ float corr_of8(const float (&v)[8], float up) {
+  float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s += (double)(float)(_Float16)(v[j] * up);
+  for (int j = 0; j < 8; ++j) s += (float)(_Float16)(v[j] * up);
   return s;
 }
-__device__ __forceinline__ void store_corr(const PackArgs& p, int r, int c, double s, int lane) {
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
-  if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = (float)(-8.0 * 0x1p-24 * s);
+__device__ __forceinline__ void store_corr(const PackArgs& p, int r, int c, float s, int lane) {
+  s += dpp<kDppXor1>(s);
+  s += dpp<kDppXor2>(s);
+  s += dpp<kDppHalfMirror>(s);
+  if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = -8.0f * 0x1p-24f * s;
 }
 
 // Rows of up to kPackRegCols columns are read once into registers (every

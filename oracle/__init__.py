@@ -66,19 +66,21 @@ def lib():
         L.ref_f16.argtypes = [ctypes.c_uint16]
         L.ref_bf16.restype = dbl
         L.ref_bf16.argtypes = [ctypes.c_uint16]
+        L.ref_code.restype = i32
+        L.ref_code.argtypes = [vp, i64, i32]
         L.ref_blob_bytes.restype = i64
-        L.ref_blob_bytes.argtypes = [i32, i32, i32]
-        L.ref_dequant.argtypes = [vp, i32, i32, i32, i32, vp]
+        L.ref_blob_bytes.argtypes = [i32, i32, i32, i32]
+        L.ref_dequant.argtypes = [vp, i32, i32, i32, i32, i32, vp]
         L.ref_silu.restype = dbl
         L.ref_silu.argtypes = [dbl]
-        L.ref_expert_ffn.argtypes = [i32, i32, i32, vp, vp, i32, vp]
+        L.ref_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp]
         L.ref_route.argtypes = [i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
         L.ref_union.restype = i32
         L.ref_union.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.ref_rmsnorm.argtypes = [i32, vp, dbl, vp]
         L.ref_layer_forward.restype = i32
-        L.ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, vp, u32,
-                                        dbl, vp, vp, vp, vp, vp, vp, vp]
+        L.ref_layer_forward.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, i32, vp, vp, vp,
+                                        u32, dbl, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -94,6 +96,11 @@ def nibble(row_codes: np.ndarray, c: int) -> int:
     return lib().ref_nibble(_p(np.ascontiguousarray(row_codes, dtype=np.uint8)), c)
 
 
+def code(row_codes: np.ndarray, c: int, bits: int = 4) -> int:
+    """Weight c of a row of `bits`-wide two's-complement codes (8, 4 or 2)."""
+    return lib().ref_code(_p(np.ascontiguousarray(row_codes, dtype=np.uint8)), c, bits)
+
+
 def f16(bits: int) -> float:
     return lib().ref_f16(bits)
 
@@ -103,15 +110,16 @@ def bf16(bits: int) -> float:
 
 
 # group: 64 (one fp16 scale per 64 consecutive weights of a row) or 0 (one
-# scale per row)
-def blob_bytes(d: int, f: int, group: int = 64) -> int:
-    return lib().ref_blob_bytes(d, f, group)
+# scale per row); bits: code width, 4 (int4), 8 (int8) or 2 (int2)
+def blob_bytes(d: int, f: int, group: int = 64, bits: int = 4) -> int:
+    return lib().ref_blob_bytes(d, f, group, bits)
 
 
-def dequant(blob: np.ndarray, d: int, f: int, which: int, group: int = 64) -> np.ndarray:
+def dequant(blob: np.ndarray, d: int, f: int, which: int, group: int = 64,
+            bits: int = 4) -> np.ndarray:
     rows, cols = (d, f) if which == 2 else (f, d)
     W = np.empty((rows, cols), dtype=np.float64)
-    lib().ref_dequant(_p(blob), d, f, group, which, _p(W))
+    lib().ref_dequant(_p(blob), d, f, group, bits, which, _p(W))
     return W
 
 
@@ -119,11 +127,12 @@ def silu(v: float) -> float:
     return lib().ref_silu(v)
 
 
-def expert_ffn(blob: np.ndarray, x: np.ndarray, d: int, f: int, group: int = 64) -> np.ndarray:
+def expert_ffn(blob: np.ndarray, x: np.ndarray, d: int, f: int, group: int = 64,
+               bits: int = 4) -> np.ndarray:
     x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
     n = x.shape[0]
     y = np.empty((n, d), dtype=np.float64)
-    lib().ref_expert_ffn(d, f, group, _p(blob), _p(x), n, _p(y))
+    lib().ref_expert_ffn(d, f, group, bits, _p(blob), _p(x), n, _p(y))
     return y
 
 
@@ -166,7 +175,8 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return xn
 
 
-def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6, group=64):
+def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6, group=64,
+                  bits=4):
     """table: sequence of E uint8 blobs (or None for experts nobody picks).
     -> dict(out [T][d] f64, idx, w, uniq, offsets, rows, reads [E])."""
     x = _xarg(x, x_bf16)
@@ -183,7 +193,7 @@ def layer_forward(x, Wr, bias, table, d, f, k, x_bf16=False, flags=0, eps=1e-6, 
     offsets = np.empty(cap + 1, dtype=np.int32)
     rows = np.empty(T * k, dtype=np.int32)
     reads = np.zeros(E, dtype=np.int32)
-    U = lib().ref_layer_forward(d, f, group, E, k, _p(x), int(x_bf16), T, _p(Wr), _p(b),
+    U = lib().ref_layer_forward(d, f, group, bits, E, k, _p(x), int(x_bf16), T, _p(Wr), _p(b),
                                 ctypes.cast(ptrs, ctypes.c_void_p), flags, eps, _p(out),
                                 _p(idx), _p(w), _p(uniq), _p(offsets), _p(rows), _p(reads))
     if U < 0:

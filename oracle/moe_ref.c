@@ -41,6 +41,12 @@
  * above (gs64, README 开始使用 › 获取模型), or 0 for one scale per row (the
  * per-row scaling of the nxmr blog, «纯C语言»): gate scales [f], up scales
  * [f], down scales [d], each weight w[r][c] = q[r][c] * s[r].
+ * They also take bits, the code width: 4 (the layout above), or the 8-bit
+ * and 2-bit codes the nxmr blog's hand-written kernels name next to packed
+ * int4 («纯C语言»): a row of `cols` weights then takes cols * bits / 8 bytes,
+ * int8 one two's-complement byte per weight, int2 four per byte (weight 4i + j
+ * in bits 2j..2j+1 of byte i, lowest first; two's complement, -2..1), and the
+ * scale tensors follow all the codes as above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +64,19 @@ int ref_nibble(const uint8_t* row_codes, int64_t c) {
   int b = row_codes[c / 2];
   int n = (c % 2 == 0) ? (b & 0xF) : (b >> 4);
   return n >= 8 ? n - 16 : n;
+}
+
+/* Weight number c of a row of `bits`-wide codes (8, 4 or 2): the byte holding
+ * it, the field (lowest first) and two's complement of that width. */
+int ref_code(const uint8_t* row_codes, int64_t c, int bits) {
+  if (bits == 4) return ref_nibble(row_codes, c);
+  if (bits == 8) {
+    int b = row_codes[c];
+    return b >= 128 ? b - 256 : b;
+  }
+  int b = row_codes[c / 4];
+  int v = (b >> (2 * (c % 4))) & 3;
+  return v >= 2 ? v - 4 : v;
 }
 
 /* IEEE 754 binary16 -> double, from the format's definition. */
@@ -88,36 +107,40 @@ double ref_bf16(uint16_t b) {
 /* Scales of one row of `cols` weights: cols / gs (gs = 64), or 1 (gs = 0). */
 static int64_t row_scales(int cols, int gs) { return gs ? cols / gs : 1; }
 
-int64_t ref_blob_bytes(int d, int f, int gs) {
-  return 3LL * f * d / 2 + 2LL * (2LL * f * row_scales(d, gs) + (int64_t)d * row_scales(f, gs));
+/* Bytes of the codes of one f x d matrix. */
+static int64_t mat_code_bytes(int d, int f, int bits) { return (int64_t)f * d * bits / 8; }
+
+int64_t ref_blob_bytes(int d, int f, int gs, int bits) {
+  return 3 * mat_code_bytes(d, f, bits) +
+         2LL * (2LL * f * row_scales(d, gs) + (int64_t)d * row_scales(f, gs));
 }
 
 /* which: 0 gate [f x d], 1 up [f x d], 2 down [d x f]. */
-static void mat_view(const uint8_t* blob, int d, int f, int gs, int which, const uint8_t** codes,
-                     const uint16_t** scales, int* rows, int* cols) {
-  int64_t fd = (int64_t)f * d;
-  *codes = blob + which * (fd / 2);
-  *scales = (const uint16_t*)(blob + 3 * (fd / 2)) + which * (f * row_scales(d, gs));
+static void mat_view(const uint8_t* blob, int d, int f, int gs, int bits, int which,
+                     const uint8_t** codes, const uint16_t** scales, int* rows, int* cols) {
+  *codes = blob + which * mat_code_bytes(d, f, bits);
+  *scales = (const uint16_t*)(blob + 3 * mat_code_bytes(d, f, bits)) + which * (f * row_scales(d, gs));
   *rows = which == 2 ? d : f;
   *cols = which == 2 ? f : d;
 }
 
 /* Row r of a matrix, dequantised: w[c] = q[r,c] * s[r, c/gs] (gs64) or
  * q[r,c] * s[r] (per row), exact in fp64. */
-static void dequant_row(const uint8_t* codes, const uint16_t* scales, int cols, int gs, int r,
-                        double* w) {
-  const uint8_t* rc = codes + (int64_t)r * (cols / 2);
+static void dequant_row(const uint8_t* codes, const uint16_t* scales, int cols, int gs, int bits,
+                        int r, double* w) {
+  const uint8_t* rc = codes + (int64_t)r * cols * bits / 8;
   const uint16_t* rs = scales + (int64_t)r * row_scales(cols, gs);
-  for (int c = 0; c < cols; ++c) w[c] = (double)ref_nibble(rc, c) * ref_f16(rs[gs ? c / gs : 0]);
+  for (int c = 0; c < cols; ++c)
+    w[c] = (double)ref_code(rc, c, bits) * ref_f16(rs[gs ? c / gs : 0]);
 }
 
 /* Dense dequantised matrix (rows x cols doubles), for tests on small shapes. */
-void ref_dequant(const uint8_t* blob, int d, int f, int gs, int which, double* W) {
+void ref_dequant(const uint8_t* blob, int d, int f, int gs, int bits, int which, double* W) {
   const uint8_t* codes;
   const uint16_t* scales;
   int rows, cols;
-  mat_view(blob, d, f, gs, which, &codes, &scales, &rows, &cols);
-  for (int r = 0; r < rows; ++r) dequant_row(codes, scales, cols, gs, r, W + (int64_t)r * cols);
+  mat_view(blob, d, f, gs, bits, which, &codes, &scales, &rows, &cols);
+  for (int r = 0; r < rows; ++r) dequant_row(codes, scales, cols, gs, bits, r, W + (int64_t)r * cols);
 }
 
 double ref_silu(double v) { return v / (1.0 + exp(-v)); }
@@ -126,13 +149,14 @@ double ref_silu(double v) { return v / (1.0 + exp(-v)); }
  *   g = Wg x, u = Wu x, a = silu(g) * u, y = Wd a.
  * The pages only say the chosen experts run their feed-forward computation
  * (colibri 技术解读, "集群模式与开放问题清单"); SwiGLU is the reading taken. */
-void ref_expert_ffn(int d, int f, int gs, const uint8_t* blob, const double* x, int n, double* y) {
+void ref_expert_ffn(int d, int f, int gs, int bits, const uint8_t* blob, const double* x, int n,
+                    double* y) {
   const uint8_t *gc, *uc, *dc;
   const uint16_t *gsc, *usc, *dsc;
   int rows, cols;
-  mat_view(blob, d, f, gs, 0, &gc, &gsc, &rows, &cols);
-  mat_view(blob, d, f, gs, 1, &uc, &usc, &rows, &cols);
-  mat_view(blob, d, f, gs, 2, &dc, &dsc, &rows, &cols);
+  mat_view(blob, d, f, gs, bits, 0, &gc, &gsc, &rows, &cols);
+  mat_view(blob, d, f, gs, bits, 1, &uc, &usc, &rows, &cols);
+  mat_view(blob, d, f, gs, bits, 2, &dc, &dsc, &rows, &cols);
   double* a = (double*)malloc(sizeof(double) * (size_t)n * f);
 #pragma omp parallel
   {
@@ -140,8 +164,8 @@ void ref_expert_ffn(int d, int f, int gs, const uint8_t* blob, const double* x, 
     double* wu = (double*)malloc(sizeof(double) * d);
 #pragma omp for schedule(static)
     for (int r = 0; r < f; ++r) {
-      dequant_row(gc, gsc, d, gs, r, wg);
-      dequant_row(uc, usc, d, gs, r, wu);
+      dequant_row(gc, gsc, d, gs, bits, r, wg);
+      dequant_row(uc, usc, d, gs, bits, r, wu);
       for (int t = 0; t < n; ++t) {
         const double* xt = x + (int64_t)t * d;
         double g = 0.0, u = 0.0;
@@ -157,7 +181,7 @@ void ref_expert_ffn(int d, int f, int gs, const uint8_t* blob, const double* x, 
     double* wd = (double*)malloc(sizeof(double) * f);
 #pragma omp for schedule(static)
     for (int c = 0; c < d; ++c) {
-      dequant_row(dc, dsc, f, gs, c, wd);
+      dequant_row(dc, dsc, f, gs, bits, c, wd);
       for (int t = 0; t < n; ++t) {
         const double* at = a + (int64_t)t * f;
         double acc = 0.0;
@@ -279,7 +303,7 @@ void ref_rmsnorm(int d, const float* h, double eps, float* xn) {
  * Outputs: out[T][d] (fp64), idx/w [T][k], uniq/offsets/rows as ref_union,
  * reads[E] += 1 for every time an expert's blob is read.  Returns U, or -1 if
  * a selected expert has no blob. */
-int ref_layer_forward(int d, int f, int gs, int E, int k, const void* x, int x_is_bf16, int T,
+int ref_layer_forward(int d, int f, int gs, int bits, int E, int k, const void* x, int x_is_bf16, int T,
                       const float* Wr, const float* bias, const uint8_t* const* table,
                       uint32_t flags, double eps, double* out, int32_t* idx, double* w,
                       int32_t* uniq, int32_t* offsets, int32_t* rows, int32_t* reads) {
@@ -310,7 +334,7 @@ int ref_layer_forward(int d, int f, int gs, int E, int k, const void* x, int x_i
       int t = rows[offsets[u] + i] / k;
       for (int c = 0; c < d; ++c) xs[(int64_t)i * d + c] = x_at(xin, xin_bf16, (int64_t)t * d + c);
     }
-    ref_expert_ffn(d, f, gs, table[e], xs, n, ys); /* the one read of expert e */
+    ref_expert_ffn(d, f, gs, bits, table[e], xs, n, ys); /* the one read of expert e */
     reads[e] += 1;
     for (int i = 0; i < n; ++i)
       memcpy(yslot + (int64_t)rows[offsets[u] + i] * d, ys + (int64_t)i * d, sizeof(double) * d);

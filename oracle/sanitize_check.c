@@ -23,16 +23,18 @@
 int ref_nibble(const uint8_t* row_codes, int64_t c);
 double ref_f16(uint16_t h);
 double ref_bf16(uint16_t b);
-int64_t ref_blob_bytes(int d, int f, int gs);
-void ref_dequant(const uint8_t* blob, int d, int f, int gs, int which, double* W);
+int ref_code(const uint8_t* row_codes, int64_t c, int bits);
+int64_t ref_blob_bytes(int d, int f, int gs, int bits);
+void ref_dequant(const uint8_t* blob, int d, int f, int gs, int bits, int which, double* W);
 double ref_silu(double v);
-void ref_expert_ffn(int d, int f, int gs, const uint8_t* blob, const double* x, int n, double* y);
+void ref_expert_ffn(int d, int f, int gs, int bits, const uint8_t* blob, const double* x, int n,
+                    double* y);
 void ref_route(int d, int E, int k, const void* x, int x_is_bf16, int T, const float* Wr,
                const float* bias, int32_t* idx, double* w, double* z_out);
 int ref_union(int E, int k, int T, const int32_t* idx, int32_t* uniq, int32_t* offsets,
               int32_t* rows);
 void ref_rmsnorm(int d, const float* h, double eps, float* xn);
-int ref_layer_forward(int d, int f, int gs, int E, int k, const void* x, int x_is_bf16, int T,
+int ref_layer_forward(int d, int f, int gs, int bits, int E, int k, const void* x, int x_is_bf16, int T,
                       const float* Wr, const float* bias, const uint8_t* const* table,
                       uint32_t flags, double eps, double* out, int32_t* idx, double* w,
                       int32_t* uniq, int32_t* offsets, int32_t* rows, int32_t* reads);
@@ -58,10 +60,10 @@ static int failures = 0;
 
 /* One expert blob in exactly its own allocation (so ASan sees its end):
  * random codes, scales = fp16 bit patterns of values in [0.004, 0.03). */
-static uint8_t* make_blob(int d, int f, int gs) {
-  const int64_t n = ref_blob_bytes(d, f, gs);
+static uint8_t* make_blob(int d, int f, int gs, int bits) {
+  const int64_t n = ref_blob_bytes(d, f, gs, bits);
   uint8_t* b = (uint8_t*)malloc((size_t)n);
-  const int64_t codes = 3LL * f * d / 2;
+  const int64_t codes = 3LL * f * d * bits / 8;
   for (int64_t i = 0; i < codes; ++i) b[i] = (uint8_t)next_u64();
   uint16_t* s = (uint16_t*)(b + codes);
   for (int64_t i = 0; i < (n - codes) / 2; ++i)
@@ -69,8 +71,8 @@ static uint8_t* make_blob(int d, int f, int gs) {
   return b;
 }
 
-static void run_layer(const char* name, int d, int f, int gs, int E, int k, int T, int bf16,
-                      uint32_t flags, int sparse_table) {
+static void run_layer(const char* name, int d, int f, int gs, int bits, int E, int k, int T,
+                      int bf16, uint32_t flags, int sparse_table) {
   float* xf = (float*)malloc(sizeof(float) * (size_t)T * d);
   uint16_t* xb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)T * d);
   for (int64_t i = 0; i < (int64_t)T * d; ++i) {
@@ -105,7 +107,7 @@ static void run_layer(const char* name, int d, int f, int gs, int E, int k, int 
   for (int e = 0; e < E; ++e) {
     int picked = 0;
     for (int64_t i = 0; i < (int64_t)T * k; ++i) picked |= idx[i] == e;
-    if (picked || !sparse_table) table[e] = owned[e] = make_blob(d, f, gs);
+    if (picked || !sparse_table) table[e] = owned[e] = make_blob(d, f, gs, bits);
   }
   const int cap = E < T * k ? E : T * k;
   double* out = (double*)malloc(sizeof(double) * (size_t)T * d);
@@ -113,7 +115,7 @@ static void run_layer(const char* name, int d, int f, int gs, int E, int k, int 
   int32_t* offs = (int32_t*)malloc(sizeof(int32_t) * (cap + 1));
   int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)T * k);
   int32_t* reads = (int32_t*)calloc(E, sizeof(int32_t));
-  const int U = ref_layer_forward(d, f, gs, E, k, bf16 && !(flags & 3u) ? (const void*)xb
+  const int U = ref_layer_forward(d, f, gs, bits, E, k, bf16 && !(flags & 3u) ? (const void*)xb
                                                                        : (const void*)xf,
                                   bf16 && !(flags & 3u), T, Wr, bias, table, flags, 1e-6, out,
                                   idx, w, uniq, offs, rows, reads);
@@ -139,11 +141,11 @@ static void run_layer(const char* name, int d, int f, int gs, int E, int k, int 
   double* xd = (double*)malloc(sizeof(double) * (size_t)T * d);
   for (int64_t i = 0; i < (int64_t)T * d; ++i) xd[i] = xf[i];
   double* y = (double*)malloc(sizeof(double) * (size_t)T * d);
-  ref_expert_ffn(d, f, gs, table[uniq[0]], xd, T, y);
+  ref_expert_ffn(d, f, gs, bits, table[uniq[0]], xd, T, y);
   for (int which = 0; which < 3; ++which) {
     const int rws = which == 2 ? d : f, cls = which == 2 ? f : d;
     double* W = (double*)malloc(sizeof(double) * (size_t)rws * cls);
-    ref_dequant(table[uniq[0]], d, f, gs, which, W);
+    ref_dequant(table[uniq[0]], d, f, gs, bits, which, W);
     free(W);
   }
 
@@ -166,13 +168,20 @@ int main(void) {
     (void)ref_bf16((uint16_t)h);
   }
   CHECK(ref_silu(-800.0) == 0.0 || ref_silu(-800.0) > -1e-300, "silu limit");
-  run_layer("tiny gs64", 128, 64, 64, 16, 2, 4, 0, 0u, 0);
-  run_layer("one token", 64, 64, 64, 8, 1, 1, 0, 0u, 1);
-  run_layer("k = E", 64, 128, 64, 8, 8, 3, 0, 0u, 0);
-  run_layer("per-row scales", 192, 64, 0, 12, 3, 5, 0, 0u, 1);
-  run_layer("bf16 input", 128, 64, 64, 10, 4, 6, 1, 0u, 1);
-  run_layer("rmsnorm + residual", 128, 128, 64, 16, 2, 3, 0, 3u, 1);
-  run_layer("wide union", 64, 64, 64, 96, 32, 3, 0, 0u, 1);
+  for (int b = 0; b < 256; ++b) {
+    const uint8_t byte = (uint8_t)b;
+    CHECK(ref_code(&byte, 0, 8) == (int8_t)byte, "int8 code %d", b);
+    for (int j = 0; j < 4; ++j) CHECK(ref_code(&byte, j, 2) >= -2 && ref_code(&byte, j, 2) <= 1, "int2");
+  }
+  run_layer("tiny gs64", 128, 64, 64, 4, 16, 2, 4, 0, 0u, 0);
+  run_layer("one token", 64, 64, 64, 4, 8, 1, 1, 0, 0u, 1);
+  run_layer("k = E", 64, 128, 64, 4, 8, 8, 3, 0, 0u, 0);
+  run_layer("per-row scales", 192, 64, 0, 4, 12, 3, 5, 0, 0u, 1);
+  run_layer("bf16 input", 128, 64, 64, 4, 10, 4, 6, 1, 0u, 1);
+  run_layer("rmsnorm + residual", 128, 128, 64, 4, 16, 2, 3, 0, 3u, 1);
+  run_layer("wide union", 64, 64, 64, 4, 96, 32, 3, 0, 0u, 1);
+  run_layer("int8 codes", 128, 64, 64, 8, 12, 3, 5, 0, 0u, 1);
+  run_layer("int2 codes, per-row", 192, 64, 0, 2, 12, 3, 5, 0, 3u, 1);
   if (failures) {
     fprintf(stderr, "sanitized oracle: %d failures\n", failures);
     return 1;

@@ -93,18 +93,19 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def blob_sizes(d: int, f: int, group: int = 64):
-    """(nibble bytes, number of fp16 scales) of one expert: three matrices of
-    f*d weights, two 4-bit codes per byte, one scale per `group` consecutive
-    weights of a row, or (group 0) one scale per row: 2f + d."""
-    nib = 3 * f * d // 2
+def blob_sizes(d: int, f: int, group: int = 64, bits: int = 4):
+    """(code bytes, number of fp16 scales) of one expert: three matrices of
+    f*d weights, `bits`-wide codes (8, 4 or 2: 1, 2 or 4 per byte), one scale
+    per `group` consecutive weights of a row, or (group 0) one scale per row:
+    2f + d."""
+    nib = 3 * f * d * bits // 8
     nsc = 3 * f * d // group if group else 2 * f + d
     return nib, nsc
 
 
 def expert_blob(seed: int, layer: int, expert: int, d: int, f: int, out=None,
-                group: int = 64) -> np.ndarray:
-    nib, nsc = blob_sizes(d, f, group)
+                group: int = 64, bits: int = 4) -> np.ndarray:
+    nib, nsc = blob_sizes(d, f, group, bits)
     if out is None:
         out = np.empty(nib + 2 * nsc, dtype=np.uint8)
     lib().synth_expert_blob(seed, layer, expert, nib, nsc, SCALE_LO, SCALE_HI, _ptr(out))
@@ -112,8 +113,8 @@ def expert_blob(seed: int, layer: int, expert: int, d: int, f: int, out=None,
 
 
 def layer_blobs(seed: int, layer: int, n_experts: int, d: int, f: int, e0: int = 0,
-                out=None, group: int = 64) -> np.ndarray:
-    nib, nsc = blob_sizes(d, f, group)
+                out=None, group: int = 64, bits: int = 4) -> np.ndarray:
+    nib, nsc = blob_sizes(d, f, group, bits)
     if out is None:
         out = np.empty((n_experts, nib + 2 * nsc), dtype=np.uint8)
     lib().synth_layer_blobs(seed, layer, e0, n_experts, nib, nsc, SCALE_LO, SCALE_HI, _ptr(out))

@@ -11,7 +11,8 @@ Distributions (every draw seeded and counter based, see gen.c):
            the prefill chunk is rounded to bf16 (round to nearest even)
   W_r    ~ N(0, 0.02) fp32, [E][d]
   bias   none for the tiny layer; -1.1*ln(e+1) (a Zipf(1.1) skew) otherwise
-  codes  every 4-bit code uniform on its 16 values, i.e. int4 uniform on [-8, 7]
+  codes  random bytes: every code uniform on its values (int4 on [-8, 7]; the
+         int8 and int2 variants on [-128, 127] and [-2, 1])
   scales fp16 uniform on [0.005, 0.02)
 """
 from __future__ import annotations
@@ -38,10 +39,11 @@ class Workload:
     layers: int = 1
     steps: int = 1
     group: int = 64             # scale group: 64, or 0 for one scale per row
+    bits: int = 4               # code width: 4 (int4), 8 (int8) or 2 (int2)
 
     @property
     def blob_bytes(self) -> int:
-        nib, nsc = blob_sizes(self.d, self.f, self.group)
+        nib, nsc = blob_sizes(self.d, self.f, self.group, self.bits)
         return nib + 2 * nsc
 
     @property
@@ -65,6 +67,19 @@ WORKLOADS = {
                                seed=1006, x_kind="shared_base", group=0),
     "prefill512_perrow": Workload("prefill512_perrow", d=6144, f=2048, n_experts=256, top_k=8,
                                   T=512, seed=1007, x_kind="bf16", group=0),
+    # the same layer with int8 and int2 codes (gs64 scales)
+    "decode1_int8": Workload("decode1_int8", d=6144, f=2048, n_experts=256, top_k=8, T=1,
+                             seed=1008, bits=8),
+    "verify8_int8": Workload("verify8_int8", d=6144, f=2048, n_experts=256, top_k=8, T=8,
+                             seed=1009, x_kind="shared_base", bits=8),
+    "prefill512_int8": Workload("prefill512_int8", d=6144, f=2048, n_experts=256, top_k=8,
+                                T=512, seed=1010, x_kind="bf16", bits=8),
+    "decode1_int2": Workload("decode1_int2", d=6144, f=2048, n_experts=256, top_k=8, T=1,
+                             seed=1011, bits=2),
+    "verify8_int2": Workload("verify8_int2", d=6144, f=2048, n_experts=256, top_k=8, T=8,
+                             seed=1012, x_kind="shared_base", bits=2),
+    "prefill512_int2": Workload("prefill512_int2", d=6144, f=2048, n_experts=256, top_k=8,
+                                T=512, seed=1013, x_kind="bf16", bits=2),
 }
 
 
@@ -94,11 +109,11 @@ def tokens(w: Workload, step: int = 0, T: int | None = None):
 def experts(w: Workload, layer: int = 0, e0: int = 0, ne: int | None = None):
     """Expert blobs [ne][blob_bytes] uint8 of one layer."""
     ne = w.n_experts - e0 if ne is None else ne
-    return layer_blobs(w.seed, layer, ne, w.d, w.f, e0=e0, group=w.group)
+    return layer_blobs(w.seed, layer, ne, w.d, w.f, e0=e0, group=w.group, bits=w.bits)
 
 
 def one_expert(w: Workload, layer: int, e: int):
-    return expert_blob(w.seed, layer, e, w.d, w.f, group=w.group)
+    return expert_blob(w.seed, layer, e, w.d, w.f, group=w.group, bits=w.bits)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

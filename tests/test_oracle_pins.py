@@ -483,3 +483,100 @@ def test_tiny_workload_golden():
     assert r["idx"].tolist() == g["idx"]
     assert r["uniq"].tolist() == g["uniq"] and r["rows"].tolist() == g["rows"]
     np.testing.assert_allclose(r["out"], np.array(g["out"]), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- int8 and int2 code formats
+# (the nxmr blog's hand-written int8 and packed int2 kernels, «纯C语言»)
+
+
+def np_codes(packed_rows: np.ndarray, cols: int, bits: int) -> np.ndarray:
+    """Independent unpacking: int8 = the byte as two's complement; int2 =
+    four fields per byte, lowest first, two's complement of width 2."""
+    b = packed_rows.astype(np.int64)
+    if bits == 8:
+        return np.where(b >= 128, b - 256, b)
+    fields = np.stack([(b >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(b.shape[0], cols)
+    return np.where(fields >= 2, fields - 4, fields)
+
+
+def np_dequant_bits(blob, d, f, which, bits, group=64):
+    fd = f * d
+    cb = fd * bits // 8
+    rows, cols = (d, f) if which == 2 else (f, d)
+    q = np_codes(blob[which * cb:(which + 1) * cb].reshape(rows, cols * bits // 8), cols, bits)
+    s_all = blob[3 * cb:].view(np.float16).astype(np.float64)
+    if group:
+        ng = [f * (d // 64), f * (d // 64), d * (f // 64)]
+        beg = sum(ng[:which])
+        s = s_all[beg:beg + ng[which]].reshape(rows, cols // 64)
+        return q * np.repeat(s, 64, axis=1)
+    beg = [0, f, 2 * f][which]
+    return q * s_all[beg:beg + rows][:, None]
+
+
+def test_int8_and_int2_decode_exhaustive():
+    for b in range(256):
+        row = np.array([b], np.uint8)
+        assert oracle.code(row, 0, 8) == (b ^ 128) - 128
+        for j in range(4):
+            v = (b >> (2 * j)) & 3
+            assert oracle.code(row, j, 2) == (v ^ 2) - 2
+    # int4 through the same accessor is the nibble decode
+    for b in range(256):
+        row = np.array([b], np.uint8)
+        assert oracle.code(row, 0, 4) == oracle.nibble(row, 0)
+        assert oracle.code(row, 1, 4) == oracle.nibble(row, 1)
+
+
+@pytest.mark.parametrize("bits", [8, 2])
+def test_code_format_blob_sizes(bits):
+    for d, f in [(6144, 2048), (256, 128)]:
+        nb = 3 * f * d * bits // 8
+        assert oracle.blob_bytes(d, f, bits=bits) == nb + 2 * 3 * f * d // 64
+        assert oracle.blob_bytes(d, f, group=0, bits=bits) == nb + 2 * (2 * f + d)
+        assert synth.expert_blob(1, 0, 0, d, f, bits=bits).size == oracle.blob_bytes(d, f, bits=bits)
+
+
+@pytest.mark.parametrize("bits,group,d,f", [(8, 64, 256, 128), (2, 64, 128, 192),
+                                            (8, 0, 192, 64), (2, 0, 64, 128)])
+def test_code_format_dequant_brute_force(bits, group, d, f):
+    blob = synth.expert_blob(5, 0, 3, d, f, group=group, bits=bits)
+    for which in range(3):
+        assert np.array_equal(oracle.dequant(blob, d, f, which, group=group, bits=bits),
+                              np_dequant_bits(blob, d, f, which, bits, group))
+
+
+@pytest.mark.parametrize("bits", [8, 2])
+def test_code_format_ffn_brute_force(bits):
+    d, f, n = 256, 128, 3
+    blob = synth.expert_blob(6, 0, 1, d, f, bits=bits)
+    x = np.random.default_rng(9).normal(size=(n, d))
+    Wg, Wu, Wd = (np_dequant_bits(blob, d, f, i, bits) for i in range(3))
+    ref = (np_silu(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    y = oracle.expert_ffn(blob, x, d, f, bits=bits)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("bits", [8, 2])
+def test_code_format_layer_brute_force(bits):
+    """A small layer: numpy routing (full sort, softmax over all experts,
+    renormalised), numpy SwiGLU on the numpy-dequantised experts, ascending
+    slot combine; against the oracle's layer."""
+    d, f, E, k, T = 128, 64, 8, 3, 5
+    rng = np.random.default_rng(bits)
+    Wr = (rng.normal(size=(E, d)) * 0.05).astype(np.float32)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    blobs = [synth.expert_blob(7, 0, e, d, f, bits=bits) for e in range(E)]
+    r = oracle.layer_forward(x, Wr, None, blobs, d, f, k, bits=bits)
+    z = x.astype(np.float64) @ Wr.astype(np.float64).T
+    out = np.zeros((T, d))
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -z[t]))[:k]
+        assert np.array_equal(r["idx"][t], order)
+        p = softmax(z[t])[order]
+        p /= p.sum()
+        for j, e in enumerate(order):
+            Wg, Wu, Wd = (np_dequant_bits(blobs[e], d, f, i, bits) for i in range(3))
+            xt = x[t].astype(np.float64)
+            out[t] += p[j] * (Wd @ (np_silu(Wg @ xt) * (Wu @ xt)))
+    np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12 * np.abs(out).max())
