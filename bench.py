@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; chain48: 2)")
     p.add_argument("--workload", default="decode1",
                    choices=["decode1", "verify8", "prefill512", "chain48", "decode1_perrow",
-                            "verify8_perrow", "prefill512_perrow"])
+                            "verify8_perrow", "prefill512_perrow", "decode1_int8", "verify8_int8",
+                            "prefill512_int8", "decode1_int2", "verify8_int2", "prefill512_int2"])
     p.add_argument("--layers", type=int, default=8, help="independent layers to rotate over")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
@@ -81,15 +82,17 @@ GEMM_SOURCES = ("device_util.h", "ffn_mfma.hip", "moe_internal.h", "pack.h", "sm
 
 
 def matrix_bytes(w):
-    """(gate + up, down) bytes of one expert: codes and fp16 scales (one per
-    64 weights of a row, or one per row)."""
+    """(gate + up, down) bytes of one expert: codes (w.bits per weight) and
+    fp16 scales (one per 64 weights of a row, or one per row)."""
     sg = w.d // 64 if w.group else 1
     sd = w.f // 64 if w.group else 1
-    return 2 * (w.f * w.d // 2 + 2 * w.f * sg), w.f * w.d // 2 + 2 * w.d * sd
+    codes = w.f * w.d * w.bits // 8
+    return 2 * (codes + 2 * w.f * sg), codes + 2 * w.d * sd
 
 
 def gateup_sources(workload):
-    return GATEUP_SOURCES if workload.startswith(("decode1", "chain48")) else GEMM_SOURCES
+    gemv = workload.startswith(("decode1", "chain48")) and not workload.endswith(("int8", "int2"))
+    return GATEUP_SOURCES if gemv else GEMM_SOURCES
 
 
 def kernel_source_hash(workload="decode1"):
@@ -212,7 +215,7 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
     K with an event pair around each step (the spread)."""
     dev = torch.device("cuda:0")
     R = len(layers)
-    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
+    dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group, code_bits=w.bits)
     blob = w.blob_bytes
     nib_gu, nib_dn = matrix_bytes(w)
     xs = []
@@ -225,9 +228,10 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
     ws = moe.make_workspace(dims, w.T, dev)
     stream = torch.cuda.current_stream()
     flags = moe.MOE_BATCH_INVARIANT if inv else 0
-    # the library's choice: one token (or the flag) takes the int8-digit GEMV
-    # kernels; 2+ tokens with d, f multiples of 512 the fp16 MFMA grouped GEMM
-    gemv = w.T == 1 or inv or w.d % 512 or w.f % 512
+    # the library's choice: int4 layers take the int8-digit GEMV kernels for
+    # one token (or with the flag), the fp16 MFMA grouped GEMM for 2+ tokens
+    # with d, f multiples of 512; int8 and int2 layers always the grouped GEMM
+    gemv = w.bits == 4 and (w.T == 1 or inv or w.d % 512 or w.f % 512)
 
     def step(i, s=None):
         L = layers[i % R]
@@ -307,12 +311,12 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if gemv else
-                  "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
+                  f"int{w.bits} weights as fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
                                f"top-{w.top_k}, T={w.T} tokens "
                                f"({'bf16' if w.x_bf16 else 'fp32'} x), "
-                               f"{'gs64' if w.group else 'per-row'} int4 experts "
+                               f"{'gs64' if w.group else 'per-row'} int{w.bits} experts "
                                f"({blob} B each)" + (", MOE_BATCH_INVARIANT" if inv else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "layers_rotated": R, "distinct_experts_per_step": float(u_steps.mean())},

@@ -38,6 +38,16 @@
  *   | gate scales [f] | up scales [f] | down scales [d]
  * so w[r][c] = q[r][c] * s[r]; 18,894,848 bytes at d = 6144, f = 2048.  Every
  * entry point takes both layouts and computes the same way on them.
+ * Code widths (dims.code_bits; the nxmr blog, «纯C语言», names hand-written
+ * int8 and packed int2 kernels beside packed int4): a row of `cols` weights
+ * takes cols * bits / 8 bytes of codes, int8 one two's-complement byte per
+ * weight, int2 four two's-complement 2-bit fields per byte (weight 4i + j in
+ * bits 2j..2j+1 of byte i); the scale tensors follow all the codes as above.
+ * 30,081,024 (int8) and 15,040,512 (int2) bytes per gs64 expert at d = 6144,
+ * f = 2048.  int8 and int2 layers run every call on the matrix cores in
+ * 16-token tiles (so d and f must be multiples of 512), where a token's result
+ * does not depend on the other tokens of its call; moe_layer_forward_cached
+ * takes int4 layers only.
  *
  * Conventions for every entry point:
  *  - Pointers are device pointers (or host memory mapped into the device
@@ -81,6 +91,8 @@ typedef struct moe_dims {
   int32_t n_experts;  /* E; 1..1024 */
   int32_t top_k;      /* k; 1..min(E, 32) */
   int32_t group_size; /* weights per fp16 scale: 64, or 0 for one scale per row */
+  int32_t code_bits;  /* code width: 4 (or 0) int4, 8 int8, 2 int2; 8 and 2 need d
+                         and f multiples of 512 (see "Code widths" below) */
 } moe_dims;
 
 /* Activation dtypes (x_dtype). */
@@ -101,7 +113,8 @@ enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* null or inconsistent argument, T < 1 */
   MOE_EUNSUPPORTED = -2, /* group_size not 64 or 0, d/f not multiples of 64, k > 32, E > 1024,
-                            bad dtype/flags,
+                            code_bits not 0, 2, 4 or 8 (8 and 2: d or f not a multiple
+                            of 512), bad dtype/flags,
                             MOE_BATCH_INVARIANT with T > 8 or T * k > 64 */
   MOE_ENOSPC = -3,       /* ws_bytes smaller than moe_workspace_bytes() */
   MOE_EHIP = -4          /* a kernel launch failed; moe_strerror() names the HIP error */

@@ -48,7 +48,8 @@ class moe_routing_offsets(ctypes.Structure):
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("f", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("code_bits", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -58,9 +59,11 @@ class Dims:
     n_experts: int
     top_k: int
     group_size: int = 64
+    code_bits: int = 4
 
     def c(self) -> moe_dims:
-        return moe_dims(self.d, self.f, self.n_experts, self.top_k, self.group_size)
+        return moe_dims(self.d, self.f, self.n_experts, self.top_k, self.group_size,
+                        self.code_bits)
 
 
 def _hip_runtimes():

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   small_route(ro, sr, wave, 16);
   if (px.mbo && wave == 15)
-    mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t, lane);
+    mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t,
+                    px.thin_all, lane);
   publish_small_route(ro, sr, table, 1024);
 }
 
@@ -595,6 +596,7 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
     px.mbo_t = map->mbo_t;
     px.blk_t = map->blk_t;
     px.mblock = map->mblock;
+    px.thin_all = map->thin_all;
   }
   return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table, px);
 }

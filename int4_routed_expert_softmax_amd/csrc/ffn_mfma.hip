@@ -86,8 +86,9 @@ __device__ __forceinline__ int find_bucket(const int32_t* p, int n, int j) {
 __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   if (p.mbo && blockIdx.x == gridDim.x - 1) {
     // thread t maps experts 4t .. 4t + 3: thin ones (at most kThinTokens
-    // tokens) take one thin block each, the others ceil(count / mblock)
-    // M-blocks; two block-wide exclusive scans place them
+    // tokens, or every expert with thin_all) take one thin block per
+    // kThinTokens tokens, the others ceil(count / mblock) M-blocks; two
+    // block-wide exclusive scans place them
     __shared__ int s_tot[2][4];
     const int U = *p.n_uniq, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     int c[4], th[4], sum = 0, sum_t = 0;
@@ -95,8 +96,9 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
       const int n = u < U ? p.offsets[u + 1] - p.offsets[u] : 0;
-      th[i] = u < U && n <= kThinTokens;
-      c[i] = u < U && !th[i] ? (n + p.mblock - 1) / p.mblock : 0;
+      const bool thin = u < U && (p.thin_all || n <= kThinTokens);
+      th[i] = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
+      c[i] = u < U && !thin ? (n + p.mblock - 1) / p.mblock : 0;
       sum += c[i];
       sum_t += th[i];
     }
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
         p.mbo[u] = run;
         p.mbo_t[u] = run_t;
         for (int j = 0; j < c[i]; ++j) p.blk_u[run + j] = u;
-        if (th[i]) p.blk_t[run_t] = u;
+        for (int j = 0; j < th[i]; ++j) p.blk_t[run_t + j] = u;
       }
       run += c[i];
       run_t += th[i];
@@ -479,16 +481,20 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- thin GEMM
-// Experts of at most kThinTokens tokens (most of a prefill chunk's union and
-// every expert of a small batch): one block = one such expert (a single
-// 16-row M-tile) x GW waves of 32 weight rows.  The weights' per-64-column
-// scales multiply the fp32 partial sum of each group instead of every weight:
-// the codes enter the MFMA as the exact fp16 subnormals (q + 8) * 2^-24 (a
-// shift and one AND/XOR per two codes), each group's partial starts from the
-// group's correction -8 * 2^-24 * sum(x') (written by k_pack), so it ends as
-// 2^-24 * sum(x' q), and partial times scale is added to the accumulator.  With
-// one M-tile per block that is about half the VALU work of scaling every
-// weight before the MFMA, and the weights stay exact (only x' is rounded).
+// One block = one 16-row M-tile of one expert (int4 layers: the experts of at
+// most kThinTokens tokens, most of a prefill chunk's union and every expert of
+// a small batch; int8 and int2 layers: every M-tile of every expert) x GW
+// waves of 32 weight rows.  The weights' per-64-column scales multiply the
+// fp32 partial sum of each group instead of every weight: the codes enter the
+// MFMA as the exact fp16 subnormals (q + o) * 2^-24, o = 8 (int4), 128
+// (int8) or 2 (int2) (a few bit operations per two codes), each group's
+// partial starts from the group's correction -o * 2^-24 * sum(x') (written by
+// k_pack), so it ends as 2^-24 * sum(x' q), and partial times scale is added
+// to the accumulator.  That is about half the VALU work of scaling every
+// weight before the MFMA, the weights stay exact (only x' is rounded), and the
+// scale's size is not limited by fp16.  Every code width feeds the MFMA the
+// same 8 columns per lane and step in the same order (column j with column
+// j + 4), so the activations are packed alike for all of them.
 // A stage (128 columns: two scale groups) holds, for every wave, its 32 rows
 // of codes, and for the block the M-tile's activation rows (copied by waves
 // 0..3) and group corrections (wave 0); the ring has R stages, R - 1 in
@@ -496,16 +502,21 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 // a time into two buffers of its own.
 constexpr int kThinWaveRows = 32;
 
-template <int GW, int R>
+template <int GW, int R, int BITS>
 struct ThinShape {
-  static constexpr int kBWave = kThinWaveRows * (kSC / 2);  // 2 KB: 32 rows x 64 B
+  static constexpr int kRowStage = 16 * BITS;                 // code bytes of a row per stage
+  static constexpr int kPieces = kRowStage / 16;              // its 16-byte pieces
+  static constexpr int kRowsPerCopy = 64 / kPieces;           // rows one 1 KB copy covers
+  static constexpr int kCopies = kThinWaveRows / kRowsPerCopy;  // code copies per wave and stage
+  static constexpr int kBWave = kThinWaveRows * kRowStage;
   static constexpr int kStageB = GW * kBWave;
-  static constexpr int kStageA = kThinTokens * kSC * 2;    // 16 rows x 256 B
-  static constexpr int kStageC = 32 * 4;                   // [2 groups][16 tokens] f32
+  static constexpr int kStageA = kThinTokens * kSC * 2;       // 16 rows x 256 B
+  static constexpr int kStageC = 32 * 4;                      // [2 groups][16 tokens] f32
   static constexpr int kStage = kStageB + kStageA + kStageC;
-  static constexpr int kScalePiece = kThinWaveRows * 16;   // [32 rows][8 groups] fp16
+  static constexpr int kScalePiece = kThinWaveRows * 16;      // [32 rows][8 groups] fp16
   static constexpr int kScaleOff = R * kStage;
   static constexpr int kLdsBytes = kScaleOff + GW * 2 * kScalePiece;
+  static_assert(BITS == 4 || BITS == 8 || BITS == 2, "code width");
   static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
   // a scale piece is copied R - 1 stages before its first use, which must
   // come after the last use of the piece two back
@@ -514,9 +525,18 @@ struct ThinShape {
   static_assert(kThinTokens == 16, "one M-tile");
 };
 
-// 8 codes (column j in bits 4j..4j+3) -> the fp16 subnormals (q + 8) * 2^-24
-// in slot order (col 0, 4, 1, 5, 2, 6, 3, 7): q + 8 is the code with its sign
-// bit flipped.
+// Slot of 16-byte piece p of row r of a wave's stage (a permutation of the
+// row's pieces that spreads neighbouring rows over the LDS banks).
+template <int BITS>
+__device__ __forceinline__ int thin_slot(int p, int r) {
+  if constexpr (BITS == 4) return p ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
+  else if constexpr (BITS == 8) return p ^ (r & 7);
+  else return p ^ ((r >> 2) & 1);
+}
+
+// 8 int4 codes (column j in bits 4j..4j+3) -> the fp16 subnormals (q + 8) *
+// 2^-24 in slot order (col 0, 4, 1, 5, 2, 6, 3, 7): q + 8 is the code with
+// its sign bit flipped.
 __device__ __forceinline__ f16x8 raw8(uint32_t w) {
   f16x8 r;
 #pragma unroll
@@ -528,6 +548,36 @@ __device__ __forceinline__ f16x8 raw8(uint32_t w) {
   }
   return r;
 }
+// 8 int8 codes (columns 0..3 in lo, 4..7 in hi) -> (q + 128) * 2^-24, same
+// slot order: byte i of lo and byte i of hi into the low bytes of the two
+// halves (v_perm), sign bits flipped.
+__device__ __forceinline__ f16x8 raw8_i8(uint32_t lo, uint32_t hi) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
+    const uint32_t h = __builtin_amdgcn_perm(hi, lo, sel) ^ 0x00800080u;
+    const f16x2 q = __builtin_bit_cast(f16x2, h);
+    r[2 * i] = q[0];
+    r[2 * i + 1] = q[1];
+  }
+  return r;
+}
+// 8 int2 codes (bytes 2j and 2j + 1 of w: columns 0..3 and 4..7) -> (q + 2) *
+// 2^-24, same slot order.
+__device__ __forceinline__ f16x8 raw8_i2(uint32_t w, int j) {
+  const uint32_t sel = (uint32_t)(2 * j) | (0x0Cu << 8) | ((uint32_t)(2 * j + 1) << 16) | (0x0Cu << 24);
+  const uint32_t x = __builtin_amdgcn_perm(w, w, sel);
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = ((x >> (2 * i)) & 0x00030003u) ^ 0x00020002u;
+    const f16x2 q = __builtin_bit_cast(f16x2, h);
+    r[2 * i] = q[0];
+    r[2 * i + 1] = q[1];
+  }
+  return r;
+}
 
 // 4-byte global -> LDS copy: lane l's word lands at lds + 4 l.
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
@@ -535,10 +585,12 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
                :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
 }
 
-template <int MODE, int GW, int R>
+template <int MODE, int GW, int R, int BITS>
 __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
-  using Shape = ThinShape<GW, R>;
-  constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB;
+  using Shape = ThinShape<GW, R, BITS>;
+  constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB, kRowStage = Shape::kRowStage;
+  constexpr int kPieces = Shape::kPieces, kRowsPerCopy = Shape::kRowsPerCopy;
+  constexpr int kCopies = Shape::kCopies;
   constexpr int kStageA = Shape::kStageA, kStage = Shape::kStage, kScalePiece = Shape::kScalePiece;
   constexpr int kHalf = kThinWaveRows / 2;
   const int t = threadIdx.x;
@@ -549,26 +601,30 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const int pr = g.L.per_row;
   const int ng = srow(K, pr);  // scales per weight row
   const int ngc = K / kGroup;  // correction groups per activation row
+  const size_t row_bytes = (size_t)K * BITS / 8;
 
-  // ---- the block's expert (at most kThinTokens tokens)
+  // ---- the block's expert and M-tile (tokens tok0 .. tok0 + 15)
   const ExpertList& L = g.L;
-  int off, cnt;
+  int off, cnt, tok0;
   const uint8_t* blob;
   if (L.single) {
-    if (jy > 0) return;
     off = 0;
     cnt = L.single_n;
+    tok0 = jy * kThinTokens;
+    if (tok0 >= cnt) return;
     blob = L.single;
   } else {
     if (jy >= g.mbo_t[*L.n_uniq]) return;
     const int u = g.blk_t[jy];
     off = L.offsets[u];
     cnt = L.offsets[u + 1] - off;
+    tok0 = (jy - g.mbo_t[u]) * kThinTokens;
     blob = L.table[L.uniq[u]];
   }
-  // packed row of the block's token i (past the last token: the last one)
+  const int mcnt = min(kThinTokens, cnt - tok0);
+  // packed row of the tile's token i (past the last token: the last one)
   auto row_of = [&](int i) -> uint32_t {
-    const int ti = min(i, cnt - 1);
+    const int ti = min(tok0 + i, cnt - 1);
     if (L.single) return (uint32_t)ti;
     const int slot = L.list[off + ti];
     return (uint32_t)(MODE == kGateUp ? slot / L.kdiv : slot);
@@ -580,28 +636,35 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const int wv = blockIdx.x * GW + wave;
   const bool active = wv < nwaves;
   const int wc = min(wv, nwaves - 1);
-  const size_t fd = (size_t)f * d;
-  const _Float16* sbase = reinterpret_cast<const _Float16*>(blob + 3 * (fd / 2));
+  const size_t mat_codes = (size_t)f * d * BITS / 8;
+  const _Float16* sbase = reinterpret_cast<const _Float16*>(blob + 3 * mat_codes);
   const size_t gate_sc = (size_t)f * srow(d, pr);
   const uint8_t *c0, *c1;
   const _Float16 *s0, *s1;
   if (MODE == kGateUp) {
-    c0 = blob + (size_t)(kHalf * wc) * (K / 2);
-    c1 = c0 + fd / 2;
+    c0 = blob + (size_t)(kHalf * wc) * row_bytes;
+    c1 = c0 + mat_codes;
     s0 = sbase + (size_t)(kHalf * wc) * ng;
     s1 = s0 + gate_sc;
   } else {
-    c0 = blob + fd + (size_t)(kThinWaveRows * wc) * (K / 2);
-    c1 = c0 + (size_t)kHalf * (K / 2);
+    c0 = blob + 2 * mat_codes + (size_t)(kThinWaveRows * wc) * row_bytes;
+    c1 = c0 + (size_t)kHalf * row_bytes;
     s0 = sbase + 2 * gate_sc + (size_t)(kThinWaveRows * wc) * ng;
     s1 = s0 + (size_t)kHalf * ng;
   }
   const int n = lane & 15, kg = lane >> 4;
 
-  // ---- per-lane copy sources (codes and activations as in k_gemm)
-  const uint32_t b_piece = (uint32_t)((lane & 3) ^ ((lane >> 3) & 3) ^ ((lane >> 5) & 1));
-  const uint32_t b_off = (uint32_t)(lane >> 2) * (uint32_t)(K / 2) + b_piece * 16u;
-  const bool a_copy = wave < 4 && 4 * wave < cnt;  // wave-uniform
+  // ---- per-lane copy sources.  Codes, copy i: lane l -> wave row
+  // r = kRowsPerCopy i + l / kPieces, LDS slot l % kPieces (holding piece
+  // slot ^ swizzle); rows 0..15 come from c0, 16..31 from c1.
+  const uint8_t* b_src[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int r = kRowsPerCopy * i + lane / kPieces;
+    const int piece = thin_slot<BITS>(lane % kPieces, r);
+    b_src[i] = (r < kHalf ? c0 : c1) + (size_t)(r % kHalf) * row_bytes + piece * 16;
+  }
+  const bool a_copy = wave < 4 && 4 * wave < mcnt;  // wave-uniform
   const int a_row = 4 * (wave & 3) + (lane >> 4);
   const uint32_t a_off = row_of(a_row) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
   // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1)
@@ -623,9 +686,9 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const int nst = K / kSC;
   auto issue = [&](int st) {
     uint8_t* base = s_lds + (st % R) * kStage;
-    const uint32_t so = (uint32_t)st * (kSC / 2);
-    dma16(c0 + b_off + so, base + wave * kBWave);
-    dma16(c1 + b_off + so, base + wave * kBWave + 1024);
+    const uint32_t so = (uint32_t)st * kRowStage;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) dma16(b_src[i] + so, base + wave * kBWave + i * 1024);
     if (a_copy) dma16(g.a + a_off + st * kSC, base + kStageB + 4 * wave * (kSC * 2));
     // the correction copy fills 32 x 4 bytes: lanes 32..63 stay out of it
     if (wave == 0 && lane < 32) dma4(c_lane + 2 * st, base + kStageB + kStageA);
@@ -649,20 +712,33 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = 16 * nt + n;
-      const int slot = (2 * gg + (kg >> 1)) ^ ((r >> 1) & 3) ^ ((r >> 3) & 1);
-      const uint2 w = *reinterpret_cast<const uint2*>(base + wave * kBWave + r * (kSC / 2) +
-                                                      slot * 16 + 8 * (kg & 1));
-      f32x4 pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, raw8(w.x), c4, 0, 0, 0);
-      pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, raw8(w.y), pg, 0, 0, 0);
+      const uint8_t* row = base + wave * kBWave + r * kRowStage;
+      f16x8 b0, b1;
+      if constexpr (BITS == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(
+            row + thin_slot<4>(2 * gg + (kg >> 1), r) * 16 + 8 * (kg & 1));
+        b0 = raw8(w.x);
+        b1 = raw8(w.y);
+      } else if constexpr (BITS == 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + thin_slot<8>(4 * gg + kg, r) * 16);
+        b0 = raw8_i8(w.x, w.y);
+        b1 = raw8_i8(w.z, w.w);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + thin_slot<2>(gg, r) * 16 + 4 * kg);
+        b0 = raw8_i2(w, 0);
+        b1 = raw8_i2(w, 1);
+      }
+      f32x4 pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, c4, 0, 0, 0);
+      pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, pg, 0, 0, 0);
       const float sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sv, pg[i], acc[nt][i]);
     }
   };
 
-  // copies a wave issues per stage besides its scale pieces: 2 of codes, 1 of
-  // activations (waves 0..3 with tokens), 1 of corrections (wave 0)
-  const int per_stage = 2 + (a_copy ? 1 : 0) + (wave == 0 ? 1 : 0);
+  // copies a wave issues per stage besides its scale pieces: kCopies of
+  // codes, 1 of activations (waves 0..3 with tokens), 1 of corrections (wave 0)
+  const int extra = (a_copy ? 1 : 0) + (wave == 0 ? 1 : 0);
 #pragma unroll
   for (int i = 0; i < R - 1; ++i)
     if (i < nst) issue(i);
@@ -672,13 +748,13 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
       if (pr) {
-        if (per_stage == 2) wait_vm_lgkm0<copies_ahead<R, PH, 2, 0, 0>()>();
-        else if (per_stage == 3) wait_vm_lgkm0<copies_ahead<R, PH, 3, 0, 0>()>();
-        else wait_vm_lgkm0<copies_ahead<R, PH, 4, 0, 0>()>();
+        if (extra == 0) wait_vm_lgkm0<copies_ahead<R, PH, kCopies, 0, 0>()>();
+        else if (extra == 1) wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 1, 0, 0>()>();
+        else wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 2, 0, 0>()>();
       } else {
-        if (per_stage == 2) wait_vm_lgkm0<copies_ahead<R, PH, 2, 0, 1>()>();
-        else if (per_stage == 3) wait_vm_lgkm0<copies_ahead<R, PH, 3, 0, 1>()>();
-        else wait_vm_lgkm0<copies_ahead<R, PH, 4, 0, 1>()>();
+        if (extra == 0) wait_vm_lgkm0<copies_ahead<R, PH, kCopies, 0, 1>()>();
+        else if (extra == 1) wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 1, 0, 1>()>();
+        else wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 2, 0, 1>()>();
       }
     } else {
       wait_vm_lgkm0<0>();
@@ -701,12 +777,12 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   }
   if (!active) return;
 
-  // epilogue: lane (n, kg) holds tokens 4 kg + i for weight rows 16 nt + n;
+  // epilogue: lane (n, kg) holds tile tokens 4 kg + i for weight rows 16 nt + n;
   // the partials were in units of 2^-24
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ti = 4 * kg + i;
-    if (ti >= cnt) continue;
+    if (4 * kg + i >= mcnt) continue;
+    const int ti = tok0 + 4 * kg + i;
     const int slot = L.single ? ti : L.list[off + ti];
     if (MODE == kGateUp) {
       const int xr = L.single ? ti : slot / L.kdiv;
@@ -722,10 +798,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   }
 }
 
-template <int MODE, int GW, int R>
+template <int MODE, int GW, int R, int BITS>
 __global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R>::kLdsBytes];
-  thin_body<MODE, GW, R>(g, s_lds, blockIdx.y);
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS>::kLdsBytes];
+  thin_body<MODE, GW, R, BITS>(g, s_lds, blockIdx.y);
 }
 
 // One launch for a batch's whole union: blocks with y < g.thick_blocks run
@@ -738,10 +814,10 @@ constexpr int kMixedThinRing = 3;
 template <int MODE>
 __global__ __launch_bounds__(1024) void k_gemm_mixed(GemmArgs g) {
   constexpr int kA = RingShape<16, 3, 64, 2>::kLdsBytes;
-  constexpr int kB = ThinShape<16, kMixedThinRing>::kLdsBytes;
+  constexpr int kB = ThinShape<16, kMixedThinRing, 4>::kLdsBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kA > kB ? kA : kB];
   if ((int)blockIdx.y < g.thick_blocks) gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, blockIdx.y);
-  else thin_body<MODE, 16, kMixedThinRing>(g, s_lds, blockIdx.y - g.thick_blocks);
+  else thin_body<MODE, 16, kMixedThinRing, 4>(g, s_lds, blockIdx.y - g.thick_blocks);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -768,6 +844,10 @@ bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 constexpr int kThinGW = 4;
 constexpr int kThinRing = 4;
 
+// The offset that makes a code of this width non-negative (its value plus
+// the offset is the field with the sign bit flipped).
+static float corr_offset(int bits) { return bits == 8 ? 128.0f : bits == 2 ? 2.0f : 8.0f; }
+
 PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   const ExpertList& L = m.L;
   PackArgs px{};
@@ -779,6 +859,8 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   px.dst = m.xh;
   px.unit = m.xunit;
   px.corr = m.xcorr;
+  px.corr_off = corr_offset(L.bits);
+  px.thin_all = L.bits != 4;
   if (!L.single) {
     px.offsets = L.offsets;
     px.n_uniq = L.n_uniq;
@@ -791,10 +873,17 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   return px;
 }
 
-// A projection: batches of at most kThinTokens rows (every expert thin) and a
-// single expert of that many run the thin GEMM alone; a single larger expert
-// the M-blocked GEMM; larger batches the mixed launch (M-blocked blocks for
-// the experts past kThinTokens tokens, then thin blocks for the others).
+// A projection.  int4: batches of at most kThinTokens rows (every expert
+// thin) and a single expert of that many run the thin GEMM alone; a single
+// larger expert the M-blocked GEMM; larger batches the mixed launch
+// (M-blocked blocks for the experts past kThinTokens tokens, then thin blocks
+// for the others).  int8 and int2: the thin GEMM over every M-tile of 16
+// tokens of every expert.
+template <int MODE, int BITS, int R>
+static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, hipStream_t s, const GemmArgs& ga) {
+  return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
+}
+
 template <int MODE>
 static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
   const ExpertList& L = m.L;
@@ -804,16 +893,18 @@ static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
   const int N = MODE == kGateUp ? m.f : m.d;  // weight rows (gate/up: gate rows; up alike)
   const int wrows = MODE == kGateUp ? 16 : 32;  // of N a wave covers
   const int nw = N / wrows;
-  if (rows <= kThinTokens) {
-    const dim3 grid((unsigned)((nw + kThinGW - 1) / kThinGW), L.single ? 1u : (unsigned)m.thin_bound);
-    return launch(kid_thin, k_gemm_thin<MODE, kThinGW, kThinRing>, grid, dim3(64 * kThinGW), s, ga);
-  }
+  const unsigned gx = (unsigned)((nw + kThinGW - 1) / kThinGW);
+  const unsigned gy = L.single ? (unsigned)((L.single_n + kThinTokens - 1) / kThinTokens)
+                               : (unsigned)m.thin_bound;
+  if (L.bits == 8) return thin_launch<MODE, 8, 3>(kid_thin, gx, gy, s, ga);
+  if (L.bits == 2) return thin_launch<MODE, 2, 4>(kid_thin, gx, gy, s, ga);
+  if (rows <= kThinTokens) return thin_launch<MODE, 4, kThinRing>(kid_thin, gx, gy, s, ga);
   if (L.single) {
     const GemmShape sh = gemm_shape(rows, true);
     const unsigned mb = (unsigned)((L.single_n + sh.mblock - 1) / sh.mblock);
-    const unsigned gx = (unsigned)((nw + sh.gw - 1) / sh.gw);
-    if (sh.gw == 4) return launch(kid, k_gemm<MODE, 4, 3, 64, 2>, dim3(gx, mb), dim3(256), s, ga);
-    return launch(kid, k_gemm<MODE, 16, 3, 64, 2>, dim3(gx, mb), dim3(1024), s, ga);
+    const unsigned gxs = (unsigned)((nw + sh.gw - 1) / sh.gw);
+    if (sh.gw == 4) return launch(kid, k_gemm<MODE, 4, 3, 64, 2>, dim3(gxs, mb), dim3(256), s, ga);
+    return launch(kid, k_gemm<MODE, 16, 3, 64, 2>, dim3(gxs, mb), dim3(1024), s, ga);
   }
   ga.thick_blocks = m.mb_bound;
   const dim3 grid((unsigned)((nw + 15) / 16), (unsigned)(m.mb_bound + m.thin_bound));
@@ -841,6 +932,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   pa.dst = m.ah;
   pa.unit = m.aunit;
   pa.corr = m.acorr;
+  pa.corr_off = corr_offset(L.bits);
   e = launch(MOE_KERNEL_DIGITIZE, k_pack, dim3((unsigned)((m.slots + 3) / 4)), dim3(256), s, pa);
   if (e != hipSuccess) return e;
 

@@ -56,7 +56,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.mbo = take((cap + 1) * sizeof(int32_t));
   L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
   L.mbot = take((cap + 1) * sizeof(int32_t));
-  L.blkt = take(cap * sizeof(int32_t));
+  L.blkt = take((cap + Tk / kThinTokens + 1) * sizeof(int32_t));
   L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
@@ -79,6 +79,9 @@ int dims_status(const moe_dims* dm) {
   if (dm->group_size != kGroup && dm->group_size != 0) return MOE_EUNSUPPORTED;
   if (dm->d % kGroup || dm->f % kGroup || dm->d > 65536 || dm->f > 65536) return MOE_EUNSUPPORTED;
   if (dm->n_experts > 1024 || dm->top_k > 32) return MOE_EUNSUPPORTED;
+  const int bits = code_bits(dm->code_bits);
+  if (bits != 4 && bits != 8 && bits != 2) return MOE_EUNSUPPORTED;
+  if (bits != 4 && !mfma_shape_ok(dm->d, dm->f)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -154,7 +157,8 @@ MOE_API size_t moe_expert_blob_bytes(const moe_dims* dm) {
   if (dims_status(dm) != MOE_OK) return 0;
   const size_t fd = (size_t)dm->f * dm->d;
   const int pr = dm->group_size == 0;
-  return 3 * fd / 2 + 2 * (2 * (size_t)dm->f * srow(dm->d, pr) + (size_t)dm->d * srow(dm->f, pr));
+  return 3 * fd * code_bits(dm->code_bits) / 8 +
+         2 * (2 * (size_t)dm->f * srow(dm->d, pr) + (size_t)dm->d * srow(dm->f, pr));
 }
 
 MOE_API size_t moe_workspace_bytes(const moe_dims* dm, int32_t T_max) {
@@ -253,7 +257,10 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   EL.single_n = n;
   EL.kdiv = 1;
   EL.per_row = dm->group_size == 0;
-  if (n >= kMfmaMinTokens && mfma_shape_ok(dm->d, dm->f)) {
+  EL.bits = code_bits(dm->code_bits);
+  // int8 and int2 experts take the matrix cores for any n (dims_status has
+  // checked the shape)
+  if ((n >= kMfmaMinTokens || EL.bits != 4) && mfma_shape_ok(dm->d, dm->f)) {
     MfmaArgs m = mfma_args(ws, L, dm->d, dm->f);
     m.L = EL;
     m.x = x;
@@ -312,9 +319,13 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.list = rows;
   EL.kdiv = k;
   EL.per_row = dm->group_size == 0;
+  EL.bits = code_bits(dm->code_bits);
   const int maxU = E < T * k ? E : T * k;
 
-  if (invariant || gemv_small_path(T, k, d, f)) {
+  // int8 and int2 layers run every batch on the thin grouped GEMM (16-token
+  // tiles), whose per-token arithmetic does not depend on the batch, so the
+  // batch-invariant flag needs no separate path for them
+  if (EL.bits == 4 && (invariant || gemv_small_path(T, k, d, f))) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (one token: in
     // every gate/up block's prologue; 2+: one k_route_small block) and
     // gate/up; 3: down + combine.  Every step keeps one order of
@@ -409,7 +420,9 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     // them, each with ceil(count / 64) < count / 64 + 1 M-blocks
     const int nthick = T * k / (kThinTokens + 1) < maxU ? T * k / (kThinTokens + 1) : maxU;
     m.mb_bound = (T * k + mfma_mblock(T) - 1) / mfma_mblock(T) + nthick;
-    m.thin_bound = maxU;
+    // int4: one thin block per thin expert; int8 / int2: one per 16 tokens of
+    // every expert (ceil(count / 16) < count / 16 + 1)
+    m.thin_bound = EL.bits == 4 ? maxU : maxU + (T * k + kThinTokens - 1) / kThinTokens;
     m.y = y;
     m.x_packed = x_packed;
     MOE_TRY(launch_ffn_mfma(m, s));
@@ -441,6 +454,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
   const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
   if (!small_batch(T, k)) return MOE_EUNSUPPORTED;
+  if (code_bits(dm->code_bits) != 4) return MOE_EUNSUPPORTED;  // the cache serves int4 layers
   const int cap = E < T * k ? E : T * k;
   if (n_slots < cap || n_slots > E) return MOE_EUNSUPPORTED;
   const Layout L = layout(d, f, E, k, T);
@@ -511,6 +525,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   EL.list = rows;
   EL.kdiv = k;
   EL.per_row = dm->group_size == 0;
+  EL.bits = 4;
   MOE_TRY(launch_gateup(EL, nullptr, cap, d, f, xd, ad, 1, T, s));
   CombineArgs cb{w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out, T, k};
   MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));

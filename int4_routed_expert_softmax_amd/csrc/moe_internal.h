@@ -61,7 +61,11 @@ struct ExpertList {
   const int32_t* list;
   int kdiv;
   int per_row;  // blobs carry one scale per row (else one per kGroup weights)
+  int bits;     // code width: 4, 8 or 2
 };
+
+// Code width of a layer: dims.code_bits, 0 meaning int4.
+inline int code_bits(int b) { return b == 0 ? 4 : b; }
 
 // Scales of one row of K weights in a blob: K / kGroup, or 1 with per-row
 // scales.  A blob's scales follow its codes: gate [f][srow(d)], up
@@ -104,7 +108,9 @@ struct PackArgs {
   const int32_t* gather;  // source row of row r (nullptr: r)
   _Float16* dst;          // [rows][K]
   float* unit;            // [rows]
-  float* corr;            // [rows][K / 64]: -8 * 2^-24 * (sum of the group's packed values)
+  float* corr;            // [rows][K / 64]: -corr_off * 2^-24 * (sum of the group's packed values)
+  float corr_off;         // the code width's offset: 8 (int4), 128 (int8), 2 (int2)
+  int thin_all;           // map every expert onto thin blocks (int8 and int2 layers)
   const int32_t* offsets;
   const int32_t* n_uniq;
   // with mbo set: experts of at most kThinTokens tokens get one thin block

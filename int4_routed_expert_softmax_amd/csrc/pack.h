@@ -40,8 +40,9 @@ __device__ __forceinline__ void load8(const void* src, int bf16, size_t i, float
 }
 
 // The thin grouped GEMM feeds the codes to the matrix cores as the fp16
-// subnormals (q + 8) * 2^-24 and starts each 64-column group's partial sum at
-// -8 * 2^-24 * (sum of the group's packed values), which makes the partial
+// subnormals (q + o) * 2^-24 (o = corr_off: 8 for int4) and starts each
+// 64-column group's partial sum at -o * 2^-24 * (sum of the group's packed
+// values), which makes the partial
 // 2^-24 * sum of q * x'.  corr_of8 sums a lane's 8 packed values (as stored),
 // the 8 lanes of a 64-column group add theirs with a DPP butterfly (quad
 // swaps, then the half-row mirror pairs the two quads), and the group's first
@@ -57,7 +58,7 @@ __device__ __forceinline__ void store_corr(const PackArgs& p, int r, int c, floa
   s += dpp<kDppXor1>(s);
   s += dpp<kDppXor2>(s);
   s += dpp<kDppHalfMirror>(s);
-  if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = -8.0f * 0x1p-24f * s;
+  if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = -p.corr_off * 0x1p-24f * s;
 }
 
 // Rows of up to kPackRegCols columns are read once into registers (every
@@ -136,8 +137,9 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
 }
 
 // M-block maps of a union of at most 64 experts (offs[0..U]), by one whole
-// wave: experts of at most kThinTokens tokens are listed in blk_t (mbo_t[u] =
-// thin experts before u, mbo_t[U] their number); each other expert gets
+// wave: experts of at most kThinTokens tokens (every expert with thin_all)
+// get one thin block per kThinTokens tokens, listed in blk_t (mbo_t[u] = thin
+// blocks before u, mbo_t[U] their number); each other expert gets
 // ceil(count / mblock) M-blocks (mbo[u] = M-blocks before u, mbo[U] the total,
 // blk_u[j] = the expert of M-block j).
 __device__ __forceinline__ int wave_excl_scan(int c, int lane, int& total) {
@@ -152,18 +154,19 @@ __device__ __forceinline__ int wave_excl_scan(int c, int lane, int& total) {
 }
 __device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int mblock,
                                                 int32_t* mbo, int32_t* blk_u, int32_t* mbo_t,
-                                                int32_t* blk_t, int lane) {
+                                                int32_t* blk_t, int thin_all, int lane) {
   const int n = lane < U ? offs[lane + 1] - offs[lane] : 0;
-  const bool thin = lane < U && n <= kThinTokens;
+  const bool thin = lane < U && (thin_all || n <= kThinTokens);
   const int c = lane < U && !thin ? (n + mblock - 1) / mblock : 0;
+  const int ct = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
   int tot, tot_t;
   const int run = wave_excl_scan(c, lane, tot);
-  const int run_t = wave_excl_scan(thin ? 1 : 0, lane, tot_t);
+  const int run_t = wave_excl_scan(ct, lane, tot_t);
   if (lane < U) {
     mbo[lane] = run;
     mbo_t[lane] = run_t;
     for (int j = 0; j < c; ++j) blk_u[run + j] = lane;
-    if (thin) blk_t[run_t] = lane;
+    for (int j = 0; j < ct; ++j) blk_t[run_t + j] = lane;
   }
   if (lane == 0) {
     mbo[U] = tot;

@@ -34,7 +34,8 @@ class DeviceLayer:
             bias = None
         self.Wr, self.bias = Wr, bias
         self.blobs = configs.experts(w, layer) if blobs is None else blobs
-        self.dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group)
+        self.dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group,
+                             code_bits=w.bits)
         self.Wr_d = torch.from_numpy(np.ascontiguousarray(Wr)).to(DEV)
         self.bias_d = None if bias is None else torch.from_numpy(bias).to(DEV)
         self.blobs_d = torch.from_numpy(self.blobs).to(DEV)

@@ -36,9 +36,12 @@ def test_per_launch_bytes_and_source_hashes():
     import bench
     from synth import configs
     for name in ("decode1", "verify8", "prefill512", "chain48", "decode1_perrow",
-                 "verify8_perrow", "prefill512_perrow"):
+                 "verify8_perrow", "prefill512_perrow", "decode1_int8", "verify8_int8",
+                 "prefill512_int8", "decode1_int2", "verify8_int2", "prefill512_int2"):
         w = configs.WORKLOADS[name]
         gu, dn = bench.matrix_bytes(w)
         assert gu + dn == w.blob_bytes
         assert len(bench.kernel_source_hash(name)) == 16
     assert bench.matrix_bytes(configs.WORKLOADS["decode1"]) == (13369344, 6684672)
+    assert bench.matrix_bytes(configs.WORKLOADS["decode1_int8"]) == (2 * (12582912 + 393216),
+                                                                     12582912 + 393216)

@@ -126,7 +126,7 @@ def run_sequence(L: DeviceLayer, cache: Cache, steps, T, flags, bf16=False, in_p
         xc = xd.clone()
         out, st = cache.forward(xc, flags, out=xc if in_place else None)
         orc = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k,
-                                   x_bf16=bf, flags=flags, group=w.group)
+                                   x_bf16=bf, flags=flags, group=w.group, bits=w.bits)
         check_layer_routing(L.dims, cache.last_ws, T, orc, f"{w.name} cached step {step}")
         assert_close(out.cpu().numpy(), orc["out"], f"{w.name} cached step {step}",
                      case=f"{w.name} cached T={T} S={cache.S} flags={flags}")

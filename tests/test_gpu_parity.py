@@ -28,9 +28,9 @@ pytestmark = pytest.mark.gpu
 W = configs.WORKLOADS
 
 
-def small(name, d, f, E, k, T, zipf=True, seed=7, x_kind="normal", group=64):
+def small(name, d, f, E, k, T, zipf=True, seed=7, x_kind="normal", group=64, bits=4):
     return configs.Workload(name, d=d, f=f, n_experts=E, top_k=k, T=T, seed=seed, zipf=zipf,
-                            x_kind=x_kind, group=group)
+                            x_kind=x_kind, group=group, bits=bits)
 
 
 def full_parity(w: configs.Workload, flags=0, layer=None):
@@ -39,7 +39,7 @@ def full_parity(w: configs.Workload, flags=0, layer=None):
     x, bf = configs.tokens(w)
     xd = L.x_device(x, bf)
     ref = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=bf,
-                               flags=flags, group=w.group)
+                               flags=flags, group=w.group, bits=w.bits)
     if not flags:
         idx, wts = L.route(xd)
         assert np.array_equal(idx, ref["idx"]), "routing indices differ"
