@@ -136,6 +136,82 @@ __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
   if (lane == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
 }
 
+// Row r of p by nw waves of one workgroup, this wave being wave `part` of them
+// (r < 0: no row; the wave still reaches the barrier).  It takes the
+// 512-column chunks part, part + nw, ... and holds up to kSplitRegChunks of
+// them in registers (more are read twice: for the maximum, then to convert).
+// The row's maximum is combined through s_m, one float per wave of the
+// workgroup with the row's nw waves consecutive and this one at s_m[slot],
+// after a workgroup barrier that every wave of the workgroup must reach.  A
+// maximum does not depend on the order it is taken in, and each 64-column
+// group's correction lies inside one chunk, so every value written is the one
+// pack_row writes.  Holding a sixth of a 6144-column row per wave keeps the
+// register count (and so the workgroups a compute unit holds at once) of the
+// kernels that pack rows this way at that of their other work.
+constexpr int kSplitRegChunks = 6;
+__device__ __forceinline__ void pack_row_split(const PackArgs& p, int r, int part, int nw,
+                                               float* s_m, int slot, int lane) {
+  const int nch = (p.K + 511) / 512;
+  const int mine = r < 0 ? 0 : (nch - part + nw - 1) / nw;  // chunks part + nw j < nch
+  const bool regs = mine <= kSplitRegChunks;
+  const size_t base = r < 0 ? 0 : (p.gather ? (size_t)p.gather[r] : (size_t)r) * p.K;
+  float v[kSplitRegChunks][8];
+  float m = 0.0f;
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < kSplitRegChunks; ++j) {
+      const int c = ((part + nw * j) * 64 + lane) * 8;
+      if (j < mine && c < p.K) {
+        load8(p.src, p.src_bf16, base + c, v[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+      }
+    }
+  } else {
+    for (int j = 0; j < mine; ++j) {
+      const int c = ((part + nw * j) * 64 + lane) * 8;
+      if (c < p.K) {
+        float t[8];
+        load8(p.src, p.src_bf16, base + c, t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(t[i]));
+      }
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) s_m[slot] = m;
+  __syncthreads();
+  if (r < 0) return;
+  m = s_m[slot - part];
+  for (int q = 1; q < nw; ++q) m = fmaxf(m, s_m[slot - part + q]);
+  int e = 0;
+  if (m > 0.0f) frexpf(m, &e);  // m < 2^e
+  const float up = m > 0.0f ? ldexpf(1.0f, kPackExp - e) : 1.0f;
+  _Float16* drow = p.dst + (size_t)r * p.K;
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < kSplitRegChunks; ++j) {
+      const int ch = part + nw * j, c = (ch * 64 + lane) * 8;
+      if (j < mine) {
+        if (c < p.K) store8(drow, c, v[j], up);
+        // K is a multiple of 512 where corrections are asked for
+        if (p.corr) store_corr(p, r, c, corr_of8(v[j], up), lane);
+      }
+    }
+  } else {
+    for (int j = 0; j < mine; ++j) {
+      const int c = ((part + nw * j) * 64 + lane) * 8;
+      float t[8] = {};
+      if (c < p.K) {
+        load8(p.src, p.src_bf16, base + c, t);
+        store8(drow, c, t, up);
+      }
+      if (p.corr) store_corr(p, r, c, corr_of8(t, up), lane);
+    }
+  }
+  if (lane == 0 && part == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
+}
+
 // M-block maps of a union of at most 64 experts (offs[0..U]), by one whole
 // wave: experts of at most kThinTokens tokens (every expert with thin_all)
 // get one thin block per kThinTokens tokens, listed in blk_t (mbo_t[u] = thin

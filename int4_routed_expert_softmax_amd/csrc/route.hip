@@ -254,19 +254,29 @@ __device__ __forceinline__ double sum_waves(const double (&p)[kRFW]) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
+// Waves per row of the x pack: all 8 of a workgroup for one row, 4 for two,
+// else 2 (a sixth of a 6144-column row each, in registers).
+__host__ __device__ inline int rf_pack_waves(int rows) { return rows <= 1 ? 8 : rows <= 2 ? 4 : 2; }
+__host__ __device__ inline int rf_pack_blocks(int rows) {
+  const int rpb = kRFW / rf_pack_waves(rows);
+  return (rows + rpb - 1) / rpb;
+}
+
 template <int TB>
 __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, d = a.d, E = a.E;
-  // the last (rows + kRFW - 1) / kRFW workgroups pack the rows for the
-  // grouped GEMM, one wave per row, alongside the logits
-  const int pack_blocks = a.px.dst ? (a.px.rows + kRFW - 1) / kRFW : 0;
+  // the last rf_pack_blocks workgroups pack the rows for the grouped GEMM,
+  // alongside the logits, each row by rf_pack_waves waves
+  const int pack_blocks = a.px.dst ? rf_pack_blocks(a.px.rows) : 0;
   if (pack_blocks) {
     const int pb = (int)gridDim.x - pack_blocks;
     if (e >= pb) {
-      const int r = (e - pb) * kRFW + wave;
-      if (r < a.px.rows) pack_row(a.px, r, lane);
+      __shared__ float s_m[kRFW];
+      const int nw = rf_pack_waves(a.px.rows);
+      const int r = (e - pb) * (kRFW / nw) + wave / nw;
+      pack_row_split(a.px, r < a.px.rows ? r : -1, wave % nw, nw, s_m, wave, lane);
       return;
     }
   }
@@ -458,7 +468,7 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 hipError_t launch_router_front(const RouterArgs& a, hipStream_t s) {
   const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + kRFW - 1) / kRFW : 0;
   if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1)) return hipErrorInvalidValue;
-  const int pack_blocks = a.px.dst ? (a.px.rows + kRFW - 1) / kRFW : 0;
+  const int pack_blocks = a.px.dst ? rf_pack_blocks(a.px.rows) : 0;
   const dim3 grid(a.E + dig_blocks + pack_blocks);
   if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(kRF), s, a);
   if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(kRF), s, a);
