@@ -281,8 +281,11 @@ size_t moe_cache_state_bytes(const moe_dims* dims, int32_t n_slots);
  * workgroup (experts of the union found in a slot keep it and count as hits;
  * each other one, in ascending id, takes the least recently used slot not
  * used by this call, ties to the lower slot, and evicts its expert); the
- * missed blobs are copied from home into their slots; the expert kernels
- * read every union expert from its slot.  The batch runs the single-token
+ * missed blobs are copied from home into their slots by the first workgroups
+ * of a launch whose other workgroups run the gate/up of the hits, so the
+ * hits compute while the misses are in flight; the misses' gate/up follows
+ * once their copies have landed, then down + combine over the whole union,
+ * every expert read from its slot.  The batch runs the single-token
  * kernel family, so out (and stats) are bit-identical to moe_layer_forward
  * with MOE_BATCH_INVARIANT (for one token: with any flags) and the blobs
  * resident, for any cache contents: where an expert's bytes come from

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(1024) void k_cache_place(CacheArgs a) {
     const uint8_t* p = a.slots + (size_t)sl * a.blob_bytes;
     a.eff[a.uniq[t]] = p;
     a.plan[t].blob = p;
+    a.hit[t] = s_slot[t] >= 0 ? 1 : 0;
   }
   if (t == 0) {
     hdr->clock = clock;
@@ -94,28 +95,12 @@ __global__ __launch_bounds__(1024) void k_cache_place(CacheArgs a) {
   }
 }
 
-// Copies blob m (m < *n_fill) from its home into its slot: grid.x blocks
-// share a blob, 16 bytes per load, four loads in flight per thread.
+// Copies blob m = blockIdx.y (m < *n_fill) from its home into its slot,
+// grid.x blocks sharing a blob.
 constexpr int kFillBlocks = 512;
 
 __global__ __launch_bounds__(256) void k_cache_fill(CacheArgs a) {
-  const int m = blockIdx.y;
-  if (m >= *a.n_fill) return;
-  const uint4* src = reinterpret_cast<const uint4*>(a.fill_src[m]);
-  uint4* dst = reinterpret_cast<uint4*>(a.fill_dst[m]);
-  const size_t n16 = a.blob_bytes / 16;
-  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
-  const size_t beg = (size_t)blockIdx.x * per;
-  const size_t end = beg + per < n16 ? beg + per : n16;
-  for (size_t i = beg + threadIdx.x; i < end; i += 4 * 256) {
-    uint4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + (size_t)j * 256 < end) v[j] = src[i + (size_t)j * 256];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (i + (size_t)j * 256 < end) dst[i + (size_t)j * 256] = v[j];
-  }
+  fill_part(a.fill_src, a.fill_dst, a.n_fill, a.blob_bytes, blockIdx.y, blockIdx.x, gridDim.x);
 }
 
 hipError_t launch_cache_place(const CacheArgs& a, hipStream_t s) {

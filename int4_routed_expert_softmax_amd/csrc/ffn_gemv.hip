@@ -26,6 +26,7 @@
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "cache.h"
 #include "pack.h"
 #include "small_route.h"
 #include "select.h"
@@ -185,25 +186,33 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t*
 // has 4 row streams x C column slices of 64 chunks (d = 6144: 192 chunks,
 // C = 3, 12 waves).  SMALL: the block first recomputes top-k and the union
 // from the logits in ro.z; block (0, 0) publishes them.
+// Block coordinates (row block rb < nx, union position u < ny, token group
+// grp < G) of flat block index F (x fastest).  With several token groups, the
+// groups of one (row block, expert) pair go to one XCD, dispatched back to
+// back: blocks go to the 8 XCDs in turn, so F maps to pair 8 (F / 8 / G) +
+// F % 8, group (F / 8) % G, and the groups' re-reads of the pair's rows meet
+// in that XCD's L2.
+__device__ __forceinline__ void gateup_coords(int F, int nx, int ny, int G, int& rb, int& u,
+                                              int& grp) {
+  if (G > 1 && (nx * ny) % 8 == 0) {
+    const int hi = F >> 3, pair = (hi / G) * 8 + (F & 7);
+    grp = hi % G;
+    rb = pair % nx;
+    u = pair / nx;
+  } else {
+    rb = F % nx;
+    u = (F / nx) % ny;
+    grp = F / (nx * ny);
+  }
+}
+
 template <int C, bool SMALL, int NT>
-__global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, int d, int f,
-                                                    Digits xd, Digits ad) {
+__device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut& ro, int d, int f,
+                                             const Digits& xd, const Digits& ad, int rb, int u,
+                                             int grp, int G) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay scalar
   const int stream = wave / C, slice = wave % C;
-  int u = blockIdx.y, rb = blockIdx.x, grp = blockIdx.z;
-  const int G = gridDim.z, npairs = gridDim.x * gridDim.y;
-  if (G > 1 && npairs % 8 == 0) {
-    // token groups of one (row block, expert) pair on one XCD, dispatched
-    // back to back: blocks go to the 8 XCDs in turn, so flat index F maps to
-    // pair 8 (F / 8 / G) + F % 8, group (F / 8) % G, and the groups' re-reads
-    // of the pair's rows meet in that XCD's L2
-    const int F = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int hi = F >> 3, pair = (hi / G) * 8 + (F & 7);
-    grp = hi % G;
-    rb = pair % gridDim.x;
-    u = pair / gridDim.x;
-  }
   __shared__ float s_g[NT][kRowsPerBlock][C], s_u[NT][kRowsPerBlock][C];
   ExpertRef ex;
   const int32_t* list;
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     kdiv = k;
   } else {
     if (!L.single && u >= *L.n_uniq) return;
+    if (L.hit && L.hit[u] != L.want_hit) return;
     ex = expert_ref(L, u);
     list = L.single ? nullptr : L.list;
     kdiv = L.kdiv;
@@ -265,6 +275,36 @@ __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, i
     }
     __syncthreads();
   }
+}
+
+template <int C, bool SMALL, int NT>
+__global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, int d, int f,
+                                                    Digits xd, Digits ad) {
+  const int F = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  int rb, u, grp;
+  gateup_coords(F, gridDim.x, gridDim.y, gridDim.z, rb, u, grp);
+  gateup_block<C, SMALL, NT>(L, ro, d, f, xd, ad, rb, u, grp, gridDim.z);
+}
+
+// The slot cache's copies and its hits' gate/up in one launch: the first
+// max_fill * kFillParts blocks copy the missed blobs (dispatched first, so
+// the slow copies start at once), the others run the single-token gate/up of
+// the positions with L.hit[u] == L.want_hit.  kFillParts is a multiple of 8,
+// so a gate/up block keeps the XCD of its flat index.
+constexpr int kFillParts = 128;
+template <int C>
+__global__ __launch_bounds__(256 * C) void k_gateup_fill(ExpertList L, int d, int f, Digits xd,
+                                                         Digits ad, int nx, int ny, int G,
+                                                         int n_fill_blocks, CacheArgs a) {
+  const int F = blockIdx.x;
+  if (F < n_fill_blocks) {
+    fill_part(a.fill_src, a.fill_dst, a.n_fill, a.blob_bytes, F / kFillParts, F % kFillParts,
+              kFillParts);
+    return;
+  }
+  int rb, u, grp;
+  gateup_coords(F - n_fill_blocks, nx, ny, G, rb, u, grp);
+  gateup_block<C, false, 1>(L, RouteOut{}, d, f, xd, ad, rb, u, grp, G);
 }
 
 // Rows [r0, r0 + 16) of the down projection for NT tokens into s_y[j][row].
@@ -573,6 +613,22 @@ hipError_t launch_gateup(const ExpertList& L, const RouteOut* ro, int max_expert
   if (tokens_per_expert_max > 1 && slices(d) < 3)
     return gateup_c<false, 2>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
   return gateup_c<false, 1>(L, RouteOut{}, max_experts, d, f, xd, ad, token_groups, s);
+}
+
+hipError_t launch_gateup_fill(const ExpertList& L, int max_experts, int d, int f, Digits xd,
+                              Digits ad, int token_groups, const CacheArgs& a, int max_fill,
+                              hipStream_t s) {
+  if (token_groups < 1 || max_fill < 1 || max_experts < 1 || a.blob_bytes % 16 || !L.hit)
+    return hipErrorInvalidValue;
+  const int nx = f / kRowsPerBlock, ny = max_experts, G = token_groups;
+  const int nfill = max_fill * kFillParts;
+  const dim3 grid(nfill + nx * ny * G);
+  const int c = slices(d);
+  if (c == 1)
+    return launch(5, k_gateup_fill<1>, grid, dim3(256), s, L, d, f, xd, ad, nx, ny, G, nfill, a);
+  if (c == 2)
+    return launch(5, k_gateup_fill<2>, grid, dim3(512), s, L, d, f, xd, ad, nx, ny, G, nfill, a);
+  return launch(5, k_gateup_fill<3>, grid, dim3(768), s, L, d, f, xd, ad, nx, ny, G, nfill, a);
 }
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,

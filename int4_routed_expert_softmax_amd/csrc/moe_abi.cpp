@@ -88,9 +88,10 @@ int dims_status(const moe_dims* dm) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // The cached layer's table and copy list follow the layout: [E] table
-// pointers, [cap] sources, [cap] destinations, the copy count.
+// pointers, [cap] sources, [cap] destinations, the copy count, [cap] hit flags.
 size_t cache_ws_bytes(int E) {
-  return align_up(8 * (size_t)E) + 2 * align_up(8 * (size_t)kSmallPicks) + align_up(4);
+  return align_up(8 * (size_t)E) + 2 * align_up(8 * (size_t)kSmallPicks) + align_up(4) +
+         align_up(4 * (size_t)kSmallPicks);
 }
 
 // What every entry point requires of ws_bytes: moe_workspace_bytes(dims, T).
@@ -478,6 +479,8 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   uint8_t** fill_dst = at<uint8_t*>(ws, o);
   o += align_up(8 * (size_t)kSmallPicks);
   int32_t* n_fill = at<int32_t>(ws, o);
+  o += align_up(4);
+  int32_t* hit = at<int32_t>(ws, o);
 
   // 1: [RMSNorm], logits, digit split
   RouterArgs ra{};
@@ -513,10 +516,12 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   ca.fill_src = fill_src;
   ca.fill_dst = fill_dst;
   ca.n_fill = n_fill;
+  ca.hit = hit;
   MOE_TRY(launch_cache_place(ca, s));
-  MOE_TRY(launch_cache_fill(ca, cap, s));
   // 5: the single-token kernels on the slots (one gate/up block per row
-  // block, expert and token; each token's arithmetic as in a resident call)
+  // block, expert and token; each token's arithmetic as in a resident call):
+  // the hits' gate/up in one launch with the misses' copies, then the
+  // misses' gate/up, then down + combine over the whole union
   ExpertList EL{};
   EL.table = eff;
   EL.uniq = uniq;
@@ -526,6 +531,10 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   EL.kdiv = k;
   EL.per_row = dm->group_size == 0;
   EL.bits = 4;
+  EL.hit = hit;
+  EL.want_hit = 1;
+  MOE_TRY(launch_gateup_fill(EL, cap, d, f, xd, ad, T, ca, cap, s));
+  EL.want_hit = 0;
   MOE_TRY(launch_gateup(EL, nullptr, cap, d, f, xd, ad, 1, T, s));
   CombineArgs cb{w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out, T, k};
   MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));

@@ -62,6 +62,10 @@ struct ExpertList {
   int kdiv;
   int per_row;  // blobs carry one scale per row (else one per kGroup weights)
   int bits;     // code width: 4, 8 or 2
+  // with hit set: only union positions u with hit[u] == want_hit are computed
+  // (the slot cache's hits, resident before the call, or its misses)
+  const int32_t* hit;
+  int want_hit;
 };
 
 // Code width of a layer: dims.code_bits, 0 meaning int4.
