@@ -126,6 +126,16 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Float sum over each row of 16 lanes in a fixed order (every lane of the row
+// gets it).  All 64 lanes must be active.
+__device__ __forceinline__ float row16_fsum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
 __device__ __forceinline__ int row16_sum(int v) {
   v += dpp_i<kDppXor1>(v);
   v += dpp_i<kDppXor2>(v);

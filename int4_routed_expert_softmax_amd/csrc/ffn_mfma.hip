@@ -159,6 +159,15 @@ struct GemmArgs {
   const int32_t* mbo_t;  // thin union: number of thin experts at [n_uniq]
   const int32_t* blk_t;  // thin union: the j-th thin expert
   int thick_blocks;      // mixed launch: M-blocked blocks before the thin ones
+  // pa: a travels packed by 64-column groups between the thin GEMMs.  Gate/up
+  // then writes a' [slots][f] fp16 in pack order, a_unit and a_corr
+  // [slots][f / 64] (corr_off: the code width's offset) instead of out; down
+  // reads unit as [rows][K / 64] per-group units.
+  int pa;
+  _Float16* a_out;
+  float* a_unit;
+  float* a_corr;
+  float corr_off;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 // a time into two buffers of its own.
 constexpr int kThinWaveRows = 32;
 
-template <int GW, int R, int BITS>
+template <int GW, int R, int BITS, bool PA = false>
 struct ThinShape {
   static constexpr int kRowStage = 16 * BITS;                 // code bytes of a row per stage
   static constexpr int kPieces = kRowStage / 16;              // its 16-byte pieces
@@ -511,11 +520,16 @@ struct ThinShape {
   static constexpr int kBWave = kThinWaveRows * kRowStage;
   static constexpr int kStageB = GW * kBWave;
   static constexpr int kStageA = kThinTokens * kSC * 2;       // 16 rows x 256 B
-  static constexpr int kStageC = 32 * 4;                      // [2 groups][16 tokens] f32
+  // [2 groups][16 tokens] f32 corrections, then (per-group A units) the
+  // same of units
+  static constexpr int kStageC = (PA ? 64 : 32) * 4;
   static constexpr int kStage = kStageB + kStageA + kStageC;
   static constexpr int kScalePiece = kThinWaveRows * 16;      // [32 rows][8 groups] fp16
   static constexpr int kScaleOff = R * kStage;
   static constexpr int kLdsBytes = kScaleOff + GW * 2 * kScalePiece;
+  // the per-group pack of a's reductions ([2][GW][16 tokens] f32) use a ring
+  // slot no wave reads after the last stage
+  static_assert(2 * GW * kThinTokens * 4 <= kStage, "reduction area fits a stage");
   static_assert(BITS == 4 || BITS == 8 || BITS == 2, "code width");
   static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
   // a scale piece is copied R - 1 stages before its first use, which must
@@ -585,9 +599,17 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
                :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
 }
 
-template <int MODE, int GW, int R, int BITS>
+// PA (per-group A): the batch's experts all run the thin GEMM and a travels
+// from gate/up to down packed by 64-column groups: gate/up forms each
+// token's group of a (its 4-wave quad's 64 columns), scales it by a power of
+// two so that the group's max|a| < 2^14, rounds it to fp16 and writes it with
+// the unit and the group correction; down takes the unit per group (beside
+// the corrections, one dword copy per stage) into the group's scale.
+template <int MODE, int GW, int R, int BITS, bool PA = false>
 __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
-  using Shape = ThinShape<GW, R, BITS>;
+  using Shape = ThinShape<GW, R, BITS, PA>;
+  constexpr bool kUnitsA = PA && MODE == kDown;
+  static_assert(!PA || GW % 4 == 0, "a group of a spans 4 waves");
   constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB, kRowStage = Shape::kRowStage;
   constexpr int kPieces = Shape::kPieces, kRowsPerCopy = Shape::kRowsPerCopy;
   constexpr int kCopies = Shape::kCopies;
@@ -667,8 +689,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const bool a_copy = wave < 4 && 4 * wave < mcnt;  // wave-uniform
   const int a_row = 4 * (wave & 3) + (lane >> 4);
   const uint32_t a_off = row_of(a_row) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
-  // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1)
-  const float* c_lane = g.corr + (size_t)row_of(lane & 15) * ngc + ((lane >> 4) & 1);
+  // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1); with
+  // per-group A units, lanes 32..63 copy the units the same way
+  const size_t cu_row = (size_t)row_of(lane & 15) * ngc + ((lane >> 4) & 1);
+  const float* cu_lane = (kUnitsA && lane >= 32 ? g.unit : g.corr) + cu_row;
   // scales: lane l < 32 -> row l of the wave, 16 bytes (8 groups) every 4 stages
   const int sr_lane = lane % kThinWaveRows;
   const _Float16* s_lane = (sr_lane < kHalf ? s0 : s1) + (size_t)(sr_lane % kHalf) * ng;
@@ -690,8 +714,9 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) dma16(b_src[i] + so, base + wave * kBWave + i * 1024);
     if (a_copy) dma16(g.a + a_off + st * kSC, base + kStageB + 4 * wave * (kSC * 2));
-    // the correction copy fills 32 x 4 bytes: lanes 32..63 stay out of it
-    if (wave == 0 && lane < 32) dma4(c_lane + 2 * st, base + kStageB + kStageA);
+    // the correction copy fills 32 x 4 bytes (64 x 4 with the units); without
+    // units lanes 32..63 stay out of it
+    if (wave == 0 && (kUnitsA || lane < 32)) dma4(cu_lane + 2 * st, base + kStageB + kStageA);
     if ((st & 3) == 0 && !pr && lane < kThinWaveRows)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * kScalePiece);
   };
@@ -709,6 +734,9 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     const f16x8 a1 = *reinterpret_cast<const f16x8*>(ar + ((p0 + 1) ^ n) * 16);
     const f32x4 c4 =
         *reinterpret_cast<const f32x4*>(base + kStageB + kStageA + (16 * gg + 4 * kg) * 4);
+    f32x4 u4 = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kUnitsA)
+      u4 = *reinterpret_cast<const f32x4*>(base + kStageB + kStageA + 128 + (16 * gg + 4 * kg) * 4);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int r = 16 * nt + n;
@@ -732,7 +760,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
       pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, pg, 0, 0, 0);
       const float sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(sv, pg[i], acc[nt][i]);
+      for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(kUnitsA ? sv * u4[i] : sv, pg[i], acc[nt][i]);
     }
   };
 
@@ -775,6 +803,68 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     step(st0 + 2, std::integral_constant<int, 2>());
     step(st0 + 3, std::integral_constant<int, 3>());
   }
+
+  if constexpr (PA && MODE == kGateUp) {
+    // lane (n, kg): a at column c = 16 wv + n for tile tokens 4 kg + i (rows
+    // past the tile repeat the last token and are not stored).  The group's
+    // max|a| and the sum of its packed values are taken over the row of 16
+    // lanes (DPP), then over the quad's 4 waves through LDS, in a fixed order;
+    // every wave of the block reaches both barriers (a quad's waves are all
+    // active or all past the last row: f / 16 is a multiple of 32).
+    const int c = kHalf * wv + n;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ti = min(tok0 + 4 * kg + i, cnt - 1);
+      const int xr = L.single ? ti : L.list[off + ti] / L.kdiv;
+      const float us = g.unit[xr] * 0x1p24f;
+      v[i] = silu(acc[0][i] * us) * (acc[1][i] * us);
+    }
+    // ring slot nst % R: its last stage (nst - R) was computed by every wave
+    // before the barrier of stage nst - 1, and no copy is issued after that
+    float* red_m = reinterpret_cast<float*>(s_lds + (nst % R) * kStage);
+    float* red_s = red_m + GW * kThinTokens;
+    const int q0 = wave & ~3;
+    float mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx[i] = row16_max(fabsf(v[i]));
+    // lane n < 4 of each row posts token 4 kg + n
+    if (n < 4) red_m[wave * kThinTokens + 4 * kg + n] = n == 0 ? mx[0] : n == 1 ? mx[1] : n == 2 ? mx[2] : mx[3];
+    __syncthreads();
+    float gm[4], up[4], hs[4];
+    int ex[4];
+    _Float16 h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * kg + i;
+      gm[i] = fmaxf(fmaxf(red_m[q0 * kThinTokens + t], red_m[(q0 + 1) * kThinTokens + t]),
+                    fmaxf(red_m[(q0 + 2) * kThinTokens + t], red_m[(q0 + 3) * kThinTokens + t]));
+      ex[i] = 0;
+      if (gm[i] > 0.0f) frexpf(gm[i], &ex[i]);  // gm < 2^ex
+      up[i] = gm[i] > 0.0f ? ldexpf(1.0f, kPackExp - ex[i]) : 1.0f;
+      h[i] = (_Float16)(v[i] * up[i]);
+      hs[i] = row16_fsum((float)h[i]);
+    }
+    if (n < 4) red_s[wave * kThinTokens + 4 * kg + n] = n == 0 ? hs[0] : n == 1 ? hs[1] : n == 2 ? hs[2] : hs[3];
+    __syncthreads();
+    if (!active) return;
+    const int grp = c / kGroup, ngroups = f / kGroup;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * kg + i >= mcnt) continue;
+      const int ti = tok0 + 4 * kg + i;
+      const int slot = L.single ? ti : L.list[off + ti];
+      g.a_out[(size_t)slot * f + (c & ~7) + slot_of_col(c & 7)] = h[i];
+      if (wave == q0 && n == i) {
+        const int t = 4 * kg + i;
+        const float sum = (red_s[q0 * kThinTokens + t] + red_s[(q0 + 1) * kThinTokens + t]) +
+                          (red_s[(q0 + 2) * kThinTokens + t] + red_s[(q0 + 3) * kThinTokens + t]);
+        g.a_corr[(size_t)slot * ngroups + grp] = -g.corr_off * 0x1p-24f * sum;
+        g.a_unit[(size_t)slot * ngroups + grp] = gm[i] > 0.0f ? ldexpf(1.0f, ex[i] - kPackExp) : 1.0f;
+      }
+    }
+    return;
+  }
   if (!active) return;
 
   // epilogue: lane (n, kg) holds tile tokens 4 kg + i for weight rows 16 nt + n;
@@ -790,7 +880,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
       const float gv = acc[0][i] * us, uv = acc[1][i] * us;
       g.out[(size_t)slot * f + kHalf * wv + n] = silu(gv) * uv;
     } else {
-      const float us = g.unit[slot] * 0x1p24f;
+      const float us = kUnitsA ? 0x1p24f : g.unit[slot] * 0x1p24f;
       float* orow = g.out + (size_t)slot * d + kThinWaveRows * wv;
       orow[n] = acc[0][i] * us;
       orow[16 + n] = acc[1][i] * us;
@@ -798,10 +888,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   }
 }
 
-template <int MODE, int GW, int R, int BITS>
+template <int MODE, int GW, int R, int BITS, bool PA>
 __global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS>::kLdsBytes];
-  thin_body<MODE, GW, R, BITS>(g, s_lds, blockIdx.y);
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS, PA>::kLdsBytes];
+  thin_body<MODE, GW, R, BITS, PA>(g, s_lds, blockIdx.y);
 }
 
 // One launch for a batch's whole union: blocks with y < g.thick_blocks run
@@ -881,7 +971,16 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
 // tokens of every expert.
 template <int MODE, int BITS, int R>
 static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, hipStream_t s, const GemmArgs& ga) {
-  return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
+  if (ga.pa)
+    return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
+  return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, false>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
+}
+
+// Every expert of the call runs the thin GEMM: int8 and int2 layers, and int4
+// batches (or a single expert) of at most kThinTokens rows.
+static bool all_thin(const MfmaArgs& m) {
+  const int rows = m.L.single ? m.L.single_n : m.x_rows;
+  return m.L.bits != 4 || rows <= kThinTokens;
 }
 
 template <int MODE>
@@ -922,8 +1021,22 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32, m.xcorr, m.mbo_t, m.blk_t, 0};
+  const bool pa_groups = all_thin(m);
+  if (pa_groups) {
+    // gate/up writes a packed by groups; no pack launch between the GEMMs
+    ga.pa = 1;
+    ga.a_out = m.ah;
+    ga.a_unit = m.aunit_g;
+    ga.a_corr = m.acorr;
+    ga.corr_off = corr_offset(L.bits);
+  }
   e = project<kGateUp>(m, ga, s);
   if (e != hipSuccess) return e;
+  if (pa_groups) {
+    GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit_g, m.y, m.acorr, m.mbo_t, m.blk_t, 0};
+    gd.pa = 1;
+    return project<kDown>(m, gd, s);
+  }
 
   PackArgs pa{};
   pa.src = m.a32;

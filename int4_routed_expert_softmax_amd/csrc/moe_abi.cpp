@@ -52,6 +52,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.a32 = take(Tk * f * sizeof(float));
   L.ah = take(Tk * f * sizeof(uint16_t));
   L.aunit = take(Tk * sizeof(float));
+  L.aunitg = take(Tk * (f / kGroup) * sizeof(float));
   L.acorr = take(Tk * (f / kGroup) * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
   L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
@@ -138,6 +139,7 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.a32 = at<float>(ws, L.a32);
   m.ah = at<_Float16>(ws, L.ah);
   m.aunit = at<float>(ws, L.aunit);
+  m.aunit_g = at<float>(ws, L.aunitg);
   m.acorr = at<float>(ws, L.acorr);
   m.mbo = at<int32_t>(ws, L.mbo);
   m.blk_u = at<int32_t>(ws, L.blku);

@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, xcorr, a32, ah, aunit, acorr, mbo, blku, mbot, blkt, plan, total;
+  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, plan, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -235,6 +235,7 @@ struct MfmaArgs {
   float* a32;
   _Float16* ah;
   float* aunit;
+  float* aunit_g;            // [slots][f / 64]: a's unit per group (every expert thin)
   float* acorr;              // [slots][f / 64]
   int32_t* mbo;              // [n_experts + 1]
   int32_t* blk_u;            // [mb_bound]
