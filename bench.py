@@ -76,8 +76,8 @@ def calibrate_copy(mib):
 
 # Sources the gate/up kernel of each path is built from: the one-token
 # GEMV path (decode, chain) and the grouped GEMM (batches of 2+ tokens).
-GATEUP_SOURCES = ("device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h", "select.h",
-                  "small_route.h")
+GATEUP_SOURCES = ("cache.h", "device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h",
+                  "select.h", "small_route.h")
 GEMM_SOURCES = ("device_util.h", "ffn_mfma.hip", "moe_internal.h", "pack.h", "small_route.h")
 
 
@@ -424,7 +424,8 @@ def mfma_figures(moe, torch, w, L0, g):
         reps = 20
         ev = ([torch.cuda.Event(enable_timing=True) for _ in range(reps)],
               [torch.cuda.Event(enable_timing=True) for _ in range(reps)])
-        kname = "gateup" if n > 16 else "gateup_thin"
+        # int8 and int2 experts run the thin GEMM at every size
+        kname = "gateup" if n > 16 and w.bits == 4 else "gateup_thin"
         h = moe.moe_timing_arm(kname, *ev)
         torch.cuda.synchronize()
         for _ in range(reps):

@@ -280,9 +280,10 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
 template <int C, bool SMALL, int NT>
 __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, int d, int f,
                                                     Digits xd, Digits ad) {
-  const int F = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  int rb, u, grp;
-  gateup_coords(F, gridDim.x, gridDim.y, gridDim.z, rb, u, grp);
+  int rb = blockIdx.x, u = blockIdx.y, grp = blockIdx.z;
+  if (gridDim.z > 1)
+    gateup_coords(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x,
+                  gridDim.y, gridDim.z, rb, u, grp);
   gateup_block<C, SMALL, NT>(L, ro, d, f, xd, ad, rb, u, grp, gridDim.z);
 }
 

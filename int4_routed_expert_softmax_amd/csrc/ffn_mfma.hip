@@ -30,6 +30,7 @@
 // (p >> 1) + 4 (p & 1).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 #include <type_traits>
 
@@ -50,6 +51,11 @@ constexpr float kBias = 1032.0f;
 
 __device__ __forceinline__ u32x4 nt_load16(const uint8_t* p) {
   return __builtin_nontemporal_load((g_u32x4_ptr)(p));
+}
+// 16 bytes through the global address space (no generic-pointer checks)
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const u32x4 v = *(g_u32x4_ptr)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // 8 codes (column j in bits 4j..4j+3) and their group's scale (both halves)
@@ -137,6 +143,52 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
       p.mbo[U] = s_tot[0][0] + s_tot[0][1] + s_tot[0][2] + s_tot[0][3];
       p.mbo_t[U] = s_tot[1][0] + s_tot[1][1] + s_tot[1][2] + s_tot[1][3];
     }
+    if (!p.xtab) return;
+    // The M-blocked experts onto the 8 XCDs (blocks of a launch go to the
+    // XCDs in turn, and an XCD's blocks share its L2): whole experts, in
+    // order of decreasing M-block count (then ascending union position),
+    // each onto the XCD with the fewest M-blocks so far (ties: the lower
+    // XCD), so the blocks of one expert read its weights and its tokens'
+    // activation rows through one L2.  No list outgrows xs (see
+    // xcd_stride); the guard only keeps a write in bounds.
+    __shared__ int s_c[4 * 256], s_beg[4 * 256], s_cmax;  // 4 experts a thread
+    if (t == 0) s_cmax = 0;
+    __syncthreads();
+    int cm = 0;
+    run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_tot[0][w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = 4 * t + i;
+      if (u < U) {
+        s_c[u] = c[i];
+        s_beg[u] = run;
+      }
+      run += c[i];
+      cm = max(cm, c[i]);
+    }
+    atomicMax(&s_cmax, cm);
+    __syncthreads();
+    if (wave != 0) return;
+    int load = 0;  // lane x < kXcds: M-blocks placed on XCD x
+    for (int cc = s_cmax; cc >= 1; --cc) {
+      for (int u0 = 0; u0 < U; u0 += 64) {
+        uint64_t pick = __ballot(u0 + lane < U && s_c[u0 + lane] == cc);
+        while (pick) {
+          const int u = u0 + __builtin_ctzll(pick);
+          pick &= pick - 1;
+          int mn = lane < kXcds ? load : INT_MAX;
+#pragma unroll
+          for (int o = 1; o < kXcds; o <<= 1) mn = min(mn, __shfl_xor(mn, o, 64));
+          const int x = __builtin_ctzll(__ballot(lane < kXcds && load == mn));
+          const int pos = __shfl(load, x, 64);
+          for (int i = lane; i < cc; i += 64)
+            if (pos + i < p.xs) p.xtab[x * p.xs + pos + i] = s_beg[u] + i;
+          if (lane == x) load += cc;
+        }
+      }
+    }
+    if (lane < kXcds) p.xcnt[lane] = min(load, p.xs);
     return;
   }
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -159,6 +211,12 @@ struct GemmArgs {
   const int32_t* mbo_t;  // thin union: number of thin experts at [n_uniq]
   const int32_t* blk_t;  // thin union: the j-th thin expert
   int thick_blocks;      // mixed launch: M-blocked blocks before the thin ones
+  // mixed launch: gx blocks along the weight rows; the M-blocked blocks of
+  // XCD x are the entries of xtab[x * xs ..] (xcnt[x] of them)
+  int gx;
+  const int32_t* xtab;
+  const int32_t* xcnt;
+  int xs;
   // pa: a travels packed by 64-column groups between the thin GEMMs.  Gate/up
   // then writes a' [slots][f] fp16 in pack order, a_unit and a_corr
   // [slots][f / 64] (corr_off: the code width's offset) instead of out; down
@@ -257,10 +315,11 @@ constexpr int copies_ahead() {
 // every copy of stage st is issued before any of stage st + 1, so "stage st has
 // landed" is "at most the copies of stage st + 1 are in flight".
 //
-// The body takes the block's LDS and its index along the M-blocks (jy), so the
+// The body takes the block's LDS and its coordinates (jx along the weight rows, jy along
+// the M-blocks), so the
 // mixed launch below can run it beside thin blocks.
 template <int MODE, int GW, int R, int MB, int NTW>
-__device__ __forceinline__ void gemm_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, uint8_t* s_lds, int jx, int jy) {
   using Shape = RingShape<GW, R, MB, NTW>;
   constexpr int kNt = Shape::kNt, kWaveRows = Shape::kWaveRows, kBWave = Shape::kBWave;
   constexpr int kScaleWave = Shape::kScaleWave;
@@ -308,7 +367,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint8_t* s_lds, int
   // ---- this wave's weight rows (ring rows 0..31 and 32..63); waves past the
   // last row copy the last wave's rows and compute nothing
   const int nwaves = MODE == kGateUp ? f / kHalf : d / kWaveRows;
-  const int wv = blockIdx.x * GW + wave;
+  const int wv = jx * GW + wave;
   const bool active = wv < nwaves;
   const int wc = min(wv, nwaves - 1);
   const size_t fd = (size_t)f * d;
@@ -486,7 +545,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, uint8_t* s_lds, int
 template <int MODE, int GW, int R, int MB, int NTW>
 __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[RingShape<GW, R, MB, NTW>::kLdsBytes];
-  gemm_body<MODE, GW, R, MB, NTW>(g, s_lds, blockIdx.y);
+  gemm_body<MODE, GW, R, MB, NTW>(g, s_lds, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------- thin GEMM
@@ -510,8 +569,9 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 // flight.  Each wave copies its rows' scales 16 bytes (8 groups, 4 stages) at
 // a time into two buffers of its own.
 constexpr int kThinWaveRows = 32;
+constexpr int kSwWindows = 4;  // scales in registers: 32-group windows, K <= 8192
 
-template <int GW, int R, int BITS, bool PA = false>
+template <int GW, int R, int BITS, bool PA = false, bool SW = false>
 struct ThinShape {
   static constexpr int kRowStage = 16 * BITS;                 // code bytes of a row per stage
   static constexpr int kPieces = kRowStage / 16;              // its 16-byte pieces
@@ -526,7 +586,8 @@ struct ThinShape {
   static constexpr int kStage = kStageB + kStageA + kStageC;
   static constexpr int kScalePiece = kThinWaveRows * 16;      // [32 rows][8 groups] fp16
   static constexpr int kScaleOff = R * kStage;
-  static constexpr int kLdsBytes = kScaleOff + GW * 2 * kScalePiece;
+  // scales in registers (SW): no scale buffers
+  static constexpr int kLdsBytes = kScaleOff + (SW ? 0 : GW * 2 * kScalePiece);
   // the per-group pack of a's reductions ([2][GW][16 tokens] f32) use a ring
   // slot no wave reads after the last stage
   static_assert(2 * GW * kThinTokens * 4 <= kStage, "reduction area fits a stage");
@@ -534,7 +595,7 @@ struct ThinShape {
   static_assert(kLdsBytes <= 160 * 1024, "fits one CU");
   // a scale piece is copied R - 1 stages before its first use, which must
   // come after the last use of the piece two back
-  static_assert(R >= 3 && R <= 5, "ring depth");
+  static_assert(R >= 3 && (SW || R <= 5), "ring depth");
   static_assert(GW >= 4, "waves 0..3 copy the 16 activation rows");
   static_assert(kThinTokens == 16, "one M-tile");
 };
@@ -599,15 +660,43 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
                :: "v"(src), "s"(lds_addr(lds)) : "memory", "m0");
 }
 
+// SW (scales in registers; group scales, K <= 8192): a 16-byte scale piece
+// per row every 4 stages would take each 128-byte line of a row's scales 8
+// times, 4 stages apart, and under a whole chip's streaming the L2 drops the
+// line between the takes (prefill: about 9 fetches per scale line).  Instead
+// all of a wave's scales are loaded into registers before the first stage,
+// each line at once: lane (n, kg) holds groups 32 w + 8 kg .. + 8 of rows n
+// and 16 + n for every window w of 32 groups, and a stage's two scales of a
+// row come from lane n + 16 ((st % 16) / 4) with a permute (those of 4
+// stages at once).  (Loaded any later, their first use would make the
+// compiler wait for every copy in flight, the ring's included.)
 // PA (per-group A): the batch's experts all run the thin GEMM and a travels
 // from gate/up to down packed by 64-column groups: gate/up forms each
 // token's group of a (its 4-wave quad's 64 columns), scales it by a power of
 // two so that the group's max|a| < 2^14, rounds it to fp16 and writes it with
 // the unit and the group correction; down takes the unit per group (beside
 // the corrections, one dword copy per stage) into the group's scale.
-template <int MODE, int GW, int R, int BITS, bool PA = false>
-__device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jy) {
-  using Shape = ThinShape<GW, R, BITS, PA>;
+// Scales in registers: the scales of groups 2 st .. 2 st + 7 (stages st ..
+// st + 3, st a multiple of 4) of rows n (sd[i][0]) and 16 + n (sd[i][1]):
+// dword i of window st / 16 in lane src = n + 16 ((st % 16) / 4).
+__device__ __forceinline__ void sw_scales(int w, int src, uint4 a0, uint4 a1, uint4 b0, uint4 b1,
+                                          uint4 c0, uint4 c1, uint4 e0, uint4 e1,
+                                          uint32_t (&sd)[4][2]) {
+  const uint4 r0 = w == 0 ? a0 : w == 1 ? b0 : w == 2 ? c0 : e0;
+  const uint4 r1 = w == 0 ? a1 : w == 1 ? b1 : w == 2 ? c1 : e1;
+  sd[0][0] = (uint32_t)__shfl((int)r0.x, src, 64);
+  sd[1][0] = (uint32_t)__shfl((int)r0.y, src, 64);
+  sd[2][0] = (uint32_t)__shfl((int)r0.z, src, 64);
+  sd[3][0] = (uint32_t)__shfl((int)r0.w, src, 64);
+  sd[0][1] = (uint32_t)__shfl((int)r1.x, src, 64);
+  sd[1][1] = (uint32_t)__shfl((int)r1.y, src, 64);
+  sd[2][1] = (uint32_t)__shfl((int)r1.z, src, 64);
+  sd[3][1] = (uint32_t)__shfl((int)r1.w, src, 64);
+}
+
+template <int MODE, int GW, int R, int BITS, bool PA = false, bool SW = false>
+__device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jx, int jy) {
+  using Shape = ThinShape<GW, R, BITS, PA, SW>;
   constexpr bool kUnitsA = PA && MODE == kDown;
   static_assert(!PA || GW % 4 == 0, "a group of a spans 4 waves");
   constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB, kRowStage = Shape::kRowStage;
@@ -655,7 +744,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   // ---- this wave's 32 weight rows (gate/up: 16 gate rows and the same 16 up
   // rows); waves past the last row copy the last wave's rows, compute nothing
   const int nwaves = MODE == kGateUp ? f / kHalf : d / kThinWaveRows;
-  const int wv = blockIdx.x * GW + wave;
+  const int wv = jx * GW + wave;
   const bool active = wv < nwaves;
   const int wc = min(wv, nwaves - 1);
   const size_t mat_codes = (size_t)f * d * BITS / 8;
@@ -697,7 +786,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const int sr_lane = lane % kThinWaveRows;
   const _Float16* s_lane = (sr_lane < kHalf ? s0 : s1) + (size_t)(sr_lane % kHalf) * ng;
   uint8_t* s_scales = s_lds + Shape::kScaleOff + wave * (2 * kScalePiece);
-  if (pr && lane < kThinWaveRows) {
+  if (!SW && pr && lane < kThinWaveRows) {
     // one scale per row: put in every group of both buffers, once (this
     // wave's own LDS; the first stage's wait covers the writes)
     const uint32_t h = *reinterpret_cast<const uint16_t*>(s_lane);
@@ -706,9 +795,22 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     *reinterpret_cast<uint4*>(s_scales + lane * 16) = v;
     *reinterpret_cast<uint4*>(s_scales + kScalePiece + lane * 16) = v;
   }
+  // SW: windows 0..3 of rows n (x0) and 16 + n (x1), 8 groups each
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 a0 = z4, a1 = z4, b0 = z4, b1 = z4, c0w = z4, c1w = z4, e0 = z4, e1 = z4;
+  if constexpr (SW) {
+    static_assert(kSwWindows == 4, "four named windows");
+    const _Float16* srw0 = s0 + (size_t)n * ng;
+    const _Float16* srw1 = s1 + (size_t)n * ng;
+    const int g0 = 8 * kg;  // ng is a multiple of 8: a lane's 8 are all in or out
+    if (g0 < ng) a0 = gload16(srw0 + g0), a1 = gload16(srw1 + g0);
+    if (g0 + 32 < ng) b0 = gload16(srw0 + g0 + 32), b1 = gload16(srw1 + g0 + 32);
+    if (g0 + 64 < ng) c0w = gload16(srw0 + g0 + 64), c1w = gload16(srw1 + g0 + 64);
+    if (g0 + 96 < ng) e0 = gload16(srw0 + g0 + 96), e1 = gload16(srw1 + g0 + 96);
+  }
 
   const int nst = K / kSC;
-  auto issue = [&](int st) {
+  auto issue = [&](int st) __attribute__((always_inline)) {
     uint8_t* base = s_lds + (st % R) * kStage;
     const uint32_t so = (uint32_t)st * kRowStage;
 #pragma unroll
@@ -717,14 +819,14 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     // the correction copy fills 32 x 4 bytes (64 x 4 with the units); without
     // units lanes 32..63 stay out of it
     if (wave == 0 && (kUnitsA || lane < 32)) dma4(cu_lane + 2 * st, base + kStageB + kStageA);
-    if ((st & 3) == 0 && !pr && lane < kThinWaveRows)
+    if (!SW && (st & 3) == 0 && !pr && lane < kThinWaveRows)
       dma16(s_lane + 2 * st, s_scales + ((st >> 2) & 1) * kScalePiece);
   };
 
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // group 2 st + gg of a landed stage: lane (n, kg) takes, for MFMA step j,
   // columns 16 kg + 8 j .. + 8 of the group
-  auto group = [&](int st, int gg) {
+  auto group = [&](int st, int gg, const uint32_t (&sd)[2]) __attribute__((always_inline)) {
     const uint8_t* base = s_lds + (st % R) * kStage;
     const int gi = 2 * st + gg;
     const uint8_t* sc = s_scales + ((gi >> 3) & 1) * kScalePiece + (gi & 7) * 2;
@@ -758,7 +860,11 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
       }
       f32x4 pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, c4, 0, 0, 0);
       pg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, pg, 0, 0, 0);
-      const float sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
+      float sv;
+      if constexpr (SW)
+        sv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sd[nt] >> (16 * gg)));
+      else
+        sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf(kUnitsA ? sv * u4[i] : sv, pg[i], acc[nt][i]);
     }
@@ -770,12 +876,12 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
   for (int i = 0; i < R - 1; ++i)
     if (i < nst) issue(i);
-  auto step = [&](int st, auto phase) {
-    constexpr int PH = decltype(phase)::value;
+  auto step = [&](int st, auto phase, const uint32_t (&sd)[2]) __attribute__((always_inline)) {
+    constexpr int PH = decltype(phase)::value;  // stage % 4
     if (st + R - 2 < nst) {
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
-      if (pr) {
+      if (SW || pr) {
         if (extra == 0) wait_vm_lgkm0<copies_ahead<R, PH, kCopies, 0, 0>()>();
         else if (extra == 1) wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 1, 0, 0>()>();
         else wait_vm_lgkm0<copies_ahead<R, PH, kCopies + 2, 0, 0>()>();
@@ -793,15 +899,22 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     // every wave is past stage st - 1: its ring slot takes stage st + R - 1
     if (st + R - 1 < nst) issue(st + R - 1);
     if (active) {
-      group(st, 0);
-      group(st, 1);
+      group(st, 0, sd);
+      group(st, 1, sd);
     }
   };
   for (int st0 = 0; st0 < nst; st0 += 4) {  // nst is a multiple of 4
-    step(st0, std::integral_constant<int, 0>());
-    step(st0 + 1, std::integral_constant<int, 1>());
-    step(st0 + 2, std::integral_constant<int, 2>());
-    step(st0 + 3, std::integral_constant<int, 3>());
+    // SW: a stage's scales of rows n and 16 + n (both lanes' permutes run in
+    // every wave, active or not)
+    uint32_t sd[4][2] = {};
+    if constexpr (SW) {
+      const int src = n + 16 * ((st0 & 15) >> 2), w = st0 >> 4;
+      sw_scales(w, src, a0, a1, b0, b1, c0w, c1w, e0, e1, sd);
+    }
+    step(st0, std::integral_constant<int, 0>(), sd[0]);
+    step(st0 + 1, std::integral_constant<int, 1>(), sd[1]);
+    step(st0 + 2, std::integral_constant<int, 2>(), sd[2]);
+    step(st0 + 3, std::integral_constant<int, 3>(), sd[3]);
   }
 
   if constexpr (PA && MODE == kGateUp) {
@@ -888,26 +1001,37 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   }
 }
 
-template <int MODE, int GW, int R, int BITS, bool PA>
+template <int MODE, int GW, int R, int BITS, bool PA, bool SW>
 __global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS, PA>::kLdsBytes];
-  thin_body<MODE, GW, R, BITS, PA>(g, s_lds, blockIdx.y);
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS, PA, SW>::kLdsBytes];
+  thin_body<MODE, GW, R, BITS, PA, SW>(g, s_lds, blockIdx.x, blockIdx.y);
 }
 
-// One launch for a batch's whole union: blocks with y < g.thick_blocks run
+// One launch for a batch's whole union: the first g.thick_blocks blocks run
 // the M-blocked GEMM (16 waves, 64-token M-blocks: the hot experts, whose
 // matrix-core and dequantisation work is the longest, dispatched first), the
 // others the thin GEMM (16 waves) over the experts of at most kThinTokens
 // tokens, so the streaming of the many small experts overlaps the compute of
-// the few large ones.  Both cover 512 weight rows a block.
+// the few large ones.  Both cover 512 weight rows a block.  Block F runs on
+// XCD F % 8 (blocks are dispatched to the XCDs in turn): the M-blocked
+// blocks of XCD x take the M-blocks of its list, each over all gx row
+// blocks, so an expert's blocks share one L2 (its weights across its
+// M-blocks, its activation rows across the row blocks).
 constexpr int kMixedThinRing = 3;
-template <int MODE>
+template <int MODE, bool SW>
 __global__ __launch_bounds__(1024) void k_gemm_mixed(GemmArgs g) {
   constexpr int kA = RingShape<16, 3, 64, 2>::kLdsBytes;
-  constexpr int kB = ThinShape<16, kMixedThinRing, 4>::kLdsBytes;
+  constexpr int kB = ThinShape<16, kMixedThinRing, 4, false, SW>::kLdsBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kA > kB ? kA : kB];
-  if ((int)blockIdx.y < g.thick_blocks) gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, blockIdx.y);
-  else thin_body<MODE, 16, kMixedThinRing, 4>(g, s_lds, blockIdx.y - g.thick_blocks);
+  const int F = blockIdx.x;
+  if (F < g.thick_blocks) {
+    const int x = F % kXcds, q = F / kXcds, i = q / g.gx;
+    if (i >= g.xcnt[x]) return;
+    gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, q % g.gx, g.xtab[x * g.xs + i]);
+  } else {
+    const int Ft = F - g.thick_blocks;
+    thin_body<MODE, 16, kMixedThinRing, 4, false, SW>(g, s_lds, Ft % g.gx, Ft / g.gx);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -959,6 +1083,9 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
     px.mbo_t = m.mbo_t;
     px.blk_t = m.blk_t;
     px.mblock = mfma_mblock(m.x_rows);
+    px.xtab = m.xtab;
+    px.xcnt = m.xcnt;
+    px.xs = m.xs;
   }
   return px;
 }
@@ -969,11 +1096,28 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
 // (M-blocked blocks for the experts past kThinTokens tokens, then thin blocks
 // for the others).  int8 and int2: the thin GEMM over every M-tile of 16
 // tokens of every expert.
+// Scales in registers (SW) with one scale per 64 weights (a row's scales then
+// fill whole 8-group lane slices: K is a multiple of 512) and K <= 8192.
+static bool scales_in_regs(const GemmArgs& ga, int K) {
+  return K % 512 == 0 && K <= 32 * 64 * kSwWindows && !ga.L.per_row;
+}
+
+// big: a batch of more than kThinTokens rows (prefill of int8 and int2
+// layers).  Only there does the whole chip stream at once, so that the L2
+// drops scale lines between the takes of a per-stage piece: with a few
+// experts the pieces hit, and the register windows only cost (decode of an
+// int8 layer: gate/up 41.7 -> 45.8 us with them).
 template <int MODE, int BITS, int R>
-static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, hipStream_t s, const GemmArgs& ga) {
-  if (ga.pa)
-    return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
-  return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, false>, dim3(gx, gy), dim3(64 * kThinGW), s, ga);
+static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, bool big, hipStream_t s,
+                              const GemmArgs& ga) {
+  const dim3 grid(gx, gy), block(64 * kThinGW);
+  const bool sw = big && scales_in_regs(ga, MODE == kGateUp ? ga.d : ga.f);
+  if (ga.pa) {
+    if (sw) return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, true>, grid, block, s, ga);
+    return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, false>, grid, block, s, ga);
+  }
+  if (sw) return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, false, true>, grid, block, s, ga);
+  return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, false, false>, grid, block, s, ga);
 }
 
 // Every expert of the call runs the thin GEMM: int8 and int2 layers, and int4
@@ -995,9 +1139,10 @@ static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
   const unsigned gx = (unsigned)((nw + kThinGW - 1) / kThinGW);
   const unsigned gy = L.single ? (unsigned)((L.single_n + kThinTokens - 1) / kThinTokens)
                                : (unsigned)m.thin_bound;
-  if (L.bits == 8) return thin_launch<MODE, 8, 3>(kid_thin, gx, gy, s, ga);
-  if (L.bits == 2) return thin_launch<MODE, 2, 4>(kid_thin, gx, gy, s, ga);
-  if (rows <= kThinTokens) return thin_launch<MODE, 4, kThinRing>(kid_thin, gx, gy, s, ga);
+  const bool big = rows > kThinTokens;
+  if (L.bits == 8) return thin_launch<MODE, 8, 3>(kid_thin, gx, gy, big, s, ga);
+  if (L.bits == 2) return thin_launch<MODE, 2, 4>(kid_thin, gx, gy, big, s, ga);
+  if (rows <= kThinTokens) return thin_launch<MODE, 4, kThinRing>(kid_thin, gx, gy, false, s, ga);
   if (L.single) {
     const GemmShape sh = gemm_shape(rows, true);
     const unsigned mb = (unsigned)((L.single_n + sh.mblock - 1) / sh.mblock);
@@ -1005,9 +1150,15 @@ static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
     if (sh.gw == 4) return launch(kid, k_gemm<MODE, 4, 3, 64, 2>, dim3(gxs, mb), dim3(256), s, ga);
     return launch(kid, k_gemm<MODE, 16, 3, 64, 2>, dim3(gxs, mb), dim3(1024), s, ga);
   }
-  ga.thick_blocks = m.mb_bound;
-  const dim3 grid((unsigned)((nw + 15) / 16), (unsigned)(m.mb_bound + m.thin_bound));
-  return launch(kid, k_gemm_mixed<MODE>, grid, dim3(1024), s, ga);
+  ga.gx = (nw + 15) / 16;
+  ga.xtab = m.xtab;
+  ga.xcnt = m.xcnt;
+  ga.xs = m.xs;
+  ga.thick_blocks = kXcds * ga.gx * m.xs;
+  const dim3 grid((unsigned)(ga.thick_blocks + ga.gx * m.thin_bound));
+  if (scales_in_regs(ga, MODE == kGateUp ? m.d : m.f))
+    return launch(kid, k_gemm_mixed<MODE, true>, grid, dim3(1024), s, ga);
+  return launch(kid, k_gemm_mixed<MODE, false>, grid, dim3(1024), s, ga);
 }
 
 hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {

@@ -58,6 +58,7 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
   L.mbot = take((cap + 1) * sizeof(int32_t));
   L.blkt = take((cap + Tk / kThinTokens + 1) * sizeof(int32_t));
+  L.xtab = take(((size_t)kXcds * xcd_stride(T, k, (int)cap) + kXcds) * sizeof(int32_t));
   L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
@@ -145,6 +146,7 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.blk_u = at<int32_t>(ws, L.blku);
   m.mbo_t = at<int32_t>(ws, L.mbot);
   m.blk_t = at<int32_t>(ws, L.blkt);
+  m.xtab = at<int32_t>(ws, L.xtab);
   return m;
 }
 
@@ -419,10 +421,9 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.x_bf16 = xr_bf16;
     m.x_rows = T;
     m.slots = T * k;
-    // experts past kThinTokens tokens: fewer than T k / (kThinTokens + 1) of
-    // them, each with ceil(count / 64) < count / 64 + 1 M-blocks
-    const int nthick = T * k / (kThinTokens + 1) < maxU ? T * k / (kThinTokens + 1) : maxU;
-    m.mb_bound = (T * k + mfma_mblock(T) - 1) / mfma_mblock(T) + nthick;
+    m.mb_bound = mixed_mb_bound(T, k, maxU);
+    m.xs = xcd_stride(T, k, maxU);
+    m.xcnt = m.xtab + (size_t)kXcds * m.xs;
     // int4: one thin block per thin expert; int8 / int2: one per 16 tokens of
     // every expert (ceil(count / 16) < count / 16 + 1)
     m.thin_bound = EL.bits == 4 ? maxU : maxU + (T * k + kThinTokens - 1) / kThinTokens;

@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, plan, total;
+  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, xtab, plan, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -125,6 +125,12 @@ struct PackArgs {
   int32_t* mbo_t;
   int32_t* blk_t;
   int mblock;
+  // with xtab set: the M-blocked experts placed on the 8 XCDs (each expert's
+  // M-blocks on one, largest first onto the least loaded): xtab[x * xs + i]
+  // = the i-th M-block index of XCD x, xcnt[x] = their number
+  int32_t* xtab;
+  int32_t* xcnt;
+  int xs;
 };
 
 // Arguments of the small-batch router front end (optional RMSNorm, logits and
@@ -241,6 +247,9 @@ struct MfmaArgs {
   int32_t* blk_u;            // [mb_bound]
   int32_t* mbo_t;            // [n_experts + 1]
   int32_t* blk_t;            // [n_experts]
+  int32_t* xtab;             // [kXcds][xs] M-blocks per XCD
+  int32_t* xcnt;             // [kXcds]
+  int xs;
   float* y;
   int x_packed;              // xh, xunit, xcorr and the M-block maps are already written
 };
@@ -249,6 +258,20 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m);
 // M-block (tokens per GEMM block) for a batch of `rows` activation rows.
 int mfma_mblock(int rows);
 constexpr int kMinMBlock = 16;
+// The mixed launch of a union's grouped GEMM: an upper bound on its M-blocks
+// (experts past kThinTokens tokens: fewer than T k / (kThinTokens + 1) of
+// them, each with ceil(count / 64) < count / 64 + 1 M-blocks), and the length
+// of each XCD's list of M-blocks.  Placing whole experts, each onto the XCD
+// least loaded so far, leaves no XCD more than floor(total / 8) plus one
+// expert's M-blocks (at most ceil(T / 64): an expert has at most T tokens).
+constexpr int kXcds = 8;
+inline int mixed_mb_bound(int T, int k, int maxU) {
+  const int nthick = T * k / (kThinTokens + 1) < maxU ? T * k / (kThinTokens + 1) : maxU;
+  return (T * k + 63) / 64 + nthick;
+}
+inline int xcd_stride(int T, int k, int maxU) {
+  return mixed_mb_bound(T, k, maxU) / kXcds + (T + 63) / 64 + 1;
+}
 // The grouped GEMM needs d and f to be multiples of 512.
 bool mfma_shape_ok(int d, int f);
 // Batches from this many tokens on take the grouped GEMM when the shape
