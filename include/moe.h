@@ -318,7 +318,8 @@ int moe_layer_forward_cached(const moe_dims* dims, const void* x, int x_dtype, i
  * expert table, out and stats.
  *   - A call needs moe_workspace_bytes(dims, T) <= MOE_NOALLOC_SCRATCH_BYTES
  *     (GLM-5.2-shaped layers, d = 6144, f = 2048, 256 experts, top-8: up to
- *     T = 64 tokens); larger calls return MOE_ENOSPC and enqueue nothing.
+ *     T = 64 tokens and a little more: 79 with the current workspace layout);
+ *     larger calls return MOE_ENOSPC and enqueue nothing.
  *   - Every call on a GPU shares that GPU's array, which keeps the last
  *     call's contents (no part of it needs to start at zero: every call
  *     writes each word before it reads it).  Calls that overlap in time on
