@@ -117,9 +117,13 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
   __shared__ SmallRoute sr;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   small_route(ro, sr, wave, 16);
-  if (px.mbo && wave == 15)
+  if (px.mbo && wave == 15) {
     mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t,
                     px.thin_all, lane);
+    if (px.tt)
+      thin_tiles_wave(sr.offsets, sr.uniq, sr.rows, sr.n, px.table, px.tt, px.tslot, px.tt_n,
+                      px.thin_all, lane);
+  }
   publish_small_route(ro, sr, table, 1024);
 }
 
@@ -654,6 +658,11 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
     px.blk_t = map->blk_t;
     px.mblock = map->mblock;
     px.thin_all = map->thin_all;
+    px.tt = map->tt;
+    px.tslot = map->tslot;
+    px.tt_n = map->tt_n;
+    px.table = map->table;
+    if (px.tt && (!px.tslot || !px.table)) return hipErrorInvalidValue;
   }
   return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table, px);
 }

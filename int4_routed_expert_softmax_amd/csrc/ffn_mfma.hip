@@ -97,11 +97,12 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
     // block-wide exclusive scans place them
     __shared__ int s_tot[2][4];
     const int U = *p.n_uniq, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int c[4], th[4], sum = 0, sum_t = 0;
+    int c[4], th[4], nn[4], sum = 0, sum_t = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
       const int n = u < U ? p.offsets[u + 1] - p.offsets[u] : 0;
+      nn[i] = n;
       const bool thin = u < U && (p.thin_all || n <= kThinTokens);
       th[i] = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
       c[i] = u < U && !thin ? (n + p.mblock - 1) / p.mblock : 0;
@@ -135,14 +136,33 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
         p.mbo_t[u] = run_t;
         for (int j = 0; j < c[i]; ++j) p.blk_u[run + j] = u;
         for (int j = 0; j < th[i]; ++j) p.blk_t[run_t + j] = u;
+        if (p.tt && th[i] > 0) {
+          // the expert's thin tiles (same order as blk_t)
+          const uint8_t* blob = p.table[p.uniq[u]];
+          const int off = p.offsets[u], n = nn[i];
+          for (int j = 0; j < th[i] && run_t + j < p.tt_n; ++j) {
+            ThinTile r{};
+            r.blob = blob;
+            r.off = off;
+            r.cnt = n;
+            r.tok0 = j * kThinTokens;
+            p.tt[run_t + j] = r;
+            for (int q = 0; q < kTileSlots; ++q)
+              p.tslot[(size_t)(run_t + j) * kTileSlots + q] =
+                  p.list[off + min(j * kThinTokens + q, n - 1)];
+          }
+        }
       }
       run += c[i];
       run_t += th[i];
     }
+    const int tot_t = s_tot[1][0] + s_tot[1][1] + s_tot[1][2] + s_tot[1][3];
     if (t == 0) {
       p.mbo[U] = s_tot[0][0] + s_tot[0][1] + s_tot[0][2] + s_tot[0][3];
-      p.mbo_t[U] = s_tot[1][0] + s_tot[1][1] + s_tot[1][2] + s_tot[1][3];
+      p.mbo_t[U] = tot_t;
     }
+    if (p.tt)
+      for (int j = tot_t + t; j < p.tt_n; j += (int)blockDim.x) p.tt[j] = ThinTile{};
     if (!p.xtab) return;
     // The M-blocked experts onto the 8 XCDs (blocks of a launch go to the
     // XCDs in turn, and an XCD's blocks share its L2): whole experts, in
@@ -208,8 +228,8 @@ struct GemmArgs {
   const float* unit;     // [rows]
   float* out;            // gate/up: silu(g) * u [slots][f]; down: y [slots][d]
   const float* corr;     // thin: [rows][K / 64] group corrections of A
-  const int32_t* mbo_t;  // thin union: number of thin experts at [n_uniq]
-  const int32_t* blk_t;  // thin union: the j-th thin expert
+  const ThinTile* tt;    // thin union: the record of thin block jy
+  const int32_t* tslot;  // thin union: [jy][kTileSlots] the tile's slots
   int thick_blocks;      // mixed launch: M-blocked blocks before the thin ones
   // mixed launch: gx blocks along the weight rows; the M-blocked blocks of
   // XCD x are the entries of xtab[x * xs ..] (xcnt[x] of them)
@@ -725,21 +745,41 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     if (tok0 >= cnt) return;
     blob = L.single;
   } else {
-    if (jy >= g.mbo_t[*L.n_uniq]) return;
-    const int u = g.blk_t[jy];
-    off = L.offsets[u];
-    cnt = L.offsets[u + 1] - off;
-    tok0 = (jy - g.mbo_t[u]) * kThinTokens;
-    blob = L.table[L.uniq[u]];
+    // the tile's record: expert, tokens (one dependent load)
+    const ThinTile tile = g.tt[jy];
+    if (!tile.blob) return;
+    off = tile.off;
+    cnt = tile.cnt;
+    tok0 = tile.tok0;
+    blob = tile.blob;
   }
+  (void)off;
   const int mcnt = min(kThinTokens, cnt - tok0);
-  // packed row of the tile's token i (past the last token: the last one)
+  const int32_t* tsl = L.single ? nullptr : g.tslot + (size_t)jy * kTileSlots;
+  // slot of the tile's token i (past the last token: the last one)
+  auto slot_of = [&](int i) -> int { return L.single ? min(tok0 + i, cnt - 1) : tsl[i]; };
+  // packed activation row of the tile's token i
   auto row_of = [&](int i) -> uint32_t {
-    const int ti = min(tok0 + i, cnt - 1);
-    if (L.single) return (uint32_t)ti;
-    const int slot = L.list[off + ti];
-    return (uint32_t)(MODE == kGateUp ? slot / L.kdiv : slot);
+    const int slot = slot_of(i);
+    return (uint32_t)(MODE == kGateUp && !L.single ? slot / L.kdiv : slot);
   };
+  // the epilogue's slots and units of this lane's tokens 4 kg + i (lane
+  // (n, kg), n = lane & 15).  4-wave blocks request them now, so that their
+  // latency hides behind the main loop; 16-wave blocks (one block a CU, long
+  // main loops) load them at the end and keep the registers
+  int eslot[4];
+  float eunit[4];
+  auto epi_load = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eslot[i] = slot_of(4 * ((threadIdx.x & 63) >> 4) + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (MODE == kGateUp) eunit[i] = g.unit[L.single ? eslot[i] : eslot[i] / L.kdiv];
+      else eunit[i] = kUnitsA ? 1.0f : g.unit[eslot[i]];
+    }
+  };
+  constexpr bool kEpiEarly = GW <= 4;
+  if constexpr (kEpiEarly) epi_load();
 
   // ---- this wave's 32 weight rows (gate/up: 16 gate rows and the same 16 up
   // rows); waves past the last row copy the last wave's rows, compute nothing
@@ -917,6 +957,8 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     step(st0 + 3, std::integral_constant<int, 3>(), sd[3]);
   }
 
+  if constexpr (!kEpiEarly) epi_load();
+
   if constexpr (PA && MODE == kGateUp) {
     // lane (n, kg): a at column c = 16 wv + n for tile tokens 4 kg + i (rows
     // past the tile repeat the last token and are not stored).  The group's
@@ -928,9 +970,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ti = min(tok0 + 4 * kg + i, cnt - 1);
-      const int xr = L.single ? ti : L.list[off + ti] / L.kdiv;
-      const float us = g.unit[xr] * 0x1p24f;
+      const float us = eunit[i] * 0x1p24f;
       v[i] = silu(acc[0][i] * us) * (acc[1][i] * us);
     }
     // ring slot nst % R: its last stage (nst - R) was computed by every wave
@@ -965,8 +1005,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (4 * kg + i >= mcnt) continue;
-      const int ti = tok0 + 4 * kg + i;
-      const int slot = L.single ? ti : L.list[off + ti];
+      const int slot = eslot[i];
       g.a_out[(size_t)slot * f + (c & ~7) + slot_of_col(c & 7)] = h[i];
       if (wave == q0 && n == i) {
         const int t = 4 * kg + i;
@@ -985,15 +1024,13 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (4 * kg + i >= mcnt) continue;
-    const int ti = tok0 + 4 * kg + i;
-    const int slot = L.single ? ti : L.list[off + ti];
+    const int slot = eslot[i];
     if (MODE == kGateUp) {
-      const int xr = L.single ? ti : slot / L.kdiv;
-      const float us = g.unit[xr] * 0x1p24f;
+      const float us = eunit[i] * 0x1p24f;
       const float gv = acc[0][i] * us, uv = acc[1][i] * us;
       g.out[(size_t)slot * f + kHalf * wv + n] = silu(gv) * uv;
     } else {
-      const float us = kUnitsA ? 0x1p24f : g.unit[slot] * 0x1p24f;
+      const float us = eunit[i] * 0x1p24f;
       float* orow = g.out + (size_t)slot * d + kThinWaveRows * wv;
       orow[n] = acc[0][i] * us;
       orow[16 + n] = acc[1][i] * us;
@@ -1057,6 +1094,10 @@ bool mfma_shape_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
 // a dozen experts still give hundreds of blocks.
 constexpr int kThinGW = 4;
 constexpr int kThinRing = 4;
+// Down (K = f, a few stages) keeps 3: with 4 stages (54 KB of LDS) many CUs
+// took only two of its blocks, and at 624 blocks over 256 CUs a second round
+// of blocks started 16 us late (verify8 down 27.5 -> 25.6 us with 3).
+constexpr int kThinRingDown = 3;
 
 // The offset that makes a code of this width non-negative (its value plus
 // the offset is the field with the sign bit flipped).
@@ -1086,6 +1127,12 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
     px.xtab = m.xtab;
     px.xcnt = m.xcnt;
     px.xs = m.xs;
+    px.tt = m.tt;
+    px.tslot = m.tslot;
+    px.tt_n = m.thin_bound;
+    px.table = L.table;
+    px.uniq = L.uniq;
+    px.list = L.list;
   }
   return px;
 }
@@ -1142,7 +1189,9 @@ static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
   const bool big = rows > kThinTokens;
   if (L.bits == 8) return thin_launch<MODE, 8, 3>(kid_thin, gx, gy, big, s, ga);
   if (L.bits == 2) return thin_launch<MODE, 2, 4>(kid_thin, gx, gy, big, s, ga);
-  if (rows <= kThinTokens) return thin_launch<MODE, 4, kThinRing>(kid_thin, gx, gy, false, s, ga);
+  if (rows <= kThinTokens)
+    return thin_launch<MODE, 4, MODE == kDown ? kThinRingDown : kThinRing>(kid_thin, gx, gy, false,
+                                                                          s, ga);
   if (L.single) {
     const GemmShape sh = gemm_shape(rows, true);
     const unsigned mb = (unsigned)((L.single_n + sh.mblock - 1) / sh.mblock);
@@ -1171,7 +1220,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     e = launch(MOE_KERNEL_DIGITIZE, k_pack, dim3(gx), dim3(256), s, px);
     if (e != hipSuccess) return e;
   }
-  GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32, m.xcorr, m.mbo_t, m.blk_t, 0};
+  GemmArgs ga{L, m.mbo, m.blk_u, m.d, m.f, m.xh, m.xunit, m.a32, m.xcorr, m.tt, m.tslot, 0};
   const bool pa_groups = all_thin(m);
   if (pa_groups) {
     // gate/up writes a packed by groups; no pack launch between the GEMMs
@@ -1184,7 +1233,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   e = project<kGateUp>(m, ga, s);
   if (e != hipSuccess) return e;
   if (pa_groups) {
-    GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit_g, m.y, m.acorr, m.mbo_t, m.blk_t, 0};
+    GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit_g, m.y, m.acorr, m.tt, m.tslot, 0};
     gd.pa = 1;
     return project<kDown>(m, gd, s);
   }
@@ -1200,7 +1249,7 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
   e = launch(MOE_KERNEL_DIGITIZE, k_pack, dim3((unsigned)((m.slots + 3) / 4)), dim3(256), s, pa);
   if (e != hipSuccess) return e;
 
-  GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y, m.acorr, m.mbo_t, m.blk_t, 0};
+  GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit, m.y, m.acorr, m.tt, m.tslot, 0};
   return project<kDown>(m, gd, s);
 }
 

@@ -59,6 +59,10 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.mbot = take((cap + 1) * sizeof(int32_t));
   L.blkt = take((cap + Tk / kThinTokens + 1) * sizeof(int32_t));
   L.xtab = take(((size_t)kXcds * xcd_stride(T, k, (int)cap) + kXcds) * sizeof(int32_t));
+  // thin tiles: at most cap + ceil(T k / kThinTokens) (the launch's thin blocks)
+  const size_t ntile = cap + (Tk + kThinTokens - 1) / kThinTokens;
+  L.tt = take(ntile * sizeof(ThinTile));
+  L.tslot = take(ntile * kTileSlots * sizeof(int32_t));
   L.plan = take(kSmallPicks * sizeof(DownPlan));
   L.total = o;
   return L;
@@ -147,6 +151,8 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.mbo_t = at<int32_t>(ws, L.mbot);
   m.blk_t = at<int32_t>(ws, L.blkt);
   m.xtab = at<int32_t>(ws, L.xtab);
+  m.tt = at<ThinTile>(ws, L.tt);
+  m.tslot = at<int32_t>(ws, L.tslot);
   return m;
 }
 
@@ -378,6 +384,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     xr_bf16 = 0;
   }
   int x_packed = 0;
+  // the thin GEMM's blocks per projection: int4, one per thin expert; int8
+  // and int2, one per 16 tokens of every expert (ceil(count / 16) < count /
+  // 16 + 1)
+  const int thin_bound =
+      EL.bits == 4 ? maxU : maxU + (T * k + kThinTokens - 1) / kThinTokens;
   if (small_batch(T, k)) {
     // a few tokens on the grouped GEMM: logits (+ bias) by the small-batch
     // router front end, top-k and union in one block
@@ -401,6 +412,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
       m.x = xr;
       m.x_bf16 = xr_bf16;
       m.x_rows = T;
+      m.thin_bound = thin_bound;
       ra.px = mfma_x_pack_args(m);
       MOE_TRY(launch_router_front(ra, s));
       MOE_TRY(launch_route_small(ro, nullptr, s, &ra.px));
@@ -424,9 +436,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.mb_bound = mixed_mb_bound(T, k, maxU);
     m.xs = xcd_stride(T, k, maxU);
     m.xcnt = m.xtab + (size_t)kXcds * m.xs;
-    // int4: one thin block per thin expert; int8 / int2: one per 16 tokens of
-    // every expert (ceil(count / 16) < count / 16 + 1)
-    m.thin_bound = EL.bits == 4 ? maxU : maxU + (T * k + kThinTokens - 1) / kThinTokens;
+    m.thin_bound = thin_bound;
     m.y = y;
     m.x_packed = x_packed;
     MOE_TRY(launch_ffn_mfma(m, s));

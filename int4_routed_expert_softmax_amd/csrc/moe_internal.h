@@ -40,7 +40,8 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, xtab, plan, total;
+  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, xtab, tt, tslot,
+      plan, total;
 };
 
 Layout layout(int d, int f, int E, int k, int T);
@@ -103,6 +104,21 @@ hipError_t launch(int kernel_id, K kernel, dim3 grid, dim3 block, hipStream_t s,
 // GEMM (one 16-row M-tile per block); the others on the M-blocked one.
 constexpr int kThinTokens = 16;
 
+// One thin-GEMM tile of a union: kThinTokens tokens of one expert.  The map
+// builder writes one record per thin block of the launch (blob == nullptr:
+// no tile, the block exits), and the tile's slot ids beside it, so a block
+// finds its expert, its tokens and their rows with one dependent load.
+struct ThinTile {
+  const uint8_t* blob;  // the expert's blob (nullptr: past the last tile)
+  int32_t off;          // the expert's first list entry
+  int32_t cnt;          // the expert's token count
+  int32_t tok0;         // the tile's first token (a multiple of kThinTokens)
+  int32_t pad[3];
+};
+// tslot[j][i]: slot of token tok0 + i of tile j (past the expert's last
+// token: its last slot).
+constexpr int kTileSlots = 16;
+
 // Rows of activations to pack into the grouped GEMM's fp16 A operand (one
 // power of two per row), their per-64-column group sums for the thin GEMM,
 // and optionally the union's M-block maps.
@@ -131,6 +147,15 @@ struct PackArgs {
   int32_t* xtab;
   int32_t* xcnt;
   int xs;
+  // with tt set: the thin tiles (tt_n records: the thin blocks of the
+  // launch, those past the last tile marked empty) and their slots; the
+  // blobs come from table[uniq[u]], the slots from the union's list
+  ThinTile* tt;
+  int32_t* tslot;  // [tt_n][kTileSlots]
+  int tt_n;
+  const uint8_t* const* table;
+  const int32_t* uniq;
+  const int32_t* list;
 };
 
 // Arguments of the small-batch router front end (optional RMSNorm, logits and
@@ -250,6 +275,8 @@ struct MfmaArgs {
   int32_t* xtab;             // [kXcds][xs] M-blocks per XCD
   int32_t* xcnt;             // [kXcds]
   int xs;
+  ThinTile* tt;              // [thin_bound] thin tiles
+  int32_t* tslot;            // [thin_bound][kTileSlots]
   float* y;
   int x_packed;              // xh, xunit, xcorr and the M-block maps are already written
 };

@@ -250,4 +250,35 @@ __device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int 
   }
 }
 
+// The thin tiles of a union of at most 64 experts (offs[0..U], uniq, rows:
+// the union's list), by one whole wave, in the order of the thin-block map
+// above (expert by expert, kThinTokens tokens a tile); the records from the
+// last tile to tt_n are marked empty.
+__device__ __forceinline__ void thin_tiles_wave(const int32_t* offs, const int32_t* uniq,
+                                                const int32_t* rows, int U,
+                                                const uint8_t* const* table, ThinTile* tt,
+                                                int32_t* tslot, int tt_n, int thin_all,
+                                                int lane) {
+  const int n = lane < U ? offs[lane + 1] - offs[lane] : 0;
+  const bool thin = lane < U && (thin_all || n <= kThinTokens);
+  const int ct = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
+  int tot;
+  const int run = wave_excl_scan(ct, lane, tot);
+  if (ct > 0) {
+    const uint8_t* blob = table[uniq[lane]];
+    const int off = offs[lane];
+    for (int j = 0; j < ct && run + j < tt_n; ++j) {
+      ThinTile r{};
+      r.blob = blob;
+      r.off = off;
+      r.cnt = n;
+      r.tok0 = j * kThinTokens;
+      tt[run + j] = r;
+      for (int i = 0; i < kTileSlots; ++i)
+        tslot[(size_t)(run + j) * kTileSlots + i] = rows[off + min(j * kThinTokens + i, n - 1)];
+    }
+  }
+  for (int j = tot + lane; j < tt_n; j += 64) tt[j] = ThinTile{};
+}
+
 }  // namespace moe
