@@ -115,16 +115,23 @@ constexpr int kDnBatch = 4;
 __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t* const* table,
                                                       PackArgs px) {
   __shared__ SmallRoute sr;
+  // the expert table travels with the logits into LDS, so the blobs of the
+  // union (down plan, thin tiles) are known without another memory round
+  // trip once it is formed
+  __shared__ const uint8_t* s_tab[kMaxE];
+  const uint8_t* const* tab = table ? table : px.tt ? px.table : nullptr;
+  if (tab)
+    for (int e = threadIdx.x; e < ro.E; e += 1024) s_tab[e] = tab[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  small_route(ro, sr, wave, 16);
+  small_route(ro, sr, wave, 16);  // ends with a block barrier
   if (px.mbo && wave == 15) {
     mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t,
                     px.thin_all, lane);
     if (px.tt)
-      thin_tiles_wave(sr.offsets, sr.uniq, sr.rows, sr.n, px.table, px.tt, px.tslot, px.tt_n,
+      thin_tiles_wave(sr.offsets, sr.uniq, sr.rows, sr.n, s_tab, px.tt, px.tslot, px.tt_n,
                       px.thin_all, lane);
   }
-  publish_small_route(ro, sr, table, 1024);
+  publish_small_route(ro, sr, table ? s_tab : nullptr, 1024);
 }
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part

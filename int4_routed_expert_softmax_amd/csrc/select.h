@@ -13,6 +13,7 @@
 #include <cfloat>
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "device_util.h"
 #include "moe_internal.h"
@@ -236,7 +237,13 @@ __device__ __forceinline__ void wave_topk(const double* zt, int E, int k, int32_
 // expert idx[l]); its key id * 64 + l orders picks by expert, then slot
 // (= token order).  A pick's rank among all keys is its position in rows; the
 // first pick of each expert opens a union entry.  uniq/offsets as
-// union_body; cnt_out[u] = picks of uniq[u].  s_sorted: n ints of scratch LDS.
+// union_body; cnt_out[u] = picks of uniq[u].  s_sorted: 64 ints of scratch
+// LDS, 16-byte aligned.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 __device__ __forceinline__ void wave_union_small(const int32_t* idx, int n, int E, int32_t* uniq,
                                                  int32_t* n_uniq, int32_t* offsets, int32_t* rows,
                                                  int32_t* s_sorted) {
@@ -244,15 +251,27 @@ __device__ __forceinline__ void wave_union_small(const int32_t* idx, int n, int 
   const bool valid = lane < n;
   const int id = valid ? idx[lane] : 0;
   const int key = valid ? id * 64 + lane : INT_MAX;
+  // rank = keys below this one: every lane reads all 64 keys from LDS (the
+  // same address in every lane: broadcast reads), 64 independent compares
+  s_sorted[lane] = key;
+  wave_lds_sync();
+  // (keys past n are INT_MAX: reading a few past n changes no rank)
   int rank = 0;
-  for (int s = 0; s < n; ++s) rank += __builtin_amdgcn_readlane(key, s) < key;  // lanes >= n: INT_MAX
+  auto count = [&](auto nk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < decltype(nk)::value; j += 4) {
+      const int4 kk = *reinterpret_cast<const int4*>(s_sorted + j);
+      rank += (kk.x < key) + (kk.y < key) + (kk.z < key) + (kk.w < key);
+    }
+  };
+  if (n <= 16) count(std::integral_constant<int, 16>());
+  else count(std::integral_constant<int, 64>());
+  wave_lds_sync();
   if (valid) {
     rows[rank] = lane;
     s_sorted[rank] = id;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  wave_lds_sync();
   // lane r now looks at sorted position r
   const int sid = valid ? s_sorted[lane] : 0;
   const int prev = (valid && lane > 0) ? s_sorted[lane - 1] : -1;

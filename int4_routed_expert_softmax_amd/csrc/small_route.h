@@ -25,7 +25,7 @@ struct SmallRoute {
   int32_t uniq[kSmallPicks];
   int32_t offsets[kSmallPicks + 1];
   int32_t rows[kSmallPicks];
-  int32_t sorted[kSmallPicks];
+  alignas(16) int32_t sorted[kSmallPicks];
   int32_t n;
   // per token, the best k of each 64-expert group (logit, id)
   double cz[kSmallBatch][64];
