@@ -169,6 +169,7 @@ struct RouterArgs {
   double* z;
   Digits xd;
   PackArgs px;  // px.dst set: workgroups past the logits and digit split pack px.rows rows
+  int tsplit;   // logit workgroups per expert, each over its own tokens (set by the launcher)
 };
 constexpr int kSmallBatch = 8;
 // The small-batch path recomputes routing inside the gate/up kernel with one

@@ -254,9 +254,11 @@ __device__ __forceinline__ double sum_waves(const double (&p)[kRFW]) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// Waves per row of the x pack: all 8 of a workgroup for one row, 4 for two,
-// else 2 (a sixth of a 6144-column row each, in registers).
-__host__ __device__ inline int rf_pack_waves(int rows) { return rows <= 1 ? 8 : rows <= 2 ? 4 : 2; }
+// Waves per row of the x pack: all 8 of a workgroup, one row per workgroup
+// (an eighth of a 6144-column row per wave): the pack workgroups share
+// compute units with the logit workgroups, and with 2 waves per row (4 rows a
+// workgroup) they finished after the logits (8 tokens: 7.4-8 us against 6).
+__host__ __device__ inline int rf_pack_waves(int) { return 8; }
 __host__ __device__ inline int rf_pack_blocks(int rows) {
   const int rpb = kRFW / rf_pack_waves(rows);
   return (rows + rpb - 1) / rpb;
@@ -264,14 +266,21 @@ __host__ __device__ inline int rf_pack_blocks(int rows) {
 
 template <int TB>
 __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
-  const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, d = a.d, E = a.E;
+  // workgroups [0, E tsplit): the logits of expert bx % E for tokens t0 ..
+  // t0 + Tl - 1 (tsplit > 1 only without RMSNorm or digit split); the others
+  // are numbered as if tsplit were 1
+  const int nlog = E * a.tsplit, bx = blockIdx.x;
+  const int e = bx < nlog ? bx % E : bx - nlog + E;
+  const int t0 = bx < nlog ? (bx / E) * TB : 0;
+  const int Tl = bx < nlog ? min(TB, T - t0) : T;
+  const int gx = (int)gridDim.x - nlog + E;
   // the last rf_pack_blocks workgroups pack the rows for the grouped GEMM,
   // alongside the logits, each row by rf_pack_waves waves
   const int pack_blocks = a.px.dst ? rf_pack_blocks(a.px.rows) : 0;
   if (pack_blocks) {
-    const int pb = (int)gridDim.x - pack_blocks;
+    const int pb = gx - pack_blocks;
     if (e >= pb) {
       __shared__ float s_m[kRFW];
       const int nw = rf_pack_waves(a.px.rows);
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
     for (int m = 0; m < kReg; ++m) {
       const int i4 = tid + kRF * m;
       if (e < E && i4 < n4) wr[m] = reinterpret_cast<const float4*>(a.Wr + (size_t)e * d)[i4];
-      if (TB == 1 && i4 < n4) xr[m] = xval4(0, i4);
+      if (TB == 1 && i4 < n4) xr[m] = xval4(t0, i4);
     }
   }
   if (a.prenorm) {
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
     // columns of a token
     const int nb = d / 64, nch = d / kChunk, ng = d / kXGroup;
     for (int it = (e - E) * kRFW + wave; it < T * nb;
-         it += ((int)gridDim.x - E - pack_blocks) * kRFW) {
+         it += (gx - E - pack_blocks) * kRFW) {
       const int t = it / nb, col = (it % nb) * 64 + lane;
       digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
                  a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
         for (int j = 0; j < TB; ++j) {
           // unconditional loads (rows past the batch repeat the last one,
           // their sums are never stored): all rows' loads go out together
-          const int jj = TB == 1 ? 0 : (j < T ? j : T - 1);
+          const int jj = t0 + (TB == 1 ? 0 : (j < Tl ? j : Tl - 1));
           const float4 v = TB == 1 ? xr[m] : xval4(jj, i4);
           acc[j] += (double)w.x * (double)norm(jj, v.x);
           acc[j] += (double)w.y * (double)norm(jj, v.y);
@@ -398,11 +407,11 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
       const float4 w = w4[i];
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
-        if (j < T) {
-          acc[j] += (double)w.x * (double)xin(j, 4 * i);
-          acc[j] += (double)w.y * (double)xin(j, 4 * i + 1);
-          acc[j] += (double)w.z * (double)xin(j, 4 * i + 2);
-          acc[j] += (double)w.w * (double)xin(j, 4 * i + 3);
+        if (j < Tl) {
+          acc[j] += (double)w.x * (double)xin(t0 + j, 4 * i);
+          acc[j] += (double)w.y * (double)xin(t0 + j, 4 * i + 1);
+          acc[j] += (double)w.z * (double)xin(t0 + j, 4 * i + 2);
+          acc[j] += (double)w.w * (double)xin(t0 + j, 4 * i + 3);
         }
       }
     }
@@ -414,9 +423,9 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
     if (lane == 0) part[j][wave] = sj;
   }
   __syncthreads();
-  if (tid < T) {
+  if (tid < Tl) {
     const double sj = sum_waves(part[tid]);
-    a.z[(size_t)tid * E + e] = sj + (a.bias ? (double)a.bias[e] : 0.0);
+    a.z[(size_t)(t0 + tid) * E + e] = sj + (a.bias ? (double)a.bias[e] : 0.0);
   }
 }
 
@@ -465,14 +474,18 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
                 rows, stats);
 }
 
-hipError_t launch_router_front(const RouterArgs& a, hipStream_t s) {
+hipError_t launch_router_front(const RouterArgs& a_in, hipStream_t s) {
+  RouterArgs a = a_in;
   const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + kRFW - 1) / kRFW : 0;
   if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1)) return hipErrorInvalidValue;
   const int pack_blocks = a.px.dst ? rf_pack_blocks(a.px.rows) : 0;
-  const dim3 grid(a.E + dig_blocks + pack_blocks);
+  // without RMSNorm and digit split (the grouped GEMM's small batches), 5 to
+  // 8 tokens take two workgroups per expert, each over its own tokens
+  a.tsplit = (!dig_blocks && !a.prenorm && a.T > 4) ? 2 : 1;
+  const dim3 grid(a.E * a.tsplit + dig_blocks + pack_blocks);
   if (a.T <= 1) return launch(1, k_router_front<1>, grid, dim3(kRF), s, a);
   if (a.T <= 2) return launch(1, k_router_front<2>, grid, dim3(kRF), s, a);
-  if (a.T <= 4) return launch(1, k_router_front<4>, grid, dim3(kRF), s, a);
+  if (a.T <= 4 || a.tsplit == 2) return launch(1, k_router_front<4>, grid, dim3(kRF), s, a);
   return launch(1, k_router_front<8>, grid, dim3(kRF), s, a);
 }
 
