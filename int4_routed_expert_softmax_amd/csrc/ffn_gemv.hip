@@ -499,7 +499,10 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.x * R;
-  const int U = *n_uniq;
+  // one token picks k distinct experts: the union has k entries, known
+  // without waiting for the published count
+  const int U = cb.k;
+  (void)n_uniq;
   const int nch = f / kChunk, nga = srow(f, pr);
   const size_t fd = (size_t)f * d;
   __shared__ float s_y[kSmallPicks][R];
