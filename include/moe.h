@@ -365,6 +365,52 @@ enum {
 int moe_timing_arm(int kernel, void* const* start_events, void* const* stop_events, int n);
 
 /*
+ * Phase trace — instrumentation, not part of the layer's computation.  Only
+ * lib/libmoe_trace.so (the same sources built with MOE_PHASE_TRACE, same
+ * entry points) records; in libmoe.so both calls return MOE_EUNSUPPORTED and
+ * the kernels carry no trace code.  Every workgroup of a traced kernel writes
+ * a record of 8 uint64 words, record b for workgroup index b (flattened over
+ * the grid, modulo 32768), after it finishes:
+ *   [0] start, [1..5] the kernel's trace points (0: not reached), [6] end:
+ *       readings of the device's 100 MHz clock (one counter for the whole
+ *       chip, so records of one launch share a time line);
+ *   [7] (compute unit id << 8) | tag.
+ * Traced kernels (`which`), their points and tags:
+ *   MOE_TRACE_GATEUP_GEMV   single-token gate/up family: 1-3 routing prologue
+ *                           (per-group sorts, merges, union; one token only),
+ *                           4 the first wave's rows streamed, 5 every wave's;
+ *                           tag 1, or 0 for a block without an expert;
+ *   MOE_TRACE_ROUTE_SMALL   k_route_small: 1 sorts, 2 merges, 3 union,
+ *                           4 maps and routing published;
+ *   MOE_TRACE_DOWN_T1       one-token down + combine: 1 the first wave's
+ *                           experts streamed, 2 every wave's;
+ *   MOE_TRACE_ROUTER_FRONT  small-batch router front end: tag 1 logits,
+ *                           2 x pack, 3 digit split;
+ *   MOE_TRACE_GATEUP_THIN, MOE_TRACE_DOWN_THIN  thin grouped GEMM alone:
+ *                           1 tile known and first copies issued (0: no
+ *                           tile), 2 first stage landed, 3 last stage done;
+ *   MOE_TRACE_GATEUP_MIXED, MOE_TRACE_DOWN_MIXED  mixed launch: start and end
+ *                           only; tag 1 M-blocked, 2 thin, 3 empty M-block slot.
+ * moe_trace_read copies the first `bytes` bytes (at most 32768 records) of a
+ * kernel's records into host memory `dst`, synchronously; moe_trace_reset
+ * zeroes every record.  Records stay until a later launch of the kernel
+ * overwrites them.  Neither call may run while traced kernels are in flight.
+ */
+enum {
+  MOE_TRACE_GATEUP_GEMV = 0,
+  MOE_TRACE_ROUTE_SMALL = 1,
+  MOE_TRACE_DOWN_T1 = 2,
+  MOE_TRACE_ROUTER_FRONT = 3,
+  MOE_TRACE_GATEUP_THIN = 4,
+  MOE_TRACE_DOWN_THIN = 5,
+  MOE_TRACE_GATEUP_MIXED = 6,
+  MOE_TRACE_DOWN_MIXED = 7,
+  MOE_TRACE_COUNT = 8
+};
+int moe_trace_read(int which, void* dst, size_t bytes);
+int moe_trace_reset(void);
+
+/*
  * moe_hbm_read_probe — measurement helper, not part of the layer: one kernel
  * that streams `bytes` bytes of device memory at `buf` (16-byte aligned,
  * bytes a multiple of 16) through non-temporal 16-byte loads, eight in

@@ -14,7 +14,11 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
+# MOE_PHASE_TRACE=1 in the environment loads lib/libmoe_trace.so instead: the
+# same library with the phase trace compiled in (moe_trace_read), for
+# measurement only.
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe_trace.so" if os.environ.get("MOE_PHASE_TRACE") == "1"
+                        else "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_PRENORM_RMS, MOE_RESIDUAL, MOE_BATCH_INVARIANT = 1, 2, 4
@@ -25,10 +29,15 @@ EXPORTS = ("moe_expert_blob_bytes", "moe_workspace_bytes", "moe_workspace_routin
            "moe_strerror", "moe_route",
            "moe_union", "moe_expert_ffn", "moe_layer_forward", "moe_cache_state_bytes",
            "moe_layer_forward_cached", "moe_layer_forward_noalloc", "moe_timing_arm",
-           "moe_hbm_read_probe")
+           "moe_trace_read", "moe_trace_reset", "moe_hbm_read_probe")
 
 # Bytes of the library's own per-GPU workspace behind moe_layer_forward_noalloc.
 NOALLOC_SCRATCH_BYTES = 32 << 20
+
+# Traced kernels for moe_trace_read (records of 8 uint64 words per workgroup).
+TRACES = {"gateup_gemv": 0, "route_small": 1, "down_t1": 2, "router_front": 3,
+          "gateup_thin": 4, "down_thin": 5, "gateup_mixed": 6, "down_mixed": 7}
+TRACE_RECORDS, TRACE_WORDS = 32768, 8
 
 # Kernel ids for moe_timing_arm.
 KERNELS = {"rmsnorm": 0, "logits": 1, "topk": 2, "union": 3, "digitize": 4, "gateup": 5,
@@ -116,6 +125,10 @@ def _load():
                                             ctypes.c_float, vp, vp]
     L.moe_timing_arm.restype = ctypes.c_int
     L.moe_timing_arm.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int]
+    L.moe_trace_read.restype = ctypes.c_int
+    L.moe_trace_read.argtypes = [ctypes.c_int, vp, sz]
+    L.moe_trace_reset.restype = ctypes.c_int
+    L.moe_trace_reset.argtypes = []
     L.moe_hbm_read_probe.restype = ctypes.c_int
     L.moe_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     rt = _hip_runtimes()
@@ -296,6 +309,19 @@ def moe_timing_arm(kernel: str, start_events, stop_events):
 def moe_timing_disarm(handle) -> int:
     """Disarm; returns how many launches were recorded."""
     return lib.moe_timing_arm(handle[0], None, None, 0)
+
+
+def moe_trace_read(kernel: str, records: int = TRACE_RECORDS):
+    """The first `records` phase-trace records of `kernel` as a uint64 array
+    [records][8] (libmoe_trace.so only; MoeError MOE_EUNSUPPORTED otherwise)."""
+    import numpy as np
+    out = np.zeros((records, TRACE_WORDS), dtype=np.uint64)
+    _check(lib.moe_trace_read(TRACES[kernel], out.ctypes.data, out.nbytes), "moe_trace_read")
+    return out
+
+
+def moe_trace_reset():
+    _check(lib.moe_trace_reset(), "moe_trace_reset")
 
 
 def moe_hbm_read_probe(buf, sink, blocks: int, stream=None):

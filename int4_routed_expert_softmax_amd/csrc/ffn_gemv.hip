@@ -27,11 +27,18 @@
 #include "device_util.h"
 #include "moe_internal.h"
 #include "cache.h"
+#include "trace.h"
 #include "pack.h"
 #include "small_route.h"
 #include "select.h"
 
 namespace moe {
+
+MOE_TRACE_STORAGE(g_trace_gemv, 3)
+hipError_t trace_read_gemv(int slot, void* dst, size_t bytes) {
+  return g_trace_gemv_read(slot, dst, bytes);
+}
+hipError_t trace_reset_gemv() { return g_trace_gemv_reset(); }
 
 constexpr int kStreams = 4;                          // row streams per block
 constexpr int kRowsPerStream = 16;
@@ -123,7 +130,10 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
   if (tab)
     for (int e = threadIdx.x; e < ro.E; e += 1024) s_tab[e] = tab[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  small_route(ro, sr, wave, 16);  // ends with a block barrier
+  // trace points: 1 per-group sorts, 2 merges, 3 union, 4 published
+  BlockTrace tr;
+  tr.start();
+  small_route(ro, sr, wave, 16, &tr);  // ends with a block barrier
   if (px.mbo && wave == 15) {
     mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t,
                     px.thin_all, lane);
@@ -132,6 +142,11 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
                       px.thin_all, lane);
   }
   publish_small_route(ro, sr, table ? s_tab : nullptr, 1024);
+  if constexpr (kTrace) {
+    __syncthreads();
+    tr.mark(4);
+    tr.store(g_trace_gemv, 1, 0, 1);
+  }
 }
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
@@ -224,6 +239,11 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay scalar
   const int stream = wave / C, slice = wave % C;
+  // trace points: 1-3 the routing prologue's (one token: sorts, merges,
+  // union), 4 the first wave's rows streamed, 5 every wave's (block barrier)
+  BlockTrace tr;
+  tr.start();
+  const unsigned tblock = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   __shared__ float s_g[NT][kRowsPerBlock][C], s_u[NT][kRowsPerBlock][C];
   ExpertRef ex;
   const int32_t* list;
@@ -235,17 +255,22 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
     // in LDS once the union is known
     __shared__ const uint8_t* s_tab[kMaxE];
     for (int e = threadIdx.x; e < E; e += 256 * C) s_tab[e] = L.table[e];
-    small_route(ro, sr, wave, 4 * C);
+    small_route(ro, sr, wave, 4 * C, &tr);
     if (rb == 0 && u == 0) publish_small_route(ro, sr, s_tab, 256 * C);
-    if (u >= sr.n) return;
+    if (u >= sr.n) {
+      tr.store(g_trace_gemv, 0, tblock, 0);
+      return;
+    }
     ex.blob = s_tab[sr.uniq[u]];
     ex.beg = sr.offsets[u];
     ex.n = sr.offsets[u + 1] - ex.beg;
     list = sr.rows;
     kdiv = k;
   } else {
-    if (!L.single && u >= *L.n_uniq) return;
-    if (L.hit && L.hit[u] != L.want_hit) return;
+    if ((!L.single && u >= *L.n_uniq) || (L.hit && L.hit[u] != L.want_hit)) {
+      tr.store(g_trace_gemv, 0, tblock, 0);
+      return;
+    }
     ex = expert_ref(L, u);
     list = L.single ? nullptr : L.list;
     kdiv = L.kdiv;
@@ -268,7 +293,9 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
     for (int j = 0; j < NT; ++j) xrow[j] = j < nt ? slot_at(t0 + j) / kdiv : 0;
     gateup_rows<C, NT>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u,
                        L.per_row);
+    if (t0 == grp * NT) tr.mark(4);
     __syncthreads();
+    if (t0 == grp * NT) tr.mark(5);
     if (wave < nt) {
       // wave j: token j, the block's 64 rows (four 16-wide groups of a)
       const int j = wave;
@@ -286,6 +313,7 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
     }
     __syncthreads();
   }
+  tr.store(g_trace_gemv, 0, tblock, 1);
 }
 
 template <int C, bool SMALL, int NT>
@@ -505,6 +533,9 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
   (void)n_uniq;
   const int nch = f / kChunk, nga = srow(f, pr);
   const size_t fd = (size_t)f * d;
+  // trace points: 1 the first wave's experts streamed, 2 every wave's
+  BlockTrace tr;
+  tr.start();
   __shared__ float s_y[kSmallPicks][R];
   __shared__ float s_w[kSmallPicks];
   // epilogue operands first: thread t < R owns output row r0 + t
@@ -544,13 +575,16 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
       }
     }
   }
+  tr.mark(1);
   __syncthreads();
+  tr.mark(2);
   if (owner) {
     float acc = 0.0f;
     for (int j = 0; j < cb.k; ++j) acc += s_w[j] * s_y[j][threadIdx.x];
     if (cb.resid) acc = res + acc;
     cb.out[r0 + threadIdx.x] = acc;
   }
+  tr.store(g_trace_gemv, 2, blockIdx.x, 1);
 }
 
 // out[t][c] = (x[t][c] if resid) + sum_j w[t][j] * y[t*k + j][c], ascending j.

@@ -38,8 +38,15 @@
 #include "moe.h"
 #include "moe_internal.h"
 #include "pack.h"
+#include "trace.h"
 
 namespace moe {
+
+MOE_TRACE_STORAGE(g_trace_mfma, 4)
+hipError_t trace_read_mfma(int slot, void* dst, size_t bytes) {
+  return g_trace_mfma_read(slot, dst, bytes);
+}
+hipError_t trace_reset_mfma() { return g_trace_mfma_reset(); }
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -714,8 +721,12 @@ __device__ __forceinline__ void sw_scales(int w, int src, uint4 a0, uint4 a1, ui
   sd[3][1] = (uint32_t)__shfl((int)r1.w, src, 64);
 }
 
-template <int MODE, int GW, int R, int BITS, bool PA = false, bool SW = false>
-__device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jx, int jy) {
+// Trace points (tr): 1 the tile known and its first copies issued, 2 the
+// first stage landed, 3 the last stage computed.
+template <int MODE, int GW, int R, int BITS, bool PA = false, bool SW = false,
+          typename Marks = NoMarks>
+__device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jx, int jy,
+                                          Marks& tr) {
   using Shape = ThinShape<GW, R, BITS, PA, SW>;
   constexpr bool kUnitsA = PA && MODE == kDown;
   static_assert(!PA || GW % 4 == 0, "a group of a spans 4 waves");
@@ -758,28 +769,49 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   const int32_t* tsl = L.single ? nullptr : g.tslot + (size_t)jy * kTileSlots;
   // slot of the tile's token i (past the last token: the last one)
   auto slot_of = [&](int i) -> int { return L.single ? min(tok0 + i, cnt - 1) : tsl[i]; };
-  // packed activation row of the tile's token i
-  auto row_of = [&](int i) -> uint32_t {
-    const int slot = slot_of(i);
+  // packed activation row of a slot
+  auto row_of_slot = [&](int slot) -> uint32_t {
     return (uint32_t)(MODE == kGateUp && !L.single ? slot / L.kdiv : slot);
   };
   // the epilogue's slots and units of this lane's tokens 4 kg + i (lane
-  // (n, kg), n = lane & 15).  4-wave blocks request them now, so that their
-  // latency hides behind the main loop; 16-wave blocks (one block a CU, long
-  // main loops) load them at the end and keep the registers
-  int eslot[4];
+  // (n, kg), n = lane & 15).  4-wave blocks request the slots now, with the
+  // activation rows' slots (one wait covers both), and the units (which
+  // depend on the slots) at the start of the last stage, whose wait for every
+  // copy covers them too: a load of the units here would be waited for
+  // before the first copies.  16-wave blocks (one a CU, long main loops) load
+  // both at the end and keep the registers.
+  // This lane's slots: its activation row's, its correction row's and (4-wave
+  // blocks) the epilogue's, read in one branch so that a union's loads of
+  // them go out together and one wait covers them.
+  const int tl = threadIdx.x & 63, tkg = tl >> 4;
+  const int a_row = 4 * (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3) + tkg;
+  constexpr bool kEpiEarly = GW <= 4;
+  int eslot[4], sl_a, sl_c;
   float eunit[4];
-  auto epi_load = [&]() __attribute__((always_inline)) {
+  if (L.single) {
+    sl_a = min(tok0 + a_row, cnt - 1);
+    sl_c = min(tok0 + (tl & 15), cnt - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) eslot[i] = slot_of(4 * ((threadIdx.x & 63) >> 4) + i);
+    for (int i = 0; i < 4; ++i) eslot[i] = min(tok0 + 4 * tkg + i, cnt - 1);
+  } else {
+    sl_a = tsl[a_row];
+    sl_c = tsl[tl & 15];
+    if constexpr (kEpiEarly) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eslot[i] = tsl[4 * tkg + i];
+    }
+  }
+  auto epi_slots = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eslot[i] = slot_of(4 * tkg + i);
+  };
+  auto epi_units = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (MODE == kGateUp) eunit[i] = g.unit[L.single ? eslot[i] : eslot[i] / L.kdiv];
       else eunit[i] = kUnitsA ? 1.0f : g.unit[eslot[i]];
     }
   };
-  constexpr bool kEpiEarly = GW <= 4;
-  if constexpr (kEpiEarly) epi_load();
 
   // ---- this wave's 32 weight rows (gate/up: 16 gate rows and the same 16 up
   // rows); waves past the last row copy the last wave's rows, compute nothing
@@ -816,11 +848,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     b_src[i] = (r < kHalf ? c0 : c1) + (size_t)(r % kHalf) * row_bytes + piece * 16;
   }
   const bool a_copy = wave < 4 && 4 * wave < mcnt;  // wave-uniform
-  const int a_row = 4 * (wave & 3) + (lane >> 4);
-  const uint32_t a_off = row_of(a_row) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
+  const uint32_t a_off = row_of_slot(sl_a) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
   // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1); with
   // per-group A units, lanes 32..63 copy the units the same way
-  const size_t cu_row = (size_t)row_of(lane & 15) * ngc + ((lane >> 4) & 1);
+  const size_t cu_row = (size_t)row_of_slot(sl_c) * ngc + ((lane >> 4) & 1);
   const float* cu_lane = (kUnitsA && lane >= 32 ? g.unit : g.corr) + cu_row;
   // scales: lane l < 32 -> row l of the wave, 16 bytes (8 groups) every 4 stages
   const int sr_lane = lane % kThinWaveRows;
@@ -916,8 +947,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 #pragma unroll
   for (int i = 0; i < R - 1; ++i)
     if (i < nst) issue(i);
+  tr.mark(1);
   auto step = [&](int st, auto phase, const uint32_t (&sd)[2]) __attribute__((always_inline)) {
     constexpr int PH = decltype(phase)::value;  // stage % 4
+    if (kEpiEarly && st == nst - 1) epi_units();
     if (st + R - 2 < nst) {
       // stage st has landed once at most the copies of stages st + 1 ..
       // st + R - 2 are in flight
@@ -936,6 +969,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (st == 0) tr.mark(2);
     // every wave is past stage st - 1: its ring slot takes stage st + R - 1
     if (st + R - 1 < nst) issue(st + R - 1);
     if (active) {
@@ -956,8 +990,12 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     step(st0 + 2, std::integral_constant<int, 2>(), sd[2]);
     step(st0 + 3, std::integral_constant<int, 3>(), sd[3]);
   }
+  tr.mark(3);
 
-  if constexpr (!kEpiEarly) epi_load();
+  if constexpr (!kEpiEarly) {
+    epi_slots();
+    epi_units();
+  }
 
   if constexpr (PA && MODE == kGateUp) {
     // lane (n, kg): a at column c = 16 wv + n for tile tokens 4 kg + i (rows
@@ -1041,7 +1079,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
 template <int MODE, int GW, int R, int BITS, bool PA, bool SW>
 __global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS, PA, SW>::kLdsBytes];
-  thin_body<MODE, GW, R, BITS, PA, SW>(g, s_lds, blockIdx.x, blockIdx.y);
+  BlockTrace tr;
+  tr.start();
+  thin_body<MODE, GW, R, BITS, PA, SW>(g, s_lds, blockIdx.x, blockIdx.y, tr);
+  tr.store(g_trace_mfma, MODE, blockIdx.x + gridDim.x * blockIdx.y, 1);
 }
 
 // One launch for a batch's whole union: the first g.thick_blocks blocks run
@@ -1060,15 +1101,26 @@ __global__ __launch_bounds__(1024) void k_gemm_mixed(GemmArgs g) {
   constexpr int kA = RingShape<16, 3, 64, 2>::kLdsBytes;
   constexpr int kB = ThinShape<16, kMixedThinRing, 4, false, SW>::kLdsBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kA > kB ? kA : kB];
+  // trace: start and end of every workgroup, tag 1 M-blocked, 2 thin, 3 an
+  // empty M-block slot
+  BlockTrace tr;
+  tr.start();
+  NoMarks none;
   const int F = blockIdx.x;
+  int tag = 2;
   if (F < g.thick_blocks) {
     const int x = F % kXcds, q = F / kXcds, i = q / g.gx;
-    if (i >= g.xcnt[x]) return;
-    gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, q % g.gx, g.xtab[x * g.xs + i]);
+    if (i >= g.xcnt[x]) {
+      tag = 3;
+    } else {
+      gemm_body<MODE, 16, 3, 64, 2>(g, s_lds, q % g.gx, g.xtab[x * g.xs + i]);
+      tag = 1;
+    }
   } else {
     const int Ft = F - g.thick_blocks;
-    thin_body<MODE, 16, kMixedThinRing, 4, false, SW>(g, s_lds, Ft % g.gx, Ft / g.gx);
+    thin_body<MODE, 16, kMixedThinRing, 4, false, SW>(g, s_lds, Ft % g.gx, Ft / g.gx, none);
   }
+  tr.store(g_trace_mfma, 2 + MODE, F, tag);
 }
 
 // ---------------------------------------------------------------- launchers

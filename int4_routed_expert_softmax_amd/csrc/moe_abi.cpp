@@ -10,6 +10,7 @@
 
 #include "cache.h"
 #include "moe_internal.h"
+#include "trace.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -564,6 +565,29 @@ MOE_API int moe_timing_arm(int kernel, void* const* start_events, void* const* s
   t.n = n;
   t.next = 0;
   return recorded;
+}
+
+MOE_API int moe_trace_read(int which, void* dst, size_t bytes) {
+  if (which < 0 || which >= MOE_TRACE_COUNT || !dst) return MOE_EINVAL;
+  if (!kTrace) return MOE_EUNSUPPORTED;
+  if (bytes > sizeof(uint64_t) * kTraceBlocks * kTraceWords) return MOE_EINVAL;
+  hipError_t e;
+  switch (which) {
+    case MOE_TRACE_GATEUP_GEMV: e = trace_read_gemv(0, dst, bytes); break;
+    case MOE_TRACE_ROUTE_SMALL: e = trace_read_gemv(1, dst, bytes); break;
+    case MOE_TRACE_DOWN_T1: e = trace_read_gemv(2, dst, bytes); break;
+    case MOE_TRACE_ROUTER_FRONT: e = trace_read_route(0, dst, bytes); break;
+    default: e = trace_read_mfma(which - MOE_TRACE_GATEUP_THIN, dst, bytes); break;
+  }
+  return hip_status(e);
+}
+
+MOE_API int moe_trace_reset(void) {
+  if (!kTrace) return MOE_EUNSUPPORTED;
+  MOE_TRY(trace_reset_gemv());
+  MOE_TRY(trace_reset_mfma());
+  MOE_TRY(trace_reset_route());
+  return MOE_OK;
 }
 
 MOE_API int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,

@@ -15,8 +15,15 @@
 #include "moe_internal.h"
 #include "pack.h"
 #include "select.h"
+#include "trace.h"
 
 namespace moe {
+
+MOE_TRACE_STORAGE(g_trace_route, 1)
+hipError_t trace_read_route(int slot, void* dst, size_t bytes) {
+  return g_trace_route_read(slot, dst, bytes);
+}
+hipError_t trace_reset_route() { return g_trace_route_reset(); }
 
 // ---------------------------------------------------------------- RMSNorm
 // xn[t][i] = h[t][i] * r, r = 1 / sqrt(mean(h^2) + eps), mean and root in
@@ -264,8 +271,9 @@ __host__ __device__ inline int rf_pack_blocks(int rows) {
   return (rows + rpb - 1) / rpb;
 }
 
+// Returns the workgroup's kind (trace tag): 1 logits, 2 x pack, 3 digit split.
 template <int TB>
-__global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
+__device__ __forceinline__ int router_front_body(const RouterArgs& a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, d = a.d, E = a.E;
   // workgroups [0, E tsplit): the logits of expert bx % E for tokens t0 ..
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
       const int nw = rf_pack_waves(a.px.rows);
       const int r = (e - pb) * (kRFW / nw) + wave / nw;
       pack_row_split(a.px, r < a.px.rows ? r : -1, wave % nw, nw, s_m, wave, lane);
-      return;
+      return 2;
     }
   }
   __shared__ double part[TB][kRFW];
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
       digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
                  a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
     }
-    return;
+    return 3;
   }
   double acc[TB];
 #pragma unroll
@@ -427,6 +435,15 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
     const double sj = sum_waves(part[tid]);
     a.z[(size_t)(t0 + tid) * E + e] = sj + (a.bias ? (double)a.bias[e] : 0.0);
   }
+  return 1;
+}
+
+template <int TB>
+__global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
+  BlockTrace tr;
+  tr.start();
+  const int tag = router_front_body<TB>(a);
+  tr.store(g_trace_route, 0, blockIdx.x, tag);
 }
 
 // ---------------------------------------------------------------- digit split

@@ -15,6 +15,7 @@
 #include "device_util.h"
 #include "moe_internal.h"
 #include "select.h"
+#include "trace.h"
 
 namespace moe {
 
@@ -37,9 +38,9 @@ struct SmallRoute {
 // every group of every token, one wave per group, stored as runs of K2 with
 // odd groups reversed.  Stage 2: one wave per token merges its runs; lanes
 // 0..k-1 are the token's top k (its best k are among its groups' best K2).
-template <int K2>
+template <int K2, typename Marks>
 __device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, int wave,
-                                           int nwaves) {
+                                           int nwaves, Marks* tr) {
   const int T = ro.T, E = ro.E, k = ro.k;
   const int lane = threadIdx.x & 63;
   const int G = (E + 63) / 64;
@@ -64,6 +65,7 @@ __device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, i
     }
   }
   __syncthreads();
+  if (tr) tr->mark(1);
   int span = K2;
   while (span < G * K2) span *= 2;
   for (int t = wave; t < T; t += nwaves) {
@@ -79,26 +81,30 @@ __device__ __forceinline__ void small_topk(const RouteOut& ro, SmallRoute& sr, i
 // Top-k and batch union of a small batch (T <= kSmallBatch, T * k <=
 // kSmallPicks) from its complete logits ro.z, into sr, by the block's nwaves
 // waves (every thread of the block takes part).
+// Trace points (tr): 1 per-group sorts done, 2 merges done, 3 union done.
+template <typename Marks = NoMarks>
 __device__ __forceinline__ void small_route(const RouteOut& ro, SmallRoute& sr, int wave,
-                                            int nwaves) {
+                                            int nwaves, Marks* tr = nullptr) {
   const int T = ro.T, E = ro.E, k = ro.k;
   const int G = (E + 63) / 64;
   const int K2 = k <= 1 ? 1 : 1 << (32 - __builtin_clz(k - 1));
   if (G * K2 <= 64) {
     switch (K2) {
-      case 1: small_topk<1>(ro, sr, wave, nwaves); break;
-      case 2: small_topk<2>(ro, sr, wave, nwaves); break;
-      case 4: small_topk<4>(ro, sr, wave, nwaves); break;
-      case 8: small_topk<8>(ro, sr, wave, nwaves); break;
-      case 16: small_topk<16>(ro, sr, wave, nwaves); break;
-      default: small_topk<32>(ro, sr, wave, nwaves); break;
+      case 1: small_topk<1>(ro, sr, wave, nwaves, tr); break;
+      case 2: small_topk<2>(ro, sr, wave, nwaves, tr); break;
+      case 4: small_topk<4>(ro, sr, wave, nwaves, tr); break;
+      case 8: small_topk<8>(ro, sr, wave, nwaves, tr); break;
+      case 16: small_topk<16>(ro, sr, wave, nwaves, tr); break;
+      default: small_topk<32>(ro, sr, wave, nwaves, tr); break;
     }
   } else {
     for (int t = wave; t < T; t += nwaves) wave_topk(ro.z + (size_t)t * E, E, k, sr.idx + t * k, sr.w + t * k);
   }
   __syncthreads();
+  if (tr) tr->mark(2);
   if (wave == 0) wave_union_small(sr.idx, T * k, E, sr.uniq, &sr.n, sr.offsets, sr.rows, sr.sorted);
   __syncthreads();
+  if (tr) tr->mark(3);
 }
 
 // Writes a small batch's routing (ids, weights, union, slot lists, stats and,

@@ -218,3 +218,23 @@ def test_workspace_routing_rejects_bad_arguments():
     bad = moe.Dims(6144, 2048, 256, 8, 32)
     assert moe.lib.moe_workspace_routing(ctypes.byref(bad.c()), 1, ctypes.byref(o)) == \
         moe.MOE_EUNSUPPORTED
+
+
+def test_trace_calls_are_refused_by_the_product_library():
+    # libmoe.so carries no trace code: both calls say so before touching the GPU
+    import numpy as np
+    buf = np.zeros((4, moe.TRACE_WORDS), dtype=np.uint64)
+    assert moe.lib.moe_trace_read(0, buf.ctypes.data, buf.nbytes) == moe.MOE_EUNSUPPORTED
+    assert moe.lib.moe_trace_reset() == moe.MOE_EUNSUPPORTED
+    assert moe.lib.moe_trace_read(-1, buf.ctypes.data, buf.nbytes) == moe.MOE_EINVAL
+    assert moe.lib.moe_trace_read(8, buf.ctypes.data, buf.nbytes) == moe.MOE_EINVAL
+    assert moe.lib.moe_trace_read(0, None, buf.nbytes) == moe.MOE_EINVAL
+
+
+def test_trace_library_exports_the_same_abi():
+    import subprocess
+    path = os.path.join(os.path.dirname(moe.LIB_PATH), "libmoe_trace.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    ours = {l.split()[-1] for l in out.splitlines() if l.split()[-1].startswith("moe_")}
+    assert ours == set(moe.EXPORTS)
