@@ -77,8 +77,9 @@ def calibrate_copy(mib):
 # Sources the gate/up kernel of each path is built from: the one-token
 # GEMV path (decode, chain) and the grouped GEMM (batches of 2+ tokens).
 GATEUP_SOURCES = ("cache.h", "device_util.h", "ffn_gemv.hip", "moe_internal.h", "pack.h",
-                  "select.h", "small_route.h")
-GEMM_SOURCES = ("device_util.h", "ffn_mfma.hip", "moe_internal.h", "pack.h", "small_route.h")
+                  "select.h", "small_route.h", "trace.h")
+GEMM_SOURCES = ("device_util.h", "ffn_mfma.hip", "moe_internal.h", "pack.h", "small_route.h",
+                "trace.h")
 
 
 def matrix_bytes(w):
