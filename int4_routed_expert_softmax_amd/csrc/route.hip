@@ -70,10 +70,15 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, int 
   __shared__ double s_x[kLgC][kLgT + 1];
   __shared__ double s_w[kLgC][kLgE + 1];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int t0 = blockIdx.x * kLgT;
+  // workgroup F runs on XCD F % 8: every workgroup of column range F % 8
+  // shares one L2, which then fetches that range of x and of the router rows
+  // once for all its token and expert blocks
+  static_assert(kLogSplit == kXcds, "one column range per XCD");
+  const int F = blockIdx.x, split = F % kLogSplit, q = F / kLogSplit;
+  const int ntb = (T + kLgT - 1) / kLgT;
+  const int t0 = (q % ntb) * kLgT;
   const int nt = min(kLgT, T - t0);
-  const int split = blockIdx.y;
-  const int e0 = blockIdx.z * kLgE;
+  const int e0 = (q / ntb) * kLgE;
   const int nchunk = d / kLgC;
   const int c_begin = split * nchunk / kLogSplit, c_end = (split + 1) * nchunk / kLogSplit;
 
@@ -474,7 +479,7 @@ hipError_t launch_rmsnorm(const float* h, float* xn, int T, int d, float eps, hi
 
 hipError_t launch_logits(const void* x, int x_bf16, int T, int d, int E, const float* Wr,
                          double* zp, hipStream_t s) {
-  const dim3 grid((T + kLgT - 1) / kLgT, kLogSplit, (E + kLgE - 1) / kLgE);
+  const dim3 grid((unsigned)(kLogSplit * ((T + kLgT - 1) / kLgT) * ((E + kLgE - 1) / kLgE)));
   return launch(1, k_logits, grid, dim3(256), s, x, x_bf16, T, d, E, Wr, zp);
 }
 
