@@ -60,7 +60,9 @@
  *    Calls enqueue only kernels (no memset/memcpy), so they may be captured in
  *    a HIP graph.
  *  - `ws` is a caller-provided device workspace of at least
- *    moe_workspace_bytes(dims, T) bytes.  Its contents need not be
+ *    moe_workspace_bytes(dims, T) bytes, 16-byte aligned (hipMalloc and
+ *    torch's allocator return 256-byte aligned blocks; a misaligned ws is
+ *    MOE_EINVAL).  Its contents need not be
  *    initialised: every call writes each word of it before reading it.  Calls
  *    that share a workspace must not overlap in time.
  *  - All arguments are validated before anything is enqueued; on error the

@@ -135,8 +135,7 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
   tr.start();
   small_route(ro, sr, wave, 16, &tr);  // ends with a block barrier
   if (px.mbo && wave == 15) {
-    mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.mbo_t, px.blk_t,
-                    px.thin_all, lane);
+    mblock_map_wave(sr.offsets, sr.n, px.mblock, px.mbo, px.blk_u, px.thin_all, lane);
     if (px.tt)
       thin_tiles_wave(sr.offsets, sr.uniq, sr.rows, sr.n, s_tab, px.tt, px.tslot, px.tt_n,
                       px.thin_all, lane);
@@ -693,13 +692,11 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
   PackArgs px{};
   if (map) {
     // one wave maps a union of at most 64 experts
-    if (!map->mbo || !map->blk_u || !map->mbo_t || !map->blk_t || map->mblock < 1 ||
+    if (!map->mbo || !map->blk_u || map->mblock < 1 ||
         ro.T * ro.k > 64)
       return hipErrorInvalidValue;
     px.mbo = map->mbo;
     px.blk_u = map->blk_u;
-    px.mbo_t = map->mbo_t;
-    px.blk_t = map->blk_t;
     px.mblock = map->mblock;
     px.thin_all = map->thin_all;
     px.tt = map->tt;

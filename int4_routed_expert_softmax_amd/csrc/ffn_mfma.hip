@@ -94,22 +94,23 @@ __device__ __forceinline__ int find_bucket(const int32_t* p, int n, int j) {
 
 // ---------------------------------------------------------------- packing
 // One wave per row (pack.h); with mbo set, the last block instead writes the
-// union's M-block prefix: mbo[u] = sum over u' < u of ceil(count(u') /
-// mblock), u = 0..U.
+// union's M-block prefix (mbo[u] = sum over u' < u of ceil(count(u') /
+// mblock), u = 0..U), with tt set the thin tiles, with xtab set the XCD
+// placement of the M-blocks.
 __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   if (p.mbo && blockIdx.x == gridDim.x - 1) {
     // thread t maps experts 4t .. 4t + 3: thin ones (at most kThinTokens
-    // tokens, or every expert with thin_all) take one thin block per
+    // tokens, or every expert with thin_all) take one thin tile per
     // kThinTokens tokens, the others ceil(count / mblock) M-blocks; two
     // block-wide exclusive scans place them
     __shared__ int s_tot[2][4];
+    __shared__ int s_tb[4 * 256 + 1];  // thin tiles before expert u, u = 0..U
     const int U = *p.n_uniq, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int c[4], th[4], nn[4], sum = 0, sum_t = 0;
+    int c[4], th[4], sum = 0, sum_t = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = 4 * t + i;
       const int n = u < U ? p.offsets[u + 1] - p.offsets[u] : 0;
-      nn[i] = n;
       const bool thin = u < U && (p.thin_all || n <= kThinTokens);
       th[i] = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
       c[i] = u < U && !thin ? (n + p.mblock - 1) / p.mblock : 0;
@@ -140,25 +141,8 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
       const int u = 4 * t + i;
       if (u < U) {
         p.mbo[u] = run;
-        p.mbo_t[u] = run_t;
         for (int j = 0; j < c[i]; ++j) p.blk_u[run + j] = u;
-        for (int j = 0; j < th[i]; ++j) p.blk_t[run_t + j] = u;
-        if (p.tt && th[i] > 0) {
-          // the expert's thin tiles (same order as blk_t)
-          const uint8_t* blob = p.table[p.uniq[u]];
-          const int off = p.offsets[u], n = nn[i];
-          for (int j = 0; j < th[i] && run_t + j < p.tt_n; ++j) {
-            ThinTile r{};
-            r.blob = blob;
-            r.off = off;
-            r.cnt = n;
-            r.tok0 = j * kThinTokens;
-            p.tt[run_t + j] = r;
-            for (int q = 0; q < kTileSlots; ++q)
-              p.tslot[(size_t)(run_t + j) * kTileSlots + q] =
-                  p.list[off + min(j * kThinTokens + q, n - 1)];
-          }
-        }
+        s_tb[u] = run_t;
       }
       run += c[i];
       run_t += th[i];
@@ -166,10 +150,41 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
     const int tot_t = s_tot[1][0] + s_tot[1][1] + s_tot[1][2] + s_tot[1][3];
     if (t == 0) {
       p.mbo[U] = s_tot[0][0] + s_tot[0][1] + s_tot[0][2] + s_tot[0][3];
-      p.mbo_t[U] = tot_t;
+      s_tb[U] = tot_t;
     }
-    if (p.tt)
+    if (p.tt) {
+      // the thin tiles, expert by expert, kThinTokens tokens a tile: one
+      // tile a thread, its 16 slot loads issued together (an expert of
+      // several hundred tokens has tens of tiles)
+      __syncthreads();
+      const int nt = min(tot_t, p.tt_n);
+      for (int j = t; j < nt; j += (int)blockDim.x) {
+        // the tile's expert: s_tb[u] <= j < s_tb[u + 1] (experts without
+        // thin tiles have s_tb[u] == s_tb[u + 1])
+        int lo = 0, hi = U;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_tb[mid] <= j) lo = mid;
+          else hi = mid;
+        }
+        const int off = p.offsets[lo], n = p.offsets[lo + 1] - off;
+        const int tok0 = (j - s_tb[lo]) * kThinTokens;
+        int v[kTileSlots];
+#pragma unroll
+        for (int q = 0; q < kTileSlots; ++q) v[q] = p.list[off + min(tok0 + q, n - 1)];
+        ThinTile r{};
+        r.blob = p.table[p.uniq[lo]];
+        r.off = off;
+        r.cnt = n;
+        r.tok0 = tok0;
+        p.tt[j] = r;
+        int4* ds = reinterpret_cast<int4*>(p.tslot + (size_t)j * kTileSlots);
+#pragma unroll
+        for (int q = 0; q < kTileSlots / 4; ++q)
+          ds[q] = make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
       for (int j = tot_t + t; j < p.tt_n; j += (int)blockDim.x) p.tt[j] = ThinTile{};
+    }
     if (!p.xtab) return;
     // The M-blocked experts onto the 8 XCDs (blocks of a launch go to the
     // XCDs in turn, and an XCD's blocks share its L2): whole experts, in
@@ -1173,8 +1188,6 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
     px.n_uniq = L.n_uniq;
     px.mbo = m.mbo;
     px.blk_u = m.blk_u;
-    px.mbo_t = m.mbo_t;
-    px.blk_t = m.blk_t;
     px.mblock = mfma_mblock(m.x_rows);
     px.xtab = m.xtab;
     px.xcnt = m.xcnt;

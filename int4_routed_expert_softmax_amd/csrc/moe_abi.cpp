@@ -57,8 +57,6 @@ Layout layout(int d, int f, int E, int k, int T) {
   L.acorr = take(Tk * (f / kGroup) * sizeof(float));
   L.mbo = take((cap + 1) * sizeof(int32_t));
   L.blku = take((cap + Tk / kMinMBlock + 1) * sizeof(int32_t));
-  L.mbot = take((cap + 1) * sizeof(int32_t));
-  L.blkt = take((cap + Tk / kThinTokens + 1) * sizeof(int32_t));
   L.xtab = take(((size_t)kXcds * xcd_stride(T, k, (int)cap) + kXcds) * sizeof(int32_t));
   // thin tiles: at most cap + ceil(T k / kThinTokens) (the launch's thin blocks)
   const size_t ntile = cap + (Tk + kThinTokens - 1) / kThinTokens;
@@ -149,8 +147,6 @@ MfmaArgs mfma_args(void* ws, const Layout& L, int d, int f) {
   m.acorr = at<float>(ws, L.acorr);
   m.mbo = at<int32_t>(ws, L.mbo);
   m.blk_u = at<int32_t>(ws, L.blku);
-  m.mbo_t = at<int32_t>(ws, L.mbot);
-  m.blk_t = at<int32_t>(ws, L.blkt);
   m.xtab = at<int32_t>(ws, L.xtab);
   m.tt = at<ThinTile>(ws, L.tt);
   m.tslot = at<int32_t>(ws, L.tslot);
@@ -216,7 +212,7 @@ MOE_API int moe_route(const moe_dims* dm, const void* x, int x_dtype, int32_t T,
   int st = dims_status(dm);
   if (st != MOE_OK) return st;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (T < 1 || !x || !w_router || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+  if (T < 1 || !x || !w_router || !topk_idx || !topk_w || !ws || !aligned(ws, 16)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_EINVAL;
   const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, T);
   if (ws_bytes < ws_need(L, dm->n_experts)) return MOE_ENOSPC;
@@ -258,7 +254,7 @@ MOE_API int moe_expert_ffn(const moe_dims* dm, const void* expert_blob, const vo
   int st = dims_status(dm);
   if (st != MOE_OK) return st;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (n < 1 || !expert_blob || !x || !y || !ws) return MOE_EINVAL;
+  if (n < 1 || !expert_blob || !x || !y || !ws || !aligned(ws, 16)) return MOE_EINVAL;
   if (!aligned(expert_blob, 16) || !aligned(x, 4) || !aligned(y, 4)) return MOE_EINVAL;
   const Layout L = layout(dm->d, dm->f, dm->n_experts, dm->top_k, n);
   if (ws_bytes < ws_need(L, dm->n_experts)) return MOE_ENOSPC;
@@ -304,7 +300,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
   const bool invariant = (flags & MOE_BATCH_INVARIANT) != 0;
   if (invariant && T >= 1 && !small_batch(T, dm->top_k)) return MOE_EUNSUPPORTED;
-  if (T < 1 || !x || !w_router || !expert_table || !out || !ws) return MOE_EINVAL;
+  if (T < 1 || !x || !w_router || !expert_table || !out || !ws || !aligned(ws, 16)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4)) return MOE_EINVAL;
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
   const int d = dm->d, f = dm->f, E = dm->n_experts, k = dm->top_k;
@@ -461,7 +457,8 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT))
     return MOE_EUNSUPPORTED;
   if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
-  if (T < 1 || !x || !w_router || !home_table || !slots || !cache_state || !out || !ws)
+  if (T < 1 || !x || !w_router || !home_table || !slots || !cache_state || !out || !ws ||
+      !aligned(ws, 16))
     return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4) || !aligned(slots, 256) ||
       !aligned(cache_state, 4))

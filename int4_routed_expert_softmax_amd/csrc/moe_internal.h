@@ -40,7 +40,7 @@ struct Digits {
 
 struct Layout {
   size_t tickets, z, xn, xq, xsx, xsc, idx, w, uniq, offs, nuniq, rows, aq, asx, asc, y;
-  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, mbot, blkt, xtab, tt, tslot,
+  size_t xh, xunit, xcorr, a32, ah, aunit, aunitg, acorr, mbo, blku, xtab, tt, tslot,
       plan, total;
 };
 
@@ -133,13 +133,11 @@ struct PackArgs {
   int thin_all;           // map every expert onto thin blocks (int8 and int2 layers)
   const int32_t* offsets;
   const int32_t* n_uniq;
-  // with mbo set: experts of at most kThinTokens tokens get one thin block
-  // each (mbo_t[u] = thin experts before u, blk_t[j] = the j-th), the others
-  // ceil(count / mblock) M-blocks (mbo[u] prefix, blk_u[j] = expert of M-block j)
+  // with mbo set: experts of more than kThinTokens tokens (none with
+  // thin_all) get ceil(count / mblock) M-blocks (mbo[u] prefix, blk_u[j] =
+  // expert of M-block j); the others run as thin tiles (tt below)
   int32_t* mbo;
   int32_t* blk_u;
-  int32_t* mbo_t;
-  int32_t* blk_t;
   int mblock;
   // with xtab set: the M-blocked experts placed on the 8 XCDs (each expert's
   // M-blocks on one, largest first onto the least loaded): xtab[x * xs + i]
@@ -271,8 +269,6 @@ struct MfmaArgs {
   float* acorr;              // [slots][f / 64]
   int32_t* mbo;              // [n_experts + 1]
   int32_t* blk_u;            // [mb_bound]
-  int32_t* mbo_t;            // [n_experts + 1]
-  int32_t* blk_t;            // [n_experts]
   int32_t* xtab;             // [kXcds][xs] M-blocks per XCD
   int32_t* xcnt;             // [kXcds]
   int xs;

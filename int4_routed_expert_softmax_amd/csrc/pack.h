@@ -212,12 +212,11 @@ __device__ __forceinline__ void pack_row_split(const PackArgs& p, int r, int par
   if (lane == 0 && part == 0) p.unit[r] = m > 0.0f ? ldexpf(1.0f, e - kPackExp) : 1.0f;
 }
 
-// M-block maps of a union of at most 64 experts (offs[0..U]), by one whole
-// wave: experts of at most kThinTokens tokens (every expert with thin_all)
-// get one thin block per kThinTokens tokens, listed in blk_t (mbo_t[u] = thin
-// blocks before u, mbo_t[U] their number); each other expert gets
+// M-block map of a union of at most 64 experts (offs[0..U]), by one whole
+// wave: experts of more than kThinTokens tokens (none with thin_all) get
 // ceil(count / mblock) M-blocks (mbo[u] = M-blocks before u, mbo[U] the total,
-// blk_u[j] = the expert of M-block j).
+// blk_u[j] = the expert of M-block j); the others run as thin tiles
+// (thin_tiles_wave).
 __device__ __forceinline__ int wave_excl_scan(int c, int lane, int& total) {
   int incl = c;
 #pragma unroll
@@ -229,25 +228,18 @@ __device__ __forceinline__ int wave_excl_scan(int c, int lane, int& total) {
   return incl - c;
 }
 __device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int mblock,
-                                                int32_t* mbo, int32_t* blk_u, int32_t* mbo_t,
-                                                int32_t* blk_t, int thin_all, int lane) {
+                                                int32_t* mbo, int32_t* blk_u, int thin_all,
+                                                int lane) {
   const int n = lane < U ? offs[lane + 1] - offs[lane] : 0;
   const bool thin = lane < U && (thin_all || n <= kThinTokens);
   const int c = lane < U && !thin ? (n + mblock - 1) / mblock : 0;
-  const int ct = thin ? (n + kThinTokens - 1) / kThinTokens : 0;
-  int tot, tot_t;
+  int tot;
   const int run = wave_excl_scan(c, lane, tot);
-  const int run_t = wave_excl_scan(ct, lane, tot_t);
   if (lane < U) {
     mbo[lane] = run;
-    mbo_t[lane] = run_t;
     for (int j = 0; j < c; ++j) blk_u[run + j] = lane;
-    for (int j = 0; j < ct; ++j) blk_t[run_t + j] = lane;
   }
-  if (lane == 0) {
-    mbo[U] = tot;
-    mbo_t[U] = tot_t;
-  }
+  if (lane == 0) mbo[U] = tot;
 }
 
 // The thin tiles of a union of at most 64 experts (offs[0..U], uniq, rows:

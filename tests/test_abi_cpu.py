@@ -91,6 +91,7 @@ def test_route_rejects_bad_arguments():
     assert call_route(GLM, x=FAKE + 4) == moe.MOE_EINVAL  # misaligned
     assert call_route(GLM, dtype=7) == moe.MOE_EUNSUPPORTED
     assert call_route(GLM, ws=None) == moe.MOE_EINVAL
+    assert call_route(GLM, ws=FAKE + 8) == moe.MOE_EINVAL  # workspace not 16-byte aligned
     assert call_route(GLM, ws_bytes=16) == moe.MOE_ENOSPC
     assert moe.lib.moe_route(None, FAKE, 0, 1, FAKE, None, FAKE, FAKE, FAKE, 1 << 30,
                              None) == moe.MOE_EINVAL

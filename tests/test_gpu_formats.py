@@ -92,20 +92,21 @@ def test_formats_glm(name):
     full_parity(W[name])
 
 
-def test_formats_glm_prefill512_int8_every_token():
-    w = W["prefill512_int8"]
+@pytest.mark.parametrize("bits", [8, 2])
+def test_formats_glm_prefill512_every_token(bits):
+    name = f"prefill512_int{bits}"
+    w = W[name]
     L = DeviceLayer(w)
     x, bf = configs.tokens(w)
-    say("prefill512_int8: layer call")
+    say(f"{name}: layer call")
     out, st = L.forward(L.x_device(x, bf))
-    say("prefill512_int8: oracle over all 512 tokens")
+    say(f"{name}: oracle over all 512 tokens")
     ref = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), w.d, w.f, w.top_k, x_bf16=True,
-                               bits=8)
+                               bits=bits)
     assert st[0].item() == ref["U"]
-    check_layer_routing(L.dims, L.last_ws, w.T, ref, "prefill512_int8 layer call")
-    rel = assert_close(out.cpu().numpy(), ref["out"], "prefill512_int8",
-                       case="prefill512_int8 flags=0")
-    say(f"prefill512_int8: U={ref['U']} rel err {rel:.2e}")
+    check_layer_routing(L.dims, L.last_ws, w.T, ref, f"{name} layer call")
+    rel = assert_close(out.cpu().numpy(), ref["out"], name, case=f"{name} flags=0")
+    say(f"{name}: U={ref['U']} rel err {rel:.2e}")
 
 
 def test_cached_layer_refuses_other_code_widths():
