@@ -26,6 +26,7 @@ HEADLINE = [
     ("prefill512_int8 flags=0", "int8 codes, thin GEMM, all 512 tokens"),
     ("decode1_int2 flags=0", "int2 codes, thin GEMM (T=1)"),
     ("verify8_int2 flags=0", "int2 codes, thin GEMM"),
+    ("prefill512_int2 flags=0", "int2 codes, thin GEMM, all 512 tokens"),
 ]
 
 
