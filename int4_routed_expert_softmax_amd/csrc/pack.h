@@ -243,9 +243,11 @@ __device__ __forceinline__ void mblock_map_wave(const int32_t* offs, int U, int 
 }
 
 // The thin tiles of a union of at most 64 experts (offs[0..U], uniq, rows:
-// the union's list), by one whole wave, in the order of the thin-block map
-// above (expert by expert, kThinTokens tokens a tile); the records from the
-// last tile to tt_n are marked empty.
+// the union's list), by one whole wave: the experts of at most kThinTokens
+// tokens (every expert with thin_all), expert by expert, kThinTokens tokens a
+// tile, each a record (blob, first list entry, token count, first token) and
+// its kTileSlots slot ids; the records from the last tile to tt_n are marked
+// empty.
 __device__ __forceinline__ void thin_tiles_wave(const int32_t* offs, const int32_t* uniq,
                                                 const int32_t* rows, int U,
                                                 const uint8_t* const* table, ThinTile* tt,
