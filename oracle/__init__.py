@@ -20,6 +20,7 @@ _lib = None
 
 PRENORM = 1
 RESIDUAL = 2
+I8ACT = 8  # integer activations (moe_ref.c, ref_expert_ffn_i8act)
 
 
 def build(force: bool = False) -> str:
@@ -74,6 +75,8 @@ def lib():
         L.ref_silu.restype = dbl
         L.ref_silu.argtypes = [dbl]
         L.ref_expert_ffn.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp]
+        L.ref_quant_i8.argtypes = [vp, i32, vp, vp]
+        L.ref_expert_ffn_i8act.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp]
         L.ref_route.argtypes = [i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
         L.ref_union.restype = i32
         L.ref_union.argtypes = [i32, i32, i32, vp, vp, vp, vp]
@@ -133,6 +136,26 @@ def expert_ffn(blob: np.ndarray, x: np.ndarray, d: int, f: int, group: int = 64,
     n = x.shape[0]
     y = np.empty((n, d), dtype=np.float64)
     lib().ref_expert_ffn(d, f, group, bits, _p(blob), _p(x), n, _p(y))
+    return y
+
+
+def quant_i8(v: np.ndarray):
+    """One activation row (fp32, a multiple of 64 columns) -> (q int8 [cols],
+    s float32 [cols / 64])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    q = np.empty(v.shape[-1], dtype=np.int8)
+    s = np.empty(v.shape[-1] // 64, dtype=np.float32)
+    lib().ref_quant_i8(_p(v), v.shape[-1], _p(q), _p(s))
+    return q, s
+
+
+def expert_ffn_i8act(blob: np.ndarray, x: np.ndarray, d: int, f: int, group: int = 64,
+                     bits: int = 4) -> np.ndarray:
+    """The expert FFN with integer activations; x rows are taken as fp32."""
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    n = x.shape[0]
+    y = np.empty((n, d), dtype=np.float64)
+    lib().ref_expert_ffn_i8act(d, f, group, bits, _p(blob), _p(x), n, _p(y))
     return y
 
 

@@ -55,6 +55,7 @@
 
 #define REF_PRENORM 1u
 #define REF_RESIDUAL 2u
+#define REF_I8ACT 8u
 
 /* ---- encodings ------------------------------------------------------------ */
 
@@ -194,6 +195,93 @@ void ref_expert_ffn(int d, int f, int gs, int bits, const uint8_t* blob, const d
   free(a);
 }
 
+/* ---- integer activations ------------------------------------------------- */
+
+/* The pages run the experts through hand-written integer dot-product kernels:
+ * int4 weights times integer activations, no BLAS (colibri 技术解读
+ * (linlog.top), "int4 量化与手写内核"; the nxmr blog's int8 kernels, «纯C语言»),
+ * without fixing how the activations are quantised.  Reading taken: each
+ * 64-column group of an activation row (the weights' scale group) is held as
+ * int8 q with one scale s = max|v| / 127, q = v / s rounded to the nearest
+ * integer (ties to even); a group of zeros has s = 0 and q = 0.  Both the
+ * scale and the rounding are taken in fp32 (the kernel's precision, so that
+ * both sides make the same integer decision on the same fp32 input).  cols is
+ * a multiple of 64; q[cols], s[cols / 64]. */
+void ref_quant_i8(const float* v, int cols, int8_t* q, float* s) {
+  for (int g = 0; g < cols / 64; ++g) {
+    const float* vg = v + (int64_t)g * 64;
+    float m = 0.0f;
+    for (int j = 0; j < 64; ++j)
+      if (fabsf(vg[j]) > m) m = fabsf(vg[j]);
+    const float sc = m / 127.0f;
+    s[g] = sc;
+    for (int j = 0; j < 64; ++j) {
+      float r = m > 0.0f ? rintf(vg[j] / sc) : 0.0f;
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      q[(int64_t)g * 64 + j] = (int8_t)r;
+    }
+  }
+}
+
+/* One row of a matrix times int8 activation rows: for each 64-column group g,
+ * the exact integer sum of code * q over the group, times the weight scale of
+ * the group (or of the row) and the activation scale s[g], summed over the
+ * groups in order in fp64. */
+static double row_dot_i8(const uint8_t* codes, const uint16_t* scales, int cols, int gs, int bits,
+                         int r, const int8_t* q, const float* s) {
+  const uint8_t* rc = codes + (int64_t)r * cols * bits / 8;
+  const uint16_t* rs = scales + (int64_t)r * row_scales(cols, gs);
+  double acc = 0.0;
+  for (int g = 0; g < cols / 64; ++g) {
+    int64_t dot = 0;
+    for (int j = 64 * g; j < 64 * g + 64; ++j) dot += (int64_t)ref_code(rc, j, bits) * q[j];
+    acc += ref_f16(rs[gs ? (64 * g) / gs : 0]) * (double)s[g] * (double)dot;
+  }
+  return acc;
+}
+
+/* The SwiGLU expert FFN with integer activations: x rows are quantised as
+ * above, g and u are integer dot products per group, a = silu(g) * u is
+ * rounded to fp32 (the precision the kernel holds it in) and quantised the
+ * same way, and y = Wd a is again integer dot products per group.  x[n][d]
+ * fp32 -> y[n][d] fp64; d and f multiples of 64. */
+void ref_expert_ffn_i8act(int d, int f, int gs, int bits, const uint8_t* blob, const float* x,
+                          int n, double* y) {
+  const uint8_t *gc, *uc, *dc;
+  const uint16_t *gsc, *usc, *dsc;
+  int rows, cols;
+  mat_view(blob, d, f, gs, bits, 0, &gc, &gsc, &rows, &cols);
+  mat_view(blob, d, f, gs, bits, 1, &uc, &usc, &rows, &cols);
+  mat_view(blob, d, f, gs, bits, 2, &dc, &dsc, &rows, &cols);
+  int8_t* xq = (int8_t*)malloc((size_t)n * d);
+  float* xs = (float*)malloc(sizeof(float) * (size_t)n * (d / 64));
+  for (int t = 0; t < n; ++t)
+    ref_quant_i8(x + (int64_t)t * d, d, xq + (int64_t)t * d, xs + (int64_t)t * (d / 64));
+  float* a = (float*)malloc(sizeof(float) * (size_t)n * f);
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < f; ++r)
+    for (int t = 0; t < n; ++t) {
+      const double g = row_dot_i8(gc, gsc, d, gs, bits, r, xq + (int64_t)t * d, xs + (int64_t)t * (d / 64));
+      const double u = row_dot_i8(uc, usc, d, gs, bits, r, xq + (int64_t)t * d, xs + (int64_t)t * (d / 64));
+      a[(int64_t)t * f + r] = (float)(ref_silu(g) * u);
+    }
+  int8_t* aq = (int8_t*)malloc((size_t)n * f);
+  float* as = (float*)malloc(sizeof(float) * (size_t)n * (f / 64));
+  for (int t = 0; t < n; ++t)
+    ref_quant_i8(a + (int64_t)t * f, f, aq + (int64_t)t * f, as + (int64_t)t * (f / 64));
+#pragma omp parallel for schedule(static)
+  for (int c = 0; c < d; ++c)
+    for (int t = 0; t < n; ++t)
+      y[(int64_t)t * d + c] =
+          row_dot_i8(dc, dsc, f, gs, bits, c, aq + (int64_t)t * f, as + (int64_t)t * (f / 64));
+  free(xq);
+  free(xs);
+  free(a);
+  free(aq);
+  free(as);
+}
+
 /* ---- router ---------------------------------------------------------------- */
 
 typedef struct {
@@ -300,6 +388,7 @@ void ref_rmsnorm(int d, const float* h, double eps, float* xn) {
  * memory; entries of experts no token selects may be NULL).  flags:
  *   REF_PRENORM  route and run experts on RMSNorm(x) (x fp32)
  *   REF_RESIDUAL out = x + MoE(...) (x fp32)
+ *   REF_I8ACT    the experts take integer activations (ref_expert_ffn_i8act)
  * Outputs: out[T][d] (fp64), idx/w [T][k], uniq/offsets/rows as ref_union,
  * reads[E] += 1 for every time an expert's blob is read.  Returns U, or -1 if
  * a selected expert has no blob. */
@@ -334,7 +423,15 @@ int ref_layer_forward(int d, int f, int gs, int bits, int E, int k, const void* 
       int t = rows[offsets[u] + i] / k;
       for (int c = 0; c < d; ++c) xs[(int64_t)i * d + c] = x_at(xin, xin_bf16, (int64_t)t * d + c);
     }
-    ref_expert_ffn(d, f, gs, bits, table[e], xs, n, ys); /* the one read of expert e */
+    if (flags & REF_I8ACT) {
+      /* the rows are fp32 values (fp32 or bf16 input, or the fp32 RMSNorm) */
+      float* xf = (float*)malloc(sizeof(float) * (size_t)n * d);
+      for (int64_t i = 0; i < (int64_t)n * d; ++i) xf[i] = (float)xs[i];
+      ref_expert_ffn_i8act(d, f, gs, bits, table[e], xf, n, ys); /* the one read of expert e */
+      free(xf);
+    } else {
+      ref_expert_ffn(d, f, gs, bits, table[e], xs, n, ys); /* the one read of expert e */
+    }
     reads[e] += 1;
     for (int i = 0; i < n; ++i)
       memcpy(yslot + (int64_t)rows[offsets[u] + i] * d, ys + (int64_t)i * d, sizeof(double) * d);

@@ -27,6 +27,7 @@ int ref_code(const uint8_t* row_codes, int64_t c, int bits);
 int64_t ref_blob_bytes(int d, int f, int gs, int bits);
 void ref_dequant(const uint8_t* blob, int d, int f, int gs, int bits, int which, double* W);
 double ref_silu(double v);
+void ref_quant_i8(const float* v, int cols, int8_t* q, float* s);
 void ref_expert_ffn(int d, int f, int gs, int bits, const uint8_t* blob, const double* x, int n,
                     double* y);
 void ref_route(int d, int E, int k, const void* x, int x_is_bf16, int T, const float* Wr,
@@ -182,6 +183,19 @@ int main(void) {
   run_layer("wide union", 64, 64, 64, 4, 96, 32, 3, 0, 0u, 1);
   run_layer("int8 codes", 128, 64, 64, 8, 12, 3, 5, 0, 0u, 1);
   run_layer("int2 codes, per-row", 192, 64, 0, 2, 12, 3, 5, 0, 3u, 1);
+  run_layer("integer activations", 128, 64, 64, 4, 12, 3, 5, 0, 8u, 1);
+  run_layer("integer activations, int8 codes, bf16", 128, 64, 64, 8, 10, 4, 6, 1, 8u, 1);
+  run_layer("integer activations, int2, per-row, rmsnorm + residual", 192, 64, 0, 2, 12, 3, 5, 0, 11u, 1);
+  {
+    float v[128] = {0};
+    int8_t q[128];
+    float sc[2];
+    v[70] = -1e-38f;
+    v[100] = 3e38f;
+    ref_quant_i8(v, 128, q, sc);
+    CHECK(sc[0] == 0.0f && q[0] == 0 && q[63] == 0, "quant: zero group");
+    CHECK(q[100] == 127 && q[70] == 0, "quant: extreme group");
+  }
   if (failures) {
     fprintf(stderr, "sanitized oracle: %d failures\n", failures);
     return 1;

@@ -580,3 +580,96 @@ def test_code_format_layer_brute_force(bits):
             xt = x[t].astype(np.float64)
             out[t] += p[j] * (Wd @ (np_silu(Wg @ xt) * (Wu @ xt)))
     np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12 * np.abs(out).max())
+
+
+# ---------------------------------------------------------- integer activations
+
+
+def test_quant_i8_invariants_and_ties():
+    rng = np.random.default_rng(17)
+    rows = [rng.normal(size=256) * 10.0 ** rng.integers(-6, 6),
+            np.concatenate([np.zeros(64), rng.normal(size=192)]),            # a group of zeros
+            np.concatenate([np.zeros(63), [-3.0], rng.uniform(-1, 1, 64)]),  # one non-zero, negative
+            rng.uniform(-1e-30, 1e-30, 128)]
+    for v in rows:
+        v = v.astype(np.float32)
+        q, s = oracle.quant_i8(v)
+        assert np.abs(q.astype(np.int64)).max() <= 127
+        for g in range(v.size // 64):
+            vg, qg = v[64 * g:64 * g + 64].astype(np.float64), q[64 * g:64 * g + 64]
+            m = np.abs(vg).max()
+            if m == 0:
+                assert s[g] == 0 and not qg.any()
+                continue
+            i = int(np.argmax(np.abs(vg)))
+            assert qg[i] == (127 if vg[i] > 0 else -127)           # the group's max is +-127
+            assert s[g] == np.float32(np.float32(m) / np.float32(127))
+            err = np.abs(vg - qg.astype(np.float64) * float(s[g]))
+            assert err.max() <= 0.5 * float(s[g]) * (1 + 2.0 ** -20)  # round to nearest
+    # integers with a 127 in the group: scale 1, codes equal to the values;
+    # halves go to the even neighbour
+    v = np.zeros(64, dtype=np.float32)
+    v[:8] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, 3.0, -126]
+    q, s = oracle.quant_i8(v)
+    assert s[0] == 1.0
+    assert list(q[:8]) == [127, 0, 2, 2, 0, -2, 3, -126]
+
+
+def grid_rows(rng, n, d, step=2.0 ** -4):
+    """Rows whose every 64-group holds integers times step with a +-127 in
+    it: on the int8 grid of their own group scale (s = step exactly)."""
+    q = rng.integers(-127, 128, size=(n, d))
+    q[:, ::64] = 127 * rng.choice([-1, 1], size=(n, d // 64))
+    return (q * step).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+def test_i8act_ffn_exact_gateup_and_bounded_down(bits):
+    """x on the int8 grid of its group scales reproduces x exactly, so gate
+    and up are the exact products; the only difference from the fp64 FFN is
+    the rounding of a to int8, bounded per output by sum_r |Wd[c,r]| s_a/2
+    (s_a: the fp32 scale of r's group of a)."""
+    d, f, n = 256, 128, 3
+    rng = np.random.default_rng(30 + bits)
+    blob = synth.expert_blob(8, 0, 3, d, f, bits=bits)
+    x = grid_rows(rng, n, d)
+    Wg, Wu, Wd = (np_dequant(blob, d, f, i) if bits == 4 else np_dequant_bits(blob, d, f, i, bits)
+                  for i in range(3))
+    xd = x.astype(np.float64)
+    a = np_silu(xd @ Wg.T) * (xd @ Wu.T)
+    exact = a @ Wd.T
+    y = oracle.expert_ffn_i8act(blob, x, d, f, bits=bits)
+    a32 = a.astype(np.float32)
+    for t in range(n):
+        s_a = np.repeat(np.abs(a32[t]).reshape(-1, 64).max(axis=1).astype(np.float32)
+                        / np.float32(127), 64).astype(np.float64)
+        bound = np.abs(Wd) @ (0.5 * s_a) * (1 + 1e-6) + 1e-9 * np.abs(exact[t]).max()
+        assert np.all(np.abs(y[t] - exact[t]) <= bound)
+        # and the rounding of a is really there: not the exact FFN
+        assert np.abs(y[t] - exact[t]).max() > 0
+
+
+def test_i8act_perrow_is_gs64_with_the_row_scale():
+    d, f = 256, 128
+    blob = synth.expert_blob(9, 0, 1, d, f, group=0)
+    x = np.random.default_rng(4).normal(size=(2, d)).astype(np.float32)
+    y_row = oracle.expert_ffn_i8act(blob, x, d, f, group=0)
+    y_gs = oracle.expert_ffn_i8act(perrow_as_gs64(blob, d, f), x, d, f, group=64)
+    assert np.array_equal(y_row, y_gs)
+
+
+def test_i8act_layer_is_the_mixture_of_integer_expert_ffns():
+    d, f, E, k, T = 128, 64, 8, 3, 5
+    rng = np.random.default_rng(12)
+    Wr = (rng.normal(size=(E, d)) * 0.05).astype(np.float32)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    blobs = [synth.expert_blob(7, 1, e, d, f) for e in range(E)]
+    r = oracle.layer_forward(x, Wr, None, blobs, d, f, k, flags=oracle.I8ACT)
+    r0 = oracle.layer_forward(x, Wr, None, blobs, d, f, k)
+    assert np.array_equal(r["idx"], r0["idx"]) and np.array_equal(r["w"], r0["w"])
+    out = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            e = r["idx"][t, j]
+            out[t] += r["w"][t, j] * oracle.expert_ffn_i8act(blobs[e], x[t], d, f)[0]
+    np.testing.assert_allclose(r["out"], out, rtol=1e-13, atol=1e-15 * np.abs(out).max())
