@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--batch-invariant", action="store_true",
                    help="verify8: run the batch with MOE_BATCH_INVARIANT (each token computed "
                         "exactly as in a one-token call)")
+    p.add_argument("--int8-act", action="store_true",
+                   help="run the layer with MOE_INT8_ACT: integer activations (int8 per 64-column "
+                        "group, exact group dot products on the int8 matrix cores)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 20 plain device-to-device copies of this many MiB (the known-size "
                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -92,7 +95,8 @@ def matrix_bytes(w):
 
 
 def gateup_sources(workload):
-    gemv = workload.startswith(("decode1", "chain48")) and not workload.endswith(("int8", "int2"))
+    gemv = (workload.startswith(("decode1", "chain48")) and not workload.endswith(("int8", "int2"))
+            and "i8act" not in workload)
     return GATEUP_SOURCES if gemv else GEMM_SOURCES
 
 
@@ -137,12 +141,16 @@ def main():
                           "layer is measured at one GPU's share"}), flush=True)
         sys.exit(2)
 
+    if a.int8_act and a.workload == "chain48":
+        sys.exit("--int8-act: the 48-layer chain runs the unquantised layer")
     if a.workload == "chain48":
         a.steps = 64 if a.steps is None else a.steps
         a.warmup = 2 if a.warmup is None else a.warmup
         return run_chain(a)
     a.steps = 200 if a.steps is None else a.steps
     a.warmup = 10 if a.warmup is None else a.warmup
+    if a.int8_act and a.host_tier:
+        sys.exit("--int8-act: the slot cache (--host-tier) serves the GEMV path only")
     if a.host_tier:
         return run_host_tier(a)
 
@@ -171,16 +179,16 @@ def main():
         print(f"bench: layer {l} resident", file=sys.stderr, flush=True)
 
     res = measure(moe, torch, w, layers, a.steps, a.warmup, a.batch_invariant,
-                  lambda l: configs.tokens(w, l))
+                  lambda l: configs.tokens(w, l), i8=a.int8_act)
     res["config"]["workload"] += f", {a.layers} rotating HBM-resident layers"
     ceil = hbm_ceiling(moe, torch)
     res["hbm_read_ceiling"] = ceil
     for key in ("roofline", "roofline_down"):
         res[key]["frac_of_read_ceiling"] = round(res[key]["achieved"] / ceil["GBps"], 4)
-    if w.T > 8:
+    if w.T > 8 and not a.int8_act:
         res["mfma"] = mfma_figures(moe, torch, w, layers[0], res.pop("_gateup"))
     res.pop("_gateup", None)
-    if a.workload == "decode1" and not a.no_extra:
+    if a.workload == "decode1" and not a.no_extra and not a.int8_act:
         # the other two single-layer workloads, measured on the same resident
         # layers (same shape and weight distributions; their own token recipes)
         extra = {}
@@ -208,12 +216,13 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def measure(moe, torch, w, layers, K, warmup, inv, tokens):
+def measure(moe, torch, w, layers, K, warmup, inv, tokens, i8=False):
     """One workload on resident layers: `warmup` untimed steps, then K steps
     timed as one HIP graph replay (step i on layer i mod len(layers), each
     layer with its own seeded tokens), K eager steps for comparison, K more
     with HIP events around every gate/up and down launch (the roofline), and
-    K with an event pair around each step (the spread)."""
+    K with an event pair around each step (the spread).  i8: the layer calls
+    take MOE_INT8_ACT."""
     dev = torch.device("cuda:0")
     R = len(layers)
     dims = moe.Dims(w.d, w.f, w.n_experts, w.top_k, group_size=w.group, code_bits=w.bits)
@@ -228,11 +237,12 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
     stats = torch.zeros(R, 1 + w.n_experts, dtype=torch.int32, device=dev)
     ws = moe.make_workspace(dims, w.T, dev)
     stream = torch.cuda.current_stream()
-    flags = moe.MOE_BATCH_INVARIANT if inv else 0
+    flags = (moe.MOE_BATCH_INVARIANT if inv else 0) | (moe.MOE_INT8_ACT if i8 else 0)
     # the library's choice: int4 layers take the int8-digit GEMV kernels for
     # one token (or with the flag), the fp16 MFMA grouped GEMM for 2+ tokens
-    # with d, f multiples of 512; int8 and int2 layers always the grouped GEMM
-    gemv = w.bits == 4 and (w.T == 1 or inv or w.d % 512 or w.f % 512)
+    # with d, f multiples of 512; int8 and int2 layers, and integer
+    # activations, always the grouped GEMM
+    gemv = w.bits == 4 and not i8 and (w.T == 1 or inv or w.d % 512 or w.f % 512)
 
     def step(i, s=None):
         L = layers[i % R]
@@ -312,13 +322,16 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if gemv else
+                  f"int{w.bits} weights x int8 activations (one scale per 64 columns), MFMA i32 "
+                  f"per group, f32 accumulate" if i8 else
                   f"int{w.bits} weights as fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name}: one MoE layer, d={w.d} f={w.f} E={w.n_experts} "
                                f"top-{w.top_k}, T={w.T} tokens "
                                f"({'bf16' if w.x_bf16 else 'fp32'} x), "
                                f"{'gs64' if w.group else 'per-row'} int{w.bits} experts "
-                               f"({blob} B each)" + (", MOE_BATCH_INVARIANT" if inv else ""),
+                               f"({blob} B each)" + (", MOE_BATCH_INVARIANT" if inv else "")
+                               + (", MOE_INT8_ACT" if i8 else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "layers_rotated": R, "distinct_experts_per_step": float(u_steps.mean())},
         "step_us_p10_p50_p90": [round(float(v), 2) for v in np.percentile(step_us, [10, 50, 90])],
@@ -327,7 +340,7 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens):
         "roofline": {"bound": "hbm", "kernel": "gateup (gate+up projections, SwiGLU)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": committed_traffic(w.name),
+                     "traffic": committed_traffic(w.name + ("_i8act" if i8 else "")),
                      "bytes_per_launch": float(gu_bytes.mean()),
                      "avg_launch_us": round(float(dur["gateup"].mean() * 1e6), 3),
                      "launch_us_p10_p50_p90": [round(float(v) * 1e6, 3) for v in

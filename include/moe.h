@@ -107,7 +107,8 @@ enum {
                               layer input itself (h_{l+1} = h_l + MoE(RMSNorm(h_l))): no
                               separate residual pointer is taken, so a residual other than
                               x cannot be expressed; callers with one add it themselves */
-  MOE_BATCH_INVARIANT = 4u /* each token's result as if it were alone in the call (see below) */
+  MOE_BATCH_INVARIANT = 4u, /* each token's result as if it were alone in the call (see below) */
+  MOE_INT8_ACT = 8u         /* integer activations: int8 per 64-column group (see below) */
 };
 
 /* Return codes. */
@@ -236,6 +237,24 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 Source: drafts and their batched verification must compute
  *                 the same function, pinned to one kernel family — README
  *                 工作原理 › 诚实的推测解码; 技术解读, "精度与语义：速度可以牺牲，语义不能".
+ *                 | MOE_INT8_ACT (d and f multiples of 512, else
+ *                 MOE_EUNSUPPORTED): the experts take integer activations, as
+ *                 the pages' hand-written integer dot-product kernels do (int4
+ *                 weights times integer activations, no BLAS — 技术解读,
+ *                 "int4 量化与手写内核"; the nxmr blog's int8 kernels, «纯C语言»).
+ *                 Each 64-column group of an expert's input row (x', and
+ *                 a = silu(g) * u) is held as int8 q = v / s rounded to the
+ *                 nearest integer (ties to even), s = max|v| / 127, both in
+ *                 fp32 (a group of zeros: s = 0); each group's dot product
+ *                 with the weight codes is exact in int32 on the int8 matrix
+ *                 cores, then times the weight scale and s in fp32.  Routing
+ *                 is unchanged.  The result is this quantised function: within
+ *                 2e-3 * max|ref| of an fp64 evaluation of it, and about
+ *                 1e-2 * max|ref| from the unquantised layer (the int8
+ *                 rounding of the activations).  Every batch size runs the
+ *                 thin grouped GEMM in 16-token tiles, so a token's result
+ *                 does not depend on its batch; with MOE_BATCH_INVARIANT too
+ *                 it is bit-identical to its one-token call.
  *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
  *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]
  *                 = number of tokens that picked expert e

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoe_trace.so" if os.environ.get("MOE_P
                         else "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_PRENORM_RMS, MOE_RESIDUAL, MOE_BATCH_INVARIANT = 1, 2, 4
+MOE_PRENORM_RMS, MOE_RESIDUAL, MOE_BATCH_INVARIANT, MOE_INT8_ACT = 1, 2, 4, 8
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4
 
 # Every function include/moe.h declares.

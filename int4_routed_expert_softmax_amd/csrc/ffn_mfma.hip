@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs p) {
   }
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= p.rows) return;
-  pack_row(p, r, threadIdx.x & 63);
+  if (p.i8) pack_row_i8(p, r, threadIdx.x & 63);
+  else pack_row(p, r, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------- projection
@@ -268,6 +269,10 @@ struct GemmArgs {
   float* a_unit;
   float* a_corr;
   float corr_off;
+  // ia (integer activations, with pa): a is int8 [rows][K] (bytes) with one
+  // fp32 scale per 64-column group in corr; gate/up writes a as int8 into
+  // a_out and its group scales into a_corr
+  int ia;
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(64 * GW) void k_gemm(GemmArgs g) {
 constexpr int kThinWaveRows = 32;
 constexpr int kSwWindows = 4;  // scales in registers: 32-group windows, K <= 8192
 
-template <int GW, int R, int BITS, bool PA = false, bool SW = false>
+template <int GW, int R, int BITS, bool PA = false, bool SW = false, bool IA = false>
 struct ThinShape {
   static constexpr int kRowStage = 16 * BITS;                 // code bytes of a row per stage
   static constexpr int kPieces = kRowStage / 16;              // its 16-byte pieces
@@ -621,10 +626,11 @@ struct ThinShape {
   static constexpr int kCopies = kThinWaveRows / kRowsPerCopy;  // code copies per wave and stage
   static constexpr int kBWave = kThinWaveRows * kRowStage;
   static constexpr int kStageB = GW * kBWave;
-  static constexpr int kStageA = kThinTokens * kSC * 2;       // 16 rows x 256 B
-  // [2 groups][16 tokens] f32 corrections, then (per-group A units) the
-  // same of units
-  static constexpr int kStageC = (PA ? 64 : 32) * 4;
+  // 16 activation rows of 128 columns: fp16 (256 B a row), or int8 (IA)
+  static constexpr int kStageA = kThinTokens * kSC * (IA ? 1 : 2);
+  // [2 groups][16 tokens] f32 corrections (IA: the activations' group
+  // scales), then (per-group A units) the same of units
+  static constexpr int kStageC = (PA && !IA ? 64 : 32) * 4;
   static constexpr int kStage = kStageB + kStageA + kStageC;
   static constexpr int kScalePiece = kThinWaveRows * 16;      // [32 rows][8 groups] fp16
   static constexpr int kScaleOff = R * kStage;
@@ -639,6 +645,7 @@ struct ThinShape {
   // come after the last use of the piece two back
   static_assert(R >= 3 && (SW || R <= 5), "ring depth");
   static_assert(GW >= 4, "waves 0..3 copy the 16 activation rows");
+  static_assert(!IA || PA, "integer activations: a travels as int8 by groups");
   static_assert(kThinTokens == 16, "one M-tile");
 };
 
@@ -736,14 +743,37 @@ __device__ __forceinline__ void sw_scales(int w, int src, uint4 a0, uint4 a1, ui
   sd[3][1] = (uint32_t)__shfl((int)r1.w, src, 64);
 }
 
+// Integer activations: a lane's 16 weights of a group (columns 16 kg ..
+// 16 kg + 15) as 16 signed bytes in column order, the B operand of
+// v_mfma_i32_16x16x64_i8 (lane (n, kg): K bytes 16 kg .. 16 kg + 15 of row or
+// column n, for A and B alike).  A byte field b of width w in two's
+// complement becomes its int8 value as ((b ^ 2^(w-1)) + 0x80 - 2^(w-1)) ^
+// 0x80 per byte: the sum stays below 0x100, so no byte carries into the next.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// 8 int4 codes (column j in bits 4j..4j+3) -> columns 0..3 and 4..7
+__device__ __forceinline__ void i4x8_to_i8(uint32_t w, int& c03, int& c47) {
+  const uint32_t lo = (((w & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;  // 0 2 4 6
+  const uint32_t hi = ((((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;  // 1 3 5 7
+  c03 = (int)__builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  c47 = (int)__builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+// 4 int2 codes (byte t: column j in bits 2j..2j+1) -> 4 bytes
+__device__ __forceinline__ int i2x4_to_i8(uint32_t t) {
+  const uint32_t x = (t | (t << 6) | (t << 12) | (t << 18)) & 0x03030303u;
+  return (int)(((x ^ 0x02020202u) + 0x7E7E7E7Eu) ^ 0x80808080u);
+}
+
 // Trace points (tr): 1 the tile known and its first copies issued, 2 the
 // first stage landed, 3 the last stage computed.
-template <int MODE, int GW, int R, int BITS, bool PA = false, bool SW = false,
+template <int MODE, int GW, int R, int BITS, bool PA = false, bool SW = false, bool IA = false,
           typename Marks = NoMarks>
 __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int jx, int jy,
                                           Marks& tr) {
-  using Shape = ThinShape<GW, R, BITS, PA, SW>;
-  constexpr bool kUnitsA = PA && MODE == kDown;
+  using Shape = ThinShape<GW, R, BITS, PA, SW, IA>;
+  // IA (integer activations): A is int8 [rows][K] with one fp32 scale per
+  // 64-column group in corr; each group is one v_mfma_i32_16x16x64_i8 per
+  // 16 weight rows (exact), times the weight scale and the A scale in fp32.
+  constexpr bool kUnitsA = PA && MODE == kDown && !IA;
   static_assert(!PA || GW % 4 == 0, "a group of a spans 4 waves");
   constexpr int kBWave = Shape::kBWave, kStageB = Shape::kStageB, kRowStage = Shape::kRowStage;
   constexpr int kPieces = Shape::kPieces, kRowsPerCopy = Shape::kRowsPerCopy;
@@ -799,7 +829,10 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   // blocks) the epilogue's, read in one branch so that a union's loads of
   // them go out together and one wait covers them.
   const int tl = threadIdx.x & 63, tkg = tl >> 4;
-  const int a_row = 4 * (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3) + tkg;
+  // the activation row this lane copies: 16 lanes (fp16) or 8 lanes (int8)
+  // a row, waves 0..3 (fp16) or 0..1 (int8)
+  const int a_row = IA ? 8 * (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) + (tl >> 3)
+                       : 4 * (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 3) + tkg;
   constexpr bool kEpiEarly = GW <= 4;
   int eslot[4], sl_a, sl_c;
   float eunit[4];
@@ -823,7 +856,8 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   auto epi_units = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (MODE == kGateUp) eunit[i] = g.unit[L.single ? eslot[i] : eslot[i] / L.kdiv];
+      if (IA) eunit[i] = 1.0f;  // the A scales were applied per group
+      else if (MODE == kGateUp) eunit[i] = g.unit[L.single ? eslot[i] : eslot[i] / L.kdiv];
       else eunit[i] = kUnitsA ? 1.0f : g.unit[eslot[i]];
     }
   };
@@ -862,8 +896,12 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     const int piece = thin_slot<BITS>(lane % kPieces, r);
     b_src[i] = (r < kHalf ? c0 : c1) + (size_t)(r % kHalf) * row_bytes + piece * 16;
   }
-  const bool a_copy = wave < 4 && 4 * wave < mcnt;  // wave-uniform
-  const uint32_t a_off = row_of_slot(sl_a) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
+  const bool a_copy = IA ? wave < 2 && 8 * wave < mcnt : wave < 4 && 4 * wave < mcnt;  // wave-uniform
+  // fp16: 16-byte piece (lane & 15) ^ row of a 256-byte row stage; int8:
+  // piece (lane & 7) ^ (row & 7) of a 128-byte one (elements of the row)
+  const uint32_t a_off =
+      IA ? row_of_slot(sl_a) * (uint32_t)K + (uint32_t)((lane & 7) ^ (a_row & 7)) * 16u
+         : row_of_slot(sl_a) * (uint32_t)K + (uint32_t)((lane & 15) ^ (a_row & 15)) * 8u;
   // corrections: lane l -> token l & 15, group 2 st + ((l >> 4) & 1); with
   // per-group A units, lanes 32..63 copy the units the same way
   const size_t cu_row = (size_t)row_of_slot(sl_c) * ngc + ((lane >> 4) & 1);
@@ -901,7 +939,13 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     const uint32_t so = (uint32_t)st * kRowStage;
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) dma16(b_src[i] + so, base + wave * kBWave + i * 1024);
-    if (a_copy) dma16(g.a + a_off + st * kSC, base + kStageB + 4 * wave * (kSC * 2));
+    if (a_copy) {
+      if constexpr (IA)
+        dma16(reinterpret_cast<const int8_t*>(g.a) + a_off + st * kSC,
+              base + kStageB + 8 * wave * kSC);
+      else
+        dma16(g.a + a_off + st * kSC, base + kStageB + 4 * wave * (kSC * 2));
+    }
     // the correction copy fills 32 x 4 bytes (64 x 4 with the units); without
     // units lanes 32..63 stay out of it
     if (wave == 0 && (kUnitsA || lane < 32)) dma4(cu_lane + 2 * st, base + kStageB + kStageA);
@@ -916,6 +960,44 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     const uint8_t* base = s_lds + (st % R) * kStage;
     const int gi = 2 * st + gg;
     const uint8_t* sc = s_scales + ((gi >> 3) & 1) * kScalePiece + (gi & 7) * 2;
+    if constexpr (IA) {
+      // A: token n's 16 bytes of the group (piece 4 gg + kg, swizzled by the
+      // row), its scales for tokens 4 kg .. 4 kg + 3
+      const uint8_t* ar = base + kStageB + n * kSC;
+      const i32x4 av = *reinterpret_cast<const i32x4*>(ar + (((4 * gg + kg) ^ (n & 7)) * 16));
+      const f32x4 s4 =
+          *reinterpret_cast<const f32x4*>(base + kStageB + kStageA + (16 * gg + 4 * kg) * 4);
+      const i32x4 z4 = {0, 0, 0, 0};
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = 16 * nt + n;
+        const uint8_t* row = base + wave * kBWave + r * kRowStage;
+        i32x4 bv;
+        if constexpr (BITS == 4) {
+          const uint2 w = *reinterpret_cast<const uint2*>(
+              row + thin_slot<4>(2 * gg + (kg >> 1), r) * 16 + 8 * (kg & 1));
+          int b0, b1, b2, b3;
+          i4x8_to_i8(w.x, b0, b1);
+          i4x8_to_i8(w.y, b2, b3);
+          bv = i32x4{b0, b1, b2, b3};
+        } else if constexpr (BITS == 8) {
+          bv = *reinterpret_cast<const i32x4*>(row + thin_slot<8>(4 * gg + kg, r) * 16);
+        } else {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(row + thin_slot<2>(gg, r) * 16 + 4 * kg);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) bv[m] = i2x4_to_i8((w >> (8 * m)) & 0xFFu);
+        }
+        const i32x4 pi = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, z4, 0, 0, 0);
+        float sv;
+        if constexpr (SW)
+          sv = (float)__builtin_bit_cast(_Float16, (uint16_t)(sd[nt] >> (16 * gg)));
+        else
+          sv = (float)*reinterpret_cast<const _Float16*>(sc + r * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] = fmaf((float)pi[i], sv * s4[i], acc[nt][i]);
+      }
+      return;
+    }
     const uint8_t* ar = base + kStageB + n * (kSC * 2);
     const int p0 = 8 * gg + 2 * kg;
     const f16x8 a0 = *reinterpret_cast<const f16x8*>(ar + (p0 ^ n) * 16);
@@ -1023,7 +1105,7 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float us = eunit[i] * 0x1p24f;
+      const float us = IA ? 1.0f : eunit[i] * 0x1p24f;
       v[i] = silu(acc[0][i] * us) * (acc[1][i] * us);
     }
     // ring slot nst % R: its last stage (nst - R) was computed by every wave
@@ -1037,6 +1119,27 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     // lane n < 4 of each row posts token 4 kg + n
     if (n < 4) red_m[wave * kThinTokens + 4 * kg + n] = n == 0 ? mx[0] : n == 1 ? mx[1] : n == 2 ? mx[2] : mx[3];
     __syncthreads();
+    if constexpr (IA) {
+      // a's group of 64 columns as int8: q = a / s to the nearest (ties to
+      // even), s = max|a| / 127 in fp32, into a_out (bytes, column order) and
+      // s into a_corr
+      if (!active) return;
+      const int grp = c / kGroup, ngroups = f / kGroup;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * kg + i >= mcnt) continue;
+        const int t = 4 * kg + i;
+        const float gmi =
+            fmaxf(fmaxf(red_m[q0 * kThinTokens + t], red_m[(q0 + 1) * kThinTokens + t]),
+                  fmaxf(red_m[(q0 + 2) * kThinTokens + t], red_m[(q0 + 3) * kThinTokens + t]));
+        const float sa = gmi / 127.0f;
+        const float q = gmi > 0.0f ? fminf(fmaxf(rintf(v[i] / sa), -127.0f), 127.0f) : 0.0f;
+        const int slot = eslot[i];
+        reinterpret_cast<int8_t*>(g.a_out)[(size_t)slot * f + c] = (int8_t)(int)q;
+        if (wave == q0 && n == i) g.a_corr[(size_t)slot * ngroups + grp] = sa;
+      }
+      return;
+    }
     float gm[4], up[4], hs[4];
     int ex[4];
     _Float16 h[4];
@@ -1079,11 +1182,11 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
     if (4 * kg + i >= mcnt) continue;
     const int slot = eslot[i];
     if (MODE == kGateUp) {
-      const float us = eunit[i] * 0x1p24f;
+      const float us = IA ? 1.0f : eunit[i] * 0x1p24f;
       const float gv = acc[0][i] * us, uv = acc[1][i] * us;
       g.out[(size_t)slot * f + kHalf * wv + n] = silu(gv) * uv;
     } else {
-      const float us = eunit[i] * 0x1p24f;
+      const float us = IA ? 1.0f : eunit[i] * 0x1p24f;
       float* orow = g.out + (size_t)slot * d + kThinWaveRows * wv;
       orow[n] = acc[0][i] * us;
       orow[16 + n] = acc[1][i] * us;
@@ -1091,12 +1194,13 @@ __device__ __forceinline__ void thin_body(const GemmArgs& g, uint8_t* s_lds, int
   }
 }
 
-template <int MODE, int GW, int R, int BITS, bool PA, bool SW>
+template <int MODE, int GW, int R, int BITS, bool PA, bool SW, bool IA = false>
 __global__ __launch_bounds__(64 * GW) void k_gemm_thin(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[ThinShape<GW, R, BITS, PA, SW>::kLdsBytes];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t s_lds[ThinShape<GW, R, BITS, PA, SW, IA>::kLdsBytes];
   BlockTrace tr;
   tr.start();
-  thin_body<MODE, GW, R, BITS, PA, SW>(g, s_lds, blockIdx.x, blockIdx.y, tr);
+  thin_body<MODE, GW, R, BITS, PA, SW, IA>(g, s_lds, blockIdx.x, blockIdx.y, tr);
   tr.store(g_trace_mfma, MODE, blockIdx.x + gridDim.x * blockIdx.y, 1);
 }
 
@@ -1182,7 +1286,8 @@ PackArgs mfma_x_pack_args(const MfmaArgs& m) {
   px.unit = m.xunit;
   px.corr = m.xcorr;
   px.corr_off = corr_offset(L.bits);
-  px.thin_all = L.bits != 4;
+  px.thin_all = L.bits != 4 || m.i8act;
+  px.i8 = m.i8act;
   if (!L.single) {
     px.offsets = L.offsets;
     px.n_uniq = L.n_uniq;
@@ -1224,6 +1329,11 @@ static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, bool big, hipSt
                               const GemmArgs& ga) {
   const dim3 grid(gx, gy), block(64 * kThinGW);
   const bool sw = big && scales_in_regs(ga, MODE == kGateUp ? ga.d : ga.f);
+  if (ga.ia) {
+    if (!ga.pa) return hipErrorInvalidValue;
+    if (sw) return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, true, true>, grid, block, s, ga);
+    return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, false, true>, grid, block, s, ga);
+  }
   if (ga.pa) {
     if (sw) return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, true>, grid, block, s, ga);
     return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, true, false>, grid, block, s, ga);
@@ -1232,11 +1342,12 @@ static hipError_t thin_launch(int kid, unsigned gx, unsigned gy, bool big, hipSt
   return launch(kid, k_gemm_thin<MODE, kThinGW, R, BITS, false, false>, grid, block, s, ga);
 }
 
-// Every expert of the call runs the thin GEMM: int8 and int2 layers, and int4
-// batches (or a single expert) of at most kThinTokens rows.
+// Every expert of the call runs the thin GEMM: int8 and int2 layers, integer
+// activations, and int4 batches (or a single expert) of at most kThinTokens
+// rows.
 static bool all_thin(const MfmaArgs& m) {
   const int rows = m.L.single ? m.L.single_n : m.x_rows;
-  return m.L.bits != 4 || rows <= kThinTokens;
+  return m.L.bits != 4 || m.i8act || rows <= kThinTokens;
 }
 
 template <int MODE>
@@ -1254,8 +1365,8 @@ static hipError_t project(const MfmaArgs& m, GemmArgs ga, hipStream_t s) {
   const bool big = rows > kThinTokens;
   if (L.bits == 8) return thin_launch<MODE, 8, 3>(kid_thin, gx, gy, big, s, ga);
   if (L.bits == 2) return thin_launch<MODE, 2, 4>(kid_thin, gx, gy, big, s, ga);
-  if (rows <= kThinTokens)
-    return thin_launch<MODE, 4, MODE == kDown ? kThinRingDown : kThinRing>(kid_thin, gx, gy, false,
+  if (rows <= kThinTokens || ga.ia)
+    return thin_launch<MODE, 4, MODE == kDown ? kThinRingDown : kThinRing>(kid_thin, gx, gy, big,
                                                                           s, ga);
   if (L.single) {
     const GemmShape sh = gemm_shape(rows, true);
@@ -1294,12 +1405,14 @@ hipError_t launch_ffn_mfma(const MfmaArgs& m, hipStream_t s) {
     ga.a_unit = m.aunit_g;
     ga.a_corr = m.acorr;
     ga.corr_off = corr_offset(L.bits);
+    ga.ia = m.i8act;
   }
   e = project<kGateUp>(m, ga, s);
   if (e != hipSuccess) return e;
   if (pa_groups) {
     GemmArgs gd{L, m.mbo, m.blk_u, m.d, m.f, m.ah, m.aunit_g, m.y, m.acorr, m.tt, m.tslot, 0};
     gd.pa = 1;
+    gd.ia = m.i8act;
     return project<kDown>(m, gd, s);
   }
 

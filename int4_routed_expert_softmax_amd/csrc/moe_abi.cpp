@@ -295,11 +295,14 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   int st = dims_status(dm);
   if (st != MOE_OK) return st;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT))
+  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT | MOE_INT8_ACT))
     return MOE_EUNSUPPORTED;
   if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
   const bool invariant = (flags & MOE_BATCH_INVARIANT) != 0;
+  const bool i8act = (flags & MOE_INT8_ACT) != 0;
   if (invariant && T >= 1 && !small_batch(T, dm->top_k)) return MOE_EUNSUPPORTED;
+  // integer activations run on the thin grouped GEMM (int8 matrix cores)
+  if (i8act && !mfma_shape_ok(dm->d, dm->f)) return MOE_EUNSUPPORTED;
   if (T < 1 || !x || !w_router || !expert_table || !out || !ws || !aligned(ws, 16)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4)) return MOE_EINVAL;
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
@@ -330,10 +333,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.bits = code_bits(dm->code_bits);
   const int maxU = E < T * k ? E : T * k;
 
-  // int8 and int2 layers run every batch on the thin grouped GEMM (16-token
-  // tiles), whose per-token arithmetic does not depend on the batch, so the
-  // batch-invariant flag needs no separate path for them
-  if (EL.bits == 4 && (invariant || gemv_small_path(T, k, d, f))) {
+  // int8 and int2 layers, and integer activations, run every batch on the
+  // thin grouped GEMM (16-token tiles), whose per-token arithmetic does not
+  // depend on the batch, so the batch-invariant flag needs no separate path
+  // for them
+  if (EL.bits == 4 && !i8act && (invariant || gemv_small_path(T, k, d, f))) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (one token: in
     // every gate/up block's prologue; 2+: one k_route_small block) and
     // gate/up; 3: down + combine.  Every step keeps one order of
@@ -382,10 +386,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   }
   int x_packed = 0;
   // the thin GEMM's blocks per projection: int4, one per thin expert; int8
-  // and int2, one per 16 tokens of every expert (ceil(count / 16) < count /
-  // 16 + 1)
-  const int thin_bound =
-      EL.bits == 4 ? maxU : maxU + (T * k + kThinTokens - 1) / kThinTokens;
+  // and int2 layers and integer activations, one per 16 tokens of every
+  // expert (ceil(count / 16) < count / 16 + 1)
+  const int thin_bound = EL.bits == 4 && !i8act
+                             ? maxU
+                             : maxU + (T * k + kThinTokens - 1) / kThinTokens;
   if (small_batch(T, k)) {
     // a few tokens on the grouped GEMM: logits (+ bias) by the small-batch
     // router front end, top-k and union in one block
@@ -410,6 +415,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
       m.x_bf16 = xr_bf16;
       m.x_rows = T;
       m.thin_bound = thin_bound;
+      m.i8act = i8act;  // int8 rows (the front end's pack workgroups) and every expert thin
       ra.px = mfma_x_pack_args(m);
       MOE_TRY(launch_router_front(ra, s));
       MOE_TRY(launch_route_small(ro, nullptr, s, &ra.px));
@@ -436,6 +442,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.thin_bound = thin_bound;
     m.y = y;
     m.x_packed = x_packed;
+    m.i8act = i8act;
     MOE_TRY(launch_ffn_mfma(m, s));
   } else {
     MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));

@@ -130,7 +130,10 @@ struct PackArgs {
   float* unit;            // [rows]
   float* corr;            // [rows][K / 64]: -corr_off * 2^-24 * (sum of the group's packed values)
   float corr_off;         // the code width's offset: 8 (int4), 128 (int8), 2 (int2)
-  int thin_all;           // map every expert onto thin blocks (int8 and int2 layers)
+  int thin_all;           // map every expert onto thin blocks (int8 and int2 layers,
+                          // integer activations)
+  int i8;                 // integer activations: rows -> int8 per 64-column group
+                          // (dst as bytes, the group scales in corr)
   const int32_t* offsets;
   const int32_t* n_uniq;
   // with mbo set: experts of more than kThinTokens tokens (none with
@@ -276,6 +279,8 @@ struct MfmaArgs {
   int32_t* tslot;            // [thin_bound][kTileSlots]
   float* y;
   int x_packed;              // xh, xunit, xcorr and the M-block maps are already written
+  int i8act;                 // integer activations (MOE_INT8_ACT): xh and ah hold int8 rows,
+                             // xcorr and acorr their group scales; every expert thin
 };
 // The x pack (and M-block map) launch_ffn_mfma would run for m.
 PackArgs mfma_x_pack_args(const MfmaArgs& m);

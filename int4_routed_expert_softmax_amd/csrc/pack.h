@@ -77,6 +77,40 @@ __device__ __forceinline__ void store8(_Float16* drow, int c, const float (&v)[8
   *reinterpret_cast<f16x8_t*>(drow + c) = hv;
 }
 
+// Integer activations: row r of p as int8, each 64-column group as q = v / s
+// rounded to the nearest integer (ties to even), s = max|v| / 127, both in
+// fp32 (a group of zeros: s = 0, q = 0); q in column order into dst (bytes),
+// s into corr[r][K / 64].  A whole wave takes the row's 512-column chunks
+// part, part + nw, ... (one wave: all of them); K is a multiple of 512, so
+// in every step all 64 lanes hold a chunk and the 8 lanes of a group take its
+// maximum with DPP (quad swaps, then the half-row mirror pairs the two
+// quads).  No group spans two chunks, so the waves of a row need no exchange.
+__device__ __forceinline__ void pack_row_i8(const PackArgs& p, int r, int lane, int part = 0,
+                                            int nw = 1) {
+  const size_t base = (p.gather ? (size_t)p.gather[r] : (size_t)r) * p.K;
+  int8_t* drow = reinterpret_cast<int8_t*>(p.dst) + (size_t)r * p.K;
+  for (int c = (part * 64 + lane) * 8; c < p.K; c += 512 * nw) {
+    float v[8];
+    load8(p.src, p.src_bf16, base + c, v);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = fmaxf(m, dpp<kDppXor1>(m));
+    m = fmaxf(m, dpp<kDppXor2>(m));
+    m = fmaxf(m, dpp<kDppHalfMirror>(m));
+    const float s = m / 127.0f;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float q = m > 0.0f ? fminf(fmaxf(rintf(v[j] / s), -127.0f), 127.0f) : 0.0f;
+      w[j >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint2*>(drow + c) = make_uint2(w[0], w[1]);
+    if ((lane & 7) == 0) p.corr[(size_t)r * (p.K / 64) + c / 64] = s;
+  }
+  if (part == 0 && lane == 0 && p.unit) p.unit[r] = 1.0f;
+}
+
 // Row r of p, by one whole wave (lane = its lane).
 __device__ __forceinline__ void pack_row(const PackArgs& p, int r, int lane) {
   const size_t src_row = p.gather ? (size_t)p.gather[r] : (size_t)r;

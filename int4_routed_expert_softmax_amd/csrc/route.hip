@@ -298,7 +298,12 @@ __device__ __forceinline__ int router_front_body(const RouterArgs& a) {
       __shared__ float s_m[kRFW];
       const int nw = rf_pack_waves(a.px.rows);
       const int r = (e - pb) * (kRFW / nw) + wave / nw;
-      pack_row_split(a.px, r < a.px.rows ? r : -1, wave % nw, nw, s_m, wave, lane);
+      if (a.px.i8) {
+        // int8 groups need no row-wide maximum: no barrier
+        if (r < a.px.rows) pack_row_i8(a.px, r, lane, wave % nw, nw);
+      } else {
+        pack_row_split(a.px, r < a.px.rows ? r : -1, wave % nw, nw, s_m, wave, lane);
+      }
       return 2;
     }
   }
@@ -499,7 +504,8 @@ hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, 
 hipError_t launch_router_front(const RouterArgs& a_in, hipStream_t s) {
   RouterArgs a = a_in;
   const int dig_blocks = a.xd.q ? (a.T * (a.d / 64) + kRFW - 1) / kRFW : 0;
-  if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1)) return hipErrorInvalidValue;
+  if (a.px.dst && (a.px.K % 8 != 0 || a.px.rows < 1 || (a.px.i8 && a.px.K % 512 != 0)))
+    return hipErrorInvalidValue;
   const int pack_blocks = a.px.dst ? rf_pack_blocks(a.px.rows) : 0;
   // without RMSNorm and digit split (the grouped GEMM's small batches), 5 to
   // 8 tokens take two workgroups per expert, each over its own tokens

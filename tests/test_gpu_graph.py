@@ -23,6 +23,8 @@ pytestmark = pytest.mark.gpu
     (small("g_t40", 1024, 512, 64, 8, 40, x_kind="bf16"), 0),        # large batch, grouped GEMM
     (small("g_inv", 512, 512, 32, 4, 6), moe.MOE_BATCH_INVARIANT),
     (small("g_perrow", 512, 512, 32, 8, 5, group=0), 0),
+    (small("g_i8act_t3", 512, 512, 16, 4, 3), moe.MOE_INT8_ACT),   # integer activations
+    (small("g_i8act_t40", 1024, 512, 64, 8, 40, x_kind="bf16"), moe.MOE_INT8_ACT),
 ], ids=lambda v: v.name if hasattr(v, "name") else str(v))
 def test_graph_replays_match_eager(w, flags):
     L = DeviceLayer(w)
