@@ -251,10 +251,13 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 is unchanged.  The result is this quantised function: within
  *                 2e-3 * max|ref| of an fp64 evaluation of it, and about
  *                 1e-2 * max|ref| from the unquantised layer (the int8
- *                 rounding of the activations).  Every batch size runs the
- *                 thin grouped GEMM in 16-token tiles, so a token's result
- *                 does not depend on its batch; with MOE_BATCH_INVARIANT too
- *                 it is bit-identical to its one-token call.
+ *                 rounding of the activations).  int4 layers run one token
+ *                 (and, with MOE_BATCH_INVARIANT, batches of up to 8) on the
+ *                 single-token kernel family with these int8 values in its
+ *                 digit form, other batches on the int8 matrix cores; int8
+ *                 and int2 layers run every batch on the matrix cores, in
+ *                 16-token tiles, so there a token's result never depends on
+ *                 its batch.  MOE_BATCH_INVARIANT keeps its meaning.
  *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
  *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]
  *                 = number of tokens that picked expert e

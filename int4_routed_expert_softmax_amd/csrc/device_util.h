@@ -185,6 +185,33 @@ __device__ __forceinline__ void digitize32(float v, int col, bool valid, int8_t*
   }
 }
 
+// Integer activations (int8 per 64-column group) in the same digit form: the
+// wave's 64 lanes hold the 64 columns of one group (col & 63 == lane), and
+// q = rint(v / s) (ties to even), s = max|v| / 127 in fp32 (a group of
+// zeros: s = 0, q = 0).  X = q is stored as D0 in [-64, 63], D1 in [-1, 1],
+// D2 = 0 with unit s in both 32-column halves, so the digit dot products give
+// exactly sum q_w q, times s.  All 64 lanes must be active.
+__device__ __forceinline__ void digitize64_i8(float v, int col, bool valid, int8_t* q_row,
+                                              int32_t* sx_row, float* sc_row) {
+  const float hm = half_max(fabsf(v));
+  const float m = fmaxf(hm, __shfl_xor(hm, 32, 64));
+  const float s = m / 127.0f;
+  const int X = m > 0.0f ? (int)fminf(fmaxf(rintf(v / s), -127.0f), 127.0f) : 0;
+  const int D0 = ((X + 64) & 127) - 64;
+  const int D1 = (X - D0) / 128;
+  const int sx = half_sum(X);
+  if (!valid) return;
+  int8_t* plane = q_row + (size_t)(col >> 5) * kChunkDigitBytes;
+  const int pos = digit_pos(col & 31);
+  plane[pos] = (int8_t)D0;
+  plane[kChunk + pos] = (int8_t)D1;
+  plane[2 * kChunk + pos] = 0;
+  if ((col & 31) == 0) {
+    sx_row[col >> 5] = sx;
+    sc_row[col >> 5] = s;
+  }
+}
+
 // Digits of one chunk held in registers: w[p][i] is word i of plane p.
 struct ChunkDigits {
   int w[kPlanes][8];

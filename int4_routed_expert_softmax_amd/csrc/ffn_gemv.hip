@@ -306,9 +306,15 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
       }
       const int slot = slot_at(t0 + j);
       const int nca = f / kChunk, nga = f / kXGroup;
-      digitize32(silu(g) * uu, rb * kRowsPerBlock + lane, true,
-                 ad.q + (size_t)slot * nca * kChunkDigitBytes, ad.sx + (size_t)slot * nga,
-                 ad.sc + (size_t)slot * nga);
+      // integer activations: the block's 64 rows are one 64-column group of a
+      if (L.i8act)
+        digitize64_i8(silu(g) * uu, rb * kRowsPerBlock + lane, true,
+                      ad.q + (size_t)slot * nca * kChunkDigitBytes, ad.sx + (size_t)slot * nga,
+                      ad.sc + (size_t)slot * nga);
+      else
+        digitize32(silu(g) * uu, rb * kRowsPerBlock + lane, true,
+                   ad.q + (size_t)slot * nca * kChunkDigitBytes, ad.sx + (size_t)slot * nga,
+                   ad.sc + (size_t)slot * nga);
     }
     __syncthreads();
   }

@@ -333,11 +333,13 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   EL.bits = code_bits(dm->code_bits);
   const int maxU = E < T * k ? E : T * k;
 
-  // int8 and int2 layers, and integer activations, run every batch on the
-  // thin grouped GEMM (16-token tiles), whose per-token arithmetic does not
-  // depend on the batch, so the batch-invariant flag needs no separate path
-  // for them
-  if (EL.bits == 4 && !i8act && (invariant || gemv_small_path(T, k, d, f))) {
+  EL.i8act = i8act;
+  // int8 and int2 layers run every batch on the thin grouped GEMM (16-token
+  // tiles), whose per-token arithmetic does not depend on the batch, so the
+  // batch-invariant flag needs no separate path for them.  Integer
+  // activations on int4 layers take this path as the others do: the digit
+  // split then holds one int8 per column (one scale per 64 columns).
+  if (EL.bits == 4 && (invariant || gemv_small_path(T, k, d, f))) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (one token: in
     // every gate/up block's prologue; 2+: one k_route_small block) and
     // gate/up; 3: down + combine.  Every step keeps one order of
@@ -357,6 +359,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     ra.bias = bias;
     ra.z = z;
     ra.xd = xd;
+    ra.i8 = i8act;
     MOE_TRY(launch_router_front(ra, s));
     DownPlan* plan = at<DownPlan>(ws, L.plan);
     RouteOut ro{z, T, E, k, idx, w, uniq, nuniq, offs, rows, stats, plan};

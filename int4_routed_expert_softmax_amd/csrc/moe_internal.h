@@ -63,6 +63,7 @@ struct ExpertList {
   int kdiv;
   int per_row;  // blobs carry one scale per row (else one per kGroup weights)
   int bits;     // code width: 4, 8 or 2
+  int i8act;    // integer activations: a is digit-split as int8 per 64 columns
   // with hit set: only union positions u with hit[u] == want_hit are computed
   // (the slot cache's hits, resident before the call, or its misses)
   const int32_t* hit;
@@ -171,6 +172,7 @@ struct RouterArgs {
   Digits xd;
   PackArgs px;  // px.dst set: workgroups past the logits and digit split pack px.rows rows
   int tsplit;   // logit workgroups per expert, each over its own tokens (set by the launcher)
+  int i8;       // the digit split as integer activations (int8 per 64 columns)
 };
 constexpr int kSmallBatch = 8;
 // The small-batch path recomputes routing inside the gate/up kernel with one

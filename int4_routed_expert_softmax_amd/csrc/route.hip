@@ -392,8 +392,12 @@ __device__ __forceinline__ int router_front_body(const RouterArgs& a) {
     for (int it = (e - E) * kRFW + wave; it < T * nb;
          it += (gx - E - pack_blocks) * kRFW) {
       const int t = it / nb, col = (it % nb) * 64 + lane;
-      digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
-                 a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
+      if (a.i8)
+        digitize64_i8(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
+                      a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
+      else
+        digitize32(xin(t, col), col, true, a.xd.q + (size_t)t * nch * kChunkDigitBytes,
+                   a.xd.sx + (size_t)t * ng, a.xd.sc + (size_t)t * ng);
     }
     return 3;
   }

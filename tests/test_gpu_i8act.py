@@ -5,9 +5,12 @@ Every expert input row (x', and a = silu(g) * u) is int8 per 64-column group
 with an fp32 scale max|v| / 127, each group's dot product is exact on the
 int8 matrix cores.  Against the oracle's integer-activation layer
 (REF_I8ACT): routing, union and slot lists bit-exact (as the call left them
-in its workspace), outputs within 2e-3 * max|ref|.  Batches are bit-identical
-to their one-token calls, and the distance from the unquantised layer (the
-int8 rounding of the activations) stays within its derived bound."""
+in its workspace), outputs within 2e-3 * max|ref|, on both int4 kernel
+families (one token and batch-invariant batches: the single-token GEMV with
+int8 digits; other batches: the int8 matrix cores).  Batch-invariant batches
+(and every batch of int8 or int2 codes) are bit-identical to their one-token
+calls, and the distance from the unquantised layer (the int8 rounding of the
+activations) stays within its derived bound."""
 import numpy as np
 import pytest
 import torch
@@ -67,10 +70,14 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("flags", [I8, I8 | moe.MOE_BATCH_INVARIANT,
-                                   I8 | NORM_RES | moe.MOE_BATCH_INVARIANT])
-def test_i8act_batch_matches_single_tokens(flags):
-    w = small("i8act_inv", 512, 512, 32, 8, 8, x_kind="shared_base")
+@pytest.mark.parametrize("flags,bits", [
+    (I8 | moe.MOE_BATCH_INVARIANT, 4),
+    (I8 | NORM_RES | moe.MOE_BATCH_INVARIANT, 4),
+    (I8, 8),   # int8 codes: every batch on the thin GEMM, invariant without the flag
+    (I8, 2),
+])
+def test_i8act_batch_matches_single_tokens(flags, bits):
+    w = small(f"i8act_inv_i{bits}", 512, 512, 32, 8, 8, x_kind="shared_base", bits=bits)
     L = DeviceLayer(w)
     x, bf = configs.tokens(w)
     xd = L.x_device(x, bf)
@@ -83,18 +90,20 @@ def test_i8act_batch_matches_single_tokens(flags):
     got = bits_of(out)
     for t in range(w.T):
         assert np.array_equal(got[t], solo[t]), f"token {t} differs from its one-token call"
-    say(f"i8act flags={flags}: {w.T} tokens bit-identical to their one-token calls")
+    say(f"i8act int{bits} flags={flags}: {w.T} tokens bit-identical to their one-token calls")
 
 
-@pytest.mark.parametrize("name", ["decode1", "verify8"])
-def test_i8act_glm(name):
-    L, ref, out = full_parity(W[name], flags=I8)
+@pytest.mark.parametrize("name,flags", [("decode1", I8), ("verify8", I8),
+                                        ("verify8", I8 | moe.MOE_BATCH_INVARIANT)])
+def test_i8act_glm(name, flags):
+    L, ref, out = full_parity(W[name], flags=flags)
     # the quantised function's distance from the unquantised layer
     x, bf = configs.tokens(W[name])
     ref0 = oracle.layer_forward(x, L.Wr, L.bias, L.oracle_table(), L.w.d, L.w.f, L.w.top_k,
                                 x_bf16=bf)
     dist = np.abs(out.cpu().numpy() - ref0["out"]).max() / np.abs(ref0["out"]).max()
-    record_margin(f"{name} int8 activations vs unquantised layer", dist, what="distance")
+    record_margin(f"{name} flags={flags} int8 activations vs unquantised layer", dist,
+                  what="distance")
     say(f"{name}: int8-activation layer vs the unquantised one: {dist:.2e} of max|out|")
     assert dist <= I8_DIST
 
