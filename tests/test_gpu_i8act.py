@@ -103,7 +103,7 @@ def test_i8act_glm(name, flags):
                                 x_bf16=bf)
     dist = np.abs(out.cpu().numpy() - ref0["out"]).max() / np.abs(ref0["out"]).max()
     record_margin(f"{name} flags={flags} int8 activations vs unquantised layer", dist,
-                  what="distance")
+                  what="distance", tol=I8_DIST)
     say(f"{name}: int8-activation layer vs the unquantised one: {dist:.2e} of max|out|")
     assert dist <= I8_DIST
 
