@@ -149,8 +149,6 @@ def main():
         return run_chain(a)
     a.steps = 200 if a.steps is None else a.steps
     a.warmup = 10 if a.warmup is None else a.warmup
-    if a.int8_act and a.host_tier:
-        sys.exit("--int8-act: the slot cache (--host-tier) serves the GEMV path only")
     if a.host_tier:
         return run_host_tier(a)
 
@@ -505,8 +503,11 @@ def run_host_tier(a):
         out = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
         ws = moe.make_workspace(dims, w.T, dev)
 
+        flags = moe.MOE_INT8_ACT if a.int8_act else 0
+
         def step(i):
-            moe.moe_layer_forward_cached(dims, x[i], Wr, bias, home, slots, S, state, out, ws=ws)
+            moe.moe_layer_forward_cached(dims, x[i], Wr, bias, home, slots, S, state, out,
+                                         flags=flags, ws=ws)
 
         for i in range(a.warmup):
             step(i)
@@ -528,11 +529,14 @@ def run_host_tier(a):
         "metric": METRIC, "value": round(w.T / sec, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(sec * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 weights x int8-digit activations, i32 dot, f32 accumulate",
+        "dtype": ("int4 weights x int8 activations (one scale per 64 columns), i32 dot, f32 "
+                  "accumulate" if a.int8_act else
+                  "int4 weights x int8-digit activations, i32 dot, f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts)",
         "config": {"workload": f"{w.name} host tier: one layer, d={w.d} f={w.f} E={w.n_experts} "
                                f"top-{w.top_k}, T={w.T}, experts in pinned host memory behind "
-                               f"{S} HBM slots, a new batch of tokens per step",
+                               f"{S} HBM slots, a new batch of tokens per step"
+                               + (", MOE_INT8_ACT" if a.int8_act else ""),
                    "T": w.T, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "slots": S},
         "cache": {"hit_rate": round(hits / max(hits + misses, 1), 4),

@@ -237,8 +237,7 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 Source: drafts and their batched verification must compute
  *                 the same function, pinned to one kernel family — README
  *                 工作原理 › 诚实的推测解码; 技术解读, "精度与语义：速度可以牺牲，语义不能".
- *                 | MOE_INT8_ACT (d and f multiples of 512, else
- *                 MOE_EUNSUPPORTED): the experts take integer activations, as
+ *                 | MOE_INT8_ACT: the experts take integer activations, as
  *                 the pages' hand-written integer dot-product kernels do (int4
  *                 weights times integer activations, no BLAS — 技术解读,
  *                 "int4 量化与手写内核"; the nxmr blog's int8 kernels, «纯C语言»).
@@ -252,12 +251,14 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 2e-3 * max|ref| of an fp64 evaluation of it, and about
  *                 1e-2 * max|ref| from the unquantised layer (the int8
  *                 rounding of the activations).  int4 layers run one token
- *                 (and, with MOE_BATCH_INVARIANT, batches of up to 8) on the
+ *                 (and, with MOE_BATCH_INVARIANT, batches of up to 8; and
+ *                 every batch when d or f is not a multiple of 512) on the
  *                 single-token kernel family with these int8 values in its
  *                 digit form, other batches on the int8 matrix cores; int8
  *                 and int2 layers run every batch on the matrix cores, in
  *                 16-token tiles, so there a token's result never depends on
- *                 its batch.  MOE_BATCH_INVARIANT keeps its meaning.
+ *                 its batch.  MOE_BATCH_INVARIANT keeps its meaning, and
+ *                 moe_layer_forward_cached takes the flag too.
  *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
  *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]
  *                 = number of tokens that picked expert e
@@ -300,7 +301,7 @@ size_t moe_cache_state_bytes(const moe_dims* dims, int32_t n_slots);
  *               256-byte aligned, owned by the cache
  *   n_slots     min(E, T * k) <= n_slots <= E
  *   cache_state device buffer of moe_cache_state_bytes(dims, n_slots)
- *   other arguments as moe_layer_forward (all three flags accepted).
+ *   other arguments as moe_layer_forward (every flag accepted).
  * Per call, on the device: the router and the union; placement in one
  * workgroup (experts of the union found in a slot keep it and count as hits;
  * each other one, in ascending id, takes the least recently used slot not
@@ -311,7 +312,7 @@ size_t moe_cache_state_bytes(const moe_dims* dims, int32_t n_slots);
  * once their copies have landed, then down + combine over the whole union,
  * every expert read from its slot.  The batch runs the single-token
  * kernel family, so out (and stats) are bit-identical to moe_layer_forward
- * with MOE_BATCH_INVARIANT (for one token: with any flags) and the blobs
+ * with MOE_BATCH_INVARIANT added (for one token: with the same flags) and the blobs
  * resident, for any cache contents: where an expert's bytes come from
  * decides only the speed.  Calls sharing one
  * cache state must be ordered (one stream); the clock wraps after 2^32 calls.

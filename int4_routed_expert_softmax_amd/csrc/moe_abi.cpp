@@ -301,8 +301,6 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   const bool invariant = (flags & MOE_BATCH_INVARIANT) != 0;
   const bool i8act = (flags & MOE_INT8_ACT) != 0;
   if (invariant && T >= 1 && !small_batch(T, dm->top_k)) return MOE_EUNSUPPORTED;
-  // integer activations run on the thin grouped GEMM (int8 matrix cores)
-  if (i8act && !mfma_shape_ok(dm->d, dm->f)) return MOE_EUNSUPPORTED;
   if (T < 1 || !x || !w_router || !expert_table || !out || !ws || !aligned(ws, 16)) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 4)) return MOE_EINVAL;
   if ((flags & MOE_PRENORM_RMS) && !(rms_eps >= 0.0f)) return MOE_EINVAL;
@@ -448,7 +446,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
     m.i8act = i8act;
     MOE_TRY(launch_ffn_mfma(m, s));
   } else {
-    MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s));
+    MOE_TRY(launch_digitize(xr, xr_bf16, nullptr, T, d, xd, s, i8act));
     MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, T, 1, s));
     MOE_TRY(launch_down(EL, maxU, d, f, ad, y, T, s));
   }
@@ -464,7 +462,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   int st = dims_status(dm);
   if (st != MOE_OK) return st;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT))
+  if (flags & ~(uint32_t)(MOE_PRENORM_RMS | MOE_RESIDUAL | MOE_BATCH_INVARIANT | MOE_INT8_ACT))
     return MOE_EUNSUPPORTED;
   if ((flags & (MOE_PRENORM_RMS | MOE_RESIDUAL)) && x_dtype != MOE_F32) return MOE_EUNSUPPORTED;
   if (T < 1 || !x || !w_router || !home_table || !slots || !cache_state || !out || !ws ||
@@ -517,6 +515,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   ra.bias = bias;
   ra.z = z;
   ra.xd = xd;
+  ra.i8 = (flags & MOE_INT8_ACT) != 0;
   MOE_TRY(launch_router_front(ra, s));
   // 2: top-k, union and the down plan (blobs at home for now)
   const uint8_t* const* home = reinterpret_cast<const uint8_t* const*>(home_table);
@@ -552,6 +551,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   EL.kdiv = k;
   EL.per_row = dm->group_size == 0;
   EL.bits = 4;
+  EL.i8act = (flags & MOE_INT8_ACT) != 0;
   EL.hit = hit;
   EL.want_hit = 1;
   MOE_TRY(launch_gateup_fill(EL, cap, d, f, xd, ad, T, ca, cap, s));

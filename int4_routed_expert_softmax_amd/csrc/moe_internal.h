@@ -228,8 +228,9 @@ hipError_t launch_topk(const double* z, int nsplit, const float* bias, int T, in
                        int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_union(const int32_t* idx, int T, int E, int k, int32_t* uniq, int32_t* n_uniq,
                         int32_t* offsets, int32_t* rows, int32_t* stats, hipStream_t s);
+// i8: integer activations (int8 per 64 columns, digitize64_i8)
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
-                           Digits out, hipStream_t s);
+                           Digits out, hipStream_t s, int i8 = 0);
 hipError_t launch_gateup(const ExpertList& L, const RouteOut* small_route, int max_experts, int d,
                          int f, Digits xd, Digits ad, int tokens_per_expert_max, int token_groups,
                          hipStream_t s);

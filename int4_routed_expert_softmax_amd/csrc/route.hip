@@ -462,10 +462,10 @@ __global__ __launch_bounds__(kRF) void k_router_front(RouterArgs a) {
 
 // ---------------------------------------------------------------- digit split
 // One wave per 64 columns of a row; gather[r] (if given) selects the source
-// row of output row r.
+// row of output row r.  i8: integer activations (int8 per 64 columns).
 __global__ __launch_bounds__(256) void k_digitize(const void* __restrict__ x, int x_bf16,
                                                   const int32_t* __restrict__ gather, int rows,
-                                                  int K, Digits out) {
+                                                  int K, Digits out, int i8) {
   const int lane = threadIdx.x & 63;
   const int nb = K / 64, nch = K / kChunk, ng = K / kXGroup;
   const long items = (long)rows * nb;
@@ -475,8 +475,12 @@ __global__ __launch_bounds__(256) void k_digitize(const void* __restrict__ x, in
     const size_t i = (size_t)src * K + col;
     const float v = x_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[i] << 16)
                            : static_cast<const float*>(x)[i];
-    digitize32(v, col, true, out.q + (size_t)r * nch * kChunkDigitBytes, out.sx + (size_t)r * ng,
-               out.sc + (size_t)r * ng);
+    if (i8)
+      digitize64_i8(v, col, true, out.q + (size_t)r * nch * kChunkDigitBytes,
+                    out.sx + (size_t)r * ng, out.sc + (size_t)r * ng);
+    else
+      digitize32(v, col, true, out.q + (size_t)r * nch * kChunkDigitBytes,
+                 out.sx + (size_t)r * ng, out.sc + (size_t)r * ng);
   }
 }
 
@@ -522,11 +526,11 @@ hipError_t launch_router_front(const RouterArgs& a_in, hipStream_t s) {
 }
 
 hipError_t launch_digitize(const void* x, int x_bf16, const int32_t* gather, int rows, int K,
-                           Digits out, hipStream_t s) {
+                           Digits out, hipStream_t s, int i8) {
   const long items = (long)rows * (K / kGroup);
   const long blocks = (items + 3) / 4;
   const int grid = (int)(blocks < 4096 ? blocks : 4096);
-  return launch(4, k_digitize, dim3(grid), dim3(256), s, x, x_bf16, gather, rows, K, out);
+  return launch(4, k_digitize, dim3(grid), dim3(256), s, x, x_bf16, gather, rows, K, out, i8);
 }
 
 }  // namespace moe

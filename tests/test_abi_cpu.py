@@ -130,11 +130,6 @@ def test_layer_forward_rejects_bad_arguments():
     assert call(out=None) == moe.MOE_EINVAL
     assert call(T=-1) == moe.MOE_EINVAL
     assert call(flags=16) == moe.MOE_EUNSUPPORTED  # no such flag
-    # integer activations run on the matrix-core path: d and f multiples of 512
-    d320 = moe.Dims(320, 512, 16, 2)
-    assert f(ctypes.byref(d320.c()), FAKE, moe.MOE_F32, 2, FAKE, None, FAKE, FAKE,
-             moe.MOE_INT8_ACT, 1e-6, None, FAKE, moe.workspace_bytes(d320, 2),
-             None) == moe.MOE_EUNSUPPORTED
     # batch invariance covers the single-token family's batch limits only
     ws9 = moe.workspace_bytes(GLM, 9)
     assert call(flags=moe.MOE_BATCH_INVARIANT, T=9, wsb=ws9) == moe.MOE_EUNSUPPORTED
@@ -175,7 +170,7 @@ def test_cached_layer_rejects_bad_arguments():
     assert call(T=2, S=15, wsb=moe.workspace_bytes(GLM, 2)) == moe.MOE_EUNSUPPORTED
     assert call(S=257) == moe.MOE_EUNSUPPORTED             # more slots than experts
     assert call(T=9, S=72, wsb=moe.workspace_bytes(GLM, 9)) == moe.MOE_EUNSUPPORTED  # past the small-batch limits
-    assert call(flags=moe.MOE_INT8_ACT) == moe.MOE_EUNSUPPORTED  # the cache serves the GEMV path
+    assert call(flags=16) == moe.MOE_EUNSUPPORTED  # no such flag
     assert call(wsb=ws - 256) == moe.MOE_ENOSPC
 
 

@@ -193,6 +193,14 @@ def test_small_layers(w, S, T, bf16):
         home.free()
 
 
+def test_int8_activations_from_device_home(glm):
+    """MOE_INT8_ACT through the slot cache: bit-identical to the resident
+    layer's integer-activation call (batch-invariant for batches)."""
+    cache = Cache(glm, glm.table, 32)  # a batch of 4 can hold 32 distinct experts
+    run_sequence(glm, cache, range(6), 1, moe.MOE_INT8_ACT)
+    run_sequence(glm, cache, range(6, 10), 4, moe.MOE_INT8_ACT | NORM_RES, in_place=True)
+
+
 def test_glm_perrow_decode_from_device_home():
     """The GLM-shaped layer with per-row experts, a new token per call, 12 slots."""
     L = DeviceLayer(configs.WORKLOADS["decode1_perrow"])

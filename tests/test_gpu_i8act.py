@@ -50,6 +50,17 @@ def test_i8act_small_shapes(bits, shape):
     full_parity(small(f"i8act_i{bits}_{name}", **sh, bits=bits), flags=I8)
 
 
+@pytest.mark.parametrize("w", [
+    small("i8act_t1_odd", 192, 128, 16, 2, 1),        # one token, d and f not multiples of 512
+    small("i8act_T3_odd", 320, 192, 32, 4, 3),        # small batch on the single-token kernels
+    small("i8act_ragged", 320, 192, 100, 5, 130),     # large batch: digit split + GEMV
+], ids=lambda v: v.name)
+def test_i8act_other_shapes_on_the_gemv(w):
+    """Shapes off the matrix-core grid run the digit GEMV at every batch size,
+    with the int8 values in its digit form."""
+    full_parity(w, flags=I8)
+
+
 def test_i8act_prenorm_residual():
     full_parity(small("i8act_chain", 512, 512, 16, 4, 6), flags=I8 | NORM_RES)
 
