@@ -141,8 +141,6 @@ def main():
                           "layer is measured at one GPU's share"}), flush=True)
         sys.exit(2)
 
-    if a.int8_act and a.workload == "chain48":
-        sys.exit("--int8-act: the 48-layer chain runs the unquantised layer")
     if a.workload == "chain48":
         a.steps = 64 if a.steps is None else a.steps
         a.warmup = 2 if a.warmup is None else a.warmup
@@ -569,7 +567,7 @@ def run_chain(a):
     L = w.layers
     K, Wm = a.steps, a.warmup
     eps = 1e-6
-    flags = moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL
+    flags = moe.MOE_PRENORM_RMS | moe.MOE_RESIDUAL | (moe.MOE_INT8_ACT if a.int8_act else 0)
     print(f"bench: chain48 generating + uploading {L * w.n_experts * blob / 1e9:.1f} GB",
           file=sys.stderr, flush=True)
     layers = []
@@ -673,13 +671,15 @@ def run_chain(a):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if w.T <= 8 else
+        "dtype": ("int4 weights x int8 activations (one scale per 64 columns, as int8 digits), "
+                  "i32 dot, f32 accumulate" if a.int8_act else
+                  "int4 weights x int8-digit activations, i32 dot, f32 accumulate" if w.T <= 8 else
                   "int4 weights dequantised to fp16 x fp16 activations, MFMA f32 accumulate"),
         "data": "synthetic (seeded; random-init GLM-5.2-shaped experts, 48 fresh layers)",
         "config": {"workload": f"chain48: {L} chained decode layers h <- h + MoE(RMSNorm(h)), T=1, "
                                f"d={w.d} f={w.f} E={w.n_experts} top-{w.top_k}, all "
                                f"{L * w.n_experts} experts resident ({L * w.n_experts * blob / 1e9:.1f} GB), "
-                               f"one HIP graph of {K} steps",
+                               f"one HIP graph of {K} steps" + (", MOE_INT8_ACT" if a.int8_act else ""),
                    "T": 1, "d": w.d, "f": w.f, "n_experts": w.n_experts, "top_k": w.top_k,
                    "layers": L, "distinct_experts_per_layer": float(U.mean())},
         "ms_per_step_eager": round(eager * 1e3, 4),
@@ -696,14 +696,14 @@ def run_chain(a):
                           "avg_launch_us": round(float(dur["down"].mean() * 1e6), 3)},
     }
     if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline_chain(w, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_chain(w, a.cpu_seconds, a.int8_act)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_chain(w, seconds):
+def cpu_baseline_chain(w, seconds, i8=False):
     """The CPU oracle on the chain: layer after layer of step 0 (RMSNorm,
-    residual), each layer's experts generated on demand, until `seconds`
-    have passed; tokens/s = layers/s / 48."""
+    residual; i8: integer activations), each layer's experts generated on
+    demand, until `seconds` have passed; tokens/s = layers/s / 48."""
     import oracle
     from synth import configs
 
@@ -718,7 +718,8 @@ def cpu_baseline_chain(w, seconds):
         for e in set(int(e) for e in idx.reshape(-1)):
             table[e] = configs.one_expert(w, n, e)
         t1 = time.perf_counter()
-        h = oracle.layer_forward(h, Wr, bias, table, w.d, w.f, w.top_k, flags=3,
+        h = oracle.layer_forward(h, Wr, bias, table, w.d, w.f, w.top_k,
+                                 flags=3 | (oracle.I8ACT if i8 else 0),
                                  eps=1e-6)["out"].astype(np.float32)
         t_ffn += time.perf_counter() - t1
         n += 1

@@ -38,7 +38,7 @@ class Chain:
         self.zero = torch.zeros(self.blob_bytes, dtype=torch.uint8, device=DEV)
         self.stats = torch.zeros(1 + W.n_experts, dtype=torch.int32, device=DEV)
 
-    def layer(self, layer: int, h: np.ndarray, check_output: bool) -> np.ndarray:
+    def layer(self, layer: int, h: np.ndarray, check_output: bool, flags=FLAGS) -> np.ndarray:
         Wr, bias = configs.router(W, layer)
         idx, wts, _ = oracle.route(oracle.rmsnorm(h, EPS), Wr, bias, W.top_k)
         sel = sorted(set(int(e) for e in idx.reshape(-1)))
@@ -51,7 +51,7 @@ class Chain:
         hd = torch.from_numpy(np.ascontiguousarray(h, dtype=np.float32)).to(DEV)
         self.stats.zero_()
         moe.moe_layer_forward(self.dims, hd, torch.from_numpy(Wr).to(DEV),
-                              torch.from_numpy(bias).to(DEV), table, hd, flags=FLAGS,
+                              torch.from_numpy(bias).to(DEV), table, hd, flags=flags,
                               rms_eps=EPS, stats=self.stats, ws=self.ws)
         torch.cuda.synchronize()
         st = self.stats.cpu().numpy()
@@ -65,7 +65,7 @@ class Chain:
         out = hd.cpu().numpy()
         if check_output:
             ref = oracle.layer_forward(h, Wr, bias, [host.get(e) for e in range(W.n_experts)],
-                                       W.d, W.f, W.top_k, flags=FLAGS, eps=EPS)
+                                       W.d, W.f, W.top_k, flags=flags, eps=EPS)
             # the layer's own contribution h_{l+1} - h_l is what the experts compute
             got = out.astype(np.float64) - h
             want = ref["out"] - h
@@ -95,3 +95,15 @@ def test_chain_teacher_forced(chain, step):
     assert np.all(np.isfinite(h))
     record_margin(f"chain48 step {step} worst of 48 layers", chain.worst)
     say(f"chain: step {step} done, |h|max {np.abs(h).max():.3f}, worst rel err {chain.worst:.2e}")
+
+
+def test_chain_teacher_forced_int8_activations(chain):
+    """The same chain with MOE_INT8_ACT (each layer's experts on int8
+    activations, the oracle's integer-activation layer as reference)."""
+    h, _ = configs.tokens(W, 0)
+    chain.worst = 0.0
+    for layer in range(W.layers):
+        h = chain.layer(layer, h, True, flags=FLAGS | moe.MOE_INT8_ACT)
+    assert np.all(np.isfinite(h))
+    record_margin("chain48 step 0 int8 activations worst of 48 layers", chain.worst)
+    say(f"chain int8 activations: step 0 done, worst rel err {chain.worst:.2e}")
