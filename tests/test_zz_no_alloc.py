@@ -48,6 +48,9 @@ def test_glm_batch_then_single_token():
     same(L, x, bf, 0, "verify8")
     same(L, x[5:6], bf, 0, "decode after verify8")
     same(L, x[2:3], bf, NORM_RES, "decode, RMSNorm + residual")
+    # integer activations: int8 rows on the array, then the digit form
+    same(L, x, bf, moe.MOE_INT8_ACT, "verify8, int8 activations")
+    same(L, x[1:2], bf, moe.MOE_INT8_ACT, "decode, int8 activations")
 
 
 def test_large_batch_then_small_batch():
