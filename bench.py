@@ -95,8 +95,7 @@ def matrix_bytes(w):
 
 
 def gateup_sources(workload):
-    gemv = (workload.startswith(("decode1", "chain48")) and not workload.endswith(("int8", "int2"))
-            and "i8act" not in workload)
+    gemv = workload.startswith(("decode1", "chain48"))  # one token: every width, either activation
     return GATEUP_SOURCES if gemv else GEMM_SOURCES
 
 
@@ -234,11 +233,11 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens, i8=False):
     ws = moe.make_workspace(dims, w.T, dev)
     stream = torch.cuda.current_stream()
     flags = (moe.MOE_BATCH_INVARIANT if inv else 0) | (moe.MOE_INT8_ACT if i8 else 0)
-    # the library's choice: int4 layers take the int8-digit GEMV kernels for
-    # one token (or with the flag), the fp16 MFMA grouped GEMM for 2+ tokens
-    # with d, f multiples of 512; int8 and int2 layers, and integer
-    # activations, always the grouped GEMM
-    gemv = w.bits == 4 and not i8 and (w.T == 1 or inv or w.d % 512 or w.f % 512)
+    # the library's choice: every layer takes the int8-digit GEMV kernels for
+    # one token (or with the flag), int4 layers also for shapes off the 512
+    # grid; other batches take the grouped GEMM (fp16 MFMA, or int8 MFMA with
+    # integer activations)
+    gemv = w.T == 1 or inv or (w.bits == 4 and (w.d % 512 or w.f % 512))
 
     def step(i, s=None):
         L = layers[i % R]
@@ -317,7 +316,9 @@ def measure(moe, torch, w, layers, K, warmup, inv, tokens, i8=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int4 weights x int8-digit activations, i32 dot, f32 accumulate" if gemv else
+        "dtype": (f"int{w.bits} weights x int8 activations (one scale per 64 columns, as int8 "
+                  f"digits), i32 dot, f32 accumulate" if gemv and i8 else
+                  f"int{w.bits} weights x int8-digit activations, i32 dot, f32 accumulate" if gemv else
                   f"int{w.bits} weights x int8 activations (one scale per 64 columns), MFMA i32 "
                   f"per group, f32 accumulate" if i8 else
                   f"int{w.bits} weights as fp16 x fp16 activations, MFMA f32 accumulate"),

@@ -43,11 +43,14 @@
  * takes cols * bits / 8 bytes of codes, int8 one two's-complement byte per
  * weight, int2 four two's-complement 2-bit fields per byte (weight 4i + j in
  * bits 2j..2j+1 of byte i); the scale tensors follow all the codes as above.
- * 30,081,024 (int8) and 15,040,512 (int2) bytes per gs64 expert at d = 6144,
- * f = 2048.  int8 and int2 layers run every call on the matrix cores in
- * 16-token tiles (so d and f must be multiples of 512), where a token's result
- * does not depend on the other tokens of its call; moe_layer_forward_cached
- * takes int4 layers only.
+ * 38,928,384 (int8) and 10,616,832 (int2) bytes per gs64 expert at d = 6144,
+ * f = 2048.  d and f must be multiples of 512 for both.  int8 layers run
+ * every call on the matrix cores in 16-token tiles, where a token's result
+ * does not depend on the other tokens of its call.  int2 layers take the
+ * single-token kernel family for one token (and for MOE_BATCH_INVARIANT
+ * batches) in moe_layer_forward, as int4 layers do, and the matrix cores for
+ * other batches and in moe_expert_ffn.  moe_layer_forward_cached takes int4
+ * layers only.
  *
  * Conventions for every entry point:
  *  - Pointers are device pointers (or host memory mapped into the device
@@ -250,14 +253,14 @@ int moe_expert_ffn(const moe_dims* dims, const void* expert_blob, const void* x,
  *                 is unchanged.  The result is this quantised function: within
  *                 2e-3 * max|ref| of an fp64 evaluation of it, and about
  *                 1e-2 * max|ref| from the unquantised layer (the int8
- *                 rounding of the activations).  int4 layers run one token
- *                 (and, with MOE_BATCH_INVARIANT, batches of up to 8; and
- *                 every batch when d or f is not a multiple of 512) on the
- *                 single-token kernel family with these int8 values in its
- *                 digit form, other batches on the int8 matrix cores; int8
- *                 and int2 layers run every batch on the matrix cores, in
- *                 16-token tiles, so there a token's result never depends on
- *                 its batch.  MOE_BATCH_INVARIANT keeps its meaning, and
+ *                 rounding of the activations).  int4 and int2 layers run one
+ *                 token (and, with MOE_BATCH_INVARIANT, batches of up to 8;
+ *                 int4 also every batch when d or f is not a multiple of 512)
+ *                 on the single-token kernel family with these int8 values in
+ *                 its digit form, other batches on the int8 matrix cores; int8
+ *                 layers run every batch on the matrix cores, in 16-token
+ *                 tiles, so there a token's result never depends on its
+ *                 batch.  MOE_BATCH_INVARIANT keeps its meaning, and
  *                 moe_layer_forward_cached takes the flag too.
  *   rms_eps       RMSNorm epsilon (used with MOE_PRENORM_RMS)
  *   stats         device [1 + E] int32 out, or NULL: stats[0] = U, stats[1+e]

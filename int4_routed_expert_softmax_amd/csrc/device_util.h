@@ -257,6 +257,68 @@ __device__ __forceinline__ int chunk_dot(const uint4 codes, const ChunkDigits& c
   return acc;
 }
 
+// The same for int2 codes: a chunk's 32 columns are 8 bytes, column 4b + j
+// of each 32-bit word in bits 2j..2j+1 of its byte b.  Flipping the top bit
+// of every field makes it n'_c = q_c + 2 in [0, 3].  v_perm pairs the low and
+// high nibbles of two neighbouring bytes into one word whose byte i holds
+// columns 2i and 2i + 1 of an 8-column block (bits 0-1 and 2-3), so one mask
+// gives the block's even columns and a shift and mask its odd ones, in the
+// order the digit planes hold them.  The caller subtracts 2 * sum(X).
+__device__ __forceinline__ int chunk_dot2(const uint2 codes, const ChunkDigits& cd) {
+  const uint32_t cw[2] = {codes.x, codes.y};
+  int ev[4], od[4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t v = cw[m] ^ 0xAAAAAAAAu;
+    const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // bytes [lo(b), hi(b), lo(b + 1), hi(b + 1)] for b = 2h
+      const uint32_t s = __builtin_amdgcn_perm(hi, lo, h ? 0x07030602u : 0x05010400u);
+      ev[2 * m + h] = (int)(s & 0x03030303u);
+      od[2 * m + h] = (int)((s >> 2) & 0x03030303u);
+    }
+  }
+  int acc = 0;
+#pragma unroll
+  for (int p = kPlanes - 1; p >= 0; --p) {
+    if (p != kPlanes - 1) acc *= 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_amdgcn_sdot4(ev[i], cd.w[p][2 * i], acc, false);
+      acc = __builtin_amdgcn_sdot4(od[i], cd.w[p][2 * i + 1], acc, false);
+    }
+  }
+  return acc;
+}
+
+// The same for int8 codes (32 bytes, column order): v_perm gathers each
+// 8-column block's even and odd columns.  The codes are signed, so no offset
+// is subtracted.  A plane's sum is exact in int32 (|sum| < 2^19), but the
+// chunk's total can reach 2^32, so the three planes' sums are combined in
+// fp32: sum = P2 * 2^14 + (P1 * 2^7 + P0), the bracket exact in int32, one
+// rounding converting it and one in the fma (relative error < 2^-23).
+__device__ __forceinline__ float chunk_dot8(const uint4 c0, const uint4 c1, const ChunkDigits& cd) {
+  const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  int ev[4], od[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    ev[b] = (int)__builtin_amdgcn_perm(cw[2 * b + 1], cw[2 * b], 0x06040200u);  // 0 2 4 6
+    od[b] = (int)__builtin_amdgcn_perm(cw[2 * b + 1], cw[2 * b], 0x07050301u);  // 1 3 5 7
+  }
+  static_assert(kPlanes == 3, "three digit planes");
+  int P[kPlanes] = {0, 0, 0};
+#pragma unroll
+  for (int p = 0; p < kPlanes; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      P[p] = __builtin_amdgcn_sdot4(ev[i], cd.w[p][2 * i], P[p], false);
+      P[p] = __builtin_amdgcn_sdot4(od[i], cd.w[p][2 * i + 1], P[p], false);
+    }
+  }
+  return fmaf((float)P[2], 16384.0f, (float)(P[1] * 128 + P[0]));
+}
+
 __device__ __forceinline__ float f16_to_f32(const _Float16* p) { return (float)*p; }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }

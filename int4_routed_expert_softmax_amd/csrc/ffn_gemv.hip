@@ -66,19 +66,22 @@ __device__ __forceinline__ ExpertRef expert_ref(const ExpertList& L, int u) {
 // Digit form of chunk c of activation row `row` (zeros when inactive).
 struct ChunkAct {
   ChunkDigits dig;
-  int sx8;   // 8 * (sum of X) over the chunk
+  int sxo;   // the codes' offset (8 int4, 2 int2, 0 int8) times the sum of X over the chunk
   float sc;  // value of one unit of X
 };
 
+template <int BITS = 4>
 __device__ __forceinline__ ChunkAct load_act(const Digits& D, int row, int nch, int c, bool act) {
+  static_assert(BITS == 4 || BITS == 2 || BITS == 8, "int4, int2 or int8 codes");
+  constexpr int kOff = BITS == 4 ? 8 : BITS == 2 ? 2 : 0;
   ChunkAct a;
   if (act) {
     a.dig = load_chunk_digits(D.q + ((size_t)row * nch + c) * kChunkDigitBytes);
-    a.sx8 = 8 * D.sx[(size_t)row * nch + c];
+    a.sxo = kOff ? kOff * D.sx[(size_t)row * nch + c] : 0;
     a.sc = D.sc[(size_t)row * nch + c];
   } else {
     a.dig = ChunkDigits{};
-    a.sx8 = 0;
+    a.sxo = 0;
     a.sc = 0.0f;
   }
   return a;
@@ -87,7 +90,18 @@ __device__ __forceinline__ ChunkAct load_act(const Digits& D, int row, int nch, 
 // sum over a chunk of q * x: the exact integer sum, times the activation
 // group's unit and the weight row's group scale s.
 __device__ __forceinline__ float chunk_term(uint4 codes, float s, const ChunkAct& a) {
-  return (float)(chunk_dot(codes, a.dig) - a.sx8) * (s * a.sc);
+  return (float)(chunk_dot(codes, a.dig) - a.sxo) * (s * a.sc);
+}
+// int2 codes (8 bytes a chunk)
+__device__ __forceinline__ float chunk_term(uint2 codes, float s, const ChunkAct& a) {
+  return (float)(chunk_dot2(codes, a.dig) - a.sxo) * (s * a.sc);
+}
+// int8 codes (32 bytes a chunk)
+struct I8Chunk {
+  uint4 lo, hi;
+};
+__device__ __forceinline__ float chunk_term(const I8Chunk& codes, float s, const ChunkAct& a) {
+  return chunk_dot8(codes.lo, codes.hi, a.dig) * (s * a.sc);
 }
 
 // Weight bytes are read once per batch and never again soon: non-temporal
@@ -101,14 +115,42 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t* p) {
   const v4u v = __builtin_nontemporal_load((gv4u_ptr)(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const v2u* gv2u_ptr;
+__device__ __forceinline__ uint2 stream_load8(const uint8_t* p) {
+  const v2u v = __builtin_nontemporal_load((gv2u_ptr)(p));
+  return make_uint2(v.x, v.y);
+}
+// A chunk of codes (32 columns): 16 bytes of int4, 8 of int2 or 32 of int8,
+// and its load.
+template <int BITS>
+struct CodeChunk;
+template <>
+struct CodeChunk<4> {
+  using T = uint4;
+  static __device__ __forceinline__ T load(const uint8_t* p) { return stream_load16(p); }
+};
+template <>
+struct CodeChunk<2> {
+  using T = uint2;
+  static __device__ __forceinline__ T load(const uint8_t* p) { return stream_load8(p); }
+};
+template <>
+struct CodeChunk<8> {
+  using T = I8Chunk;
+  static __device__ __forceinline__ T load(const uint8_t* p) {
+    return I8Chunk{stream_load16(p), stream_load16(p + 16)};
+  }
+};
 __device__ __forceinline__ float stream_scale(const _Float16* p) {
   const unsigned short b = __builtin_nontemporal_load((gu16_ptr)(p));
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
 // Rows are processed in batches whose loads are all issued before any is
-// used, so each lane keeps 2 * kBatch (gate/up) or kBatch (down) 16-byte
-// loads in flight.  Lanes whose chunk lies past the end of the row read chunk
+// used, so each lane keeps 2 * kBatch (gate/up) or kBatch (down) code loads
+// (16 bytes of int4, 8 of int2) in flight; int8 gate/up takes batches of
+// kBatch / 2 rows of 32 bytes (the same registers).  Lanes whose chunk lies past the end of the row read chunk
 // 0 of the row instead (always in bounds) and add zero (their activation
 // digits and units are zero).
 constexpr int kGUBatch = 4;
@@ -150,7 +192,7 @@ __global__ __launch_bounds__(1024) void k_route_small(RouteOut ro, const uint8_t
 
 // Rows [r0, r0 + 16) of gate and up for NT tokens: per row, the slice's part
 // of g and u, reduced over the wave, is left in s_g / s_u[j][row][slice].
-template <int C, int NT>
+template <int C, int NT, int BITS>
 __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t* ucode,
                                             const _Float16* gsc, const _Float16* usc, int d,
                                             int r0, int rl0, int slice, int lane,
@@ -158,21 +200,27 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t*
                                             float (*s_g)[kRowsPerBlock][C],
                                             float (*s_u)[kRowsPerBlock][C], int pr) {
   const int nch = d / kChunk, ngx = srow(d, pr);
-  constexpr int kB = kGUBatch, kNB = kRowsPerStream / kGUBatch;
+  const size_t row_bytes = (size_t)d * BITS / 8;
+  constexpr unsigned kCB = 4 * BITS;  // code bytes of a chunk
+  using Codes = typename CodeChunk<BITS>::T;
+  constexpr int kB = BITS == 8 ? kGUBatch / 2 : kGUBatch, kNB = kRowsPerStream / kB;
+  // batches whose 2 * kB gate and up terms fill one 8-value reduction
+  constexpr int kP = 4 / kB;
+  static_assert(2 * kB * kP == 8 && kNB % kP == 0, "whole reductions");
   for (int p = 0; p * 64 * C < nch; ++p) {
     const int c = (p * C + slice) * 64 + lane;
     const bool act = c < nch;
     const int cl = act ? c : 0;
     // software pipeline: the loads of batch i+1 are in flight while batch i
     // is computed
-    uint4 wg[2][kB], wu[2][kB];
+    Codes wg[2][kB], wu[2][kB];
     float sg[2][kB], su[2][kB];
     auto issue = [&](int buf, int rb0) {
 #pragma unroll
       for (int b = 0; b < kB; ++b) {
         const size_t r = (size_t)r0 + rb0 + b;
-        wg[buf][b] = stream_load16(gcode + r * (d / 2) + (unsigned)cl * 16u);
-        wu[buf][b] = stream_load16(ucode + r * (d / 2) + (unsigned)cl * 16u);
+        wg[buf][b] = CodeChunk<BITS>::load(gcode + r * row_bytes + (unsigned)cl * kCB);
+        wu[buf][b] = CodeChunk<BITS>::load(ucode + r * row_bytes + (unsigned)cl * kCB);
         sg[buf][b] = stream_scale(gsc + r * ngx + scol((unsigned)cl, pr));
         su[buf][b] = stream_scale(usc + r * ngx + scol((unsigned)cl, pr));
       }
@@ -180,24 +228,27 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* gcode, const uint8_t*
     issue(0, 0);
     ChunkAct xa[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) xa[j] = load_act(xd, xrow[j], nch, c, act && j < nt);
+    for (int j = 0; j < NT; ++j) xa[j] = load_act<BITS>(xd, xrow[j], nch, c, act && j < nt);
+    float v[NT][8];
 #pragma unroll
     for (int i = 0; i < kNB; ++i) {
       const int cur = i & 1;
       if (i + 1 < kNB) issue(cur ^ 1, (i + 1) * kB);
+      const int v0 = (i % kP) * 2 * kB;  // this batch's place in the reduction
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        float v[8];
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
-          v[b] = chunk_term(wg[cur][b], sg[cur][b], xa[j]);
-          v[kB + b] = chunk_term(wu[cur][b], su[cur][b], xa[j]);
+          v[j][v0 + b] = chunk_term(wg[cur][b], sg[cur][b], xa[j]);
+          v[j][v0 + kB + b] = chunk_term(wu[cur][b], su[cur][b], xa[j]);
         }
-        const float tot = reduce8(v, lane);  // lanes 8m..8m+7: value m
+        if (i % kP != kP - 1) continue;
+        const float tot = reduce8(v[j], lane);  // lanes 8m..8m+7: value m
         if ((lane & 7) == 0) {
-          const int m = lane >> 3;
-          const int row = rl0 + i * kB + (m & (kB - 1));
-          float* dst = m < kB ? &s_g[j][row][slice] : &s_u[j][row][slice];
+          // value m: batch i - kP + 1 + m / (2 kB), gate then up rows
+          const int m = lane >> 3, w = m % (2 * kB);
+          const int row = rl0 + (i - kP + 1 + m / (2 * kB)) * kB + (w & (kB - 1));
+          float* dst = w < kB ? &s_g[j][row][slice] : &s_u[j][row][slice];
           *dst = p == 0 ? tot : *dst + tot;
         }
       }
@@ -231,7 +282,7 @@ __device__ __forceinline__ void gateup_coords(int F, int nx, int ny, int G, int&
   }
 }
 
-template <int C, bool SMALL, int NT>
+template <int C, bool SMALL, int NT, int BITS>
 __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut& ro, int d, int f,
                                              const Digits& xd, const Digits& ad, int rb, int u,
                                              int grp, int G) {
@@ -274,10 +325,10 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
     list = L.single ? nullptr : L.list;
     kdiv = L.kdiv;
   }
-  const size_t fd = (size_t)f * d;
+  const size_t fdb = (size_t)f * d * BITS / 8;  // code bytes of one matrix
   const uint8_t* gcode = ex.blob;
-  const uint8_t* ucode = ex.blob + fd / 2;
-  const _Float16* gsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fd / 2);
+  const uint8_t* ucode = ex.blob + fdb;
+  const _Float16* gsc = reinterpret_cast<const _Float16*>(ex.blob + 3 * fdb);
   const _Float16* usc = gsc + (size_t)f * srow(d, L.per_row);
   const int rl0 = stream * kRowsPerStream;
   const int r0 = rb * kRowsPerBlock + rl0;
@@ -290,7 +341,7 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
     int xrow[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) xrow[j] = j < nt ? slot_at(t0 + j) / kdiv : 0;
-    gateup_rows<C, NT>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u,
+    gateup_rows<C, NT, BITS>(gcode, ucode, gsc, usc, d, r0, rl0, slice, lane, xd, xrow, nt, s_g, s_u,
                        L.per_row);
     if (t0 == grp * NT) tr.mark(4);
     __syncthreads();
@@ -321,14 +372,14 @@ __device__ __forceinline__ void gateup_block(const ExpertList& L, const RouteOut
   tr.store(g_trace_gemv, 0, tblock, 1);
 }
 
-template <int C, bool SMALL, int NT>
+template <int C, bool SMALL, int NT, int BITS = 4>
 __global__ __launch_bounds__(256 * C) void k_gateup(ExpertList L, RouteOut ro, int d, int f,
                                                     Digits xd, Digits ad) {
   int rb = blockIdx.x, u = blockIdx.y, grp = blockIdx.z;
   if (gridDim.z > 1)
     gateup_coords(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x,
                   gridDim.y, gridDim.z, rb, u, grp);
-  gateup_block<C, SMALL, NT>(L, ro, d, f, xd, ad, rb, u, grp, gridDim.z);
+  gateup_block<C, SMALL, NT, BITS>(L, ro, d, f, xd, ad, rb, u, grp, gridDim.z);
 }
 
 // The slot cache's copies and its hits' gate/up in one launch: the first
@@ -349,7 +400,7 @@ __global__ __launch_bounds__(256 * C) void k_gateup_fill(ExpertList L, int d, in
   }
   int rb, u, grp;
   gateup_coords(F - n_fill_blocks, nx, ny, G, rb, u, grp);
-  gateup_block<C, false, 1>(L, RouteOut{}, d, f, xd, ad, rb, u, grp, G);
+  gateup_block<C, false, 1, 4>(L, RouteOut{}, d, f, xd, ad, rb, u, grp, G);
 }
 
 // Rows [r0, r0 + 16) of the down projection for NT tokens into s_y[j][row].
@@ -444,7 +495,7 @@ __global__ __launch_bounds__(256) void k_down(ExpertList L, int d, int f, Digits
 constexpr int kDcRows = 8;
 constexpr int kDcWaves = 4;
 
-template <int NT>
+template <int NT, int BITS = 4>
 __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* __restrict__ plan,
                                                                  const int32_t* __restrict__ n_uniq,
                                                                  int d, int f, Digits ad,
@@ -454,7 +505,9 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
   const int r0 = blockIdx.x * kDcRows;
   const int U = *n_uniq;
   const int nch = f / kChunk, nga = srow(f, pr);
-  const size_t fd = (size_t)f * d;
+  const size_t fdb = (size_t)f * d * BITS / 8, row_bytes = (size_t)f * BITS / 8;
+  constexpr unsigned kCB = 4 * BITS;
+  using Codes = typename CodeChunk<BITS>::T;
   __shared__ float s_y[kSmallPicks][kDcRows];
   __shared__ float s_w[kSmallPicks];
   // epilogue operands first: thread i < T * 8 owns (token i / 8, row i % 8)
@@ -464,9 +517,9 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
   const size_t o = (size_t)(threadIdx.x / kDcRows) * d + r0 + threadIdx.x % kDcRows;
   const float res = (owner && cb.resid) ? cb.resid[o] : 0.0f;
 
-  auto dcode = [&](const uint8_t* blob) { return blob + fd + (size_t)r0 * (f / 2); };
+  auto dcode = [&](const uint8_t* blob) { return blob + 2 * fdb + (size_t)r0 * row_bytes; };
   auto dscale = [&](const uint8_t* blob) {
-    return reinterpret_cast<const _Float16*>(blob + 3 * fd / 2) + 2 * (size_t)f * srow(d, pr) +
+    return reinterpret_cast<const _Float16*>(blob + 3 * fdb) + 2 * (size_t)f * srow(d, pr) +
            (size_t)r0 * nga;
   };
   for (int u = wave; u < U; u += kDcWaves) {
@@ -477,11 +530,11 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
       const int c = p * 64 + lane;
       const bool act = c < nch;
       const unsigned cl = act ? (unsigned)c : 0u;
-      uint4 wd[kDcRows];
+      Codes wd[kDcRows];
       float sd[kDcRows];
 #pragma unroll
       for (int b = 0; b < kDcRows; ++b) {
-        wd[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
+        wd[b] = CodeChunk<BITS>::load(dc + (size_t)b * row_bytes + cl * kCB);
         sd[b] = stream_scale(ds + (size_t)b * nga + scol(cl, pr));
       }
       for (int t0 = 0; t0 < pl.n; t0 += NT) {
@@ -491,7 +544,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           slot[j] = j < nt ? pl.slot[t0 + j] : 0;
-          aa[j] = load_act(ad, slot[j], nch, c, act && j < nt);
+          aa[j] = load_act<BITS>(ad, slot[j], nch, c, act && j < nt);
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -523,7 +576,7 @@ __global__ __launch_bounds__(64 * kDcWaves) void k_down_combine(const DownPlan* 
 // loaded once per R rows and each lane has R weight loads in flight.
 constexpr int kD1Waves = 8;
 
-template <int R>
+template <int R, int BITS = 4>
 __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPlan* __restrict__ plan,
                                                                      const int32_t* __restrict__ n_uniq,
                                                                      int d, int f, Digits ad,
@@ -537,7 +590,9 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
   const int U = cb.k;
   (void)n_uniq;
   const int nch = f / kChunk, nga = srow(f, pr);
-  const size_t fd = (size_t)f * d;
+  const size_t fdb = (size_t)f * d * BITS / 8, row_bytes = (size_t)f * BITS / 8;
+  constexpr unsigned kCB = 4 * BITS;
+  using Codes = typename CodeChunk<BITS>::T;
   // trace points: 1 the first wave's experts streamed, 2 every wave's
   BlockTrace tr;
   tr.start();
@@ -551,22 +606,22 @@ __global__ __launch_bounds__(64 * kD1Waves) void k_down_combine_t1(const DownPla
   for (int u = wave; u < U; u += kD1Waves) {
     const DownPlan pl = plan[u];
     const int slot = pl.slot[0];
-    const uint8_t* dc = pl.blob + fd + (size_t)r0 * (f / 2);
+    const uint8_t* dc = pl.blob + 2 * fdb + (size_t)r0 * row_bytes;
     const _Float16* ds =
-        reinterpret_cast<const _Float16*>(pl.blob + 3 * fd / 2) + 2 * (size_t)f * srow(d, pr) +
+        reinterpret_cast<const _Float16*>(pl.blob + 3 * fdb) + 2 * (size_t)f * srow(d, pr) +
         (size_t)r0 * nga;
     for (int p = 0; p * 64 < nch; ++p) {
       const int c = p * 64 + lane;
       const bool act = c < nch;
       const unsigned cl = act ? (unsigned)c : 0u;
-      uint4 wv[R];
+      Codes wv[R];
       float sv[R];
 #pragma unroll
       for (int b = 0; b < R; ++b) {
-        wv[b] = stream_load16(dc + (size_t)b * (f / 2) + cl * 16u);
+        wv[b] = CodeChunk<BITS>::load(dc + (size_t)b * row_bytes + cl * kCB);
         sv[b] = stream_scale(ds + (size_t)b * nga + scol(cl, pr));
       }
-      const ChunkAct a = load_act(ad, slot, nch, c, act);
+      const ChunkAct a = load_act<BITS>(ad, slot, nch, c, act);
 #pragma unroll
       for (int g = 0; g < R / 8; ++g) {
         float v[8];
@@ -637,16 +692,31 @@ static int slices(int K) {
   return c < 1 ? 1 : (c > 3 ? 3 : c);
 }
 
+template <bool SMALL, int NT, int BITS>
+static hipError_t gateup_cb(const ExpertList& L, const RouteOut& ro, int maxU, int d, int f,
+                            Digits xd, Digits ad, int groups, hipStream_t s) {
+  const dim3 grid(f / kRowsPerBlock, maxU, groups);
+  const int c = slices(d);
+  if (c == 1)
+    return launch(5, k_gateup<1, SMALL, NT, BITS>, grid, dim3(256), s, L, ro, d, f, xd, ad);
+  if (c == 2)
+    return launch(5, k_gateup<2, SMALL, NT, BITS>, grid, dim3(512), s, L, ro, d, f, xd, ad);
+  // two tokens at a time fit a block's registers only up to 2 slices
+  if constexpr (NT == 1)
+    return launch(5, k_gateup<3, SMALL, NT, BITS>, grid, dim3(768), s, L, ro, d, f, xd, ad);
+  return hipErrorInvalidValue;
+}
+
+// int4 codes, or int2 and int8 codes one token at a time (the layer's
+// single-token path)
 template <bool SMALL, int NT>
 static hipError_t gateup_c(const ExpertList& L, const RouteOut& ro, int maxU, int d, int f,
                            Digits xd, Digits ad, int groups, hipStream_t s) {
-  const dim3 grid(f / kRowsPerBlock, maxU, groups);
-  const int c = slices(d);
-  if (c == 1) return launch(5, k_gateup<1, SMALL, NT>, grid, dim3(256), s, L, ro, d, f, xd, ad);
-  if (c == 2) return launch(5, k_gateup<2, SMALL, NT>, grid, dim3(512), s, L, ro, d, f, xd, ad);
-  // two tokens at a time fit a block's registers only up to 2 slices
-  if constexpr (NT == 1)
-    return launch(5, k_gateup<3, SMALL, NT>, grid, dim3(768), s, L, ro, d, f, xd, ad);
+  if (L.bits == 4) return gateup_cb<SMALL, NT, 4>(L, ro, maxU, d, f, xd, ad, groups, s);
+  if constexpr (NT == 1) {
+    if (L.bits == 2) return gateup_cb<SMALL, 1, 2>(L, ro, maxU, d, f, xd, ad, groups, s);
+    if (L.bits == 8) return gateup_cb<SMALL, 1, 8>(L, ro, maxU, d, f, xd, ad, groups, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -687,6 +757,7 @@ hipError_t launch_gateup_fill(const ExpertList& L, int max_experts, int d, int f
 
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
                        int tokens_per_expert_max, hipStream_t s) {
+  if (L.bits != 4) return hipErrorInvalidValue;
   const dim3 grid(d / kRowsPerBlock, max_experts);
   if (tokens_per_expert_max <= 1) return launch(6, k_down<1>, grid, dim3(256), s, L, d, f, ad, y);
   return launch(6, k_down<2>, grid, dim3(256), s, L, d, f, ad, y);
@@ -714,17 +785,33 @@ hipError_t launch_route_small(const RouteOut& ro, const uint8_t* const* table, h
   return launch(3, k_route_small, dim3(1), dim3(1024), s, ro, table, px);
 }
 
-hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, int per_row, hipStream_t s) {
+template <int BITS>
+static hipError_t down_combine_b(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
+                                 Digits ad, const CombineArgs& cb, int per_row, hipStream_t s) {
   if (cb.T == 1) {
-    if (d % 24 == 0)
-      return launch(6, k_down_combine_t1<24>, dim3(d / 24), dim3(64 * kD1Waves), s, plan, n_uniq, d,
-                    f, ad, cb, per_row);
-    return launch(6, k_down_combine_t1<16>, dim3(d / 16), dim3(64 * kD1Waves), s, plan, n_uniq, d,
-                  f, ad, cb, per_row);
+    // int8: 8 rows of 32 bytes a lane hold as many registers as 16 of int4
+    if constexpr (BITS == 8) {
+      return launch(6, k_down_combine_t1<8, 8>, dim3(d / 8), dim3(64 * kD1Waves), s, plan, n_uniq,
+                    d, f, ad, cb, per_row);
+    } else {
+      if (d % 24 == 0)
+        return launch(6, k_down_combine_t1<24, BITS>, dim3(d / 24), dim3(64 * kD1Waves), s, plan,
+                      n_uniq, d, f, ad, cb, per_row);
+      return launch(6, k_down_combine_t1<16, BITS>, dim3(d / 16), dim3(64 * kD1Waves), s, plan,
+                    n_uniq, d, f, ad, cb, per_row);
+    }
   }
-  return launch(6, k_down_combine<2>, dim3(d / kDcRows), dim3(64 * kDcWaves), s, plan, n_uniq, d,
-                f, ad, cb, per_row);
+  return launch(6, k_down_combine<2, BITS>, dim3(d / kDcRows), dim3(64 * kDcWaves), s, plan,
+                n_uniq, d, f, ad, cb, per_row);
+}
+
+hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
+                               Digits ad, const CombineArgs& cb, int per_row, int bits,
+                               hipStream_t s) {
+  if (bits == 4) return down_combine_b<4>(plan, n_uniq, d, f, ad, cb, per_row, s);
+  if (bits == 2) return down_combine_b<2>(plan, n_uniq, d, f, ad, cb, per_row, s);
+  if (bits == 8) return down_combine_b<8>(plan, n_uniq, d, f, ad, cb, per_row, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,

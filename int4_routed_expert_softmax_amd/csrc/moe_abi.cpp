@@ -332,12 +332,11 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
   const int maxU = E < T * k ? E : T * k;
 
   EL.i8act = i8act;
-  // int8 and int2 layers run every batch on the thin grouped GEMM (16-token
-  // tiles), whose per-token arithmetic does not depend on the batch, so the
-  // batch-invariant flag needs no separate path for them.  Integer
-  // activations on int4 layers take this path as the others do: the digit
-  // split then holds one int8 per column (one scale per 64 columns).
-  if (EL.bits == 4 && (invariant || gemv_small_path(T, k, d, f))) {
+  // One token, and batch-invariant batches, on the single-token kernel
+  // family, for every code width.  Integer activations take this path as the
+  // others do: the digit split then holds one int8 per column (one scale per
+  // 64 columns).
+  if (invariant || gemv_small_path(T, k, d, f)) {
     // 1: [RMSNorm], logits, digit split; 2: top-k + union (one token: in
     // every gate/up block's prologue; 2+: one k_route_small block) and
     // gate/up; 3: down + combine.  Every step keeps one order of
@@ -373,7 +372,7 @@ MOE_API int moe_layer_forward(const moe_dims* dm, const void* x, int x_dtype, in
       MOE_TRY(launch_gateup(EL, nullptr, maxU, d, f, xd, ad, 1, T, s));
     }
     CombineArgs cb{w, resid, out, T, k};
-    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));
+    MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, EL.bits, s));
     return MOE_OK;
   }
 
@@ -558,7 +557,7 @@ MOE_API int moe_layer_forward_cached(const moe_dims* dm, const void* x, int x_dt
   EL.want_hit = 0;
   MOE_TRY(launch_gateup(EL, nullptr, cap, d, f, xd, ad, 1, T, s));
   CombineArgs cb{w, (flags & MOE_RESIDUAL) ? static_cast<const float*>(x) : nullptr, out, T, k};
-  MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, s));
+  MOE_TRY(launch_down_combine(plan, nuniq, d, f, ad, cb, EL.per_row, EL.bits, s));
   return MOE_OK;
 }
 

@@ -238,7 +238,8 @@ hipError_t launch_gateup(const ExpertList& L, const RouteOut* small_route, int m
 hipError_t launch_down(const ExpertList& L, int max_experts, int d, int f, Digits ad, float* y,
                        int tokens_per_expert_max, hipStream_t s);
 
-// Down projection fused with the combine, for small batches (T * k <= 64).
+// Down projection fused with the combine, for small batches (T * k <= 64),
+// of int4, int2 or int8 codes (bits).
 struct CombineArgs {
   const float* w;      // [T][k] router weights
   const float* resid;  // [T][d] or nullptr
@@ -246,7 +247,8 @@ struct CombineArgs {
   int T, k;
 };
 hipError_t launch_down_combine(const DownPlan* plan, const int32_t* n_uniq, int d, int f,
-                               Digits ad, const CombineArgs& cb, int per_row, hipStream_t s);
+                               Digits ad, const CombineArgs& cb, int per_row, int bits,
+                               hipStream_t s);
 hipError_t launch_combine(const float* y, const float* w, const float* resid, float* out, int T,
                           int d, int k, hipStream_t s);
 

@@ -108,7 +108,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="decode1",
                     choices=["decode1", "verify8", "prefill512", "decode1_int8", "verify8_int8",
-                             "verify8_int2"])
+                             "decode1_int2", "verify8_int2"])
     ap.add_argument("--layers", type=int, default=None, help="rotating resident layers")
     ap.add_argument("--calls", type=int, default=3, help="traced calls (after 10 untimed ones)")
     a = ap.parse_args()

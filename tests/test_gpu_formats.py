@@ -2,10 +2,12 @@
 packed int2 kernels next to packed int4, «纯C语言») on every path the layer
 call takes for them, against the CPU oracle with the same code width: routing,
 union and slot lists bit-exact (as the call left them in its workspace),
-outputs within 2e-3 * max|ref|.  These layers run on the thin grouped GEMM in
-16-token tiles at every batch size, so a token's result must not depend on
-the rest of its batch: with MOE_BATCH_INVARIANT (and without it) every token
-of a batch is compared bit for bit with its one-token call."""
+outputs within 2e-3 * max|ref|.  Both widths run one token (and, with
+MOE_BATCH_INVARIANT, batches of up to 8) on the single-token kernel family,
+as int4 layers do, with 8 (int2) or 32 (int8) bytes of codes per 32-column
+chunk, and other batches on the thin grouped GEMM in 16-token tiles.  With
+MOE_BATCH_INVARIANT every token of a batch is compared bit for bit with its
+one-token call."""
 import numpy as np
 import pytest
 import torch
@@ -69,7 +71,7 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 
 
 @pytest.mark.parametrize("bits", [8, 2])
-@pytest.mark.parametrize("flags", [0, moe.MOE_BATCH_INVARIANT, NORM_RES | moe.MOE_BATCH_INVARIANT])
+@pytest.mark.parametrize("flags", [moe.MOE_BATCH_INVARIANT, NORM_RES | moe.MOE_BATCH_INVARIANT])
 def test_formats_batch_matches_single_tokens(bits, flags):
     w = small(f"i{bits}_inv", 512, 512, 32, 8, 8, bits=bits, x_kind="shared_base")
     L = DeviceLayer(w)
@@ -85,6 +87,25 @@ def test_formats_batch_matches_single_tokens(bits, flags):
     for t in range(w.T):
         assert np.array_equal(got[t], solo[t]), f"token {t} differs from its one-token call"
     say(f"int{bits} flags={flags}: {w.T} tokens bit-identical to their one-token calls")
+
+
+@pytest.mark.parametrize("bits", [8, 2])
+@pytest.mark.parametrize("shape,flags", [
+    (dict(name="t1_bf16", d=512, f=1024, E=32, k=8, T=1, x_kind="bf16"), 0),
+    (dict(name="t1_perrow", d=512, f=512, E=16, k=4, T=1, group=0), 0),
+    (dict(name="t1_c1", d=1536, f=512, E=16, k=2, T=1), 0),    # one column slice; 24-row down blocks (int2)
+    (dict(name="t1_wide", d=8192, f=4096, E=8, k=4, T=1), 0),  # two passes over gate/up and down rows
+    (dict(name="t1_res", d=512, f=512, E=16, k=4, T=1), NORM_RES),
+    (dict(name="inv_T5", d=512, f=1024, E=32, k=8, T=5), moe.MOE_BATCH_INVARIANT),
+    (dict(name="inv_T8_perrow", d=1024, f=512, E=32, k=4, T=8, group=0),
+     NORM_RES | moe.MOE_BATCH_INVARIANT),
+], ids=lambda v: v["name"] if isinstance(v, dict) else f"flags{v}")
+def test_other_widths_on_the_single_token_kernels(bits, shape, flags):
+    """int8 and int2 codes on the digit GEMV: one token, and batch-invariant
+    batches."""
+    sh = dict(shape)
+    name = sh.pop("name")
+    full_parity(small(f"i{bits}_{name}", **sh, bits=bits), flags=flags)
 
 
 @pytest.mark.parametrize("name", ["decode1_int8", "verify8_int8", "decode1_int2", "verify8_int2"])

@@ -25,6 +25,9 @@ pytestmark = pytest.mark.gpu
     (small("g_perrow", 512, 512, 32, 8, 5, group=0), 0),
     (small("g_i8act_t3", 512, 512, 16, 4, 3), moe.MOE_INT8_ACT),   # integer activations
     (small("g_i8act_t40", 1024, 512, 64, 8, 40, x_kind="bf16"), moe.MOE_INT8_ACT),
+    (small("g_int2_t1", 512, 512, 16, 4, 1, bits=2), 0),           # int2 codes on the GEMV
+    (small("g_int8_t1", 512, 512, 16, 4, 1, bits=8), 0),           # int8 codes on the GEMV
+    (small("g_int2_inv", 512, 512, 16, 4, 5, bits=2), moe.MOE_BATCH_INVARIANT),
 ], ids=lambda v: v.name if hasattr(v, "name") else str(v))
 def test_graph_replays_match_eager(w, flags):
     L = DeviceLayer(w)

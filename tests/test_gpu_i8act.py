@@ -5,11 +5,10 @@ Every expert input row (x', and a = silu(g) * u) is int8 per 64-column group
 with an fp32 scale max|v| / 127, each group's dot product is exact on the
 int8 matrix cores.  Against the oracle's integer-activation layer
 (REF_I8ACT): routing, union and slot lists bit-exact (as the call left them
-in its workspace), outputs within 2e-3 * max|ref|, on both int4 kernel
-families (one token and batch-invariant batches: the single-token GEMV with
-int8 digits; other batches: the int8 matrix cores).  Batch-invariant batches
-(and every batch of int8 or int2 codes) are bit-identical to their one-token
-calls, and the distance from the unquantised layer (the int8 rounding of the
+in its workspace), outputs within 2e-3 * max|ref|, on both kernel families
+(one token and batch-invariant batches: the single-token GEMV with int8
+digits; other batches: the int8 matrix cores), for int4, int8 and int2
+codes.  Batch-invariant batches are bit-identical to their one-token calls, and the distance from the unquantised layer (the int8 rounding of the
 activations) stays within its derived bound."""
 import numpy as np
 import pytest
@@ -84,8 +83,8 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
 @pytest.mark.parametrize("flags,bits", [
     (I8 | moe.MOE_BATCH_INVARIANT, 4),
     (I8 | NORM_RES | moe.MOE_BATCH_INVARIANT, 4),
-    (I8, 8),   # int8 codes: every batch on the thin GEMM, invariant without the flag
-    (I8, 2),
+    (I8 | moe.MOE_BATCH_INVARIANT, 8),
+    (I8 | moe.MOE_BATCH_INVARIANT, 2),
 ])
 def test_i8act_batch_matches_single_tokens(flags, bits):
     w = small(f"i8act_inv_i{bits}", 512, 512, 32, 8, 8, x_kind="shared_base", bits=bits)
