@@ -21,10 +21,10 @@ HEADLINE = [
     ("chain48 step 1 worst of 48 layers", "same"),
     ("chain48 step 63 worst of 48 layers", "same"),
     ("decode1 cached T=1 S=12 flags=0", "slot cache, host-mapped home"),
-    ("decode1_int8 flags=0", "int8 codes, thin GEMM (T=1)"),
+    ("decode1_int8 flags=0", "int8 codes, digit GEMV (T=1)"),
     ("verify8_int8 flags=0", "int8 codes, thin GEMM"),
     ("prefill512_int8 flags=0", "int8 codes, thin GEMM, all 512 tokens"),
-    ("decode1_int2 flags=0", "int2 codes, thin GEMM (T=1)"),
+    ("decode1_int2 flags=0", "int2 codes, digit GEMV (T=1)"),
     ("verify8_int2 flags=0", "int2 codes, thin GEMM"),
     ("prefill512_int2 flags=0", "int2 codes, thin GEMM, all 512 tokens"),
     ("decode1 flags=8", "integer activations, GEMV with int8 digits (T=1)"),
