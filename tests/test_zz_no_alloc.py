@@ -63,6 +63,19 @@ def test_large_batch_then_small_batch():
     same(L, x[10:13], bf, moe.MOE_BATCH_INVARIANT, "T=3 batch-invariant")
 
 
+@pytest.mark.parametrize("bits", [8, 2])
+def test_other_code_widths_batch_then_single_token(bits):
+    # int8 / int2 codes: a batch on the thin grouped GEMM, then one token and
+    # a batch-invariant batch on the single-token kernels, on the same array
+    w = configs.Workload(f"na_i{bits}", d=512, f=1024, n_experts=32, top_k=8, T=12, seed=52,
+                         bits=bits)
+    L = DeviceLayer(w)
+    x, bf = configs.tokens(w)
+    same(L, x, bf, 0, f"int{bits} T=12")
+    same(L, x[4:5], bf, 0, f"int{bits} decode")
+    same(L, x[:5], bf, moe.MOE_BATCH_INVARIANT, f"int{bits} T=5 batch-invariant")
+
+
 def test_refuses_calls_past_the_array():
     dims = moe.Dims(6144, 2048, 256, 8)
     assert moe.workspace_bytes(dims, 64) <= moe.NOALLOC_SCRATCH_BYTES
