@@ -259,22 +259,22 @@ __device__ __forceinline__ int chunk_dot(const uint4 codes, const ChunkDigits& c
 
 // The same for int2 codes: a chunk's 32 columns are 8 bytes, column 4b + j
 // of each 32-bit word in bits 2j..2j+1 of its byte b.  Flipping the top bit
-// of every field makes it n'_c = q_c + 2 in [0, 3].  v_perm pairs the low and
-// high nibbles of two neighbouring bytes into one word whose byte i holds
-// columns 2i and 2i + 1 of an 8-column block (bits 0-1 and 2-3), so one mask
-// gives the block's even columns and a shift and mask its odd ones, in the
-// order the digit planes hold them.  The caller subtracts 2 * sum(X).
+// of every field makes it n'_c = q_c + 2 in [0, 3].  v_perm takes two
+// neighbouring bytes from the word and from the word shifted right by 4, so
+// that byte i of the result holds columns 2i and 2i + 1 of an 8-column block
+// in bits 0-1 and 2-3 (its bits 4-7, from the next byte, are masked off): one
+// mask gives the block's even columns and a shift and mask its odd ones, in
+// the order the digit planes hold them.  The caller subtracts 2 * sum(X).
 __device__ __forceinline__ int chunk_dot2(const uint2 codes, const ChunkDigits& cd) {
   const uint32_t cw[2] = {codes.x, codes.y};
   int ev[4], od[4];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const uint32_t v = cw[m] ^ 0xAAAAAAAAu;
-    const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+    const uint32_t v = cw[m] ^ 0xAAAAAAAAu, v4 = v >> 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // bytes [lo(b), hi(b), lo(b + 1), hi(b + 1)] for b = 2h
-      const uint32_t s = __builtin_amdgcn_perm(hi, lo, h ? 0x07030602u : 0x05010400u);
+      // bytes [v(b), v4(b), v(b + 1), v4(b + 1)] for b = 2h
+      const uint32_t s = __builtin_amdgcn_perm(v4, v, h ? 0x07030602u : 0x05010400u);
       ev[2 * m + h] = (int)(s & 0x03030303u);
       od[2 * m + h] = (int)((s >> 2) & 0x03030303u);
     }
