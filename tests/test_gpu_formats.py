@@ -96,6 +96,7 @@ def test_formats_batch_matches_single_tokens(bits, flags):
     (dict(name="t1_c1", d=1536, f=512, E=16, k=2, T=1), 0),    # one column slice; 24-row down blocks (int2)
     (dict(name="t1_wide", d=8192, f=4096, E=8, k=4, T=1), 0),  # two passes over gate/up and down rows
     (dict(name="t1_res", d=512, f=512, E=16, k=4, T=1), NORM_RES),
+    (dict(name="t1_k16", d=512, f=512, E=64, k=16, T=1), 0),   # two experts per down wave
     (dict(name="inv_T5", d=512, f=1024, E=32, k=8, T=5), moe.MOE_BATCH_INVARIANT),
     (dict(name="inv_T8_perrow", d=1024, f=512, E=32, k=4, T=8, group=0),
      NORM_RES | moe.MOE_BATCH_INVARIANT),
